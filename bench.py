@@ -1,0 +1,307 @@
+"""Benchmark of the tiled-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs] [--stack] [--no-cpu-baseline]
+
+Headline workload (one step): one Llama-3.1-8B-shaped attention layer at seq 8192
+(batch 1, 32 query heads, 8 KV heads, head_dim 128, bf16, Q/K/V iid N(0,1)):
+the layer router reads the layer's queries (first/last 100 tokens -> MLP ->
+argmax), its mode is copied to the host, and the per-layer dispatcher runs the
+selected prefill kernel -- dense causal, which the router's head bias selects
+for this layer because the workload is defined as dense causal.
+`value` = useful prefill TFLOP/s (4*B*Hq*d per allowed query-key pair) of the
+whole step.
+
+Secondary legs (same JSON line, "legs"): block-sparse prefill at seq 65536,
+GQA decode over a 262144-token bf16 cache (dense and sparse; HBM GB/s and
+tok/s), and with --stack the 36-layer routed prefill stack at seq 131072.
+
+The roofline object is for the dominant kernel (dense prefill), timed with HIP
+events on the stream the kernel runs on.  cpu_baseline times the fp64 CPU
+oracle on a bounded sample of the same workload (rank 0, N=1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "prefill useful TFLOP/s + decode HBM GB/s (tok/s), % of roofline, 1 MI355X"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def causal_pairs(S: int) -> int:
+    return S * (S + 1) // 2
+
+
+def csr_pairs(row_ptr, col_idx, S: int, block: int = 64) -> int:
+    """Allowed (query, key) pairs of a causal block mask: full off-diagonal blocks, triangular diagonal."""
+    total = 0
+    for I in range(len(row_ptr) - 1):
+        qn = min(S, (I + 1) * block) - I * block
+        for J in col_idx[row_ptr[I]:row_ptr[I + 1]]:
+            kn = min(S, (int(J) + 1) * block) - int(J) * block
+            total += qn * (qn + 1) // 2 if J == I else qn * kn
+    return total
+
+
+class KernelTimer:
+    """HIP events around each launch on the current stream; mean duration in ms."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def record(self, fn):
+        import torch
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", dest="legs", action="store_true", default=True)
+    ap.add_argument("--no-legs", dest="legs", action="store_false")
+    ap.add_argument("--stack", action="store_true", help="also time the 36-layer routed stack at seq 131072")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false", default=True)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the kernels run on one "
+              "GPU's share; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_attention_tiled_amd as fa
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------------------------------------------------------- headline: routed dense layer, S=8192
+    B, S, Hq, Hkv, d = 1, 8192, 32, 8, 128
+    scale = 1.0 / math.sqrt(d)
+    log("generating headline inputs")
+    q = synth.torch_normal((B, S, Hq, d), 1002, torch.bfloat16)
+    k = synth.torch_normal((B, S, Hkv, d), 1003, torch.bfloat16)
+    v = synth.torch_normal((B, S, Hkv, d), 1004, torch.bfloat16)
+    o = torch.empty((B, S, Hq, d), dtype=torch.bfloat16, device=dev)
+    w = synth.router_weights(1, Hq * d, 256, seed=1005)
+    w_enc, b_enc, w_head, b_head = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in w)
+    b_head[0, 0] += 8.0   # the workload is dense causal: the head bias makes the router select index 0
+    modes_dev = torch.empty(1, dtype=torch.int32, device=dev)
+    modes_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
+    timer = KernelTimer()
+    useful = 4.0 * B * Hq * d * causal_pairs(S)
+
+    def step(record=False):
+        fa.flux_route_layers([q[0]], w_enc, b_enc, w_head, b_head, modes_dev, None, pool_tokens=100)
+        modes_host.copy_(modes_dev, non_blocking=True)
+        torch.cuda.current_stream().synchronize()          # the one D2H sync per request
+        m = modes_host.numpy().copy()
+        call = lambda: fa.flux_attn_prefill_layers(m, [q], [k], [v], [o], None, block=64, sink_tokens=128,
+                                                   window_tokens=2048)
+        if record:
+            timer.record(call)
+        else:
+            call()
+
+    log("timing headline")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    assert int(modes_host[0]) == fa.FLUX_MODE_DENSE
+    kern_ms = timer.mean_ms()
+    value = useful / (ms_per_step * 1e-3) / 1e12
+    achieved = useful / (kern_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic iid N(0,1) Q/K/V rounded to bf16; seeded random router weights",
+        "config": {"workload": "llama3.1-8b-layer routed dense-causal prefill", "batch": B, "seq_len": S,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "block": 64, "out_dtype": "bf16",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_bf16_kernel<128, dense causal, bf16 out>",
+                     "kernel_ms": round(kern_ms, 4), "useful_flops_per_launch": useful},
+    }
+    del q, k, v, o
+    torch.cuda.empty_cache()
+
+    legs = {}
+    if args.legs:
+        legs.update(run_legs(fa, synth, torch, dev))
+    if args.stack:
+        legs["stack_s131072"] = run_stack(fa, synth, torch, dev)
+    if legs:
+        result["legs"] = legs
+        if "decode_dense_L262144" in legs:
+            dd = legs["decode_dense_L262144"]
+            result["decode"] = {"GB/s": dd["GB/s"], "tok/s": dd["tok/s"], "frac_hbm": dd["frac"]}
+
+    if args.cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(result), flush=True)
+
+
+def run_legs(fa, synth, torch, dev):
+    legs = {}
+    # ---- block-sparse prefill, seq 65536
+    B, S, Hq, Hkv, d = 1, 65536, 32, 8, 128
+    log("leg: sparse prefill S=65536")
+    q = synth.torch_normal((B, S, Hq, d), 1102, torch.bfloat16)
+    k = synth.torch_normal((B, S, Hkv, d), 1103, torch.bfloat16)
+    v = synth.torch_normal((B, S, Hkv, d), 1104, torch.bfloat16)
+    o = torch.empty((B, S, Hq, d), dtype=torch.bfloat16, device=dev)
+    rp, ci = fa.flux_build_block_mask(S, S, 64, 128, 2048, 1, fa.FLUX_MODE_SPARSE)
+    rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+    useful = 4.0 * B * Hq * d * csr_pairs(rp, ci, S)
+    call = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_SPARSE, sink_tokens=128,
+                                        window_tokens=2048, blk_row_ptr=rpd, blk_col_idx=cid)
+    ms = time_steps(call, 20, 3)
+    legs["sparse_prefill_s65536"] = {"ms": round(ms, 4), "useful_flops": useful, "nnz_blocks": int(len(ci)),
+                                     "TFLOP/s": round(useful / ms / 1e9, 2),
+                                     "frac": round(useful / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    # dense at the same length, for the sparse-vs-full ratio of the method
+    log("leg: dense prefill S=65536")
+    calld = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_DENSE)
+    msd = time_steps(calld, 3, 1)
+    usefuld = 4.0 * B * Hq * d * causal_pairs(S)
+    legs["dense_prefill_s65536"] = {"ms": round(msd, 4), "TFLOP/s": round(usefuld / msd / 1e9, 2),
+                                    "frac": round(usefuld / msd / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                    "sparse_speedup": round(msd / ms, 3)}
+    del q, k, v, o
+    torch.cuda.empty_cache()
+
+    # ---- decode, B=8, L=262144
+    B, L, Hq, Hkv, d = 8, 262144, 32, 8, 128
+    log("leg: decode L=262144")
+    qd = synth.torch_normal((B, Hq, d), 1202, torch.bfloat16)
+    kc = synth.torch_normal((B, L, Hkv, d), 1203, torch.bfloat16)
+    vc = synth.torch_normal((B, L, Hkv, d), 1204, torch.bfloat16)
+    od = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    for mode, name in ((fa.FLUX_MODE_DENSE, "decode_dense_L262144"), (fa.FLUX_MODE_SPARSE, "decode_sparse_L262144")):
+        wsb = fa.flux_decode_workspace_size(B, Hq, Hkv, L, d, mode, 64, 128, 2048, 0)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        n_keys = L if mode == fa.FLUX_MODE_DENSE else 128 + 2048
+        nbytes = B * Hkv * n_keys * d * 2 * 2 + 2 * B * Hq * d * 2
+        call = lambda: fa.flux_attn_decode(qd, kc, vc, od, None, mode=mode, sink_tokens=128, window_tokens=2048,
+                                           workspace=ws)
+        ms = time_steps(call, 20 if mode == 0 else 100, 3)
+        gbs = nbytes / ms / 1e6
+        legs[name] = {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                      "tok/s": round(B / (ms * 1e-3), 1)}
+    legs["decode_sparse_L262144"]["speedup_vs_dense"] = round(
+        legs["decode_dense_L262144"]["ms"] / legs["decode_sparse_L262144"]["ms"], 2)
+    del qd, kc, vc, od
+    torch.cuda.empty_cache()
+    return legs
+
+
+def run_stack(fa, synth, torch, dev):
+    """36 layers, seq 131072, 12 dense + 24 sparse by a seeded draw encoded in the router's head bias."""
+    L, S, Hq, Hkv, d = 36, 131072, 32, 8, 128
+    log("leg: 36-layer stack, generating inputs")
+    plan = synth.layer_mode_draw(L, 12, seed=1004)
+    qs = [synth.torch_normal((1, S, Hq, d), 2000 + 3 * l, torch.bfloat16) for l in range(L)]
+    ks = [synth.torch_normal((1, S, Hkv, d), 2001 + 3 * l, torch.bfloat16) for l in range(L)]
+    vs = [synth.torch_normal((1, S, Hkv, d), 2002 + 3 * l, torch.bfloat16) for l in range(L)]
+    o = torch.empty((1, S, Hq, d), dtype=torch.bfloat16, device=dev)
+    w = synth.router_weights(L, Hq * d, 256, seed=1006)
+    w_enc, b_enc, w_head, b_head = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in w)
+    for l in range(L):
+        b_head[l, int(plan[l])] += 8.0
+    rp, ci = fa.flux_build_block_mask(S, S, 64, 128, 2048, 1, fa.FLUX_MODE_SPARSE)
+    rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+    modes_dev = torch.empty(L, dtype=torch.int32, device=dev)
+    useful = 4.0 * Hq * d * (12 * causal_pairs(S) + 24 * csr_pairs(rp, ci, S))
+
+    def step():
+        fa.flux_route_layers([x[0] for x in qs], w_enc, b_enc, w_head, b_head, modes_dev, None, pool_tokens=100)
+        m = modes_dev.cpu().numpy()
+        fa.flux_attn_prefill_layers(m, qs, ks, vs, [o] * L, None, block=64, sink_tokens=128, window_tokens=2048,
+                                    blk_row_ptr=rpd, blk_col_idx=cid)
+        return m
+
+    m = step()
+    torch.cuda.synchronize()
+    assert np.array_equal(m, plan), (m, plan)
+    ms = time_steps(step, 2, 0)
+    res = {"ms": round(ms, 2), "useful_flops": useful, "TFLOP/s": round(useful / ms / 1e9, 2),
+           "frac": round(useful / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "dense_layers": int((plan == 0).sum())}
+    del qs, ks, vs, o
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(synth):
+    """fp64 CPU oracle on a bounded sample of the headline layer: every 32nd query row, all 32 heads."""
+    import oracle
+    B, S, Hq, Hkv, d = 1, 8192, 32, 8, 128
+    log("cpu baseline: generating inputs")
+    q, k, v = synth.qkv_bf16(B, S, Hq, Hkv, d, seed=1002)
+    stride = 32
+    rows = np.array([(0, h, i) for i in range(stride - 1, S, stride) for h in range(Hq)], np.int64)
+    pairs = int(sum(i + 1 for _, _, i in rows))
+    cores = len(os.sched_getaffinity(0))
+    log(f"cpu baseline: {len(rows)} rows on {cores} threads")
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, 1.0 / math.sqrt(d), causal=True, rows=rows, n_threads=cores)
+    sec = time.perf_counter() - t0
+    flops = 4.0 * d * pairs
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"dense causal S=8192 layer, every {stride}th query row x 32 heads ({len(rows)} rows, "
+                      f"{flops:.3e} useful flops) in {sec:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

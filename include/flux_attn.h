@@ -1,0 +1,214 @@
+/*
+ * flux_attn.h -- C ABI of the MI355X (gfx950) tiled attention library.
+ *
+ * Exact softmax attention computed tile by tile with an online softmax
+ * (running row maximum and running row sum; earlier partial results are
+ * rescaled by exp(m_old - m_new) when the maximum grows), in the two per-layer
+ * modes of Flux Attention:
+ *   - FLUX_MODE_DENSE  ("full attention", router index 0): every causal key;
+ *   - FLUX_MODE_SPARSE ("sparse attention", router index 1): 64x64 blocks, an
+ *     always-kept sink of leading blocks and a causal local window of blocks;
+ *     blocks outside that set are skipped and their K/V are never read.
+ *
+ * Sources (pages on the method):
+ *   [FA]  "Flux Attention: context-aware hybrid attention for efficient LLM
+ *         inference" (aitrends.kr): router paragraphs (prefix/suffix pooling of
+ *         xQ [s x h x d'], MLP context encoder, router head with logits
+ *         (pi_FA, pi_SA), argmax at inference), layer-granularity paragraph,
+ *         architecture paragraph (KV loading bypassed in sparse mode) and
+ *         implementation paragraph (64-granular blocks, 128-token sink).
+ *   [NL]  openads.co.kr FlashAttention newsletter: sections "Softmax is not a
+ *         simple function" (attention definition), "The hidden cost of
+ *         numerical stability" (max subtraction), "FlashAttention: reduce memory
+ *         movement" (tiling, one HBM round trip) and "Online Softmax".
+ *   [SA]  "After self-attention: what comes after transformers"
+ *         (datadaily.news): "why self-attention is expensive" (plain attention
+ *         with scale 1/sqrt(d_k); tensors (batch, seq_len, d_model)) and the
+ *         hybrid-architectures section (sliding window, cost O(N*W)).
+ *
+ * Conventions for every entry point:
+ *   - Returns an int status (FLUX_OK = 0); never throws; never allocates
+ *     device memory; never synchronizes the stream unless stated.
+ *   - All arguments are validated on the host before any launch; on failure
+ *     nothing is written to any output and flux_last_error_detail() names the
+ *     offending argument.
+ *   - Device buffers are owned by the caller.  Results are valid once the
+ *     caller has synchronized `hip_stream` (a hipStream_t; NULL = the default
+ *     stream of the current device).
+ *   - Tensors are dense row-major.  Sizes are 64-bit where they scale with
+ *     sequence length.
+ *   - Device pointers to bf16/f32 tensors must be 16-byte aligned.
+ */
+#ifndef FLUX_ATTN_H
+#define FLUX_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define FLUX_OK 0
+#define FLUX_ERR_INVALID_ARG 1 /* a pointer, size or flag is outside its documented range  */
+#define FLUX_ERR_UNSUPPORTED 2 /* valid request, but not a shape/dtype this build handles  */
+#define FLUX_ERR_CAPACITY 3    /* an output array is too small (required size reported)   */
+#define FLUX_ERR_WORKSPACE 4   /* workspace missing or smaller than the required size      */
+#define FLUX_ERR_HIP 5         /* a HIP runtime call or kernel launch failed                */
+
+/* ---- element types ----------------------------------------------------- */
+#define FLUX_DTYPE_BF16 0
+#define FLUX_DTYPE_F32 1
+
+/* ---- per-layer attention modes (router argmax index, [FA]) -------------- */
+#define FLUX_MODE_DENSE 0  /* pi_FA: full (dense) attention   */
+#define FLUX_MODE_SPARSE 1 /* pi_SA: block-sparse attention   */
+
+/* Static text for a status code (never NULL). */
+const char* flux_status_string(int status);
+
+/* Thread-local text describing the most recent failure on this thread: which
+ * argument was rejected, or the HIP error string.  Empty after success. */
+const char* flux_last_error_detail(void);
+
+/* Library ABI version (major * 100 + minor). */
+int flux_version(void);
+
+/*
+ * flux_build_block_mask -- list the active key blocks of every query block.
+ *
+ * Defines the block-sparse pattern of [FA] implementation paragraph: key and
+ * query positions are cut into blocks of `block` tokens (64 in the method);
+ * with mode == FLUX_MODE_SPARSE, key block J is active for query block I iff
+ *     J <= I  and  ( J < sink_tokens/block  or  I - J < window_tokens/block ),
+ * i.e. the always-kept sink blocks plus a causal local window of blocks that
+ * ends at (and includes) the query's own block ([SA] sliding window).  With
+ * mode == FLUX_MODE_DENSE every causal block (J <= I), or every block when
+ * causal == 0, is active and sink/window are ignored.
+ *
+ * Host-only and bit-exact; touches no device.  Output is CSR:
+ *   row_ptr [nbq + 1] int32 (nbq = ceil(seq_q / block)), row_ptr[0] = 0;
+ *   col_idx [nnz] int32, ascending within each row.
+ * col_idx may be NULL (with col_capacity 0) to ask only for *nnz_out; row_ptr
+ * may then be NULL too.  If col_capacity < nnz the call returns
+ * FLUX_ERR_CAPACITY, writes *nnz_out and leaves row_ptr/col_idx unspecified.
+ * Requires: seq_q, seq_k >= 1; block >= 1; sparse mode: causal == 1,
+ * sink_tokens >= 0 and window_tokens >= block, both multiples of block.
+ */
+int flux_build_block_mask(int64_t seq_q, int64_t seq_k, int32_t block, int32_t sink_tokens,
+                          int32_t window_tokens, int32_t causal, int32_t mode, int32_t* row_ptr,
+                          int32_t* col_idx, int64_t col_capacity, int64_t* nnz_out);
+
+/*
+ * flux_attn_prefill -- one layer of tiled attention for all heads.
+ *
+ * O = softmax(scale * Q K^T + mask) V per (batch, query head) ([NL] attention
+ * definition; [SA] scale 1/sqrt(d_k)), computed tile by tile with an online
+ * softmax ([NL] "Online Softmax"); the score matrix is never written.
+ *   q   [batch, seq, hq,  head_dim]   device, in_dtype
+ *   k,v [batch, seq, hkv, head_dim]   device, in_dtype
+ *   o   [batch, seq, hq,  head_dim]   device, out_dtype
+ *   lse [batch, hq, seq] float32 natural-log sum-exp of the scaled scores, or NULL
+ * Query head h reads KV head h / (hq / hkv) (grouped-query attention).
+ * mode == FLUX_MODE_DENSE: causal (key <= query) if causal != 0, else all keys.
+ * mode == FLUX_MODE_SPARSE: requires causal == 1 and the device CSR that
+ *   flux_build_block_mask(seq, seq, block, sink_tokens, window_tokens, 1,
+ *   FLUX_MODE_SPARSE, ...) produced (blk_row_ptr [nbq+1], blk_col_idx
+ *   [blk_nnz], both device int32); blk_nnz is checked against the pattern.
+ *   Inside an active block every key is visible except keys after the query
+ *   in the diagonal block.  Dense mode ignores the CSR arguments.
+ * Supported: (in, out) = (BF16, BF16), (BF16, F32), (F32, F32);
+ * head_dim in {64, 128}; block == 64; hq % hkv == 0; scale finite and > 0.
+ */
+int flux_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int32_t in_dtype, int32_t out_dtype, int64_t batch, int64_t seq, int32_t hq,
+                      int32_t hkv, int32_t head_dim, float scale, int32_t causal, int32_t mode,
+                      int32_t block, int32_t sink_tokens, int32_t window_tokens,
+                      const int32_t* blk_row_ptr, const int32_t* blk_col_idx, int64_t blk_nnz,
+                      void* hip_stream);
+
+/*
+ * flux_attn_prefill_layers -- per-layer dispatch of a routed layer stack.
+ *
+ * One mode per layer, never mixed across heads ([FA] layer-granularity
+ * paragraph).  For layer l, runs flux_attn_prefill(q[l], k[l], v[l], o[l],
+ * lse ? lse[l] : NULL, ..., causal = 1, mode = modes_host[l], ...) on
+ * `hip_stream`.  modes_host is a HOST array of n_layers entries (the router
+ * output copied to the host).  All layers share shape, dtypes, block, sink,
+ * window and the sparse CSR.  Layers are validated before the first launch.
+ */
+int flux_attn_prefill_layers(int32_t n_layers, const int32_t* modes_host, const void* const* q,
+                             const void* const* k, const void* const* v, void* const* o,
+                             float* const* lse, int32_t in_dtype, int32_t out_dtype, int64_t batch,
+                             int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                             int32_t block, int32_t sink_tokens, int32_t window_tokens,
+                             const int32_t* blk_row_ptr, const int32_t* blk_col_idx, int64_t blk_nnz,
+                             void* hip_stream);
+
+/*
+ * flux_decode_workspace_size -- bytes of workspace flux_attn_decode needs.
+ * Same meaning of arguments as flux_attn_decode (num_splits = 0: automatic;
+ * the automatic split count depends on batch * hkv, so hkv is needed here).
+ * Returns 0 if the arguments are invalid or unsupported.
+ */
+size_t flux_decode_workspace_size(int64_t batch, int32_t hq, int32_t hkv, int64_t kv_len,
+                                  int32_t head_dim, int32_t mode, int32_t block,
+                                  int32_t sink_tokens, int32_t window_tokens, int32_t num_splits);
+
+/*
+ * flux_attn_decode -- single-token GQA decode with split-KV partials.
+ *
+ * One new query per sequence at position kv_len-1, whose own K/V are already
+ * in the cache; its allowed keys are those of prefill row kv_len-1 (dense:
+ * all kv_len keys; sparse: the sink blocks and the window blocks ending at the
+ * query's block -- inactive cache blocks are never read, [FA] architecture
+ * paragraph).  The active keys are cut into `num_splits` chunks (0 = chosen by
+ * the library); each chunk's partial result (O_s, lse_s) goes to the
+ * workspace and a second kernel merges them with the online-softmax rule
+ * ([NL] "Online Softmax"): LSE = M + ln sum_s exp(lse_s - M), O = sum_s
+ * exp(lse_s - LSE) O_s, with empty chunks weighted 0.
+ *   q       [batch, hq, head_dim]                    device, bf16
+ *   k_cache [batch, kv_capacity, hkv, head_dim]      device, bf16 (positions < kv_len used)
+ *   v_cache [batch, kv_capacity, hkv, head_dim]      device, bf16
+ *   o       [batch, hq, head_dim]                    device, out_dtype
+ *   lse     [batch, hq] float32 or NULL
+ *   kv_capacity: cache length per sequence (0 means kv_len); >= kv_len.
+ *   workspace: device, >= flux_decode_workspace_size(...) bytes, 256-byte aligned.
+ * Supported: in_dtype BF16, out_dtype BF16 or F32, head_dim in {64, 128},
+ * hq/hkv in {1, 2, 4, 8}, block == 64.
+ */
+int flux_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                     int32_t in_dtype, int32_t out_dtype, int64_t batch, int64_t kv_len,
+                     int64_t kv_capacity, int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                     int32_t mode, int32_t block, int32_t sink_tokens, int32_t window_tokens,
+                     int32_t num_splits, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * flux_route_layers -- the layer router ([FA] router paragraphs).
+ *
+ * For each layer l (xQ = q_layers[l], one sequence, [seq, hq, head_dim]):
+ *   pooled = mean of xQ over token indices [0, P) U [seq-P, seq), each index
+ *            counted once (P = pool_tokens, 100 in the method), flattened to
+ *            hq*head_dim features;
+ *   z      = ReLU(w_enc[l] pooled + b_enc[l])          (context encoder MLP)
+ *   pi     = w_head[l] z + b_head[l]                    (router head: pi_FA, pi_SA)
+ *   mode   = argmax(pi), a tie selecting FLUX_MODE_DENSE.
+ * q_layers: HOST array of n_layers device pointers (in_dtype BF16 or F32).
+ * w_enc [n_layers, hidden, hq*head_dim], b_enc [n_layers, hidden],
+ * w_head [n_layers, 2, hidden], b_head [n_layers, 2]: device float32.
+ * logits_out [n_layers, 2] device float32 (may be NULL); modes_out
+ * [n_layers] device int32.  Copying modes to the host is the caller's one
+ * device-to-host synchronization per request.
+ * Supported: hq*head_dim <= 8192, hidden <= 1024, pool_tokens >= 1.
+ */
+int flux_route_layers(const void* const* q_layers, int32_t n_layers, int64_t seq, int32_t hq,
+                      int32_t head_dim, int32_t in_dtype, int32_t pool_tokens, const float* w_enc,
+                      const float* b_enc, int32_t hidden, const float* w_head, const float* b_head,
+                      float* logits_out, int32_t* modes_out, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLUX_ATTN_H */

@@ -1,0 +1,222 @@
+"""Thin Python binding over libflux_attn.so (the C ABI in include/flux_attn.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels behind the C ABI.  torch is used for device memory and streams
+(``tensor.data_ptr()``, ``torch.cuda.current_stream().cuda_stream``).  There is
+no fallback: if the library is not built, importing this package raises.
+
+Function names match the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+__all__ = [
+    "FluxError", "lib", "status_string", "last_error_detail", "flux_version",
+    "flux_build_block_mask", "flux_attn_prefill", "flux_attn_prefill_layers",
+    "flux_decode_workspace_size", "flux_attn_decode", "flux_route_layers",
+    "FLUX_OK", "FLUX_ERR_INVALID_ARG", "FLUX_ERR_UNSUPPORTED", "FLUX_ERR_CAPACITY", "FLUX_ERR_WORKSPACE",
+    "FLUX_ERR_HIP", "FLUX_DTYPE_BF16", "FLUX_DTYPE_F32", "FLUX_MODE_DENSE", "FLUX_MODE_SPARSE",
+    "EXPORTED_SYMBOLS",
+]
+
+FLUX_OK, FLUX_ERR_INVALID_ARG, FLUX_ERR_UNSUPPORTED, FLUX_ERR_CAPACITY, FLUX_ERR_WORKSPACE, FLUX_ERR_HIP = range(6)
+FLUX_DTYPE_BF16, FLUX_DTYPE_F32 = 0, 1
+FLUX_MODE_DENSE, FLUX_MODE_SPARSE = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "flux_status_string", "flux_last_error_detail", "flux_version", "flux_build_block_mask",
+    "flux_attn_prefill", "flux_attn_prefill_layers", "flux_decode_workspace_size", "flux_attn_decode",
+    "flux_route_layers",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflux_attn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m long_context_attention_tiled_amd.build` "
+        "(hipcc for gfx950).  There is no CPU fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_pp = ctypes.POINTER(ctypes.c_void_p)
+
+_lib.flux_status_string.argtypes = [ctypes.c_int]
+_lib.flux_status_string.restype = ctypes.c_char_p
+_lib.flux_last_error_detail.argtypes = []
+_lib.flux_last_error_detail.restype = ctypes.c_char_p
+_lib.flux_version.argtypes = []
+_lib.flux_version.restype = ctypes.c_int
+_lib.flux_build_block_mask.argtypes = [_i64, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
+                                       ctypes.POINTER(_i64)]
+_lib.flux_build_block_mask.restype = ctypes.c_int
+_lib.flux_attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _f32, _i32,
+                                   _i32, _i32, _i32, _i32, _vp, _vp, _i64, _vp]
+_lib.flux_attn_prefill.restype = ctypes.c_int
+_lib.flux_attn_prefill_layers.argtypes = [_i32, _vp, _pp, _pp, _pp, _pp, _pp, _i32, _i32, _i64, _i64, _i32, _i32,
+                                          _i32, _f32, _i32, _i32, _i32, _vp, _vp, _i64, _vp]
+_lib.flux_attn_prefill_layers.restype = ctypes.c_int
+_lib.flux_decode_workspace_size.argtypes = [_i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32]
+_lib.flux_decode_workspace_size.restype = _sz
+_lib.flux_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _f32,
+                                  _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+_lib.flux_attn_decode.restype = ctypes.c_int
+_lib.flux_route_layers.argtypes = [_pp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+_lib.flux_route_layers.restype = ctypes.c_int
+
+
+def lib():
+    """The loaded ctypes library (for callers that marshal raw pointers themselves)."""
+    return _lib
+
+
+class FluxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({last_error_detail()})")
+
+
+def status_string(status: int) -> str:
+    return _lib.flux_status_string(int(status)).decode()
+
+
+def last_error_detail() -> str:
+    return _lib.flux_last_error_detail().decode()
+
+
+def flux_version() -> int:
+    return int(_lib.flux_version())
+
+
+def _check(status: int, where: str):
+    if status != FLUX_OK:
+        raise FluxError(status, where)
+
+
+# ------------------------------------------------------------------ helpers
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FLUX_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FLUX_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+# ------------------------------------------------------------------ entry points
+def flux_build_block_mask(seq_q: int, seq_k: int, block: int = 64, sink_tokens: int = 128, window_tokens: int = 2048,
+                          causal: int = 1, mode: int = FLUX_MODE_SPARSE):
+    """Host CSR of the active key blocks: (row_ptr int32 [nbq+1], col_idx int32 [nnz])."""
+    nnz = _i64(0)
+    _check(_lib.flux_build_block_mask(seq_q, seq_k, block, sink_tokens, window_tokens, causal, mode, None, None, 0,
+                                      ctypes.byref(nnz)), "flux_build_block_mask")
+    nbq = -(-seq_q // block)
+    row_ptr = np.zeros(nbq + 1, np.int32)
+    col_idx = np.zeros(max(1, nnz.value), np.int32)
+    _check(_lib.flux_build_block_mask(seq_q, seq_k, block, sink_tokens, window_tokens, causal, mode,
+                                      row_ptr.ctypes.data_as(_vp), col_idx.ctypes.data_as(_vp), col_idx.size,
+                                      ctypes.byref(nnz)), "flux_build_block_mask")
+    return row_ptr, col_idx[:nnz.value]
+
+
+def flux_attn_prefill(q, k, v, o, lse=None, *, causal: int = 1, mode: int = FLUX_MODE_DENSE, block: int = 64,
+                      sink_tokens: int = 128, window_tokens: int = 2048, blk_row_ptr=None, blk_col_idx=None,
+                      scale: float | None = None, stream=None):
+    """q [B,S,Hq,d], k/v [B,S,Hkv,d], o [B,S,Hq,d] (device tensors); lse [B,Hq,S] float32 or None.
+
+    blk_row_ptr / blk_col_idx: device int32 tensors from flux_build_block_mask (sparse mode)."""
+    _contig(q, k, v, o, lse)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nnz = int(blk_col_idx.numel()) if blk_col_idx is not None else 0
+    _check(_lib.flux_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q), _dtype_code(o), B, S,
+                                  Hq, Hkv, d, scale, causal, mode, block, sink_tokens, window_tokens,
+                                  _ptr(blk_row_ptr), _ptr(blk_col_idx), nnz, _stream(stream)), "flux_attn_prefill")
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))(*[(t.data_ptr() if t is not None else None) for t in ts])
+    return ctypes.cast(arr, _pp), arr
+
+
+def flux_attn_prefill_layers(modes_host, qs, ks, vs, os_, lses=None, *, block: int = 64, sink_tokens: int = 128,
+                             window_tokens: int = 2048, blk_row_ptr=None, blk_col_idx=None,
+                             scale: float | None = None, stream=None):
+    """Per-layer dispatch: layer l runs dense or block-sparse prefill per modes_host[l] (host int32)."""
+    L = len(qs)
+    modes = np.ascontiguousarray(np.asarray(modes_host, dtype=np.int32))
+    assert modes.shape == (L,)
+    B, S, Hq, d = qs[0].shape
+    Hkv = ks[0].shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    pq, _a = _ptr_array(qs)
+    pk, _b = _ptr_array(ks)
+    pv, _c = _ptr_array(vs)
+    po, _d = _ptr_array(os_)
+    pl, _e = _ptr_array(lses) if lses is not None else (None, None)
+    nnz = int(blk_col_idx.numel()) if blk_col_idx is not None else 0
+    _check(_lib.flux_attn_prefill_layers(L, modes.ctypes.data_as(_vp), pq, pk, pv, po, pl, _dtype_code(qs[0]),
+                                         _dtype_code(os_[0]), B, S, Hq, Hkv, d, scale, block, sink_tokens,
+                                         window_tokens, _ptr(blk_row_ptr), _ptr(blk_col_idx), nnz, _stream(stream)),
+           "flux_attn_prefill_layers")
+
+
+def flux_decode_workspace_size(batch, hq, hkv, kv_len, head_dim, mode=FLUX_MODE_DENSE, block=64, sink_tokens=128,
+                               window_tokens=2048, num_splits=0) -> int:
+    return int(_lib.flux_decode_workspace_size(batch, hq, hkv, kv_len, head_dim, mode, block, sink_tokens,
+                                               window_tokens, num_splits))
+
+
+def flux_attn_decode(q, k_cache, v_cache, o, lse=None, *, kv_len: int | None = None, mode: int = FLUX_MODE_DENSE,
+                     block: int = 64, sink_tokens: int = 128, window_tokens: int = 2048, num_splits: int = 0,
+                     workspace=None, scale: float | None = None, stream=None):
+    """q [B,Hq,d], caches [B,cap,Hkv,d] bf16, o [B,Hq,d]; workspace: a uint8 device tensor."""
+    _contig(q, k_cache, v_cache, o, lse)
+    B, Hq, d = q.shape
+    cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if kv_len is None:
+        kv_len = cap
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.flux_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _dtype_code(q),
+                                 _dtype_code(o), B, kv_len, cap, Hq, Hkv, d, scale, mode, block, sink_tokens,
+                                 window_tokens, num_splits, _ptr(workspace), ws_bytes, _stream(stream)),
+           "flux_attn_decode")
+
+
+def flux_route_layers(q_layers, w_enc, b_enc, w_head, b_head, modes_out, logits_out=None, *, pool_tokens: int = 100,
+                      stream=None):
+    """q_layers: list of device tensors [S,Hq,d]; weights device float32; modes_out device int32 [L]."""
+    L = len(q_layers)
+    S, Hq, d = q_layers[0].shape
+    hidden = w_enc.shape[1]
+    pq, _keep = _ptr_array(q_layers)
+    _check(_lib.flux_route_layers(pq, L, S, Hq, d, _dtype_code(q_layers[0]), pool_tokens, _ptr(w_enc), _ptr(b_enc),
+                                  hidden, _ptr(w_head), _ptr(b_head), _ptr(logits_out), _ptr(modes_out),
+                                  _stream(stream)), "flux_route_layers")

@@ -1,0 +1,82 @@
+// flux_internal.h -- argument blocks and launchers shared by the host layer
+// (flux_api.cpp) and the gfx950 kernels (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flux {
+
+constexpr int kBlock = 64;  // block-sparse granularity and key-tile width
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;            // [B, Hq, S] or nullptr
+    int64_t batch;
+    int64_t seq;
+    int hq;
+    int hkv;
+    int head_dim;
+    float scale;           // softmax scale
+    float scale_log2;      // scale * log2(e): scores enter exp2
+    int causal;
+    int sparse;
+    int out_f32;
+    int n_qblk;            // ceil(seq / 64)
+    const int32_t* row_ptr;  // sparse CSR (device) or nullptr
+    const int32_t* col_idx;
+};
+
+struct DecodeArgs {
+    const void* q;         // [B, Hq, d] bf16
+    const void* k;         // [B, cap, Hkv, d] bf16
+    const void* v;
+    void* o;               // [B, Hq, d]
+    float* lse;            // [B, Hq] or nullptr
+    float* part_o;         // workspace [B, Hq, n_split, d] fp32 (normalised partial outputs)
+    float* part_lse;       // workspace [B, Hq, n_split] fp32 (natural log)
+    int64_t batch;
+    int64_t kv_len;
+    int64_t kv_cap;
+    int hq;
+    int hkv;
+    int head_dim;
+    float scale;
+    float scale_log2;
+    int out_f32;
+    // active key ranges: [0, r0_end) U [r1_begin, kv_len); n_active = r0_end + (kv_len - r1_begin)
+    int64_t r0_end;
+    int64_t r1_begin;
+    int64_t n_active;
+    int n_split;
+    int64_t split_len;     // active keys per split (multiple of 64)
+};
+
+constexpr int kMaxRouteLayers = 64;
+
+struct RouteArgs {
+    const void* xq[kMaxRouteLayers];
+    int n_layers;
+    int layer0;            // index of xq[0] in the stacked weight arrays
+    int64_t seq;
+    int n_feat;            // hq * head_dim
+    int in_f32;
+    int pool_tokens;
+    const float* w_enc;
+    const float* b_enc;
+    int hidden;
+    const float* w_head;
+    const float* b_head;
+    float* logits;         // nullable
+    int32_t* modes;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+}  // namespace flux

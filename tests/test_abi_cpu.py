@@ -1,0 +1,231 @@
+"""Host-side checks of the C ABI: symbols, block-mask builder, argument validation.
+
+No GPU is needed: every call here either is host-only (the mask builder,
+workspace sizing, status strings) or is rejected by validation before any HIP
+call (the device pointers below are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import long_context_attention_tiled_amd as fa
+    return fa
+
+
+def test_library_exports_every_header_symbol(fa):
+    with open(os.path.join(ROOT, "include", "flux_attn.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(flux_\w+)\s*\(", text, re.M))
+    assert declared == set(fa.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(fa.lib(), name), name
+    assert fa.flux_version() == 100
+
+
+def test_status_strings(fa):
+    for code in range(6):
+        s = fa.status_string(code)
+        assert s.startswith("FLUX_")
+    assert "unknown" in fa.status_string(99)
+
+
+def _csr_to_bitmap(row_ptr, col_idx, nbk):
+    nbq = len(row_ptr) - 1
+    bm = np.zeros((nbq, nbk), np.uint8)
+    for i in range(nbq):
+        cols = col_idx[row_ptr[i]:row_ptr[i + 1]]
+        assert np.all(np.diff(cols) > 0), "ascending, no duplicates"
+        bm[i, cols] = 1
+    return bm
+
+
+MASK_CASES = [
+    (512, 64, 128, 128), (512, 64, 128, 2048), (1000, 64, 128, 256), (97, 16, 0, 16), (64, 64, 128, 64),
+    (65536, 64, 128, 2048), (131072, 64, 128, 2048), (8192, 64, 0, 64), (777, 32, 64, 96),
+]
+
+
+@pytest.mark.parametrize("S,block,sink,window", MASK_CASES)
+def test_block_mask_bit_exact_vs_oracle(fa, S, block, sink, window):
+    rp, ci = fa.flux_build_block_mask(S, S, block, sink, window, 1, fa.FLUX_MODE_SPARSE)
+    nb = -(-S // block)
+    assert rp[0] == 0 and rp[-1] == len(ci) and len(rp) == nb + 1
+    bm = _csr_to_bitmap(rp, ci, nb)
+    ref = oracle.block_mask(S, S, block, sink, window, causal=True, sparse=True)
+    np.testing.assert_array_equal(bm, ref)
+
+
+def test_block_mask_config_counts(fa):
+    assert len(fa.flux_build_block_mask(512, 512, 64, 128, 128)[1]) == 26
+    assert len(fa.flux_build_block_mask(65536, 65536, 64, 128, 2048)[1]) == 34255
+    assert len(fa.flux_build_block_mask(131072, 131072, 64, 128, 2048)[1]) == 69071
+
+
+@pytest.mark.parametrize("S,causal", [(1000, 1), (1000, 0), (64, 1), (65, 0)])
+def test_dense_mask_bit_exact(fa, S, causal):
+    rp, ci = fa.flux_build_block_mask(S, S, 64, 0, 0, causal, fa.FLUX_MODE_DENSE)
+    nb = -(-S // 64)
+    ref = oracle.block_mask(S, S, 64, 0, 0, causal=bool(causal), sparse=False)
+    np.testing.assert_array_equal(_csr_to_bitmap(rp, ci, nb), ref)
+
+
+def _mask_call(fa, S=512, block=64, sink=128, window=128, causal=1, mode=1, cap=None, want_arrays=True):
+    nnz = ctypes.c_int64(-1)
+    nb = -(-S // max(block, 1))
+    rp = np.zeros(max(nb, 1) + 1, np.int32)
+    cap = 10 ** 6 if cap is None else cap
+    ci = np.zeros(max(cap, 1), np.int32)
+    st = fa.lib().flux_build_block_mask(S, S, block, sink, window, causal, mode,
+                                        rp.ctypes.data_as(ctypes.c_void_p) if want_arrays else None,
+                                        ci.ctypes.data_as(ctypes.c_void_p) if want_arrays else None,
+                                        cap if want_arrays else 0, ctypes.byref(nnz))
+    return st, nnz.value
+
+
+def test_block_mask_validation(fa):
+    assert _mask_call(fa)[0] == fa.FLUX_OK
+    assert _mask_call(fa, sink=100)[0] == fa.FLUX_ERR_INVALID_ARG       # sink not a multiple of block
+    assert _mask_call(fa, window=100)[0] == fa.FLUX_ERR_INVALID_ARG     # window not a multiple of block
+    assert _mask_call(fa, window=0)[0] == fa.FLUX_ERR_INVALID_ARG       # window < block in sparse mode
+    assert _mask_call(fa, causal=0)[0] == fa.FLUX_ERR_INVALID_ARG       # sparse needs causal
+    assert _mask_call(fa, mode=7)[0] == fa.FLUX_ERR_INVALID_ARG
+    assert _mask_call(fa, block=0)[0] == fa.FLUX_ERR_INVALID_ARG
+    assert _mask_call(fa, S=0)[0] == fa.FLUX_ERR_INVALID_ARG
+    st, nnz = _mask_call(fa, cap=10)
+    assert st == fa.FLUX_ERR_CAPACITY and nnz == 26
+    st, nnz = _mask_call(fa, want_arrays=False)
+    assert st == fa.FLUX_OK and nnz == 26
+    assert "window" in fa.last_error_detail() or fa.last_error_detail() == ""
+
+
+# ---------------------------------------------------------------- prefill validation
+FAKE = 0x10000  # an aligned address that validation failures never dereference
+
+
+def _prefill(fa, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, in_dtype=0, out_dtype=1, batch=1, seq=512, hq=4, hkv=2,
+                d=128, scale=0.088, causal=1, mode=0, block=64, sink=128, window=128, rp=None, ci=None, nnz=0)
+    args.update(kw)
+    return fa.lib().flux_attn_prefill(args["q"], args["k"], args["v"], args["o"], args["lse"], args["in_dtype"],
+                                      args["out_dtype"], args["batch"], args["seq"], args["hq"], args["hkv"],
+                                      args["d"], args["scale"], args["causal"], args["mode"], args["block"],
+                                      args["sink"], args["window"], args["rp"], args["ci"], args["nnz"], None)
+
+
+def test_prefill_validation(fa):
+    E, U = fa.FLUX_ERR_INVALID_ARG, fa.FLUX_ERR_UNSUPPORTED
+    assert _prefill(fa, q=None) == E
+    assert _prefill(fa, o=None) == E
+    assert _prefill(fa, k=FAKE + 2) == E                    # misaligned
+    assert _prefill(fa, lse=FAKE + 2) == E
+    assert _prefill(fa, hq=6, hkv=4) == E                   # hq % hkv != 0
+    assert _prefill(fa, hkv=0) == E
+    assert _prefill(fa, seq=0) == E
+    assert _prefill(fa, batch=0) == E
+    assert _prefill(fa, scale=0.0) == E
+    assert _prefill(fa, scale=float("inf")) == E
+    assert _prefill(fa, scale=float("nan")) == E
+    assert _prefill(fa, in_dtype=5) == E
+    assert _prefill(fa, out_dtype=5) == E
+    assert _prefill(fa, causal=2) == E
+    assert _prefill(fa, mode=3) == E
+    assert _prefill(fa, d=96) == U
+    assert _prefill(fa, block=32) == U
+    assert _prefill(fa, in_dtype=1, out_dtype=0) == U
+    # sparse-mode rules
+    assert _prefill(fa, mode=1, causal=0, rp=FAKE, ci=FAKE, nnz=26) == E
+    assert _prefill(fa, mode=1, sink=100, rp=FAKE, ci=FAKE, nnz=26) == E
+    assert _prefill(fa, mode=1, window=0, rp=FAKE, ci=FAKE, nnz=26) == E
+    assert _prefill(fa, mode=1, window=96, rp=FAKE, ci=FAKE, nnz=26) == E
+    assert _prefill(fa, mode=1, rp=None, ci=FAKE, nnz=26) == E
+    assert _prefill(fa, mode=1, rp=FAKE, ci=FAKE, nnz=25) == E   # CSR does not match the pattern
+    assert "blk_nnz" in fa.last_error_detail()
+
+
+def test_prefill_layers_validation(fa):
+    L = 2
+    P = ctypes.POINTER(ctypes.c_void_p)
+    ptrs = (ctypes.c_void_p * L)(FAKE, FAKE)
+    pp = ctypes.cast(ptrs, P)
+    modes = np.array([0, 7], np.int32)
+    st = fa.lib().flux_attn_prefill_layers(L, modes.ctypes.data_as(ctypes.c_void_p), pp, pp, pp, pp, None, 0, 1, 1,
+                                           512, 4, 2, 128, 0.088, 64, 128, 128, None, None, 0, None)
+    assert st == fa.FLUX_ERR_INVALID_ARG and "layer 1" in fa.last_error_detail()
+    st = fa.lib().flux_attn_prefill_layers(0, modes.ctypes.data_as(ctypes.c_void_p), pp, pp, pp, pp, None, 0, 1, 1,
+                                           512, 4, 2, 128, 0.088, 64, 128, 128, None, None, 0, None)
+    assert st == fa.FLUX_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- decode validation / workspace
+def test_decode_workspace_size(fa):
+    B, Hq, Hkv, L, d = 8, 32, 8, 262144, 128
+    ws = fa.flux_decode_workspace_size(B, Hq, Hkv, L, d, fa.FLUX_MODE_DENSE)
+    assert ws > 0 and ws % 256 == 0
+    # explicit split count: [B,Hq,n,d] + [B,Hq,n] floats, each part 256-aligned
+    ws7 = fa.flux_decode_workspace_size(B, Hq, Hkv, L, d, fa.FLUX_MODE_DENSE, num_splits=7)
+    rows = B * Hq * 7
+    align = lambda x: (x + 255) // 256 * 256
+    assert ws7 == align(rows * d * 4) + align(rows * 4)
+    assert fa.flux_decode_workspace_size(B, Hq, Hkv, L, d, fa.FLUX_MODE_SPARSE, 64, 128, 2048) > 0
+    assert fa.flux_decode_workspace_size(B, Hq, 5, L, d) == 0          # hq % hkv
+    assert fa.flux_decode_workspace_size(B, Hq, Hkv, L, 96) == 0       # unsupported head_dim
+    assert fa.flux_decode_workspace_size(B, Hq, Hkv, L, d, fa.FLUX_MODE_SPARSE, 64, 100, 2048) == 0
+
+
+def _decode(fa, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, in_dtype=0, out_dtype=1, batch=2, kv_len=4096, cap=0,
+                hq=8, hkv=2, d=128, scale=0.088, mode=0, block=64, sink=128, window=2048, ns=0, ws=FAKE,
+                ws_bytes=1 << 30)
+    args.update(kw)
+    return fa.lib().flux_attn_decode(args["q"], args["k"], args["v"], args["o"], args["lse"], args["in_dtype"],
+                                     args["out_dtype"], args["batch"], args["kv_len"], args["cap"], args["hq"],
+                                     args["hkv"], args["d"], args["scale"], args["mode"], args["block"],
+                                     args["sink"], args["window"], args["ns"], args["ws"], args["ws_bytes"], None)
+
+
+def test_decode_validation(fa):
+    E, U, W = fa.FLUX_ERR_INVALID_ARG, fa.FLUX_ERR_UNSUPPORTED, fa.FLUX_ERR_WORKSPACE
+    assert _decode(fa, q=None) == E
+    assert _decode(fa, v=FAKE + 8) == E
+    assert _decode(fa, hq=8, hkv=3) == E
+    assert _decode(fa, hq=32, hkv=2) == U                   # group of 16 heads
+    assert _decode(fa, kv_len=0) == E
+    assert _decode(fa, cap=100) == E                        # capacity < kv_len
+    assert _decode(fa, ns=-1) == E
+    assert _decode(fa, scale=-1.0) == E
+    assert _decode(fa, mode=1, window=0) == E
+    assert _decode(fa, mode=1, sink=64 + 3) == E
+    assert _decode(fa, d=80) == U
+    assert _decode(fa, in_dtype=1) == U
+    assert _decode(fa, ws=None) == W
+    assert _decode(fa, ws_bytes=16) == W
+    assert _decode(fa, ws=FAKE + 64) == E                   # workspace alignment
+
+
+def test_route_validation(fa):
+    P = ctypes.POINTER(ctypes.c_void_p)
+    ptrs = (ctypes.c_void_p * 2)(FAKE, None)
+    pp = ctypes.cast(ptrs, P)
+    lib = fa.lib()
+    st = lib.flux_route_layers(pp, 2, 1000, 32, 128, 0, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, None)
+    assert st == fa.FLUX_ERR_INVALID_ARG and "q_layers[1]" in fa.last_error_detail()
+    ptrs2 = (ctypes.c_void_p * 1)(FAKE)
+    pp2 = ctypes.cast(ptrs2, P)
+    assert lib.flux_route_layers(pp2, 1, 1000, 32, 128, 0, 100, None, FAKE, 256, FAKE, FAKE, None, FAKE,
+                                 None) == fa.FLUX_ERR_INVALID_ARG
+    assert lib.flux_route_layers(pp2, 1, 1000, 128, 128, 0, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE,
+                                 None) == fa.FLUX_ERR_UNSUPPORTED          # 16384 features
+    assert lib.flux_route_layers(pp2, 1, 1000, 32, 128, 0, 100, FAKE, FAKE, 2048, FAKE, FAKE, None, FAKE,
+                                 None) == fa.FLUX_ERR_UNSUPPORTED          # hidden > 1024
+    assert lib.flux_route_layers(pp2, 1, 1000, 32, 128, 0, 0, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE,
+                                 None) == fa.FLUX_ERR_INVALID_ARG          # pool_tokens < 1

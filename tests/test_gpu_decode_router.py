@@ -1,0 +1,184 @@
+"""GPU parity of split-KV decode (+ LSE combine) and of the layer router, vs the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu_helpers import bf16_tensors, check_close, check_lse, default_scale, dev_bits_to_host, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import long_context_attention_tiled_amd as fa
+    assert torch.cuda.is_available()
+    return fa
+
+
+def _decode(fa, qd, kd, vd, out_dtype, mode, kv_len=None, sink=128, window=2048, num_splits=0):
+    B, Hq, d = qd.shape
+    cap, Hkv = kd.shape[1], kd.shape[2]
+    kv_len = cap if kv_len is None else kv_len
+    ws_bytes = fa.flux_decode_workspace_size(B, Hq, Hkv, kv_len, d, mode, 64, sink, window, num_splits)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    o = torch.empty((B, Hq, d), dtype=out_dtype, device=DEV)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    fa.flux_attn_decode(qd, kd, vd, o, lse, kv_len=kv_len, mode=mode, block=64, sink_tokens=sink,
+                        window_tokens=window, num_splits=num_splits, workspace=ws)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+SMALL = [
+    # B, L, Hq, Hkv, d, mode, sink, window, num_splits
+    (1, 1, 4, 1, 128, 0, 128, 2048, 0),
+    (2, 100, 8, 2, 128, 0, 128, 2048, 0),
+    (3, 4097, 32, 8, 128, 0, 128, 2048, 0),
+    (2, 5000, 8, 1, 128, 0, 128, 2048, 7),
+    (2, 3000, 4, 4, 64, 0, 128, 2048, 2),
+    (2, 3000, 16, 2, 64, 0, 128, 2048, 0),
+    (2, 8192, 32, 8, 128, 1, 128, 2048, 0),
+    (1, 10000, 8, 2, 128, 1, 128, 1024, 3),     # ragged L, sparse
+    (2, 200, 8, 2, 128, 1, 128, 128, 0),         # window overlaps the sink
+    (1, 90, 4, 1, 128, 1, 128, 2048, 0),         # L shorter than the sink
+]
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv,d,mode,sink,window,ns", SMALL)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_decode_small_full_oracle(fa, B, L, Hq, Hkv, d, mode, sink, window, ns, out_dtype):
+    say("decode small", B, L, Hq, Hkv, d, "mode", mode, sink, window, ns, out_dtype)
+    q = synth.normal_bf16_bits((B, Hq, d), 3000 + L, 0, synth.TENSOR_Q)
+    k = synth.normal_bf16_bits((B, L, Hkv, d), 3000 + L, 0, synth.TENSOR_K)
+    v = synth.normal_bf16_bits((B, L, Hkv, d), 3000 + L, 0, synth.TENSOR_V)
+    qd, kd, vd = (synth.torch_bf16_from_bits(x) for x in (q, k, v))
+    o, lse = _decode(fa, qd, kd, vd, out_dtype, mode, sink=sink, window=window, num_splits=ns)
+    ref, ref_lse = oracle.decode(q, k, v, default_scale(d), sparse=bool(mode), block=64, sink_tokens=sink,
+                                 window_tokens=window)
+    check_close(o.float().cpu().numpy(), ref, "decode small", out_bf16=out_dtype == torch.bfloat16)
+    check_lse(lse.cpu().numpy(), ref_lse, "decode lse")
+
+
+def test_decode_uses_kv_len_inside_capacity(fa):
+    """Cache capacity larger than kv_len: positions >= kv_len are never read."""
+    B, cap, L, Hq, Hkv, d = 2, 3000, 2500, 8, 2, 128
+    say("decode capacity")
+    k = synth.normal_bf16_bits((B, cap, Hkv, d), 41, 0, 1)
+    v = synth.normal_bf16_bits((B, cap, Hkv, d), 41, 0, 2)
+    q = synth.normal_bf16_bits((B, Hq, d), 41, 0, 0)
+    kd, vd, qd = (synth.torch_bf16_from_bits(x) for x in (k, v, q))
+    kd[:, L:] = float("nan")
+    vd[:, L:] = float("nan")
+    for mode in (0, 1):
+        o, lse = _decode(fa, qd, kd, vd, torch.float32, mode, kv_len=L)
+        ref, ref_lse = oracle.decode(q, np.ascontiguousarray(k[:, :L]), np.ascontiguousarray(v[:, :L]),
+                                     default_scale(d), sparse=bool(mode), block=64, sink_tokens=128,
+                                     window_tokens=2048)
+        check_close(o.cpu().numpy(), ref, f"decode cap mode {mode}")
+
+
+def test_decode_split_count_invariance(fa):
+    B, L, Hq, Hkv, d = 2, 9000, 8, 2, 128
+    say("decode split invariance")
+    _, (qd4, kd, vd) = bf16_tensors(B, L, Hq, Hkv, d, seed=42)
+    qd = qd4[:, -1].contiguous()
+    for mode in (0, 1):
+        base, base_lse = _decode(fa, qd, kd, vd, torch.float32, mode, num_splits=1)
+        for ns in (2, 7, 0):
+            o, lse = _decode(fa, qd, kd, vd, torch.float32, mode, num_splits=ns)
+            assert (o - base).abs().max().item() <= 1e-5
+            assert (lse - base_lse).abs().max().item() <= 1e-5
+
+
+def test_decode_equals_prefill_last_row(fa):
+    B, L, Hq, Hkv, d = 1, 3000, 8, 2, 128
+    say("decode == prefill last row")
+    _, (qd, kd, vd) = bf16_tensors(B, L, Hq, Hkv, d, seed=43)
+    for mode in (0, 1):
+        o = torch.empty((B, L, Hq, d), dtype=torch.float32, device=DEV)
+        rp = ci = None
+        if mode:
+            r, c = fa.flux_build_block_mask(L, L, 64, 128, 512, 1, 1)
+            rp, ci = torch.from_numpy(r).to(DEV), torch.from_numpy(c).to(DEV)
+        fa.flux_attn_prefill(qd, kd, vd, o, None, causal=1, mode=mode, sink_tokens=128, window_tokens=512,
+                             blk_row_ptr=rp, blk_col_idx=ci)
+        dec, _ = _decode(fa, qd[:, -1].contiguous(), kd, vd, torch.float32, mode, sink=128, window=512)
+        assert (dec - o[:, -1]).abs().max().item() <= 2e-3
+
+
+def test_decode_full_size_dense_and_sparse(fa):
+    """GQA decode: batch 8, KV length 262144, 32 query heads, 8 KV heads, head_dim 128, bf16 cache."""
+    B, L, Hq, Hkv, d = 8, 262144, 32, 8, 128
+    say("decode full size")
+    qd = synth.torch_normal((B, Hq, d), 1005, torch.bfloat16)
+    kd = synth.torch_normal((B, L, Hkv, d), 1006, torch.bfloat16)
+    vd = synth.torch_normal((B, L, Hkv, d), 1007, torch.bfloat16)
+    q = dev_bits_to_host(qd)
+    for mode in (0, 1):
+        o, lse = _decode(fa, qd, kd, vd, torch.float32, mode)
+        o_h, l_h = o.cpu().numpy(), lse.cpu().numpy()
+        for b in (0, 5):
+            kb = dev_bits_to_host(kd[b:b + 1])
+            vb = dev_bits_to_host(vd[b:b + 1])
+            groups = [1, 6] if mode == 0 else list(range(Hkv))
+            rows = np.array([(0, h) for g in groups for h in range(g * 4, g * 4 + 4)], np.int64)
+            ref, ref_lse = oracle.decode(np.ascontiguousarray(q[b:b + 1]), kb, vb, default_scale(d),
+                                         sparse=bool(mode), block=64, sink_tokens=128, window_tokens=2048, rows=rows)
+            got = np.stack([o_h[b, h] for _, h in rows])
+            check_close(got, ref, f"decode full mode {mode} b {b}")
+            check_lse(np.array([l_h[b, h] for _, h in rows]), ref_lse, "decode full lse")
+    del qd, kd, vd
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ router
+def _route_gpu(fa, xs_dev, w):
+    L = len(xs_dev)
+    wd = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in w]
+    modes = torch.empty(L, dtype=torch.int32, device=DEV)
+    logits = torch.empty((L, 2), dtype=torch.float32, device=DEV)
+    fa.flux_route_layers(xs_dev, *wd, modes, logits, pool_tokens=100)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy(), modes.cpu().numpy()
+
+
+def _check_route(logits, modes, ref_logits, ref_modes, what):
+    err = np.abs(logits - ref_logits)
+    scale = np.maximum(1.0, np.abs(ref_logits))
+    assert np.all(err <= 1e-4 * scale), f"{what}: logits max err {err.max():.3e}"
+    margin = np.abs(ref_logits[:, 1] - ref_logits[:, 0])
+    decided = margin > 1e-3          # decisions fp32 rounding cannot flip
+    assert decided.mean() > 0.9, f"{what}: too many near-ties"
+    np.testing.assert_array_equal(modes[decided], ref_modes[decided])
+    # near-ties (if any) must still be the argmax of the GPU's own logits, tie -> dense
+    own = (logits[:, 1] > logits[:, 0]).astype(np.int32)
+    np.testing.assert_array_equal(modes, own)
+
+
+@pytest.mark.parametrize("S,Hq,d,L", [(1, 2, 64, 3), (150, 4, 64, 5), (200, 8, 128, 4), (5000, 32, 128, 6)])
+def test_router_small(fa, S, Hq, d, L):
+    say("router", S, Hq, d, L)
+    xs = [synth.normal_bf16_bits((S, Hq, d), 4000 + S, l, 0) for l in range(L)]
+    w = synth.router_weights(L, Hq * d, 256, seed=4001)
+    logits, modes = _route_gpu(fa, [synth.torch_bf16_from_bits(x) for x in xs], w)
+    _, ref_logits, ref_modes = oracle.route(xs, *w)
+    _check_route(logits, modes, ref_logits, ref_modes, "router small")
+
+
+def test_router_qwen_stack_shape(fa):
+    """36 layers, seq 131072, 32 heads x 128: the pooled rows are the first and last 100 tokens."""
+    S, Hq, d, L = 131072, 32, 128, 36
+    say("router 36 layers")
+    xs_dev = [synth.torch_normal((S, Hq, d), 5000 + l, torch.bfloat16) for l in range(L)]
+    w = synth.router_weights(L, Hq * d, 256, seed=4002)
+    logits, modes = _route_gpu(fa, xs_dev, w)
+    # the oracle reads the 200 pooled rows only: [0,100) U [S-100, S) as a 200-token prompt
+    xs_host = [np.concatenate([dev_bits_to_host(x[:100]), dev_bits_to_host(x[S - 100:])]) for x in xs_dev]
+    _, ref_logits, ref_modes = oracle.route(xs_host, *w)
+    _check_route(logits, modes, ref_logits, ref_modes, "router 36 layers")
+    del xs_dev
+    torch.cuda.empty_cache()

@@ -1,0 +1,192 @@
+"""GPU parity of the prefill path (dense causal, dense non-causal, block-sparse) vs the fp64 oracle.
+
+Every call goes through the C ABI (libflux_attn.so) via the thin binding.
+Inputs: seeded iid N(0,1), rounded to bf16 (the fp32 case keeps float32); the
+oracle reads exactly the same bits.  Bar: max-abs <= 1e-2 and mean-abs <= 1e-3
+with fp32 outputs; bf16 outputs may differ by a further half bf16 ulp.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu_helpers import (bf16_tensors, check_close, check_lse, default_scale, dev_bits_to_host, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import long_context_attention_tiled_amd as fa
+    assert torch.cuda.is_available()
+    return fa
+
+
+def _csr_dev(fa, S, sink, window):
+    rp, ci = fa.flux_build_block_mask(S, S, 64, sink, window, 1, fa.FLUX_MODE_SPARSE)
+    return torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+
+
+def _run_prefill(fa, qd, kd, vd, out_dtype, mode, causal=1, sink=128, window=2048, with_lse=True):
+    B, S, Hq, d = qd.shape
+    o = torch.empty((B, S, Hq, d), dtype=out_dtype, device=DEV)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV) if with_lse else None
+    rp = ci = None
+    if mode == fa.FLUX_MODE_SPARSE:
+        rp, ci = _csr_dev(fa, S, sink, window)
+    fa.flux_attn_prefill(qd, kd, vd, o, lse, causal=causal, mode=mode, block=64, sink_tokens=sink,
+                         window_tokens=window, blk_row_ptr=rp, blk_col_idx=ci)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ------------------------------------------------------------- tiny fp32 layer (both modes)
+@pytest.mark.parametrize("mode", [0, 1])
+def test_tiny_fp32_layer(fa, mode):
+    """batch 1, 2 query heads = 2 KV heads, head_dim 64, seq 512, scale 1/8; dense causal, then
+    block-sparse with block 64, sink 128 (2 blocks), window 2 blocks."""
+    B, S, H, d = 1, 512, 2, 64
+    say("tiny fp32", "mode", mode)
+    q, k, v = synth.qkv_f32(B, S, H, H, d, seed=1001)
+    qd, kd, vd = (torch.from_numpy(x).to(DEV) for x in (q, k, v))
+    o, lse = _run_prefill(fa, qd, kd, vd, torch.float32, mode, sink=128, window=128)
+    ref, ref_lse = oracle.attention(q, k, v, 1.0 / 8, causal=True, sparse=bool(mode), block=64, sink_tokens=128,
+                                    window_tokens=128)
+    check_close(o.cpu().numpy(), ref, f"tiny fp32 mode {mode}")
+    check_lse(lse.cpu().numpy(), np.transpose(ref_lse, (0, 2, 1)), "tiny fp32 lse")
+
+
+# ------------------------------------------------------------- bf16, small shapes, full oracle
+SMALL = [
+    # B, S, Hq, Hkv, d, mode, causal, sink, window
+    (1, 1, 4, 1, 128, 0, 1, 128, 2048),
+    (1, 63, 4, 1, 128, 0, 1, 128, 2048),
+    (1, 64, 2, 2, 128, 0, 1, 128, 2048),
+    (2, 129, 8, 2, 128, 0, 1, 128, 2048),
+    (1, 777, 4, 1, 128, 0, 1, 128, 2048),
+    (1, 300, 4, 2, 64, 0, 1, 128, 2048),
+    (1, 200, 2, 1, 128, 0, 0, 128, 2048),     # non-causal, ragged
+    (2, 130, 4, 4, 64, 0, 0, 128, 2048),
+    (1, 1000, 4, 1, 128, 1, 1, 128, 128),     # sparse, window 2 blocks, ragged tail
+    (1, 1024, 4, 2, 128, 1, 1, 128, 256),
+    (2, 517, 8, 2, 64, 1, 1, 64, 192),
+    (1, 640, 2, 1, 128, 1, 1, 0, 64),          # no sink, window of one block
+    (1, 100, 2, 1, 128, 1, 1, 128, 128),       # shorter than the sink
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,d,mode,causal,sink,window", SMALL)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_bf16_small_full_oracle(fa, B, S, Hq, Hkv, d, mode, causal, sink, window, out_dtype):
+    say("bf16 small", B, S, Hq, Hkv, d, "mode", mode, "causal", causal, sink, window, out_dtype)
+    (q, k, v), (qd, kd, vd) = bf16_tensors(B, S, Hq, Hkv, d, seed=2000 + S)
+    o, lse = _run_prefill(fa, qd, kd, vd, out_dtype, mode, causal=causal, sink=sink, window=window)
+    ref, ref_lse = oracle.attention(q, k, v, default_scale(d), causal=bool(causal), sparse=bool(mode), block=64,
+                                    sink_tokens=sink, window_tokens=window)
+    check_close(o.float().cpu().numpy(), ref, "bf16 small", out_bf16=out_dtype == torch.bfloat16)
+    check_lse(lse.cpu().numpy(), np.transpose(ref_lse, (0, 2, 1)), "bf16 small lse")
+
+
+def test_sparse_full_window_equals_dense(fa):
+    """A window covering every block makes the sparse path identical to dense causal."""
+    B, S, Hq, Hkv, d = 1, 700, 4, 2, 128
+    say("sparse full window == dense")
+    _, (qd, kd, vd) = bf16_tensors(B, S, Hq, Hkv, d, seed=31)
+    o_d, l_d = _run_prefill(fa, qd, kd, vd, torch.float32, 0)
+    o_s, l_s = _run_prefill(fa, qd, kd, vd, torch.float32, 1, sink=128, window=64 * 11)
+    assert torch.equal(o_d, o_s) and torch.equal(l_d, l_s)
+
+
+def test_prefill_deterministic(fa):
+    B, S, Hq, Hkv, d = 1, 1500, 8, 2, 128
+    say("determinism")
+    _, (qd, kd, vd) = bf16_tensors(B, S, Hq, Hkv, d, seed=32)
+    for mode in (0, 1):
+        a, la = _run_prefill(fa, qd, kd, vd, torch.float32, mode, sink=128, window=256)
+        b, lb = _run_prefill(fa, qd, kd, vd, torch.float32, mode, sink=128, window=256)
+        assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_gqa_matches_repeated_kv(fa):
+    B, S, Hq, Hkv, d = 1, 333, 8, 2, 128
+    say("gqa == mha repeated")
+    _, (qd, kd, vd) = bf16_tensors(B, S, Hq, Hkv, d, seed=33)
+    kr = kd.repeat_interleave(Hq // Hkv, dim=2).contiguous()
+    vr = vd.repeat_interleave(Hq // Hkv, dim=2).contiguous()
+    for mode in (0, 1):
+        a, _ = _run_prefill(fa, qd, kd, vd, torch.float32, mode, sink=64, window=128)
+        b, _ = _run_prefill(fa, qd, kr, vr, torch.float32, mode, sink=64, window=128)
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------- full-size layers, sampled rows
+def _sampled_check(fa, B, S, Hq, Hkv, d, mode, sink, window, seed, n_random, out_dtype=torch.float32):
+    say("full size", B, S, Hq, Hkv, d, "mode", mode, "out", out_dtype)
+    qd = synth.torch_normal((B, S, Hq, d), seed, torch.bfloat16)
+    kd = synth.torch_normal((B, S, Hkv, d), seed + 1, torch.bfloat16)
+    vd = synth.torch_normal((B, S, Hkv, d), seed + 2, torch.bfloat16)
+    o, lse = _run_prefill(fa, qd, kd, vd, out_dtype, mode, sink=sink, window=window)
+    rows = sample_rows(B, Hq, S, n_random, seed)
+    q = dev_bits_to_host(qd)
+    k = dev_bits_to_host(kd)
+    v = dev_bits_to_host(vd)
+    ref, ref_lse = oracle.attention(q, k, v, default_scale(d), causal=True, sparse=bool(mode), block=64,
+                                    sink_tokens=sink, window_tokens=window, rows=rows)
+    o_h = o.float().cpu().numpy()
+    l_h = lse.cpu().numpy()
+    got = np.stack([o_h[b, i, h] for b, h, i in rows])
+    got_lse = np.array([l_h[b, h, i] for b, h, i in rows])
+    check_close(got, ref, f"S={S} mode {mode}", out_bf16=out_dtype == torch.bfloat16)
+    check_lse(got_lse, ref_lse, f"S={S} lse")
+    # every output finite (no row left unnormalised)
+    assert torch.isfinite(o).all()
+    del qd, kd, vd, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_llama_layer_dense_s8192_sampled(fa):
+    """One Llama-3.1-8B-shaped layer: batch 1, seq 8192, 32 query heads, 8 KV heads, head_dim 128."""
+    _sampled_check(fa, 1, 8192, 32, 8, 128, 0, 128, 2048, seed=1002, n_random=400)
+
+
+def test_llama_layer_dense_s8192_bf16_out(fa):
+    _sampled_check(fa, 1, 8192, 32, 8, 128, 0, 128, 2048, seed=1012, n_random=200, out_dtype=torch.bfloat16)
+
+
+def test_layer_sparse_s65536_sampled(fa):
+    """Same layer at seq 65536, block-sparse: block 64, sink 128, window 2048 (32 blocks)."""
+    _sampled_check(fa, 1, 65536, 32, 8, 128, 1, 128, 2048, seed=1003, n_random=400)
+
+
+def test_routed_stack_layers_s131072_sampled(fa):
+    """Qwen3-8B-shaped stack at seq 131072 through the per-layer dispatcher: one dense and one
+    sparse layer (the dispatcher is what runs all 36 layers in the benchmark)."""
+    S, Hq, Hkv, d = 131072, 32, 8, 128
+    say("routed stack S=131072")
+    modes = np.array([0, 1], np.int32)
+    qs, ks, vs, os_, ls = [], [], [], [], []
+    for l in range(2):
+        qs.append(synth.torch_normal((1, S, Hq, d), 1004 + 10 * l, torch.bfloat16))
+        ks.append(synth.torch_normal((1, S, Hkv, d), 1005 + 10 * l, torch.bfloat16))
+        vs.append(synth.torch_normal((1, S, Hkv, d), 1006 + 10 * l, torch.bfloat16))
+        os_.append(torch.empty((1, S, Hq, d), dtype=torch.float32, device=DEV))
+        ls.append(torch.empty((1, Hq, S), dtype=torch.float32, device=DEV))
+    rp, ci = _csr_dev(fa, S, 128, 2048)
+    fa.flux_attn_prefill_layers(modes, qs, ks, vs, os_, ls, block=64, sink_tokens=128, window_tokens=2048,
+                                blk_row_ptr=rp, blk_col_idx=ci)
+    torch.cuda.synchronize()
+    for l in range(2):
+        rows = sample_rows(1, Hq, S, 64, seed=77 + l)
+        rows = rows[np.isin(rows[:, 2], [0, 1, 64, 2048, 2049, S // 2, S - 65, S - 1]) | (np.arange(len(rows)) % 7 == 0)]
+        ref, ref_lse = oracle.attention(dev_bits_to_host(qs[l]), dev_bits_to_host(ks[l]), dev_bits_to_host(vs[l]),
+                                        default_scale(d), causal=True, sparse=bool(modes[l]), block=64,
+                                        sink_tokens=128, window_tokens=2048, rows=rows)
+        o_h = os_[l].cpu().numpy()
+        l_h = ls[l].cpu().numpy()
+        check_close(np.stack([o_h[b, i, h] for b, h, i in rows]), ref, f"stack layer {l}")
+        check_lse(np.array([l_h[b, h, i] for b, h, i in rows]), ref_lse, f"stack layer {l} lse")
+    del qs, ks, vs, os_, ls
+    torch.cuda.empty_cache()
