@@ -93,9 +93,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", dest="legs", action="store_true", default=True)
-    ap.add_argument("--no-legs", dest="legs", action="store_false")
+    ap.add_argument("--legs", default="sparse,decode",
+                    help="comma list of secondary legs: sparse, dense64k, decode, stack (or 'none')")
+    ap.add_argument("--no-legs", dest="legs", action="store_const", const="none")
+    ap.add_argument("--no-headline", dest="headline", action="store_false", default=True,
+                    help="skip the headline step (profiling a single leg)")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run one plain device-to-device copy of MIB MiB (HBM counter calibration)")
     ap.add_argument("--stack", action="store_true", help="also time the 36-layer routed stack at seq 131072")
+    ap.add_argument("--steps-leg", type=int, default=20, help="timed repetitions per secondary leg")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false", default=True)
     args = ap.parse_args()
 
@@ -111,6 +117,32 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calib:
+        n = args.copy_calib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n}), flush=True)
+        return
+    legs_sel = set() if args.legs == "none" else set(x for x in args.legs.split(",") if x)
+    if args.stack:
+        legs_sel.add("stack")
+    result = {}
+    if args.headline:
+        result = headline(args, fa, synth, torch, dev)
+    legs = run_legs(fa, synth, torch, dev, legs_sel, args.steps_leg)
+    if legs:
+        result["legs"] = legs
+        if "decode_dense_L262144" in legs:
+            dd = legs["decode_dense_L262144"]
+            result["decode"] = {"GB/s": dd["GB/s"], "tok/s": dd["tok/s"], "frac_hbm": dd["frac"]}
+    if args.cpu_baseline and args.headline:
+        result["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(result), flush=True)
+
+
+def headline(args, fa, synth, torch, dev):
 
     # ---------------------------------------------------------------- headline: routed dense layer, S=8192
     B, S, Hq, Hkv, d = 1, 8192, 32, 8, 128
@@ -125,11 +157,13 @@ def main():
     b_head[0, 0] += 8.0   # the workload is dense causal: the head bias makes the router select index 0
     modes_dev = torch.empty(1, dtype=torch.int32, device=dev)
     modes_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
+    route_ws = torch.empty(fa.flux_route_workspace_size(1, Hq, d, 256), dtype=torch.uint8, device=dev)
     timer = KernelTimer()
     useful = 4.0 * B * Hq * d * causal_pairs(S)
 
     def step(record=False):
-        fa.flux_route_layers([q[0]], w_enc, b_enc, w_head, b_head, modes_dev, None, pool_tokens=100)
+        fa.flux_route_layers([q[0]], w_enc, b_enc, w_head, b_head, modes_dev, None, workspace=route_ws,
+                             pool_tokens=100)
         modes_host.copy_(modes_dev, non_blocking=True)
         torch.cuda.current_stream().synchronize()          # the one D2H sync per request
         m = modes_host.numpy().copy()
@@ -176,74 +210,68 @@ def main():
     }
     del q, k, v, o
     torch.cuda.empty_cache()
+    return result
 
+
+def run_legs(fa, synth, torch, dev, sel, reps):
     legs = {}
-    if args.legs:
-        legs.update(run_legs(fa, synth, torch, dev))
-    if args.stack:
+    if {"sparse", "dense64k"} & sel:
+        # ---- block-sparse prefill, seq 65536 (and optionally dense at the same length)
+        B, S, Hq, Hkv, d = 1, 65536, 32, 8, 128
+        log("leg: prefill S=65536")
+        q = synth.torch_normal((B, S, Hq, d), 1102, torch.bfloat16)
+        k = synth.torch_normal((B, S, Hkv, d), 1103, torch.bfloat16)
+        v = synth.torch_normal((B, S, Hkv, d), 1104, torch.bfloat16)
+        o = torch.empty((B, S, Hq, d), dtype=torch.bfloat16, device=dev)
+        rp, ci = fa.flux_build_block_mask(S, S, 64, 128, 2048, 1, fa.FLUX_MODE_SPARSE)
+        rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+        if "sparse" in sel:
+            useful = 4.0 * B * Hq * d * csr_pairs(rp, ci, S)
+            call = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_SPARSE,
+                                                sink_tokens=128, window_tokens=2048, blk_row_ptr=rpd, blk_col_idx=cid)
+            ms = time_steps(call, reps, 3)
+            legs["sparse_prefill_s65536"] = {"ms": round(ms, 4), "useful_flops": useful, "nnz_blocks": int(len(ci)),
+                                             "TFLOP/s": round(useful / ms / 1e9, 2),
+                                             "frac": round(useful / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        if "dense64k" in sel:
+            calld = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_DENSE)
+            msd = time_steps(calld, 3, 1)
+            usefuld = 4.0 * B * Hq * d * causal_pairs(S)
+            legs["dense_prefill_s65536"] = {"ms": round(msd, 4), "TFLOP/s": round(usefuld / msd / 1e9, 2),
+                                            "frac": round(usefuld / msd / 1e9 / PEAK_BF16_TFLOPS, 4)}
+            if "sparse_prefill_s65536" in legs:
+                legs["dense_prefill_s65536"]["sparse_speedup"] = round(msd / legs["sparse_prefill_s65536"]["ms"], 3)
+        del q, k, v, o
+        torch.cuda.empty_cache()
+
+    if "decode" in sel:
+        # ---- decode, B=8, L=262144
+        B, L, Hq, Hkv, d = 8, 262144, 32, 8, 128
+        log("leg: decode L=262144")
+        qd = synth.torch_normal((B, Hq, d), 1202, torch.bfloat16)
+        kc = synth.torch_normal((B, L, Hkv, d), 1203, torch.bfloat16)
+        vc = synth.torch_normal((B, L, Hkv, d), 1204, torch.bfloat16)
+        od = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+        for mode, name in ((fa.FLUX_MODE_DENSE, "decode_dense_L262144"),
+                           (fa.FLUX_MODE_SPARSE, "decode_sparse_L262144")):
+            wsb = fa.flux_decode_workspace_size(B, Hq, Hkv, L, d, mode, 64, 128, 2048, 0)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+            n_keys = L if mode == fa.FLUX_MODE_DENSE else 128 + 2048
+            nbytes = B * Hkv * n_keys * d * 2 * 2 + 2 * B * Hq * d * 2
+            timer = KernelTimer()
+            call = lambda: fa.flux_attn_decode(qd, kc, vc, od, None, mode=mode, sink_tokens=128, window_tokens=2048,
+                                               workspace=ws)
+            ms = time_steps(call, reps if mode == 0 else 5 * reps, 3)
+            gbs = nbytes / ms / 1e6
+            legs[name] = {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
+                          "frac": round(gbs / PEAK_HBM_GBS, 4), "tok/s": round(B / (ms * 1e-3), 1)}
+        legs["decode_sparse_L262144"]["speedup_vs_dense"] = round(
+            legs["decode_dense_L262144"]["ms"] / legs["decode_sparse_L262144"]["ms"], 2)
+        del qd, kc, vc, od
+        torch.cuda.empty_cache()
+
+    if "stack" in sel:
         legs["stack_s131072"] = run_stack(fa, synth, torch, dev)
-    if legs:
-        result["legs"] = legs
-        if "decode_dense_L262144" in legs:
-            dd = legs["decode_dense_L262144"]
-            result["decode"] = {"GB/s": dd["GB/s"], "tok/s": dd["tok/s"], "frac_hbm": dd["frac"]}
-
-    if args.cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(synth)
-    print(json.dumps(result), flush=True)
-
-
-def run_legs(fa, synth, torch, dev):
-    legs = {}
-    # ---- block-sparse prefill, seq 65536
-    B, S, Hq, Hkv, d = 1, 65536, 32, 8, 128
-    log("leg: sparse prefill S=65536")
-    q = synth.torch_normal((B, S, Hq, d), 1102, torch.bfloat16)
-    k = synth.torch_normal((B, S, Hkv, d), 1103, torch.bfloat16)
-    v = synth.torch_normal((B, S, Hkv, d), 1104, torch.bfloat16)
-    o = torch.empty((B, S, Hq, d), dtype=torch.bfloat16, device=dev)
-    rp, ci = fa.flux_build_block_mask(S, S, 64, 128, 2048, 1, fa.FLUX_MODE_SPARSE)
-    rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
-    useful = 4.0 * B * Hq * d * csr_pairs(rp, ci, S)
-    call = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_SPARSE, sink_tokens=128,
-                                        window_tokens=2048, blk_row_ptr=rpd, blk_col_idx=cid)
-    ms = time_steps(call, 20, 3)
-    legs["sparse_prefill_s65536"] = {"ms": round(ms, 4), "useful_flops": useful, "nnz_blocks": int(len(ci)),
-                                     "TFLOP/s": round(useful / ms / 1e9, 2),
-                                     "frac": round(useful / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
-    # dense at the same length, for the sparse-vs-full ratio of the method
-    log("leg: dense prefill S=65536")
-    calld = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_DENSE)
-    msd = time_steps(calld, 3, 1)
-    usefuld = 4.0 * B * Hq * d * causal_pairs(S)
-    legs["dense_prefill_s65536"] = {"ms": round(msd, 4), "TFLOP/s": round(usefuld / msd / 1e9, 2),
-                                    "frac": round(usefuld / msd / 1e9 / PEAK_BF16_TFLOPS, 4),
-                                    "sparse_speedup": round(msd / ms, 3)}
-    del q, k, v, o
-    torch.cuda.empty_cache()
-
-    # ---- decode, B=8, L=262144
-    B, L, Hq, Hkv, d = 8, 262144, 32, 8, 128
-    log("leg: decode L=262144")
-    qd = synth.torch_normal((B, Hq, d), 1202, torch.bfloat16)
-    kc = synth.torch_normal((B, L, Hkv, d), 1203, torch.bfloat16)
-    vc = synth.torch_normal((B, L, Hkv, d), 1204, torch.bfloat16)
-    od = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
-    for mode, name in ((fa.FLUX_MODE_DENSE, "decode_dense_L262144"), (fa.FLUX_MODE_SPARSE, "decode_sparse_L262144")):
-        wsb = fa.flux_decode_workspace_size(B, Hq, Hkv, L, d, mode, 64, 128, 2048, 0)
-        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-        n_keys = L if mode == fa.FLUX_MODE_DENSE else 128 + 2048
-        nbytes = B * Hkv * n_keys * d * 2 * 2 + 2 * B * Hq * d * 2
-        call = lambda: fa.flux_attn_decode(qd, kc, vc, od, None, mode=mode, sink_tokens=128, window_tokens=2048,
-                                           workspace=ws)
-        ms = time_steps(call, 20 if mode == 0 else 100, 3)
-        gbs = nbytes / ms / 1e6
-        legs[name] = {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
-                      "tok/s": round(B / (ms * 1e-3), 1)}
-    legs["decode_sparse_L262144"]["speedup_vs_dense"] = round(
-        legs["decode_dense_L262144"]["ms"] / legs["decode_sparse_L262144"]["ms"], 2)
-    del qd, kc, vc, od
-    torch.cuda.empty_cache()
     return legs
 
 
@@ -263,10 +291,12 @@ def run_stack(fa, synth, torch, dev):
     rp, ci = fa.flux_build_block_mask(S, S, 64, 128, 2048, 1, fa.FLUX_MODE_SPARSE)
     rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
     modes_dev = torch.empty(L, dtype=torch.int32, device=dev)
+    route_ws = torch.empty(fa.flux_route_workspace_size(L, Hq, d, 256), dtype=torch.uint8, device=dev)
     useful = 4.0 * Hq * d * (12 * causal_pairs(S) + 24 * csr_pairs(rp, ci, S))
 
     def step():
-        fa.flux_route_layers([x[0] for x in qs], w_enc, b_enc, w_head, b_head, modes_dev, None, pool_tokens=100)
+        fa.flux_route_layers([x[0] for x in qs], w_enc, b_enc, w_head, b_head, modes_dev, None, workspace=route_ws,
+                             pool_tokens=100)
         m = modes_dev.cpu().numpy()
         fa.flux_attn_prefill_layers(m, qs, ks, vs, [o] * L, None, block=64, sink_tokens=128, window_tokens=2048,
                                     blk_row_ptr=rpd, blk_col_idx=cid)

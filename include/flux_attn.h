@@ -185,6 +185,13 @@ int flux_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
                      int32_t num_splits, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * flux_route_workspace_size -- bytes of workspace flux_route_layers needs:
+ * the pooled features [n_layers, hq*head_dim] and the encoder activations
+ * [n_layers, hidden], float32, each part 256-byte aligned.  0 if invalid.
+ */
+size_t flux_route_workspace_size(int32_t n_layers, int32_t hq, int32_t head_dim, int32_t hidden);
+
+/*
  * flux_route_layers -- the layer router ([FA] router paragraphs).
  *
  * For each layer l (xQ = q_layers[l], one sequence, [seq, hq, head_dim]):
@@ -198,14 +205,16 @@ int flux_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
  * w_enc [n_layers, hidden, hq*head_dim], b_enc [n_layers, hidden],
  * w_head [n_layers, 2, hidden], b_head [n_layers, 2]: device float32.
  * logits_out [n_layers, 2] device float32 (may be NULL); modes_out
- * [n_layers] device int32.  Copying modes to the host is the caller's one
- * device-to-host synchronization per request.
- * Supported: hq*head_dim <= 8192, hidden <= 1024, pool_tokens >= 1.
+ * [n_layers] device int32.  workspace: device, 256-byte aligned, at least
+ * flux_route_workspace_size(...) bytes.  Copying modes to the host is the
+ * caller's one device-to-host synchronization per request.
+ * Supported: hq*head_dim a multiple of 8, pool_tokens >= 1.
  */
 int flux_route_layers(const void* const* q_layers, int32_t n_layers, int64_t seq, int32_t hq,
                       int32_t head_dim, int32_t in_dtype, int32_t pool_tokens, const float* w_enc,
                       const float* b_enc, int32_t hidden, const float* w_head, const float* b_head,
-                      float* logits_out, int32_t* modes_out, void* hip_stream);
+                      float* logits_out, int32_t* modes_out, void* workspace,
+                      size_t workspace_bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ import numpy as np
 __all__ = [
     "FluxError", "lib", "status_string", "last_error_detail", "flux_version",
     "flux_build_block_mask", "flux_attn_prefill", "flux_attn_prefill_layers",
-    "flux_decode_workspace_size", "flux_attn_decode", "flux_route_layers",
+    "flux_decode_workspace_size", "flux_attn_decode", "flux_route_workspace_size", "flux_route_layers",
     "FLUX_OK", "FLUX_ERR_INVALID_ARG", "FLUX_ERR_UNSUPPORTED", "FLUX_ERR_CAPACITY", "FLUX_ERR_WORKSPACE",
     "FLUX_ERR_HIP", "FLUX_DTYPE_BF16", "FLUX_DTYPE_F32", "FLUX_MODE_DENSE", "FLUX_MODE_SPARSE",
     "EXPORTED_SYMBOLS",
@@ -31,7 +31,7 @@ FLUX_MODE_DENSE, FLUX_MODE_SPARSE = 0, 1
 EXPORTED_SYMBOLS = (
     "flux_status_string", "flux_last_error_detail", "flux_version", "flux_build_block_mask",
     "flux_attn_prefill", "flux_attn_prefill_layers", "flux_decode_workspace_size", "flux_attn_decode",
-    "flux_route_layers",
+    "flux_route_workspace_size", "flux_route_layers",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,7 +39,7 @@ LIB_PATH = os.path.join(_HERE, "libflux_attn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m long_context_attention_tiled_amd.build` "
+        f"{LIB_PATH} is not built; run `python long_context_attention_tiled_amd/build.py` "
         "(hipcc for gfx950).  There is no CPU fallback.")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -66,7 +66,10 @@ _lib.flux_decode_workspace_size.restype = _sz
 _lib.flux_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _f32,
                                   _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
 _lib.flux_attn_decode.restype = ctypes.c_int
-_lib.flux_route_layers.argtypes = [_pp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+_lib.flux_route_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
+_lib.flux_route_workspace_size.restype = _sz
+_lib.flux_route_layers.argtypes = [_pp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
+                                   _sz, _vp]
 _lib.flux_route_layers.restype = ctypes.c_int
 
 
@@ -210,13 +213,23 @@ def flux_attn_decode(q, k_cache, v_cache, o, lse=None, *, kv_len: int | None = N
            "flux_attn_decode")
 
 
-def flux_route_layers(q_layers, w_enc, b_enc, w_head, b_head, modes_out, logits_out=None, *, pool_tokens: int = 100,
-                      stream=None):
-    """q_layers: list of device tensors [S,Hq,d]; weights device float32; modes_out device int32 [L]."""
+def flux_route_workspace_size(n_layers, hq, head_dim, hidden) -> int:
+    return int(_lib.flux_route_workspace_size(n_layers, hq, head_dim, hidden))
+
+
+def flux_route_layers(q_layers, w_enc, b_enc, w_head, b_head, modes_out, logits_out=None, *, workspace=None,
+                      pool_tokens: int = 100, stream=None):
+    """q_layers: list of device tensors [S,Hq,d]; weights device float32; modes_out device int32 [L];
+    workspace: uint8 device tensor of flux_route_workspace_size(...) bytes (allocated here if None)."""
     L = len(q_layers)
     S, Hq, d = q_layers[0].shape
     hidden = w_enc.shape[1]
+    if workspace is None:
+        import torch
+        workspace = torch.empty(flux_route_workspace_size(L, Hq, d, hidden), dtype=torch.uint8,
+                                device=q_layers[0].device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     pq, _keep = _ptr_array(q_layers)
     _check(_lib.flux_route_layers(pq, L, S, Hq, d, _dtype_code(q_layers[0]), pool_tokens, _ptr(w_enc), _ptr(b_enc),
                                   hidden, _ptr(w_head), _ptr(b_head), _ptr(logits_out), _ptr(modes_out),
-                                  _stream(stream)), "flux_route_layers")
+                                  _ptr(workspace), ws_bytes, _stream(stream)), "flux_route_layers")

@@ -1,6 +1,8 @@
 """Build libflux_attn.so (HIP kernels for gfx950 + the C-ABI host layer) in-tree.
 
-    python -m long_context_attention_tiled_amd.build
+    python long_context_attention_tiled_amd/build.py
+
+(run it as a script: importing the package would load the library being rebuilt)
 
 Every source under csrc/ is compiled by hipcc for gfx950 and linked into
 long_context_attention_tiled_amd/libflux_attn.so.  Packed fp32 instructions are

@@ -130,6 +130,8 @@ int check_prefill(const void* q, const void* k, const void* v, void* o, float* l
         return fail(FLUX_ERR_UNSUPPORTED, "float32 input requires float32 output");
     if (batch * (int64_t)hq * ceil_div(seq, 64) > INT32_MAX)
         return fail(FLUX_ERR_UNSUPPORTED, "batch * hq * ceil(seq/64) exceeds the launch grid");
+    if (seq * (int64_t)std::max(hq, hkv) * head_dim > INT32_MAX)
+        return fail(FLUX_ERR_UNSUPPORTED, "seq * max(hq, hkv) * head_dim must stay below 2^31 elements");
     if (ms.sparse) {
         if (!rp || !ci) return fail(FLUX_ERR_INVALID_ARG, "sparse mode needs blk_row_ptr and blk_col_idx");
         int64_t want = mask_nnz(ms);
@@ -377,10 +379,16 @@ int flux_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
     return hip_status(e, "decode launch");
 }
 
+size_t flux_route_workspace_size(int32_t n_layers, int32_t hq, int32_t head_dim, int32_t hidden) {
+    if (n_layers < 1 || hq < 1 || head_dim < 1 || hidden < 1) return 0;
+    const size_t nf = (size_t)hq * head_dim;
+    return align256((size_t)n_layers * nf * sizeof(float)) + align256((size_t)n_layers * hidden * sizeof(float));
+}
+
 int flux_route_layers(const void* const* q_layers, int32_t n_layers, int64_t seq, int32_t hq, int32_t head_dim,
                       int32_t in_dtype, int32_t pool_tokens, const float* w_enc, const float* b_enc, int32_t hidden,
                       const float* w_head, const float* b_head, float* logits_out, int32_t* modes_out,
-                      void* hip_stream) {
+                      void* workspace, size_t workspace_bytes, void* hip_stream) {
     if (!q_layers || n_layers < 1) return fail(FLUX_ERR_INVALID_ARG, "q_layers must hold n_layers >= 1 pointers");
     if (!w_enc || !b_enc || !w_head || !b_head || !modes_out)
         return fail(FLUX_ERR_INVALID_ARG, "weights and modes_out must be non-NULL");
@@ -392,10 +400,18 @@ int flux_route_layers(const void* const* q_layers, int32_t n_layers, int64_t seq
         return fail(FLUX_ERR_INVALID_ARG, "seq, hq, head_dim, hidden and pool_tokens must be >= 1");
     if (in_dtype != FLUX_DTYPE_BF16 && in_dtype != FLUX_DTYPE_F32)
         return fail(FLUX_ERR_INVALID_ARG, "in_dtype must be FLUX_DTYPE_BF16 or FLUX_DTYPE_F32");
-    int64_t nf = (int64_t)hq * head_dim;
-    if (nf > 8192 || nf % 8 != 0) return fail(FLUX_ERR_UNSUPPORTED, "hq*head_dim must be a multiple of 8 and <= 8192");
-    if (hidden > 1024) return fail(FLUX_ERR_UNSUPPORTED, "hidden must be <= 1024");
+    const int64_t nf = (int64_t)hq * head_dim;
+    if (nf % 8 != 0 || nf > (1 << 24)) return fail(FLUX_ERR_UNSUPPORTED, "hq*head_dim must be a multiple of 8");
     if (!aligned16(w_enc)) return fail(FLUX_ERR_INVALID_ARG, "w_enc must be 16-byte aligned");
+    const size_t need = flux_route_workspace_size(n_layers, hq, head_dim, hidden);
+    if (!workspace || workspace_bytes < need)
+        return fail(FLUX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(FLUX_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    float* pooled = reinterpret_cast<float*>(workspace);
+    float* z = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                        align256((size_t)n_layers * nf * sizeof(float)));
     for (int32_t l0 = 0; l0 < n_layers; l0 += flux::kMaxRouteLayers) {
         flux::RouteArgs a;
         a.n_layers = std::min(n_layers - l0, flux::kMaxRouteLayers);
@@ -412,6 +428,8 @@ int flux_route_layers(const void* const* q_layers, int32_t n_layers, int64_t seq
         a.b_head = b_head;
         a.logits = logits_out;
         a.modes = modes_out;
+        a.pooled = pooled;
+        a.z = z;
         hipError_t e = flux::launch_route(a, as_stream(hip_stream));
         if (e == hipSuccess) e = hipGetLastError();
         if (e != hipSuccess) return hip_status(e, "router launch");

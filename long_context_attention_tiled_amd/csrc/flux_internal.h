@@ -72,6 +72,8 @@ struct RouteArgs {
     const float* b_head;
     float* logits;         // nullable
     int32_t* modes;
+    float* pooled;         // workspace [L_total, n_feat]
+    float* z;              // workspace [L_total, hidden]
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);

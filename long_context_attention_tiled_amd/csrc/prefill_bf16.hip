@@ -37,6 +37,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBR = 128;       // query rows per workgroup
 constexpr int kBC = 64;        // keys per tile
@@ -66,35 +68,32 @@ __device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1)
 
 template <int D>
 struct TileRegs {
-    uint4 k[Lay<D>::K_LOADS];
-    uint2 v[Lay<D>::V_ROUNDS][4];
+    u32x4 k[Lay<D>::K_LOADS];
+    u32x2 v[Lay<D>::V_ROUNDS][4];
 };
 
+// Global -> registers for key tile kb.  Keys past the end of the sequence are
+// clamped to the last row (no branches); their scores are masked to -inf and
+// their probabilities are 0, so the duplicated rows never contribute.
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs<D>& r, const u16* __restrict__ kg, const u16* __restrict__ vg,
-                                          int64_t row_stride, int kb, int64_t seq, int tid) {
+                                          uint32_t row_stride, int kb, int last_key, int tid) {
     using L = Lay<D>;
-    const int64_t key0 = (int64_t)kb * kBC;
+    const int key0 = kb * kBC;
 #pragma unroll
     for (int i = 0; i < L::K_LOADS; ++i) {
-        int idx = tid + i * kThreads;
-        int row = idx / L::KCH, ch = idx % L::KCH;
-        int64_t key = key0 + row;
-        if ((uint64_t)key < (uint64_t)seq)
-            r.k[i] = *reinterpret_cast<const uint4*>(kg + key * row_stride + ch * 8);
-        else
-            r.k[i] = make_uint4(0, 0, 0, 0);
+        const int idx = tid + i * kThreads;
+        const int row = idx / L::KCH, ch = idx % L::KCH;
+        const uint32_t key = (uint32_t)min(key0 + row, last_key);
+        r.k[i] = *reinterpret_cast<const u32x4*>(kg + key * row_stride + ch * 8);
     }
     const int dg = tid % L::VG, kq = tid / L::VG;
 #pragma unroll
     for (int rr = 0; rr < L::V_ROUNDS; ++rr) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            int64_t key = key0 + rr * 4 * L::V_KQ + 4 * kq + e;
-            if ((uint64_t)key < (uint64_t)seq)
-                r.v[rr][e] = *reinterpret_cast<const uint2*>(vg + key * row_stride + dg * 4);
-            else
-                r.v[rr][e] = make_uint2(0, 0);
+            const uint32_t key = (uint32_t)min(key0 + rr * 4 * L::V_KQ + 4 * kq + e, last_key);
+            r.v[rr][e] = *reinterpret_cast<const u32x2*>(vg + key * row_stride + dg * 4);
         }
     }
 }
@@ -106,15 +105,15 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, u16* ks, u16* v
     for (int i = 0; i < L::K_LOADS; ++i) {
         int idx = tid + i * kThreads;
         int row = idx / L::KCH, ch = idx % L::KCH;
-        *reinterpret_cast<uint4*>(ks + row * L::KS + ch * 8) = r.k[i];
+        *reinterpret_cast<u32x4*>(ks + row * L::KS + ch * 8) = r.k[i];
     }
     const int dg = tid % L::VG, kq = tid / L::VG;
 #pragma unroll
     for (int rr = 0; rr < L::V_ROUNDS; ++rr) {
         const int pos = vt_pos(rr * 4 * L::V_KQ + 4 * kq);
-        const uint2 x0 = r.v[rr][0], x1 = r.v[rr][1], x2 = r.v[rr][2], x3 = r.v[rr][3];
+        const u32x2 x0 = r.v[rr][0], x1 = r.v[rr][1], x2 = r.v[rr][2], x3 = r.v[rr][3];
         // 4 keys x 4 d  ->  4 d x 4 keys (bf16 halves regrouped)
-        uint2 o0, o1, o2, o3;
+        u32x2 o0, o1, o2, o3;
         o0.x = (x0.x & 0xffffu) | (x1.x << 16);
         o0.y = (x2.x & 0xffffu) | (x3.x << 16);
         o1.x = (x0.x >> 16) | (x1.x & 0xffff0000u);
@@ -124,10 +123,10 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, u16* ks, u16* v
         o3.x = (x0.y >> 16) | (x1.y & 0xffff0000u);
         o3.y = (x2.y >> 16) | (x3.y & 0xffff0000u);
         u16* base = vts + (4 * dg) * L::VS + pos;
-        *reinterpret_cast<uint2*>(base) = o0;
-        *reinterpret_cast<uint2*>(base + L::VS) = o1;
-        *reinterpret_cast<uint2*>(base + 2 * L::VS) = o2;
-        *reinterpret_cast<uint2*>(base + 3 * L::VS) = o3;
+        *reinterpret_cast<u32x2*>(base) = o0;
+        *reinterpret_cast<u32x2*>(base + L::VS) = o1;
+        *reinterpret_cast<u32x2*>(base + 2 * L::VS) = o2;
+        *reinterpret_cast<u32x2*>(base + 3 * L::VS) = o3;
     }
 }
 
@@ -219,15 +218,17 @@ prefill_bf16_kernel(PrefillArgs a) {
     const int h = g * G + j;
     const int qt = (MODE == kDenseCausal) ? nqt - 1 - qt_rank : qt_rank;
 
-    const int64_t q_row_stride = (int64_t)a.hq * D;
-    const int64_t kv_row_stride = (int64_t)a.hkv * D;
+    const uint32_t q_row_stride = (uint32_t)(a.hq * D);
+    const uint32_t kv_row_stride = (uint32_t)(a.hkv * D);
+    const int seq = (int)a.seq;          // the host guarantees seq * max(hq, hkv) * d < 2^31
+    const int last_key = seq - 1;
     const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * D;
     const u16* kg = reinterpret_cast<const u16*>(a.k) + ((int64_t)b * a.seq * a.hkv + g) * D;
     const u16* vg = reinterpret_cast<const u16*>(a.v) + ((int64_t)b * a.seq * a.hkv + g) * D;
 
     const int q0 = qt * kBR + wave * 32;       // first query row of this wave
     const int qpos = q0 + n;                   // this lane's query row
-    const bool wave_live = q0 < a.seq;
+    const bool wave_live = q0 < seq;
     const bool wave_in_qb1 = wave >= 2;
     const int my_qb = qt * 2 + (wave_in_qb1 ? 1 : 0);
 
@@ -235,11 +236,12 @@ prefill_bf16_kernel(PrefillArgs a) {
     bf16x8 qreg[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        if (qpos < a.seq)
-            qreg[c] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)qpos * q_row_stride + 16 * c + 8 * hh);
-        else
-            qreg[c] = bf16x8{};
+        const uint32_t qrow = (uint32_t)min(qpos, last_key);
+        qreg[c] = *reinterpret_cast<const bf16x8*>(qg + qrow * q_row_stride + 16 * c + 8 * hh);
     }
+    // wait for Q here: otherwise the wait for Q lands inside the tile loop, where it also
+    // waits for the next tile's prefetch (vmcnt counts every outstanding load)
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
 
     f32x16 oacc[NM];
 #pragma unroll
@@ -254,7 +256,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     bool have = walk.next(kb, in0, in1);
     TileRegs<D> regs;
     if (have) {
-        load_tile<D>(regs, kg, vg, kv_row_stride, kb, a.seq, tid);
+        load_tile<D>(regs, kg, vg, kv_row_stride, kb, last_key, tid);
         store_tile<D>(regs, smem, smem + L::K_ELEMS, tid);
     }
     __syncthreads();
@@ -263,36 +265,32 @@ prefill_bf16_kernel(PrefillArgs a) {
         int kb_n;
         bool in0_n, in1_n;
         const bool have_n = walk.next(kb_n, in0_n, in1_n);
-        if (have_n) load_tile<D>(regs, kg, vg, kv_row_stride, kb_n, a.seq, tid);
+        if (have_n) load_tile<D>(regs, kg, vg, kv_row_stride, kb_n, last_key, tid);
 
         const bool mine = wave_live && (wave_in_qb1 ? in1 : in0);
         if (mine) {
             const u16* ks = smem + buf * L::STAGE;
             const u16* vts = ks + L::K_ELEMS;
-            // ---- S^T = K Q^T : two 32-key halves
-            f32x16 sacc[2];
+            // ---- S^T = K Q^T : two 32-key halves, two independent accumulation chains
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+            const u16* krow = ks + n * L::KS + 8 * hh;
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                f32x16 acc = f32x16{};
-                const u16* krow = ks + (32 * kh + n) * L::KS + 8 * hh;
-#pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    bf16x8 av = *reinterpret_cast<const bf16x8*>(krow + 16 * c);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], acc, 0, 0, 0);
-                }
-                sacc[kh] = acc;
+            for (int c = 0; c < NC; ++c) {
+                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(krow + 16 * c);
+                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(krow + 32 * L::KS + 16 * c);
+                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[c], sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[c], sacc[1], 0, 0, 0);
             }
             // lane holds S[qpos][key], key = kb*64 + 32kh + 8(r/4) + 4hh + (r%4)
-            const bool need_mask = (MODE != kDenseFull && kb >= my_qb) || (int64_t)(kb + 1) * kBC > a.seq;
+            const bool need_mask = (MODE != kDenseFull && kb >= my_qb) || (kb + 1) * kBC > seq;
             if (need_mask) {
+                // key = kb*64 + 32kh + 8(r/4) + 4hh + r%4 is masked when key > lim
+                const int lim = (MODE != kDenseFull ? min(qpos, last_key) : last_key) - (kb * kBC + 4 * hh);
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kb * kBC + 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        const bool off = key >= a.seq || (MODE != kDenseFull && key > qpos);
-                        if (off) sacc[kh][r] = -INFINITY;
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * kh + 8 * (r >> 2) + (r & 3) > lim) sacc[kh][r] = -INFINITY;
             }
             float mx = sacc[0][0];
 #pragma unroll
@@ -353,9 +351,9 @@ prefill_bf16_kernel(PrefillArgs a) {
 
     // ---- epilogue: O = O^T / l, lane holds O[qpos][32mt + 8(r/4) + 4hh + r%4]
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (!wave_live || qpos >= a.seq) return;
+    if (!wave_live || qpos >= seq) return;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const int64_t orow = ((int64_t)b * a.seq + qpos) * a.hq + h;
+    const int64_t orow = ((int64_t)b * seq + qpos) * a.hq + h;
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt)
 #pragma unroll

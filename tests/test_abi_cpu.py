@@ -212,20 +212,28 @@ def test_decode_validation(fa):
     assert _decode(fa, ws=FAKE + 64) == E                   # workspace alignment
 
 
+def test_route_workspace_size(fa):
+    align = lambda x: (x + 255) // 256 * 256
+    assert fa.flux_route_workspace_size(36, 32, 128, 256) == align(36 * 4096 * 4) + align(36 * 256 * 4)
+    assert fa.flux_route_workspace_size(0, 32, 128, 256) == 0
+
+
 def test_route_validation(fa):
     P = ctypes.POINTER(ctypes.c_void_p)
     ptrs = (ctypes.c_void_p * 2)(FAKE, None)
     pp = ctypes.cast(ptrs, P)
     lib = fa.lib()
-    st = lib.flux_route_layers(pp, 2, 1000, 32, 128, 0, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, None)
+    big = 1 << 30
+    st = lib.flux_route_layers(pp, 2, 1000, 32, 128, 0, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, FAKE, big, None)
     assert st == fa.FLUX_ERR_INVALID_ARG and "q_layers[1]" in fa.last_error_detail()
     ptrs2 = (ctypes.c_void_p * 1)(FAKE)
     pp2 = ctypes.cast(ptrs2, P)
-    assert lib.flux_route_layers(pp2, 1, 1000, 32, 128, 0, 100, None, FAKE, 256, FAKE, FAKE, None, FAKE,
-                                 None) == fa.FLUX_ERR_INVALID_ARG
-    assert lib.flux_route_layers(pp2, 1, 1000, 128, 128, 0, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE,
-                                 None) == fa.FLUX_ERR_UNSUPPORTED          # 16384 features
-    assert lib.flux_route_layers(pp2, 1, 1000, 32, 128, 0, 100, FAKE, FAKE, 2048, FAKE, FAKE, None, FAKE,
-                                 None) == fa.FLUX_ERR_UNSUPPORTED          # hidden > 1024
-    assert lib.flux_route_layers(pp2, 1, 1000, 32, 128, 0, 0, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE,
-                                 None) == fa.FLUX_ERR_INVALID_ARG          # pool_tokens < 1
+    call = lambda *a: lib.flux_route_layers(pp2, 1, *a, None)
+    assert call(1000, 32, 128, 0, 100, None, FAKE, 256, FAKE, FAKE, None, FAKE, FAKE, big) == fa.FLUX_ERR_INVALID_ARG
+    assert call(1000, 32, 128, 0, 0, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, FAKE, big) == fa.FLUX_ERR_INVALID_ARG
+    assert call(1000, 3, 3, 0, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, FAKE, big) == fa.FLUX_ERR_UNSUPPORTED
+    assert call(1000, 32, 128, 2, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, FAKE, big) == fa.FLUX_ERR_INVALID_ARG
+    assert call(1000, 32, 128, 0, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, None, big) == fa.FLUX_ERR_WORKSPACE
+    assert call(1000, 32, 128, 0, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, FAKE, 100) == fa.FLUX_ERR_WORKSPACE
+    assert call(1000, 32, 128, 0, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, FAKE + 16, big) == \
+        fa.FLUX_ERR_INVALID_ARG
