@@ -12,22 +12,29 @@
 // Layout of the work on CDNA4:
 //   * workgroup = 256 threads = 4 wave64s, 128 query rows of one (batch, head);
 //     each wave owns 32 query rows; key tiles are 64 keys (= one sparse block).
-//   * both contractions run on v_mfma_f32_32x32x16_bf16, computing the
-//     transposed products S^T = K Q^T and O^T = V^T P^T.  With that orientation a
-//     lane's 32x32 accumulator column is one query row, so the softmax statistics
-//     (row max, row sum, rescale factor) of a lane's outputs are lane-local: only
-//     one cross-lane step (lanes l and l^32) per tile for the max, none for O.
-//   * Q stays in registers as the B operand of S^T for the whole kernel.
-//   * K tiles are staged row-major in LDS; V tiles are staged transposed (Vt[d][key])
-//     with keys permuted inside each 16-key group so that one 16-byte LDS read gives a
-//     lane exactly the 8 keys its P registers hold.  The transpose happens in
-//     registers between the global load and the LDS store.
-//   * two LDS stages: the global loads of tile t+1 are in flight while tile t is
+//   * both contractions run on v_mfma_f32_32x32x16_bf16 in transposed form,
+//     S^T = K Q^T and O^T = V^T P^T.  A lane's 32x32 accumulator column is then one
+//     query row, so the softmax statistics (row max, row sum, rescale factor) of a
+//     lane's outputs are lane-local: one l <-> l^32 exchange per tile, none for O.
+//   * Q stays in registers (B operand of S^T) for the whole kernel.
+//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4: no
+//     staging registers, no LDS store instructions), row-major with an XOR swizzle
+//     of the 16-byte chunks of each row so that the operand reads are bank-conflict
+//     free.  The V^T operand is read with ds_read_b64_tr_b16, which transposes
+//     4x4 blocks of 16-bit elements across lanes: every lane receives 4 keys of its
+//     own d column per read, so V never needs a transposed copy.
+//   * two LDS stages: the loads of tile t+1 are in flight while tile t is
 //     computed; one barrier per tile.
-//   * exp2 with scale*log2(e) folded into one FMA; the O rescale is skipped when no
-//     row maximum grew (exact: the factor would be 1).
+//   * exp2 with scale*log2(e) folded into one FMA.  The running maximum is raised
+//     only when some row's new maximum exceeds it by more than 8 (log2 units):
+//     until then probabilities up to 2^8 are accumulated against the old
+//     reference, which is exact in exact arithmetic (the same reference scales
+//     numerator and denominator) and removes most O rescales; the newsletter's
+//     FlashAttention-4 section describes the m_new <= m_old special case of this.
+//   * the row sum is taken over the bf16-rounded P that enters P.V (v_dot2 against
+//     (1, 1)), so O is a convex combination of V rows up to fp32 accumulation.
 //   * workgroup order: kv-head groups are kept on one XCD (blockIdx % 8 picks the
-//     XCD) so the 4 query heads sharing K/V hit the same L2, and query tiles are
+//     XCD) so the query heads sharing K/V hit the same L2, and query tiles are
 //     issued longest-first for causal masks.
 #include "flux_internal.h"
 
@@ -35,99 +42,61 @@ namespace flux {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16;
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kBR = 128;       // query rows per workgroup
 constexpr int kBC = 64;        // keys per tile
 constexpr int kThreads = 256;
 constexpr float kNegBig = -1.0e30f;  // finite start value of the running max
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag the true max
 
 template <int D>
 struct Lay {
-    static constexpr int KS = D + 8;                       // K row stride in LDS (elements)
-    static constexpr int VS = kBC + 8;                     // Vt row stride in LDS (elements)
-    static constexpr int K_ELEMS = kBC * KS;
-    static constexpr int V_ELEMS = D * VS;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;        // elements per LDS stage
-    static constexpr int KCH = D / 8;                      // 16-byte chunks per K row
-    static constexpr int K_LOADS = kBC * KCH / kThreads;   // 16-byte K loads per thread
-    static constexpr int VG = D / 4;                       // groups of 4 d per V row
-    static constexpr int V_KQ = kThreads / VG;             // key quads per V round
-    static constexpr int V_ROUNDS = kBC / (4 * V_KQ);
-    static_assert(K_LOADS * kThreads == kBC * KCH, "K tile split");
-    static_assert(V_ROUNDS * 4 * V_KQ == kBC, "V tile split");
+    static constexpr int ROW_B = D * 2;                    // bytes per K/V row in LDS (no padding)
+    static constexpr int CH = ROW_B / 16;                  // 16-byte chunks per row
+    static constexpr int TILE_B = kBC * ROW_B;             // bytes per K (or V) tile
+    static constexpr int STAGE_B = 2 * TILE_B;             // K tile + V tile
+    static constexpr int ROWS_PER_INST = 1024 / ROW_B;     // rows one direct-load instruction fills
+    static constexpr int INSTS_PER_WAVE = TILE_B / 1024 / 4;
+    static_assert(INSTS_PER_WAVE * 4 * 1024 == TILE_B, "tile split over 4 waves");
 };
 
-// Position of key k (0..63) inside a Vt row: bits 2 and 3 swapped, so that the
-// keys a lane holds in its P registers (see kernel) are 8 consecutive entries.
-__device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
-
+// Chunk swizzles (physical chunk = logical chunk ^ swizzle(row)).  K rows are read
+// 16 (or 8) at a time at one logical chunk by the S^T operand loads; V rows are read
+// 8 at a time, 64 bytes each, by the transposing loads.
 template <int D>
-struct TileRegs {
-    u32x4 k[Lay<D>::K_LOADS];
-    u32x2 v[Lay<D>::V_ROUNDS][4];
-};
-
-// Global -> registers for key tile kb.  Keys past the end of the sequence are
-// clamped to the last row (no branches); their scores are masked to -inf and
-// their probabilities are 0, so the duplicated rows never contribute.
+__device__ __forceinline__ int swz_k(int row) {
+    if constexpr (D == 128) return row & 15;
+    else return (row ^ (row >> 3)) & 7;
+}
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const u16* __restrict__ kg, const u16* __restrict__ vg,
-                                          uint32_t row_stride, int kb, int last_key, int tid) {
-    using L = Lay<D>;
-    const int key0 = kb * kBC;
-#pragma unroll
-    for (int i = 0; i < L::K_LOADS; ++i) {
-        const int idx = tid + i * kThreads;
-        const int row = idx / L::KCH, ch = idx % L::KCH;
-        const uint32_t key = (uint32_t)min(key0 + row, last_key);
-        r.k[i] = *reinterpret_cast<const u32x4*>(kg + key * row_stride + ch * 8);
-    }
-    const int dg = tid % L::VG, kq = tid / L::VG;
-#pragma unroll
-    for (int rr = 0; rr < L::V_ROUNDS; ++rr) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t key = (uint32_t)min(key0 + rr * 4 * L::V_KQ + 4 * kq + e, last_key);
-            r.v[rr][e] = *reinterpret_cast<const u32x2*>(vg + key * row_stride + dg * 4);
-        }
-    }
+__device__ __forceinline__ int swz_v(int row) {
+    if constexpr (D == 128) return 4 * (row & 3);
+    else return 4 * ((row >> 1) & 1);
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, u16* ks, u16* vts, int tid) {
-    using L = Lay<D>;
-#pragma unroll
-    for (int i = 0; i < L::K_LOADS; ++i) {
-        int idx = tid + i * kThreads;
-        int row = idx / L::KCH, ch = idx % L::KCH;
-        *reinterpret_cast<u32x4*>(ks + row * L::KS + ch * 8) = r.k[i];
-    }
-    const int dg = tid % L::VG, kq = tid / L::VG;
-#pragma unroll
-    for (int rr = 0; rr < L::V_ROUNDS; ++rr) {
-        const int pos = vt_pos(rr * 4 * L::V_KQ + 4 * kq);
-        const u32x2 x0 = r.v[rr][0], x1 = r.v[rr][1], x2 = r.v[rr][2], x3 = r.v[rr][3];
-        // 4 keys x 4 d  ->  4 d x 4 keys (bf16 halves regrouped)
-        u32x2 o0, o1, o2, o3;
-        o0.x = (x0.x & 0xffffu) | (x1.x << 16);
-        o0.y = (x2.x & 0xffffu) | (x3.x << 16);
-        o1.x = (x0.x >> 16) | (x1.x & 0xffff0000u);
-        o1.y = (x2.x >> 16) | (x3.x & 0xffff0000u);
-        o2.x = (x0.y & 0xffffu) | (x1.y << 16);
-        o2.y = (x2.y & 0xffffu) | (x3.y << 16);
-        o3.x = (x0.y >> 16) | (x1.y & 0xffff0000u);
-        o3.y = (x2.y >> 16) | (x3.y & 0xffff0000u);
-        u16* base = vts + (4 * dg) * L::VS + pos;
-        *reinterpret_cast<u32x2*>(base) = o0;
-        *reinterpret_cast<u32x2*>(base + L::VS) = o1;
-        *reinterpret_cast<u32x2*>(base + 2 * L::VS) = o2;
-        *reinterpret_cast<u32x2*>(base + 3 * L::VS) = o3;
-    }
+// 16-byte direct HBM -> LDS load: lane l's 16 bytes land at LDS byte lds_base + 16*l
+// (lds_base is wave-uniform and goes through M0).  Written as inline asm on purpose: the
+// instruction has no destination register, and hiding it from the compiler's wait-count
+// pass stops that pass from assuming the in-flight write may alias every later LDS read
+// of the other stage (it would then wait for the whole prefetch before the P.V reads).
+// The kernel itself waits for vmcnt(0) before the barrier that publishes a tile.
+__device__ __forceinline__ void load_lds_16(const void* gptr, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
+__device__ __forceinline__ i16x4 read_tr16(const char* lds_ptr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
 }
 
 // Bijection blockIdx -> logical work id that keeps consecutive logical ids on one
@@ -191,13 +160,48 @@ struct TileWalk {
     }
 };
 
+// Issue this wave's share of the direct HBM -> LDS loads of key tile kb.  Lane l of
+// instruction inst fills LDS bytes [1024*inst + 16*l, +16): row inst*ROWS_PER_INST +
+// l/CH, physical chunk l%CH, i.e. logical chunk (l%CH) ^ swizzle(row) of that key.
+// Keys past the end of the sequence are clamped to the last one (masked to -inf in
+// the scores, probability 0 in P.V).
+template <int D>
+__device__ __forceinline__ void issue_tile(const u16* __restrict__ kg, const u16* __restrict__ vg,
+                                           uint32_t row_stride, int kb, int last_key, char* stage, int wave,
+                                           int lane, const uint32_t* koff, const uint32_t* voff) {
+    using L = Lay<D>;
+    const int key0 = kb * kBC;
+    const uint32_t ks = __builtin_amdgcn_readfirstlane(lds_addr(stage));
+    const uint32_t vs = ks + L::TILE_B;
+    if (key0 + kBC - 1 <= last_key) {
+        const u16* kt = kg + (uint32_t)key0 * row_stride;
+        const u16* vt = vg + (uint32_t)key0 * row_stride;
+#pragma unroll
+        for (int i = 0; i < L::INSTS_PER_WAVE; ++i) {
+            const int inst = wave * L::INSTS_PER_WAVE + i;
+            load_lds_16(kt + koff[i], ks + inst * 1024);
+            load_lds_16(vt + voff[i], vs + inst * 1024);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < L::INSTS_PER_WAVE; ++i) {
+            const int inst = wave * L::INSTS_PER_WAVE + i;
+            const int row = inst * L::ROWS_PER_INST + lane / L::CH;
+            const uint32_t key = (uint32_t)min(key0 + row, last_key);
+            const int pch = lane % L::CH;
+            load_lds_16(kg + key * row_stride + 8 * (pch ^ swz_k<D>(row)), ks + inst * 1024);
+            load_lds_16(vg + key * row_stride + 8 * (pch ^ swz_v<D>(row)), vs + inst * 1024);
+        }
+    }
+}
+
 template <int D, int MODE, bool OUT_F32>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2))) void
 prefill_bf16_kernel(PrefillArgs a) {
     using L = Lay<D>;
     constexpr int NC = D / 16;   // 16-wide d chunks of the S^T contraction
     constexpr int NM = D / 32;   // 32-row d tiles of O^T
-    __shared__ __attribute__((aligned(16))) u16 smem[2 * L::STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE_B];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -232,6 +236,16 @@ prefill_bf16_kernel(PrefillArgs a) {
     const bool wave_in_qb1 = wave >= 2;
     const int my_qb = qt * 2 + (wave_in_qb1 ? 1 : 0);
 
+    // per-lane element offsets of the direct loads inside a tile (tile-invariant)
+    uint32_t koff[L::INSTS_PER_WAVE], voff[L::INSTS_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < L::INSTS_PER_WAVE; ++i) {
+        const int row = (wave * L::INSTS_PER_WAVE + i) * L::ROWS_PER_INST + lane / L::CH;
+        const int pch = lane % L::CH;
+        koff[i] = row * kv_row_stride + 8 * (pch ^ swz_k<D>(row));
+        voff[i] = row * kv_row_stride + 8 * (pch ^ swz_v<D>(row));
+    }
+
     // Q rows as the B operand of S^T = K Q^T: lane holds Q[qpos][16c + 8hh .. +7]
     bf16x8 qreg[NC];
 #pragma unroll
@@ -239,9 +253,26 @@ prefill_bf16_kernel(PrefillArgs a) {
         const uint32_t qrow = (uint32_t)min(qpos, last_key);
         qreg[c] = *reinterpret_cast<const bf16x8*>(qg + qrow * q_row_stride + 16 * c + 8 * hh);
     }
-    // wait for Q here: otherwise the wait for Q lands inside the tile loop, where it also
-    // waits for the next tile's prefetch (vmcnt counts every outstanding load)
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+
+    // LDS byte offsets of this lane's operand reads (stage-relative)
+    // K: row 32kh + n, logical chunk 2c + hh -> physical (2c + hh) ^ swz_k(n)  (swz_k(32kh+n) = swz_k(n)
+    // for d = 128; for d = 64 the 32kh term is added below through the row address only)
+    uint32_t kaddr[2][NC];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            kaddr[kh][c] = (32 * kh + n) * L::ROW_B + 16 * ((2 * c + hh) ^ swz_k<D>(32 * kh + n));
+    // V (transposing reads): 16-lane group gq = lane/16 -> key quad hh = gq>>1, d half dh = gq&1;
+    // lane jj = lane&15 points at key 4hh + (jj>>2) (+ tile offsets), d = 32mt + 16dh + 4(jj&3)
+    const int jj = lane & 15, dh = (lane >> 4) & 1;
+    const int vkey = 4 * hh + (jj >> 2);
+    uint32_t vaddr[NM];
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) {
+        const int lch = 4 * mt + 2 * dh + ((jj & 3) >> 1);
+        vaddr[mt] = L::TILE_B + vkey * L::ROW_B + 16 * (lch ^ swz_v<D>(vkey)) + 8 * (jj & 1);
+    }
 
     f32x16 oacc[NM];
 #pragma unroll
@@ -254,37 +285,34 @@ prefill_bf16_kernel(PrefillArgs a) {
     int kb;
     bool in0, in1;
     bool have = walk.next(kb, in0, in1);
-    TileRegs<D> regs;
-    if (have) {
-        load_tile<D>(regs, kg, vg, kv_row_stride, kb, last_key, tid);
-        store_tile<D>(regs, smem, smem + L::K_ELEMS, tid);
-    }
+    if (have) issue_tile<D>(kg, vg, kv_row_stride, kb, last_key, smem, wave, lane, koff, voff);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): Q and tile 0 in place
     __syncthreads();
     int buf = 0;
     while (have) {
         int kb_n;
         bool in0_n, in1_n;
         const bool have_n = walk.next(kb_n, in0_n, in1_n);
-        if (have_n) load_tile<D>(regs, kg, vg, kv_row_stride, kb_n, last_key, tid);
+        if (have_n)
+            issue_tile<D>(kg, vg, kv_row_stride, kb_n, last_key, smem + (buf ^ 1) * L::STAGE_B, wave, lane, koff,
+                          voff);
 
         const bool mine = wave_live && (wave_in_qb1 ? in1 : in0);
         if (mine) {
-            const u16* ks = smem + buf * L::STAGE;
-            const u16* vts = ks + L::K_ELEMS;
+            const char* st = smem + buf * L::STAGE_B;
             // ---- S^T = K Q^T : two 32-key halves, two independent accumulation chains
             f32x16 sacc[2] = {f32x16{}, f32x16{}};
-            const u16* krow = ks + n * L::KS + 8 * hh;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(krow + 16 * c);
-                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(krow + 32 * L::KS + 16 * c);
+                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(st + kaddr[0][c]);
+                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(st + kaddr[1][c]);
                 sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[c], sacc[0], 0, 0, 0);
                 sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[c], sacc[1], 0, 0, 0);
             }
             // lane holds S[qpos][key], key = kb*64 + 32kh + 8(r/4) + 4hh + (r%4)
             const bool need_mask = (MODE != kDenseFull && kb >= my_qb) || (kb + 1) * kBC > seq;
             if (need_mask) {
-                // key = kb*64 + 32kh + 8(r/4) + 4hh + r%4 is masked when key > lim
+                // key > lim is masked, lim = last allowed key of this lane's row minus the tile/lane base
                 const int lim = (MODE != kDenseFull ? min(qpos, last_key) : last_key) - (kb * kBC + 4 * hh);
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh)
@@ -298,10 +326,18 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-            const float mc = m_new * c2;
-            float rs = 0.0f;
+            // raise the reference max only when some row outgrows it by more than the slack
+            if (__ballot((mx - m_run) * c2 > kRescaleSlack)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+                l_run *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[mt][r] *= alpha;
+                m_run = m_new;
+            }
+            const float mc = m_run * c2;
             bf16x8 pb[2][2];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
@@ -309,38 +345,40 @@ prefill_bf16_kernel(PrefillArgs a) {
                 for (int aa = 0; aa < 2; ++aa) {
                     float p[8];
 #pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) {
-                        p[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[kh][8 * aa + jj], c2, -mc));
-                        rs += p[jj];
-                    }
+                    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kh][8 * aa + e], c2, -mc));
                     pb[kh][aa] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
                                         (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
                 }
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
-            if (__ballot(alpha != 1.0f)) {
+            // row sum over the rounded P (exactly what P.V uses)
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-                for (int mt = 0; mt < NM; ++mt)
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[mt][r] *= alpha;
-            }
-            // ---- O^T += V^T P^T ; P slot jj of step (kh, aa) is key 32kh + 16aa + 8(jj/4) + 4hh + jj%4
+                for (int aa = 0; aa < 2; ++aa) {
+                    const bf16x8 v = pb[kh][aa];
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[0], v[1]}, ones, l_run, false);
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2], v[3]}, ones, l_run, false);
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[4], v[5]}, ones, l_run, false);
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[6], v[7]}, ones, l_run, false);
+                }
+            // ---- O^T += V^T P^T ; P slot e' of step (kh, aa) is key 32kh + 16aa + 8(e'/4) + 4hh + e'%4.
+            // Two transposing reads per step: keys +0..3 and +8..11 of the lane group's 4-key block.
 #pragma unroll
             for (int mt = 0; mt < NM; ++mt) {
-                const u16* vrow = vts + (32 * mt + n) * L::VS + 8 * hh;
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                     for (int aa = 0; aa < 2; ++aa) {
-                        bf16x8 av = *reinterpret_cast<const bf16x8*>(vrow + 32 * kh + 16 * aa);
-                        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kh][aa], oacc[mt], 0, 0, 0);
+                        const char* vp = st + vaddr[mt] + (32 * kh + 16 * aa) * L::ROW_B;
+                        const i16x4 lo = read_tr16(vp);
+                        const i16x4 hi = read_tr16(vp + 8 * L::ROW_B);
+                        const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                            pb[kh][aa], oacc[mt], 0, 0, 0);
                     }
             }
         }
-        if (have_n) {
-            u16* ks_n = smem + (buf ^ 1) * L::STAGE;
-            store_tile<D>(regs, ks_n, ks_n + L::K_ELEMS, tid);
-        }
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's share of tile t+1 has landed
         __syncthreads();
         buf ^= 1;
         kb = kb_n;
