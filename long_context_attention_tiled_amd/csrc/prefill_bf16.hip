@@ -81,14 +81,16 @@ __device__ __forceinline__ int swz_v(int row) {
     else return 4 * ((row >> 1) & 1);
 }
 
-// 16-byte direct HBM -> LDS load: lane l's 16 bytes land at LDS byte lds_base + 16*l
-// (lds_base is wave-uniform and goes through M0).  Written as inline asm on purpose: the
-// instruction has no destination register, and hiding it from the compiler's wait-count
-// pass stops that pass from assuming the in-flight write may alias every later LDS read
-// of the other stage (it would then wait for the whole prefetch before the P.V reads).
-// The kernel itself waits for vmcnt(0) before the barrier that publishes a tile.
-__device__ __forceinline__ void load_lds_16(const void* gptr, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+// 16-byte direct HBM -> LDS load from sbase + voff (sbase wave-uniform, in SGPRs; voff a
+// per-lane byte offset): lane l's 16 bytes land at LDS byte lds_base + 16*l (lds_base is
+// wave-uniform and goes through M0).  Written as inline asm on purpose: the instruction
+// has no destination register, and hiding it from the compiler's wait-count pass stops
+// that pass from assuming the in-flight write may alias every later LDS read of the
+// other stage (it would then wait for the whole prefetch before the P.V reads).  The
+// kernel itself waits for vmcnt(0) before the barrier that publishes a tile.
+__device__ __forceinline__ void load_lds_16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+                 : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -174,13 +176,13 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ kg, const u16
     const uint32_t ks = __builtin_amdgcn_readfirstlane(lds_addr(stage));
     const uint32_t vs = ks + L::TILE_B;
     if (key0 + kBC - 1 <= last_key) {
-        const u16* kt = kg + (uint32_t)key0 * row_stride;
+        const u16* kt = kg + (uint32_t)key0 * row_stride;   // uniform
         const u16* vt = vg + (uint32_t)key0 * row_stride;
 #pragma unroll
         for (int i = 0; i < L::INSTS_PER_WAVE; ++i) {
             const int inst = wave * L::INSTS_PER_WAVE + i;
-            load_lds_16(kt + koff[i], ks + inst * 1024);
-            load_lds_16(vt + voff[i], vs + inst * 1024);
+            load_lds_16(kt, koff[i], ks + inst * 1024);
+            load_lds_16(vt, voff[i], vs + inst * 1024);
         }
     } else {
 #pragma unroll
@@ -189,8 +191,8 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ kg, const u16
             const int row = inst * L::ROWS_PER_INST + lane / L::CH;
             const uint32_t key = (uint32_t)min(key0 + row, last_key);
             const int pch = lane % L::CH;
-            load_lds_16(kg + key * row_stride + 8 * (pch ^ swz_k<D>(row)), ks + inst * 1024);
-            load_lds_16(vg + key * row_stride + 8 * (pch ^ swz_v<D>(row)), vs + inst * 1024);
+            load_lds_16(kg, 2 * (key * row_stride + 8 * (pch ^ swz_k<D>(row))), ks + inst * 1024);
+            load_lds_16(vg, 2 * (key * row_stride + 8 * (pch ^ swz_v<D>(row))), vs + inst * 1024);
         }
     }
 }
@@ -236,14 +238,14 @@ prefill_bf16_kernel(PrefillArgs a) {
     const bool wave_in_qb1 = wave >= 2;
     const int my_qb = qt * 2 + (wave_in_qb1 ? 1 : 0);
 
-    // per-lane element offsets of the direct loads inside a tile (tile-invariant)
+    // per-lane byte offsets of the direct loads inside a tile (tile-invariant)
     uint32_t koff[L::INSTS_PER_WAVE], voff[L::INSTS_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < L::INSTS_PER_WAVE; ++i) {
         const int row = (wave * L::INSTS_PER_WAVE + i) * L::ROWS_PER_INST + lane / L::CH;
         const int pch = lane % L::CH;
-        koff[i] = row * kv_row_stride + 8 * (pch ^ swz_k<D>(row));
-        voff[i] = row * kv_row_stride + 8 * (pch ^ swz_v<D>(row));
+        koff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz_k<D>(row)));   // bytes
+        voff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz_v<D>(row)));
     }
 
     // Q rows as the B operand of S^T = K Q^T: lane holds Q[qpos][16c + 8hh .. +7]
@@ -300,15 +302,25 @@ prefill_bf16_kernel(PrefillArgs a) {
         const bool mine = wave_live && (wave_in_qb1 ? in1 : in0);
         if (mine) {
             const char* st = smem + buf * L::STAGE_B;
-            // ---- S^T = K Q^T : two 32-key halves, two independent accumulation chains
+            // ---- S^T = K Q^T : two 32-key halves, two independent accumulation chains.  The
+            // K operands of step c+1 are read from LDS while step c's MFMAs run, and the wave
+            // raises its issue priority for the MFMA phase so that the other wave on the SIMD
+            // fills the gaps with its vector work.
+            __builtin_amdgcn_s_setprio(2);
             f32x16 sacc[2] = {f32x16{}, f32x16{}};
+            bf16x8 ka[2][2];
+            ka[0][0] = *reinterpret_cast<const bf16x8*>(st + kaddr[0][0]);
+            ka[0][1] = *reinterpret_cast<const bf16x8*>(st + kaddr[1][0]);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(st + kaddr[0][c]);
-                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(st + kaddr[1][c]);
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[c], sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[c], sacc[1], 0, 0, 0);
+                if (c + 1 < NC) {
+                    ka[(c + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(st + kaddr[0][c + 1]);
+                    ka[(c + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(st + kaddr[1][c + 1]);
+                }
+                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c & 1][0], qreg[c], sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c & 1][1], qreg[c], sacc[1], 0, 0, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
             // lane holds S[qpos][key], key = kb*64 + 32kh + 8(r/4) + 4hh + (r%4)
             const bool need_mask = (MODE != kDenseFull && kb >= my_qb) || (kb + 1) * kBC > seq;
             if (need_mask) {
@@ -363,20 +375,24 @@ prefill_bf16_kernel(PrefillArgs a) {
                 }
             // ---- O^T += V^T P^T ; P slot e' of step (kh, aa) is key 32kh + 16aa + 8(e'/4) + 4hh + e'%4.
             // Two transposing reads per step: keys +0..3 and +8..11 of the lane group's 4-key block.
+            // the V operand of step i+1 is read while step i's MFMA runs
+            __builtin_amdgcn_s_setprio(2);
+            auto vread = [&](int i) {
+                const int mt = i >> 2, kh = (i >> 1) & 1, aa = i & 1;
+                const char* vp = st + vaddr[mt] + (32 * kh + 16 * aa) * L::ROW_B;
+                const i16x4 lo = read_tr16(vp);
+                const i16x4 hi = read_tr16(vp + 8 * L::ROW_B);
+                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+            bf16x8 va[2];
+            va[0] = vread(0);
 #pragma unroll
-            for (int mt = 0; mt < NM; ++mt) {
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int aa = 0; aa < 2; ++aa) {
-                        const char* vp = st + vaddr[mt] + (32 * kh + 16 * aa) * L::ROW_B;
-                        const i16x4 lo = read_tr16(vp);
-                        const i16x4 hi = read_tr16(vp + 8 * L::ROW_B);
-                        const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                                            pb[kh][aa], oacc[mt], 0, 0, 0);
-                    }
+            for (int i = 0; i < 4 * NM; ++i) {
+                if (i + 1 < 4 * NM) va[(i + 1) & 1] = vread(i + 1);
+                const int mt = i >> 2, kh = (i >> 1) & 1, aa = i & 1;
+                oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pb[kh][aa], oacc[mt], 0, 0, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's share of tile t+1 has landed
         __syncthreads();
