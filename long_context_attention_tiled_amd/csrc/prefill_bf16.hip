@@ -10,12 +10,23 @@
 // page, implementation and architecture paragraphs).
 //
 // Layout of the work on CDNA4:
-//   * workgroup = 256 threads = 4 wave64s, 128 query rows of one (batch, head);
-//     each wave owns 32 query rows; key tiles are 64 keys (= one sparse block).
+//   * workgroup = 512 threads = 8 wave64s in two groups of 4.  A group owns 128
+//     query rows of one query head (32 rows per wave); the two groups of a
+//     workgroup share every K/V tile in LDS: with an even number of query heads per
+//     KV head they are two heads of the same KV head over the same rows, otherwise
+//     two consecutive 128-row tiles of one head.  Key tiles are 64 keys (= one
+//     sparse block).
 //   * both contractions run on v_mfma_f32_32x32x16_bf16 in transposed form,
 //     S^T = K Q^T and O^T = V^T P^T.  A lane's 32x32 accumulator column is then one
-//     query row, so the softmax statistics (row max, row sum, rescale factor) of a
-//     lane's outputs are lane-local: one l <-> l^32 exchange per tile, none for O.
+//     query row, so the softmax statistics of a lane's outputs are lane-local: one
+//     lane <-> lane^32 exchange per tile (v_permlane32_swap), none for O.
+//   * ping-pong between the groups: every step has two phases separated by
+//     workgroup barriers.  In each phase one group issues matrix work (P.V of the
+//     previous tile, then S of the current tile: 32 MFMAs per wave) while the other
+//     group runs the vector work of the softmax (max, exp2, bf16 packing, row sum)
+//     of the tile it has just scored; the roles swap every phase.  The two waves
+//     sharing a SIMD therefore keep the matrix core and the vector ALU busy at the
+//     same time instead of taking turns.
 //   * Q stays in registers (B operand of S^T) for the whole kernel.
 //   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4: no
 //     staging registers, no LDS store instructions), row-major with an XOR swizzle
@@ -23,16 +34,17 @@
 //     free.  The V^T operand is read with ds_read_b64_tr_b16, which transposes
 //     4x4 blocks of 16-bit elements across lanes: every lane receives 4 keys of its
 //     own d column per read, so V never needs a transposed copy.
-//   * two LDS stages: the loads of tile t+1 are in flight while tile t is
-//     computed; one barrier per tile.
+//   * two LDS slots for K and two for V; K runs one tile ahead of V: at the start of
+//     step u the loads of K(u+1) and V(u) are issued and they only have to land by
+//     the end of step u (two phases later).
 //   * exp2 with scale*log2(e) folded into one FMA.  The running maximum is raised
 //     only when some row's new maximum exceeds it by more than 8 (log2 units):
 //     until then probabilities up to 2^8 are accumulated against the old
 //     reference, which is exact in exact arithmetic (the same reference scales
 //     numerator and denominator) and removes most O rescales; the newsletter's
 //     FlashAttention-4 section describes the m_new <= m_old special case of this.
-//   * the row sum is taken over the bf16-rounded P that enters P.V (v_dot2 against
-//     (1, 1)), so O is a convex combination of V rows up to fp32 accumulation.
+//   * P enters P.V rounded to bf16; the row sum is accumulated in fp32 from the
+//     unrounded probabilities.
 //   * workgroup order: kv-head groups are kept on one XCD (blockIdx % 8 picks the
 //     XCD) so the query heads sharing K/V hit the same L2, and query tiles are
 //     issued longest-first for causal masks.
@@ -42,16 +54,15 @@ namespace flux {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kBR = 128;       // query rows per workgroup
+constexpr int kBR = 128;       // query rows per wave group
 constexpr int kBC = 64;        // keys per tile
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1.0e30f;  // finite start value of the running max
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag the true max
@@ -61,10 +72,12 @@ struct Lay {
     static constexpr int ROW_B = D * 2;                    // bytes per K/V row in LDS (no padding)
     static constexpr int CH = ROW_B / 16;                  // 16-byte chunks per row
     static constexpr int TILE_B = kBC * ROW_B;             // bytes per K (or V) tile
-    static constexpr int STAGE_B = 2 * TILE_B;             // K tile + V tile
+    static constexpr int K_BASE = 0;                       // two K slots
+    static constexpr int V_BASE = 2 * TILE_B;              // two V slots
+    static constexpr int SMEM_B = 4 * TILE_B;
     static constexpr int ROWS_PER_INST = 1024 / ROW_B;     // rows one direct-load instruction fills
-    static constexpr int INSTS_PER_WAVE = TILE_B / 1024 / 4;
-    static_assert(INSTS_PER_WAVE * 4 * 1024 == TILE_B, "tile split over 4 waves");
+    static constexpr int INSTS_PER_WAVE = TILE_B / 1024 / kWaves;
+    static_assert(INSTS_PER_WAVE * kWaves * 1024 == TILE_B, "tile split over the waves");
 };
 
 // Chunk swizzles (physical chunk = logical chunk ^ swizzle(row)).  K rows are read
@@ -86,11 +99,19 @@ __device__ __forceinline__ int swz_v(int row) {
 // wave-uniform and goes through M0).  Written as inline asm on purpose: the instruction
 // has no destination register, and hiding it from the compiler's wait-count pass stops
 // that pass from assuming the in-flight write may alias every later LDS read of the
-// other stage (it would then wait for the whole prefetch before the P.V reads).  The
-// kernel itself waits for vmcnt(0) before the barrier that publishes a tile.
+// other slots (it would then wait for the whole prefetch before the operand reads).
+// The kernel itself waits for vmcnt(0) before the barrier that publishes a tile.
 __device__ __forceinline__ void load_lds_16(const void* sbase, uint32_t voff, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
                  : "memory", "m0");
+}
+
+// The same pointer value taken from the first active lane, so that it lives in SGPRs.
+__device__ __forceinline__ const u16* uniform_ptr(const u16* p) {
+    const uint64_t x = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return (const u16*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -99,6 +120,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 __device__ __forceinline__ i16x4 read_tr16(const char* lds_ptr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
+}
+
+// x + (value of x in lane ^ 32) and max of the two, through v_permlane32_swap (no LDS).
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Bijection blockIdx -> logical work id that keeps consecutive logical ids on one
@@ -112,78 +143,81 @@ __device__ __forceinline__ int xcd_remap(int x, int total) {
 
 enum Mode { kDenseCausal = 0, kDenseFull = 1, kSparse = 2 };
 
-// Walks the key tiles of a workgroup (query blocks qb0 = 2*qt and qb1 = qb0+1):
-// dense -- tiles 0..last; sparse -- the sorted union of the two CSR rows.
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
+// Walks the key tiles of a workgroup, whose query rows span the 64-row query blocks
+// qb_base .. qb_base + nrows - 1 (nrows = 2 or 4): dense -- tiles 0..last; sparse -- the
+// sorted union of those blocks' CSR rows.  next() also returns which of the query
+// blocks use the tile (bit r: block qb_base + r).
 template <int MODE>
 struct TileWalk {
-    int next_kb, last_kb, qb0, qb1;
-    int p0, e0, p1, e1;
+    int next_kb, last_kb, qb_base, nvalid;
+    int p0, p1, p2, p3, e0, e1, e2, e3;   // CSR cursors and ends of the (up to 4) query blocks
     const int32_t* ci;
 
-    __device__ void init(int qt, int n_qblk, const int32_t* rp, const int32_t* ci_) {
-        qb0 = 2 * qt;
-        qb1 = 2 * qt + 1;
+    __device__ void init(int qb_base_, int nrows, int n_qblk, const int32_t* rp, const int32_t* ci_) {
+        qb_base = qb_base_;
+        nvalid = max(0, min(nrows, n_qblk - qb_base));
         ci = ci_;
         if constexpr (MODE == kSparse) {
-            p0 = rp[qb0];
-            e0 = rp[qb0 + 1];
-            if (qb1 < n_qblk) {
-                p1 = rp[qb1];
-                e1 = rp[qb1 + 1];
-            } else {
-                p1 = e1 = 0;
-            }
+            p0 = p1 = p2 = p3 = e0 = e1 = e2 = e3 = 0;
+            if (nvalid > 0) p0 = rp[qb_base], e0 = rp[qb_base + 1];
+            if (nvalid > 1) p1 = rp[qb_base + 1], e1 = rp[qb_base + 2];
+            if (nvalid > 2) p2 = rp[qb_base + 2], e2 = rp[qb_base + 3];
+            if (nvalid > 3) p3 = rp[qb_base + 3], e3 = rp[qb_base + 4];
         } else {
             next_kb = 0;
-            last_kb = MODE == kDenseCausal ? min(qb1, n_qblk - 1) : n_qblk - 1;
+            last_kb = MODE == kDenseCausal ? qb_base + nvalid - 1 : n_qblk - 1;
         }
     }
 
-    // Next tile; in0/in1: whether query block qb0/qb1 uses it.
-    __device__ bool next(int& kb, bool& in0, bool& in1) {
+    __device__ bool next(int& kb, uint32_t& in) {
         if constexpr (MODE == kSparse) {
             const int big = 0x7fffffff;
-            int c0 = p0 < e0 ? ci[p0] : big;
-            int c1 = p1 < e1 ? ci[p1] : big;
-            kb = min(c0, c1);
+            const int c0 = p0 < e0 ? ci[p0] : big;
+            const int c1 = p1 < e1 ? ci[p1] : big;
+            const int c2 = p2 < e2 ? ci[p2] : big;
+            const int c3 = p3 < e3 ? ci[p3] : big;
+            kb = min(min(c0, c1), min(c2, c3));
             if (kb == big) return false;
-            in0 = c0 == kb;
-            in1 = c1 == kb;
-            p0 += in0;
-            p1 += in1;
+            const bool h0 = c0 == kb, h1 = c1 == kb, h2 = c2 == kb, h3 = c3 == kb;
+            p0 += h0;
+            p1 += h1;
+            p2 += h2;
+            p3 += h3;
+            in = (uint32_t)h0 | ((uint32_t)h1 << 1) | ((uint32_t)h2 << 2) | ((uint32_t)h3 << 3);
             return true;
         } else {
             if (next_kb > last_kb) return false;
             kb = next_kb++;
-            in0 = MODE == kDenseFull || kb <= qb0;
-            in1 = MODE == kDenseFull || kb <= qb1;
+            in = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                in |= (uint32_t)(r < nvalid && (MODE == kDenseFull || kb <= qb_base + r)) << r;
             return true;
         }
     }
 };
 
-// Issue this wave's share of the direct HBM -> LDS loads of key tile kb.  Lane l of
-// instruction inst fills LDS bytes [1024*inst + 16*l, +16): row inst*ROWS_PER_INST +
-// l/CH, physical chunk l%CH, i.e. logical chunk (l%CH) ^ swizzle(row) of that key.
-// Keys past the end of the sequence are clamped to the last one (masked to -inf in
-// the scores, probability 0 in P.V).
-template <int D>
-__device__ __forceinline__ void issue_tile(const u16* __restrict__ kg, const u16* __restrict__ vg,
-                                           uint32_t row_stride, int kb, int last_key, char* stage, int wave,
-                                           int lane, const uint32_t* koff, const uint32_t* voff) {
+// Issue this wave's share of the direct HBM -> LDS loads of one K (or V) tile kb into
+// the LDS slot at byte address slot.  Lane l of instruction inst fills bytes
+// [1024*inst + 16*l, +16) of the slot: row inst*ROWS_PER_INST + l/CH, physical chunk
+// l%CH, i.e. logical chunk (l%CH) ^ swizzle(row) of that key.  Keys past the end of
+// the sequence are clamped to the last one (masked to -inf in the scores,
+// probability 0 in P.V).
+template <int D, bool IS_V>
+__device__ __forceinline__ void issue_tile(const u16* __restrict__ gbase, uint32_t row_stride, int kb, int last_key,
+                                           uint32_t slot, int wave, int lane, const uint32_t* off) {
     using L = Lay<D>;
     const int key0 = kb * kBC;
-    const uint32_t ks = __builtin_amdgcn_readfirstlane(lds_addr(stage));
-    const uint32_t vs = ks + L::TILE_B;
     if (key0 + kBC - 1 <= last_key) {
-        const u16* kt = kg + (uint32_t)key0 * row_stride;   // uniform
-        const u16* vt = vg + (uint32_t)key0 * row_stride;
+        const u16* t = uniform_ptr(gbase + (uint32_t)key0 * row_stride);
 #pragma unroll
-        for (int i = 0; i < L::INSTS_PER_WAVE; ++i) {
-            const int inst = wave * L::INSTS_PER_WAVE + i;
-            load_lds_16(kt, koff[i], ks + inst * 1024);
-            load_lds_16(vt, voff[i], vs + inst * 1024);
-        }
+        for (int i = 0; i < L::INSTS_PER_WAVE; ++i)
+            load_lds_16(t, off[i], slot + (wave * L::INSTS_PER_WAVE + i) * 1024);
     } else {
 #pragma unroll
         for (int i = 0; i < L::INSTS_PER_WAVE; ++i) {
@@ -191,52 +225,72 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ kg, const u16
             const int row = inst * L::ROWS_PER_INST + lane / L::CH;
             const uint32_t key = (uint32_t)min(key0 + row, last_key);
             const int pch = lane % L::CH;
-            load_lds_16(kg, 2 * (key * row_stride + 8 * (pch ^ swz_k<D>(row))), ks + inst * 1024);
-            load_lds_16(vg, 2 * (key * row_stride + 8 * (pch ^ swz_v<D>(row))), vs + inst * 1024);
+            const int sw = IS_V ? swz_v<D>(row) : swz_k<D>(row);
+            load_lds_16(uniform_ptr(gbase), 2 * (key * row_stride + 8 * (pch ^ sw)), slot + inst * 1024);
         }
     }
 }
 
 template <int D, int MODE, bool OUT_F32>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2))) void
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2))) void
 prefill_bf16_kernel(PrefillArgs a) {
     using L = Lay<D>;
     constexpr int NC = D / 16;   // 16-wide d chunks of the S^T contraction
     constexpr int NM = D / 32;   // 32-row d tiles of O^T
-    __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE_B];
+    __shared__ __attribute__((aligned(1024))) char smem[L::SMEM_B];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;   // wave group
+    const int wq = wave & 3;     // wave inside its group
     const int n = lane & 31;     // query column of this lane inside the wave's 32 rows
     const int hh = lane >> 5;    // which half of the k-slots / accumulator rows
 
-    const int nqt = (int)((a.seq + kBR - 1) / kBR);
+    // ---- work unit: (batch, kv head g, two slots of 128 query rows)
+    const int seq = (int)a.seq;          // the host guarantees seq * max(hq, hkv) * d < 2^31
+    const int nqt = (seq + kBR - 1) / kBR;
     const int G = a.hq / a.hkv;
-    const int total = (int)(a.batch * a.hq) * nqt;
+    const bool pair_heads = (G & 1) == 0;
+    const int per_g = pair_heads ? (G / 2) * nqt : G * ((nqt + 1) / 2);
+    const int total = (int)a.batch * a.hkv * per_g;
     int lid = xcd_remap((int)blockIdx.x, total);
-    const int j = lid % G;
-    lid /= G;
-    const int qt_rank = lid % nqt;
-    lid /= nqt;
+    const int unit = lid % per_g;
+    lid /= per_g;
     const int g = lid % a.hkv;
     const int b = lid / a.hkv;
-    const int h = g * G + j;
-    const int qt = (MODE == kDenseCausal) ? nqt - 1 - qt_rank : qt_rank;
+    int h, qt, qb_base, my_r, nrows;
+    if (pair_heads) {                    // groups = query heads 2jp, 2jp+1 of g, same rows
+        const int jp = unit % (G / 2);
+        const int rank = unit / (G / 2);
+        qt = (MODE == kDenseCausal) ? nqt - 1 - rank : rank;
+        h = g * G + 2 * jp + grp;
+        qb_base = 2 * qt;
+        my_r = wq >> 1;
+        nrows = 2;
+    } else {                             // groups = query tiles 2qp, 2qp+1 of one head
+        const int npq = (nqt + 1) / 2;
+        const int j = unit % G;
+        const int rank = unit / G;
+        const int qp = (MODE == kDenseCausal) ? npq - 1 - rank : rank;
+        h = g * G + j;
+        qt = 2 * qp + grp;
+        qb_base = 4 * qp;
+        my_r = 2 * grp + (wq >> 1);
+        nrows = 4;
+    }
 
     const uint32_t q_row_stride = (uint32_t)(a.hq * D);
     const uint32_t kv_row_stride = (uint32_t)(a.hkv * D);
-    const int seq = (int)a.seq;          // the host guarantees seq * max(hq, hkv) * d < 2^31
     const int last_key = seq - 1;
     const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * D;
     const u16* kg = reinterpret_cast<const u16*>(a.k) + ((int64_t)b * a.seq * a.hkv + g) * D;
     const u16* vg = reinterpret_cast<const u16*>(a.v) + ((int64_t)b * a.seq * a.hkv + g) * D;
 
-    const int q0 = qt * kBR + wave * 32;       // first query row of this wave
-    const int qpos = q0 + n;                   // this lane's query row
+    const int q0 = qt * kBR + wq * 32;       // first query row of this wave
+    const int qpos = q0 + n;                 // this lane's query row
     const bool wave_live = q0 < seq;
-    const bool wave_in_qb1 = wave >= 2;
-    const int my_qb = qt * 2 + (wave_in_qb1 ? 1 : 0);
+    const int my_qb = qb_base + my_r;
 
     // per-lane byte offsets of the direct loads inside a tile (tile-invariant)
     uint32_t koff[L::INSTS_PER_WAVE], voff[L::INSTS_PER_WAVE];
@@ -256,9 +310,8 @@ prefill_bf16_kernel(PrefillArgs a) {
         qreg[c] = *reinterpret_cast<const bf16x8*>(qg + qrow * q_row_stride + 16 * c + 8 * hh);
     }
 
-    // LDS byte offsets of this lane's operand reads (stage-relative)
-    // K: row 32kh + n, logical chunk 2c + hh -> physical (2c + hh) ^ swz_k(n)  (swz_k(32kh+n) = swz_k(n)
-    // for d = 128; for d = 64 the 32kh term is added below through the row address only)
+    // LDS byte offsets of this lane's operand reads (slot-relative)
+    // K: row 32kh + n, logical chunk 2c + hh -> physical (2c + hh) ^ swz_k(32kh + n)
     uint32_t kaddr[2][NC];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -273,138 +326,199 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) {
         const int lch = 4 * mt + 2 * dh + ((jj & 3) >> 1);
-        vaddr[mt] = L::TILE_B + vkey * L::ROW_B + 16 * (lch ^ swz_v<D>(vkey)) + 8 * (jj & 1);
+        vaddr[mt] = vkey * L::ROW_B + 16 * (lch ^ swz_v<D>(vkey)) + 8 * (jj & 1);
     }
 
     f32x16 oacc[NM];
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) oacc[mt] = f32x16{};
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    bf16x8 pb[2][2];
     float m_run = kNegBig, l_run = 0.0f;
     const float c2 = a.scale_log2;
+    const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
-    TileWalk<MODE> walk;
-    walk.init(qt, a.n_qblk, a.row_ptr, a.col_idx);
-    int kb;
-    bool in0, in1;
-    bool have = walk.next(kb, in0, in1);
-    if (have) issue_tile<D>(kg, vg, kv_row_stride, kb, last_key, smem, wave, lane, koff, voff);
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): Q and tile 0 in place
-    __syncthreads();
-    int buf = 0;
-    while (have) {
-        int kb_n;
-        bool in0_n, in1_n;
-        const bool have_n = walk.next(kb_n, in0_n, in1_n);
-        if (have_n)
-            issue_tile<D>(kg, vg, kv_row_stride, kb_n, last_key, smem + (buf ^ 1) * L::STAGE_B, wave, lane, koff,
-                          voff);
-
-        const bool mine = wave_live && (wave_in_qb1 ? in1 : in0);
-        if (mine) {
-            const char* st = smem + buf * L::STAGE_B;
-            // ---- S^T = K Q^T : two 32-key halves, two independent accumulation chains.  The
-            // K operands of step c+1 are read from LDS while step c's MFMAs run, and the wave
-            // raises its issue priority for the MFMA phase so that the other wave on the SIMD
-            // fills the gaps with its vector work.
-            __builtin_amdgcn_s_setprio(2);
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
-            bf16x8 ka[2][2];
-            ka[0][0] = *reinterpret_cast<const bf16x8*>(st + kaddr[0][0]);
-            ka[0][1] = *reinterpret_cast<const bf16x8*>(st + kaddr[1][0]);
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                if (c + 1 < NC) {
-                    ka[(c + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(st + kaddr[0][c + 1]);
-                    ka[(c + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(st + kaddr[1][c + 1]);
-                }
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c & 1][0], qreg[c], sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c & 1][1], qreg[c], sacc[1], 0, 0, 0);
-            }
-            __builtin_amdgcn_s_setprio(0);
-            // lane holds S[qpos][key], key = kb*64 + 32kh + 8(r/4) + 4hh + (r%4)
-            const bool need_mask = (MODE != kDenseFull && kb >= my_qb) || (kb + 1) * kBC > seq;
-            if (need_mask) {
-                // key > lim is masked, lim = last allowed key of this lane's row minus the tile/lane base
-                const int lim = (MODE != kDenseFull ? min(qpos, last_key) : last_key) - (kb * kBC + 4 * hh);
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (32 * kh + 8 * (r >> 2) + (r & 3) > lim) sacc[kh][r] = -INFINITY;
-            }
-            float mx = sacc[0][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            // raise the reference max only when some row outgrows it by more than the slack
-            if (__ballot((mx - m_run) * c2 > kRescaleSlack)) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-                l_run *= alpha;
-#pragma unroll
-                for (int mt = 0; mt < NM; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[mt][r] *= alpha;
-                m_run = m_new;
-            }
-            const float mc = m_run * c2;
-            bf16x8 pb[2][2];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int aa = 0; aa < 2; ++aa) {
-                    float p[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kh][8 * aa + e], c2, -mc));
-                    pb[kh][aa] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
-                                        (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
-                }
-            // row sum over the rounded P (exactly what P.V uses)
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int aa = 0; aa < 2; ++aa) {
-                    const bf16x8 v = pb[kh][aa];
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[0], v[1]}, ones, l_run, false);
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2], v[3]}, ones, l_run, false);
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[4], v[5]}, ones, l_run, false);
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[6], v[7]}, ones, l_run, false);
-                }
-            // ---- O^T += V^T P^T ; P slot e' of step (kh, aa) is key 32kh + 16aa + 8(e'/4) + 4hh + e'%4.
-            // Two transposing reads per step: keys +0..3 and +8..11 of the lane group's 4-key block.
-            // the V operand of step i+1 is read while step i's MFMA runs
-            __builtin_amdgcn_s_setprio(2);
-            auto vread = [&](int i) {
-                const int mt = i >> 2, kh = (i >> 1) & 1, aa = i & 1;
-                const char* vp = st + vaddr[mt] + (32 * kh + 16 * aa) * L::ROW_B;
+    // ---- matrix work of one phase: O^T += V^T P^T for the previous tile (V slot vs), then
+    // S^T = K Q^T for the current tile (K slot ks), as one sequence of up to 32 MFMAs whose
+    // LDS operands are read kPrefetch MFMAs ahead (one 32x32x16 MFMA runs 32 cycles, an LDS
+    // read under load takes several times that).  The wave raises its issue priority so
+    // that the vector work of the other group fills the MFMA shadow rather than delaying
+    // the next MFMA.
+    constexpr int kPrefetch = 6;
+    auto mseq = [&](auto pv_tag, auto s_tag, int vs, int ks) {
+        constexpr bool PV = decltype(pv_tag)::value;
+        constexpr bool S = decltype(s_tag)::value;
+        constexpr int NPV = PV ? 4 * NM : 0;    // P.V steps: (kh, aa) major, d tile mt minor
+        constexpr int NT = NPV + (S ? 2 * NC : 0);
+        const char* vt = smem + L::V_BASE + vs * L::TILE_B;
+        const char* kt = smem + L::K_BASE + ks * L::TILE_B;
+        // operand of step i.  P.V step (kh, aa, mt): P slot e' is key 32kh + 16aa + 8(e'/4) +
+        // 4hh + e'%4, so two transposing reads (keys +0..3 and +8..11 of the lane group's 4-key
+        // block).  S step (c, kh): K rows 32kh + n, d chunk c.
+        auto operand = [&](int i) -> bf16x8 {
+            if (i < NPV) {
+                const int kk = i / NM, mt = i % NM;
+                const char* vp = vt + vaddr[mt] + (32 * (kk >> 1) + 16 * (kk & 1)) * L::ROW_B;
                 const i16x4 lo = read_tr16(vp);
                 const i16x4 hi = read_tr16(vp + 8 * L::ROW_B);
                 return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            };
-            bf16x8 va[2];
-            va[0] = vread(0);
-#pragma unroll
-            for (int i = 0; i < 4 * NM; ++i) {
-                if (i + 1 < 4 * NM) va[(i + 1) & 1] = vread(i + 1);
-                const int mt = i >> 2, kh = (i >> 1) & 1, aa = i & 1;
-                oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pb[kh][aa], oacc[mt], 0, 0, 0);
             }
-            __builtin_amdgcn_s_setprio(0);
+            const int j = i - NPV;
+            return *reinterpret_cast<const bf16x8*>(kt + kaddr[j & 1][j >> 1]);
+        };
+        bf16x8 ring[kPrefetch];
+#pragma unroll
+        for (int i = 0; i < kPrefetch; ++i)
+            if (i < NT) ring[i] = operand(i);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const bf16x8 op = ring[i % kPrefetch];
+            if (i + kPrefetch < NT) ring[i % kPrefetch] = operand(i + kPrefetch);
+            if (i < NPV) {
+                const int kk = i / NM, mt = i % NM;
+                oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pb[kk >> 1][kk & 1], oacc[mt], 0, 0, 0);
+            } else {
+                const int j = i - NPV;   // two independent chains: 32-key halves kh = j & 1
+                const f32x16 acc = j < 2 ? f32x16{} : sacc[j & 1];
+                sacc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qreg[j >> 1], acc, 0, 0, 0);
+            }
+            // keep the written order (read i+kPrefetch, MFMA i): the scheduler would otherwise
+            // hoist every read of the phase and run out of registers
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's share of tile t+1 has landed
+    };
+    auto mwork = [&](auto pv_tag, auto s_tag, int vs, int ks) {
+        __builtin_amdgcn_s_setprio(2);
+        mseq(pv_tag, s_tag, vs, ks);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // ---- vector work: online softmax of the scores of key tile kb -> P (bf16) in pb.
+    // Lane holds S[qpos][key], key = kb*64 + 32kh + 8(r/4) + 4hh + (r%4).
+    auto vwork = [&](bool mine, int kb) {
+        if (!mine) {   // tile not used by this wave's rows: its P.V adds exact zeros
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int aa = 0; aa < 2; ++aa) pb[kh][aa] = bf16x8{};
+            return;
+        }
+        const bool need_mask = (MODE != kDenseFull && kb >= my_qb) || (kb + 1) * kBC > seq;
+        if (need_mask) {
+            // key > lim is masked, lim = last allowed key of this lane's row minus the tile/lane base
+            const int lim = (MODE != kDenseFull ? min(qpos, last_key) : last_key) - (kb * kBC + 4 * hh);
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kh + 8 * (r >> 2) + (r & 3) > lim) sacc[kh][r] = -INFINITY;
+        }
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+        mx = max_halves(mx);
+        // raise the reference max only when some row outgrows it by more than the slack
+        if (__ballot((mx - m_run) * c2 > kRescaleSlack)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+            l_run *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[mt][r] *= alpha;
+            m_run = m_new;
+        }
+        const float mc = m_run * c2;
+        float lsum[2][2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int aa = 0; aa < 2; ++aa) {
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kh][8 * aa + e], c2, -mc));
+                pb[kh][aa] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
+                                    (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+                lsum[kh][aa] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            }
+        // row sum in fp32 over the unrounded probabilities (plain adds: cheaper than bf16 dot
+        // products in this phase)
+        l_run += (lsum[0][0] + lsum[0][1]) + (lsum[1][0] + lsum[1][1]);
+    };
+
+    // ---- tile pipeline.  Tile t's K goes to K slot t&1, its V to V slot t&1.  Step u (one per
+    // tile, plus a final one) issues the loads of K(u+1) and V(u), then runs two phases:
+    //   phase A: group 0 matrix work (P.V of tile u-1, S of tile u) | group 1 softmax of tile u-1
+    //   phase B: group 0 softmax of tile u | group 1 matrix work (P.V of tile u-1, S of tile u)
+    // The first step has no P.V and the final step no S; every wave of a group issues the
+    // same MFMAs (a wave whose rows skip a tile multiplies zero probabilities), so the
+    // loop body has a single form.
+    constexpr BoolTag<true> kOn{};
+    constexpr BoolTag<false> kOff{};
+    TileWalk<MODE> walk;
+    walk.init(qb_base, nrows, a.n_qblk, a.row_ptr, a.col_idx);
+    uint32_t in;
+    int kb_p = 0, kb_c = 0, kb_n = 0;
+    bool mine_p = false;
+    const bool have_any = walk.next(kb_c, in);   // uniform over the workgroup; true for every valid launch
+    bool mine_c = have_any && wave_live && ((in >> my_r) & 1);
+    bool have_n = have_any && walk.next(kb_n, in);
+    bool mine_n = have_n && wave_live && ((in >> my_r) & 1);
+    if (have_any) issue_tile<D, false>(kg, kv_row_stride, kb_c, last_key, smem_lds + L::K_BASE, wave, lane, koff);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): Q and K of tile 0 in place
+    __syncthreads();
+    auto run = [&](auto group_tag) {
+        constexpr bool kG1 = decltype(group_tag)::value;
+        if (!have_any) return;
+        // step 0
+        if (have_n)
+            issue_tile<D, false>(kg, kv_row_stride, kb_n, last_key, smem_lds + L::K_BASE + L::TILE_B, wave, lane,
+                                 koff);
+        issue_tile<D, true>(vg, kv_row_stride, kb_c, last_key, smem_lds + L::V_BASE, wave, lane, voff);
+        if constexpr (!kG1) mwork(kOff, kOn, 0, 0);
         __syncthreads();
-        buf ^= 1;
-        kb = kb_n;
-        in0 = in0_n;
-        in1 = in1_n;
-        have = have_n;
-    }
+        if constexpr (!kG1) vwork(mine_c, kb_c);
+        else mwork(kOff, kOn, 0, 0);
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of K(1), V(0) landed
+        __syncthreads();
+        // steps 1 .. T-1
+        int sl = 1;
+        while (have_n) {
+            kb_p = kb_c;
+            mine_p = mine_c;
+            kb_c = kb_n;
+            mine_c = mine_n;
+            have_n = walk.next(kb_n, in);
+            mine_n = have_n && wave_live && ((in >> my_r) & 1);
+            if (have_n)
+                issue_tile<D, false>(kg, kv_row_stride, kb_n, last_key,
+                                     smem_lds + L::K_BASE + (sl ^ 1) * L::TILE_B, wave, lane, koff);
+            issue_tile<D, true>(vg, kv_row_stride, kb_c, last_key, smem_lds + L::V_BASE + sl * L::TILE_B, wave,
+                                lane, voff);
+            if constexpr (!kG1) mwork(kOn, kOn, sl ^ 1, sl);
+            else vwork(mine_p, kb_p);
+            __syncthreads();
+            if constexpr (!kG1) vwork(mine_c, kb_c);
+            else mwork(kOn, kOn, sl ^ 1, sl);
+            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of K(u+1), V(u) landed
+            __syncthreads();
+            sl ^= 1;
+        }
+        // final step: P.V of the last tile (its V is in slot sl ^ 1)
+        if constexpr (!kG1) mwork(kOn, kOff, sl ^ 1, 0);
+        else vwork(mine_c, kb_c);
+        __syncthreads();
+        if constexpr (kG1) mwork(kOn, kOff, sl ^ 1, 0);
+    };
+    if (grp == 0)
+        run(BoolTag<false>{});
+    else
+        run(BoolTag<true>{});
 
     // ---- epilogue: O = O^T / l, lane holds O[qpos][32mt + 8(r/4) + 4hh + r%4]
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = sum_halves(l_run);
     if (!wave_live || qpos >= seq) return;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const int64_t orow = ((int64_t)b * seq + qpos) * a.hq + h;
@@ -432,7 +546,9 @@ prefill_bf16_kernel(PrefillArgs a) {
 template <int D, int MODE>
 hipError_t launch_mode(const PrefillArgs& a, hipStream_t s) {
     const int64_t nqt = (a.seq + kBR - 1) / kBR;
-    const int64_t grid = a.batch * a.hq * nqt;
+    const int64_t G = a.hq / a.hkv;
+    const int64_t per_g = (G % 2 == 0) ? (G / 2) * nqt : G * ((nqt + 1) / 2);
+    const int64_t grid = a.batch * a.hkv * per_g;
     if (a.out_f32)
         hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     else
