@@ -106,15 +106,31 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
     const float c2 = a.scale_log2;
 
+    // K and V of a 64-key step are loaded into registers one step ahead, so that a step's
+    // arithmetic overlaps the next step's HBM reads.
+    uint4 kcur[KPL], vcur[KPS];
+    auto load_step = [&](int64_t t0, uint4* kr, uint4* vr) {
+        const int64_t kidx = t0 + sk;
+        const u16* krow = kg + key_of(a, min(kidx, a1 - 1)) * row_stride;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) kr[i] = *reinterpret_cast<const uint4*>(krow + (part + 4 * i) * 8);
+#pragma unroll
+        for (int i = 0; i < KPS; ++i) {
+            const int64_t idx = min(t0 + kslot + i * KSLOTS, a1 - 1);
+            vr[i] = *reinterpret_cast<const uint4*>(vg + key_of(a, idx) * row_stride + dch * 8);
+        }
+    };
+    if (a0 < a1) load_step(a0, kcur, vcur);
+
     int buf = 0;
     for (int64_t t0 = a0; t0 < a1; t0 += kSub, buf ^= 1) {
-        // V loads for this step go out first; they are consumed after two barriers
+        uint4 knext[KPL], vnext[KPS];
+        if (t0 + kSub < a1) load_step(t0 + kSub, knext, vnext);
         uint4 vreg[KPS];
 #pragma unroll
         for (int i = 0; i < KPS; ++i) {
-            const int64_t idx = t0 + kslot + i * KSLOTS;
-            vreg[i] = idx < a1 ? *reinterpret_cast<const uint4*>(vg + key_of(a, idx) * row_stride + dch * 8)
-                               : make_uint4(0, 0, 0, 0);
+            // keys past the chunk end are clamped to its last key above; their V is zeroed here
+            vreg[i] = t0 + kslot + i * KSLOTS < a1 ? vcur[i] : make_uint4(0, 0, 0, 0);
         }
         {
             const int64_t idx = t0 + sk;
@@ -122,14 +138,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             float sc[G];
 #pragma unroll
             for (int hq = 0; hq < G; ++hq) sc[hq] = 0.0f;
-            if (valid) {
-                const u16* krow = kg + key_of(a, idx) * row_stride;
 #pragma unroll
-                for (int i = 0; i < KPL; ++i) {
-                    const uint4 kx = *reinterpret_cast<const uint4*>(krow + (part + 4 * i) * 8);
+            for (int i = 0; i < KPL; ++i) {
 #pragma unroll
-                    for (int hq = 0; hq < G; ++hq) sc[hq] = dot8(kx, qreg[hq][i], sc[hq]);
-                }
+                for (int hq = 0; hq < G; ++hq) sc[hq] = dot8(kcur[i], qreg[hq][i], sc[hq]);
             }
 #pragma unroll
             for (int hq = 0; hq < G; ++hq) {
@@ -175,6 +187,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[hq][e] = fmaf(p, vf[e], o[hq][e]);
             }
+        }
+        if (t0 + kSub < a1) {
+#pragma unroll
+            for (int i = 0; i < KPL; ++i) kcur[i] = knext[i];
+#pragma unroll
+            for (int i = 0; i < KPS; ++i) vcur[i] = vnext[i];
         }
     }
 
