@@ -5,8 +5,9 @@
 Headline workload (one step): one Llama-3.1-8B-shaped attention layer at seq 8192
 (batch 1, 32 query heads, 8 KV heads, head_dim 128, bf16, Q/K/V iid N(0,1)):
 the layer router reads the layer's queries (first/last 100 tokens -> MLP ->
-argmax), its mode is copied to the host, and the per-layer dispatcher runs the
-selected prefill kernel -- dense causal, which the router's head bias selects
+argmax) and leaves the mode on the device, and the routed dispatcher's prefill
+kernel reads it and runs the selected attention -- dense causal, which the
+router's head bias selects
 for this layer because the workload is defined as dense causal.
 `value` = useful prefill TFLOP/s (4*B*Hq*d per allowed query-key pair) of the
 whole step.
@@ -74,6 +75,29 @@ class KernelTimer:
 
     def mean_ms(self):
         return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_dense_causal_s8192_traffic.txt")
+PREFILL_SRC = os.path.join(ROOT, "long_context_attention_tiled_amd", "csrc", "prefill_bf16.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dense prefill kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the summary was taken on
+    another version of the kernel source."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+        src_hash = hashlib.sha256(open(PREFILL_SRC, "rb").read()).hexdigest()
+        if kv.get("prefill_source_sha256") != src_hash:
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def time_steps(step, steps, warmup):
@@ -156,19 +180,21 @@ def headline(args, fa, synth, torch, dev):
     w_enc, b_enc, w_head, b_head = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in w)
     b_head[0, 0] += 8.0   # the workload is dense causal: the head bias makes the router select index 0
     modes_dev = torch.empty(1, dtype=torch.int32, device=dev)
-    modes_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
     route_ws = torch.empty(fa.flux_route_workspace_size(1, Hq, d, 256), dtype=torch.uint8, device=dev)
     timer = KernelTimer()
     useful = 4.0 * B * Hq * d * causal_pairs(S)
+    algo_bytes = 2 * B * S * (2 * Hq + 2 * Hkv) * d   # Q, K, V read once and O written once, bf16
+
+    rp, ci = fa.flux_build_block_mask(S, S, 64, 128, 2048, 1, fa.FLUX_MODE_SPARSE)
+    rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
 
     def step(record=False):
+        # router -> device mode -> prefill kernels that read the mode themselves: no host round trip
         fa.flux_route_layers([q[0]], w_enc, b_enc, w_head, b_head, modes_dev, None, workspace=route_ws,
                              pool_tokens=100)
-        modes_host.copy_(modes_dev, non_blocking=True)
-        torch.cuda.current_stream().synchronize()          # the one D2H sync per request
-        m = modes_host.numpy().copy()
-        call = lambda: fa.flux_attn_prefill_layers(m, [q], [k], [v], [o], None, block=64, sink_tokens=128,
-                                                   window_tokens=2048)
+        call = lambda: fa.flux_attn_prefill_layers_routed(modes_dev, [q], [k], [v], [o], None, block=64,
+                                                          sink_tokens=128, window_tokens=2048, blk_row_ptr=rpd,
+                                                          blk_col_idx=cid)
         if record:
             timer.record(call)
         else:
@@ -183,7 +209,7 @@ def headline(args, fa, synth, torch, dev):
         step(record=True)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    assert int(modes_host[0]) == fa.FLUX_MODE_DENSE
+    assert int(modes_dev.cpu()[0]) == fa.FLUX_MODE_DENSE
     kern_ms = timer.mean_ms()
     value = useful / (ms_per_step * 1e-3) / 1e12
     achieved = useful / (kern_ms * 1e-3) / 1e12
@@ -204,7 +230,8 @@ def headline(args, fa, synth, torch, dev):
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "block": 64, "out_dtype": "bf16",
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                     "algorithmic_bytes": algo_bytes,
                      "kernel": "prefill_bf16_kernel<128, dense causal, bf16 out>",
                      "kernel_ms": round(kern_ms, 4), "useful_flops_per_launch": useful},
     }
@@ -297,13 +324,12 @@ def run_stack(fa, synth, torch, dev):
     def step():
         fa.flux_route_layers([x[0] for x in qs], w_enc, b_enc, w_head, b_head, modes_dev, None, workspace=route_ws,
                              pool_tokens=100)
-        m = modes_dev.cpu().numpy()
-        fa.flux_attn_prefill_layers(m, qs, ks, vs, [o] * L, None, block=64, sink_tokens=128, window_tokens=2048,
-                                    blk_row_ptr=rpd, blk_col_idx=cid)
-        return m
+        fa.flux_attn_prefill_layers_routed(modes_dev, qs, ks, vs, [o] * L, None, block=64, sink_tokens=128,
+                                           window_tokens=2048, blk_row_ptr=rpd, blk_col_idx=cid)
 
-    m = step()
+    step()
     torch.cuda.synchronize()
+    m = modes_dev.cpu().numpy()
     assert np.array_equal(m, plan), (m, plan)
     ms = time_steps(step, 2, 0)
     res = {"ms": round(ms, 2), "useful_flops": useful, "TFLOP/s": round(useful / ms / 1e9, 2),
@@ -313,23 +339,29 @@ def run_stack(fa, synth, torch, dev):
     return res
 
 
-def cpu_baseline(synth):
-    """fp64 CPU oracle on a bounded sample of the headline layer: every 32nd query row, all 32 heads."""
+def cpu_baseline(synth, target_s: float = 15.0):
+    """fp64 CPU oracle on a bounded sample of the headline layer: every stride-th query row of
+    all 32 heads, the stride chosen from a short calibration run so the sample takes about
+    target_s seconds on the machine's CPU share (at most 16 threads)."""
     import oracle
     B, S, Hq, Hkv, d = 1, 8192, 32, 8, 128
     log("cpu baseline: generating inputs")
     q, k, v = synth.qkv_bf16(B, S, Hq, Hkv, d, seed=1002)
-    stride = 32
-    rows = np.array([(0, h, i) for i in range(stride - 1, S, stride) for h in range(Hq)], np.int64)
-    pairs = int(sum(i + 1 for _, _, i in rows))
-    cores = len(os.sched_getaffinity(0))
-    log(f"cpu baseline: {len(rows)} rows on {cores} threads")
-    t0 = time.perf_counter()
-    oracle.attention(q, k, v, 1.0 / math.sqrt(d), causal=True, rows=rows, n_threads=cores)
-    sec = time.perf_counter() - t0
-    flops = 4.0 * d * pairs
+    cores = min(16, len(os.sched_getaffinity(0)))
+
+    def sample(stride, offset):
+        rows = np.array([(0, h, i) for i in range(offset, S, stride) for h in range(Hq)], np.int64)
+        pairs = int(sum(i + 1 for _, _, i in rows))
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, 1.0 / math.sqrt(d), causal=True, rows=rows, n_threads=cores)
+        return len(rows), 4.0 * d * pairs, time.perf_counter() - t0
+
+    _, f_cal, t_cal = sample(256, 255)
+    stride = int(max(1, min(256, round(256 * t_cal / target_s))))
+    log(f"cpu baseline: calibration {t_cal:.2f} s -> stride {stride} on {cores} threads")
+    n_rows, flops, sec = sample(stride, stride - 1)
     return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"dense causal S=8192 layer, every {stride}th query row x 32 heads ({len(rows)} rows, "
+            "sample": f"dense causal S=8192 layer, every {stride}th query row x 32 heads ({n_rows} rows, "
                       f"{flops:.3e} useful flops) in {sec:.2f} s"}
 
 

@@ -147,6 +147,29 @@ int flux_attn_prefill_layers(int32_t n_layers, const int32_t* modes_host, const 
                              void* hip_stream);
 
 /*
+ * flux_attn_prefill_layers_routed -- per-layer dispatch driven by the router's
+ * DEVICE output, with no host round trip.
+ *
+ * Same as flux_attn_prefill_layers, except that the mode of layer l is read by
+ * the prefill kernels themselves from modes_device[l] (device int32, as written
+ * by flux_route_layers into modes_out: 0 = dense causal, any other value =
+ * block-sparse) when they start.  The router ([FA] router paragraphs: argmax of
+ * the router head at inference) and the attention of the layer therefore run
+ * back to back on `hip_stream`; the host never waits for the mode.  Because
+ * any layer may turn out sparse, the CSR arguments are required and checked as
+ * for FLUX_MODE_SPARSE.  modes_device must stay valid until the launches have
+ * run.
+ */
+int flux_attn_prefill_layers_routed(int32_t n_layers, const int32_t* modes_device,
+                                    const void* const* q, const void* const* k,
+                                    const void* const* v, void* const* o, float* const* lse,
+                                    int32_t in_dtype, int32_t out_dtype, int64_t batch, int64_t seq,
+                                    int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                                    int32_t block, int32_t sink_tokens, int32_t window_tokens,
+                                    const int32_t* blk_row_ptr, const int32_t* blk_col_idx,
+                                    int64_t blk_nnz, void* hip_stream);
+
+/*
  * flux_decode_workspace_size -- bytes of workspace flux_attn_decode needs.
  * Same meaning of arguments as flux_attn_decode (num_splits = 0: automatic;
  * the automatic split count depends on batch * hkv, so hkv is needed here).

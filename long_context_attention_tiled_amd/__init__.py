@@ -17,7 +17,7 @@ import numpy as np
 
 __all__ = [
     "FluxError", "lib", "status_string", "last_error_detail", "flux_version",
-    "flux_build_block_mask", "flux_attn_prefill", "flux_attn_prefill_layers",
+    "flux_build_block_mask", "flux_attn_prefill", "flux_attn_prefill_layers", "flux_attn_prefill_layers_routed",
     "flux_decode_workspace_size", "flux_attn_decode", "flux_route_workspace_size", "flux_route_layers",
     "FLUX_OK", "FLUX_ERR_INVALID_ARG", "FLUX_ERR_UNSUPPORTED", "FLUX_ERR_CAPACITY", "FLUX_ERR_WORKSPACE",
     "FLUX_ERR_HIP", "FLUX_DTYPE_BF16", "FLUX_DTYPE_F32", "FLUX_MODE_DENSE", "FLUX_MODE_SPARSE",
@@ -30,7 +30,8 @@ FLUX_MODE_DENSE, FLUX_MODE_SPARSE = 0, 1
 
 EXPORTED_SYMBOLS = (
     "flux_status_string", "flux_last_error_detail", "flux_version", "flux_build_block_mask",
-    "flux_attn_prefill", "flux_attn_prefill_layers", "flux_decode_workspace_size", "flux_attn_decode",
+    "flux_attn_prefill", "flux_attn_prefill_layers", "flux_attn_prefill_layers_routed",
+    "flux_decode_workspace_size", "flux_attn_decode",
     "flux_route_workspace_size", "flux_route_layers",
 )
 
@@ -61,6 +62,9 @@ _lib.flux_attn_prefill.restype = ctypes.c_int
 _lib.flux_attn_prefill_layers.argtypes = [_i32, _vp, _pp, _pp, _pp, _pp, _pp, _i32, _i32, _i64, _i64, _i32, _i32,
                                           _i32, _f32, _i32, _i32, _i32, _vp, _vp, _i64, _vp]
 _lib.flux_attn_prefill_layers.restype = ctypes.c_int
+_lib.flux_attn_prefill_layers_routed.argtypes = [_i32, _vp, _pp, _pp, _pp, _pp, _pp, _i32, _i32, _i64, _i64, _i32,
+                                                 _i32, _i32, _f32, _i32, _i32, _i32, _vp, _vp, _i64, _vp]
+_lib.flux_attn_prefill_layers_routed.restype = ctypes.c_int
 _lib.flux_decode_workspace_size.argtypes = [_i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32]
 _lib.flux_decode_workspace_size.restype = _sz
 _lib.flux_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _f32,
@@ -187,6 +191,33 @@ def flux_attn_prefill_layers(modes_host, qs, ks, vs, os_, lses=None, *, block: i
                                          _dtype_code(os_[0]), B, S, Hq, Hkv, d, scale, block, sink_tokens,
                                          window_tokens, _ptr(blk_row_ptr), _ptr(blk_col_idx), nnz, _stream(stream)),
            "flux_attn_prefill_layers")
+
+
+def flux_attn_prefill_layers_routed(modes_dev, qs, ks, vs, os_, lses=None, *, block: int = 64,
+                                    sink_tokens: int = 128, window_tokens: int = 2048, blk_row_ptr=None,
+                                    blk_col_idx=None, scale: float | None = None, stream=None):
+    """Per-layer dispatch with the modes left on the device (int32 tensor of len(qs) entries, e.g. the
+    modes_out of flux_route_layers): the kernels read layer l's mode themselves, no host round trip.
+    The block-sparse CSR is required."""
+    L = len(qs)
+    import torch
+    if modes_dev.dtype != torch.int32 or modes_dev.numel() != L or not modes_dev.is_contiguous():
+        raise ValueError("modes_dev must be a contiguous int32 device tensor with one entry per layer")
+    B, S, Hq, d = qs[0].shape
+    Hkv = ks[0].shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    pq, _a = _ptr_array(qs)
+    pk, _b = _ptr_array(ks)
+    pv, _c = _ptr_array(vs)
+    po, _d = _ptr_array(os_)
+    pl, _e = _ptr_array(lses) if lses is not None else (None, None)
+    nnz = int(blk_col_idx.numel()) if blk_col_idx is not None else 0
+    _check(_lib.flux_attn_prefill_layers_routed(L, _ptr(modes_dev), pq, pk, pv, po, pl, _dtype_code(qs[0]),
+                                                _dtype_code(os_[0]), B, S, Hq, Hkv, d, scale, block, sink_tokens,
+                                                window_tokens, _ptr(blk_row_ptr), _ptr(blk_col_idx), nnz,
+                                                _stream(stream)),
+           "flux_attn_prefill_layers_routed")
 
 
 def flux_decode_workspace_size(batch, hq, hkv, kv_len, head_dim, mode=FLUX_MODE_DENSE, block=64, sink_tokens=128,

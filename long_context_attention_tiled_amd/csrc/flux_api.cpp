@@ -157,6 +157,7 @@ int check_prefill(const void* q, const void* k, const void* v, void* o, float* l
     a->n_qblk = (int)ceil_div(seq, 64);
     a->row_ptr = ms.sparse ? rp : nullptr;
     a->col_idx = ms.sparse ? ci : nullptr;
+    a->mode_dev = nullptr;
     return FLUX_OK;
 }
 
@@ -309,6 +310,41 @@ int flux_attn_prefill_layers(int32_t n_layers, const int32_t* modes_host, const 
         check_prefill(q[l], k[l], v[l], o[l], lse ? lse[l] : nullptr, in_dtype, out_dtype, batch, seq, hq, hkv,
                       head_dim, scale, 1, modes_host[l], block, sink_tokens, window_tokens, blk_row_ptr, blk_col_idx,
                       blk_nnz, &a);
+        int st = launch_prefill(a, in_dtype, as_stream(hip_stream));
+        if (st != FLUX_OK) return st;
+    }
+    return ok();
+}
+
+int flux_attn_prefill_layers_routed(int32_t n_layers, const int32_t* modes_device, const void* const* q,
+                                    const void* const* k, const void* const* v, void* const* o, float* const* lse,
+                                    int32_t in_dtype, int32_t out_dtype, int64_t batch, int64_t seq, int32_t hq,
+                                    int32_t hkv, int32_t head_dim, float scale, int32_t block, int32_t sink_tokens,
+                                    int32_t window_tokens, const int32_t* blk_row_ptr, const int32_t* blk_col_idx,
+                                    int64_t blk_nnz, void* hip_stream) {
+    if (n_layers < 1) return fail(FLUX_ERR_INVALID_ARG, "n_layers must be >= 1");
+    if (!modes_device || !q || !k || !v || !o) return fail(FLUX_ERR_INVALID_ARG, "layer arrays must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(modes_device) & 3u)
+        return fail(FLUX_ERR_INVALID_ARG, "modes_device must be 4-byte aligned");
+    // every layer is validated as block-sparse (the stricter case: it needs the CSR); the
+    // kernels read the layer's mode from modes_device[l] when they start
+    for (int32_t l = 0; l < n_layers; ++l) {
+        flux::PrefillArgs a;
+        int st = check_prefill(q[l], k[l], v[l], o[l], lse ? lse[l] : nullptr, in_dtype, out_dtype, batch, seq, hq,
+                               hkv, head_dim, scale, 1, FLUX_MODE_SPARSE, block, sink_tokens, window_tokens,
+                               blk_row_ptr, blk_col_idx, blk_nnz, &a);
+        if (st != FLUX_OK) {
+            char tmp[512];
+            snprintf(tmp, sizeof tmp, "layer %d: %s", l, g_detail);
+            return fail(st, "%s", tmp);
+        }
+    }
+    for (int32_t l = 0; l < n_layers; ++l) {
+        flux::PrefillArgs a;
+        check_prefill(q[l], k[l], v[l], o[l], lse ? lse[l] : nullptr, in_dtype, out_dtype, batch, seq, hq, hkv,
+                      head_dim, scale, 1, FLUX_MODE_SPARSE, block, sink_tokens, window_tokens, blk_row_ptr,
+                      blk_col_idx, blk_nnz, &a);
+        a.mode_dev = modes_device + l;
         int st = launch_prefill(a, in_dtype, as_stream(hip_stream));
         if (st != FLUX_OK) return st;
     }

@@ -28,6 +28,8 @@ struct PrefillArgs {
     int n_qblk;            // ceil(seq / 64)
     const int32_t* row_ptr;  // sparse CSR (device) or nullptr
     const int32_t* col_idx;
+    const int32_t* mode_dev;  // device-resident mode of this layer (0 dense causal, else sparse),
+                              // read by the kernel; nullptr when the mode is fixed by `sparse`
 };
 
 struct DecodeArgs {

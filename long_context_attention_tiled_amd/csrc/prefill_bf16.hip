@@ -141,7 +141,8 @@ __device__ __forceinline__ int xcd_remap(int x, int total) {
     return (x % kXcd) * per + x / kXcd;
 }
 
-enum Mode { kDenseCausal = 0, kDenseFull = 1, kSparse = 2 };
+// kRouted: causal, dense or sparse as the layer's device-resident mode says (read at start)
+enum Mode { kDenseCausal = 0, kDenseFull = 1, kSparse = 2, kRouted = 3 };
 
 template <bool B>
 struct BoolTag {
@@ -157,25 +158,27 @@ struct TileWalk {
     int next_kb, last_kb, qb_base, nvalid;
     int p0, p1, p2, p3, e0, e1, e2, e3;   // CSR cursors and ends of the (up to 4) query blocks
     const int32_t* ci;
+    bool sparse;
 
-    __device__ void init(int qb_base_, int nrows, int n_qblk, const int32_t* rp, const int32_t* ci_) {
+    __device__ void init(int qb_base_, int nrows, int n_qblk, const int32_t* rp, const int32_t* ci_,
+                         const int32_t* mode_dev) {
         qb_base = qb_base_;
         nvalid = max(0, min(nrows, n_qblk - qb_base));
         ci = ci_;
-        if constexpr (MODE == kSparse) {
+        sparse = MODE == kSparse || (MODE == kRouted && mode_dev[0] != 0);
+        next_kb = 0;
+        last_kb = MODE == kDenseFull ? n_qblk - 1 : qb_base + nvalid - 1;
+        if (sparse) {
             p0 = p1 = p2 = p3 = e0 = e1 = e2 = e3 = 0;
             if (nvalid > 0) p0 = rp[qb_base], e0 = rp[qb_base + 1];
             if (nvalid > 1) p1 = rp[qb_base + 1], e1 = rp[qb_base + 2];
             if (nvalid > 2) p2 = rp[qb_base + 2], e2 = rp[qb_base + 3];
             if (nvalid > 3) p3 = rp[qb_base + 3], e3 = rp[qb_base + 4];
-        } else {
-            next_kb = 0;
-            last_kb = MODE == kDenseCausal ? qb_base + nvalid - 1 : n_qblk - 1;
         }
     }
 
     __device__ bool next(int& kb, uint32_t& in) {
-        if constexpr (MODE == kSparse) {
+        if (sparse) {
             const int big = 0x7fffffff;
             const int c0 = p0 < e0 ? ci[p0] : big;
             const int c1 = p1 < e1 ? ci[p1] : big;
@@ -263,7 +266,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     if (pair_heads) {                    // groups = query heads 2jp, 2jp+1 of g, same rows
         const int jp = unit % (G / 2);
         const int rank = unit / (G / 2);
-        qt = (MODE == kDenseCausal) ? nqt - 1 - rank : rank;
+        qt = (MODE != kDenseFull) ? nqt - 1 - rank : rank;   // causal: longest first
         h = g * G + 2 * jp + grp;
         qb_base = 2 * qt;
         my_r = wq >> 1;
@@ -272,7 +275,7 @@ prefill_bf16_kernel(PrefillArgs a) {
         const int npq = (nqt + 1) / 2;
         const int j = unit % G;
         const int rank = unit / G;
-        const int qp = (MODE == kDenseCausal) ? npq - 1 - rank : rank;
+        const int qp = (MODE != kDenseFull) ? npq - 1 - rank : rank;
         h = g * G + j;
         qt = 2 * qp + grp;
         qb_base = 4 * qp;
@@ -458,7 +461,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     constexpr BoolTag<true> kOn{};
     constexpr BoolTag<false> kOff{};
     TileWalk<MODE> walk;
-    walk.init(qb_base, nrows, a.n_qblk, a.row_ptr, a.col_idx);
+    walk.init(qb_base, nrows, a.n_qblk, a.row_ptr, a.col_idx, a.mode_dev);
     uint32_t in;
     int kb_p = 0, kb_c = 0, kb_n = 0;
     bool mine_p = false;
@@ -558,6 +561,7 @@ hipError_t launch_mode(const PrefillArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_dim(const PrefillArgs& a, hipStream_t s) {
+    if (a.mode_dev) return launch_mode<D, kRouted>(a, s);
     if (a.sparse) return launch_mode<D, kSparse>(a, s);
     if (a.causal) return launch_mode<D, kDenseCausal>(a, s);
     return launch_mode<D, kDenseFull>(a, s);

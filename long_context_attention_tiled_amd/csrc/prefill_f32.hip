@@ -46,15 +46,16 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
     float m_run = kNegBig, l_run = 0.0f;
     const float c2 = a.scale_log2;
 
+    const bool sparse = a.mode_dev ? a.mode_dev[0] != 0 : a.sparse != 0;
     int p = 0, e = 0;
-    if (a.sparse) {
+    if (sparse) {
         p = a.row_ptr[qb];
         e = a.row_ptr[qb + 1];
     } else {
         e = a.causal ? qb + 1 : a.n_qblk;
     }
     for (; p < e; ++p) {
-        const int kb = a.sparse ? a.col_idx[p] : p;
+        const int kb = sparse ? a.col_idx[p] : p;
         __syncthreads();
         for (int idx = tid; idx < kTile * D / 4; idx += kThreads) {
             const int row = idx / (D / 4), c4 = idx % (D / 4);
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
             acc += __shfl_xor(acc, 1);
             acc += __shfl_xor(acc, 2);
             const int64_t key = (int64_t)kb * kTile + jk;
-            const bool off = key >= a.seq || ((a.causal || a.sparse) && key > qpos);
+            const bool off = key >= a.seq || ((a.causal || sparse) && key > qpos);
             s[jk] = off ? -INFINITY : acc;
             mx = fmaxf(mx, s[jk]);
         }

@@ -6,8 +6,9 @@
 // Three small kernels over a caller-provided workspace, each spread over the
 // whole chip (the encoder weights, 4 MiB per layer at 32 heads x 128 and hidden
 // 256, are the bulk of the bytes):
-//   pool    -- grid (layers, features/256): a thread owns one feature and sums
-//              the P + P pooled rows (coalesced across threads) -> pooled [L, F];
+//   pool    -- grid (layers, features/512), 16 waves: a lane owns 8 features (one
+//              16-byte load per token), the pooled tokens are dealt to the waves and
+//              the 16 partial sums are added in a fixed order -> pooled [L, F];
 //   encoder -- grid (layers, hidden/4): one wave per hidden unit, 16-byte weight
 //              loads, wave reduction, ReLU -> z [L, hidden];
 //   head    -- one wave per layer: both logits, argmax (a tie selects dense).
@@ -16,7 +17,8 @@
 namespace flux {
 namespace {
 
-constexpr int kPoolThreads = 256;
+constexpr int kPoolWaves = 16;     // pooled tokens are dealt to 16 waves
+constexpr int kPoolFeat = 512;     // features per pooling workgroup (64 lanes x 8)
 constexpr int kEncThreads = 256;   // 4 waves = 4 hidden units per workgroup
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -25,26 +27,51 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-__global__ __launch_bounds__(256) void route_pool_kernel(RouteArgs a) {
+__global__ __launch_bounds__(kPoolWaves * 64) void route_pool_kernel(RouteArgs a) {
+    __shared__ float red[kPoolWaves][kPoolFeat];
     const int li = blockIdx.x;
-    const int f = blockIdx.y * kPoolThreads + threadIdx.x;
-    if (f >= a.n_feat) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t nf = a.n_feat;
+    const int64_t f0 = (int64_t)blockIdx.y * kPoolFeat + lane * 8;   // this lane's 8 features
     const int64_t P = a.pool_tokens;
     const int64_t head_end = min<int64_t>(P, a.seq);
     const int64_t tail_begin = max<int64_t>(a.seq - P, head_end);   // token indices counted once
     const int64_t n_tok = head_end + (a.seq - tail_begin);
-    const int64_t nf = a.n_feat;
-    float acc = 0.0f;
-    if (a.in_f32) {
-        const float* x = reinterpret_cast<const float*>(a.xq[li]) + f;
-        for (int64_t t = 0; t < head_end; ++t) acc += x[t * nf];
-        for (int64_t t = tail_begin; t < a.seq; ++t) acc += x[t * nf];
-    } else {
-        const unsigned short* x = reinterpret_cast<const unsigned short*>(a.xq[li]) + f;
-        for (int64_t t = 0; t < head_end; ++t) acc += __uint_as_float((unsigned)x[t * nf] << 16);
-        for (int64_t t = tail_begin; t < a.seq; ++t) acc += __uint_as_float((unsigned)x[t * nf] << 16);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (f0 < nf) {
+        // pooled token j (wave-strided): j < head_end -> token j, else tail_begin + j - head_end
+#pragma unroll 4
+        for (int64_t j = wave; j < n_tok; j += kPoolWaves) {
+            const int64_t t = j < head_end ? j : tail_begin + (j - head_end);
+            if (a.in_f32) {
+                const float4* x = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.xq[li]) + t * nf + f0);
+                const float4 u0 = x[0], u1 = x[1];
+                acc[0] += u0.x; acc[1] += u0.y; acc[2] += u0.z; acc[3] += u0.w;
+                acc[4] += u1.x; acc[5] += u1.y; acc[6] += u1.z; acc[7] += u1.w;
+            } else {
+                const uint4 u = *reinterpret_cast<const uint4*>(
+                    reinterpret_cast<const unsigned short*>(a.xq[li]) + t * nf + f0);
+                const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += __uint_as_float(w[e] << 16);
+                    acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+                }
+            }
+        }
     }
-    a.pooled[(int64_t)(a.layer0 + li) * nf + f] = acc / (float)n_tok;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][lane * 8 + e] = acc[e];
+    __syncthreads();
+    // fixed-order sum over the waves: the result does not depend on scheduling
+    const int c = threadIdx.x;
+    const int64_t f = (int64_t)blockIdx.y * kPoolFeat + c;
+    if (c < kPoolFeat && f < nf) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kPoolWaves; ++w) sum += red[w][c];
+        a.pooled[(int64_t)(a.layer0 + li) * nf + f] = sum / (float)n_tok;
+    }
 }
 
 __global__ __launch_bounds__(256) void route_encoder_kernel(RouteArgs a) {
@@ -56,6 +83,7 @@ __global__ __launch_bounds__(256) void route_encoder_kernel(RouteArgs a) {
     const float4* w = reinterpret_cast<const float4*>(a.w_enc + ((int64_t)layer * a.hidden + u) * a.n_feat);
     const float4* x = reinterpret_cast<const float4*>(a.pooled + (int64_t)layer * a.n_feat);
     float acc = 0.0f;
+#pragma unroll 4
     for (int i = lane; i < nf4; i += 64) {
         const float4 wv = w[i], xv = x[i];
         acc = fmaf(wv.x, xv.x, acc);
@@ -91,8 +119,8 @@ __global__ __launch_bounds__(64) void route_head_kernel(RouteArgs a) {
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(route_pool_kernel, dim3(a.n_layers, (a.n_feat + kPoolThreads - 1) / kPoolThreads),
-                       dim3(kPoolThreads), 0, s, a);
+    hipLaunchKernelGGL(route_pool_kernel, dim3(a.n_layers, (a.n_feat + kPoolFeat - 1) / kPoolFeat),
+                       dim3(kPoolWaves * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(route_encoder_kernel, dim3(a.n_layers, (a.hidden + 3) / 4), dim3(kEncThreads), 0, s, a);

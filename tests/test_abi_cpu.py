@@ -166,6 +166,25 @@ def test_prefill_layers_validation(fa):
     assert st == fa.FLUX_ERR_INVALID_ARG
 
 
+def test_prefill_layers_routed_validation(fa):
+    """Device-mode dispatch: every layer is checked as block-sparse (the CSR is required), the
+    modes pointer must be present and aligned; all failures are reported before any launch."""
+    L = 2
+    P = ctypes.POINTER(ctypes.c_void_p)
+    ptrs = (ctypes.c_void_p * L)(FAKE, FAKE)
+    pp = ctypes.cast(ptrs, P)
+
+    def call(n_layers=L, modes=FAKE, rp=FAKE, ci=FAKE, nnz=26, seq=512):
+        return fa.lib().flux_attn_prefill_layers_routed(n_layers, modes, pp, pp, pp, pp, None, 0, 1, 1, seq, 4, 2,
+                                                        128, 0.088, 64, 128, 128, rp, ci, nnz, None)
+    E = fa.FLUX_ERR_INVALID_ARG
+    assert call(n_layers=0) == E
+    assert call(modes=None) == E
+    assert call(modes=FAKE + 2) == E and "modes_device" in fa.last_error_detail()
+    assert call(rp=None) == E and "layer 0" in fa.last_error_detail()
+    assert call(nnz=25) == E and "blk_nnz" in fa.last_error_detail()
+
+
 # ---------------------------------------------------------------- decode validation / workspace
 def test_decode_workspace_size(fa):
     B, Hq, Hkv, L, d = 8, 32, 8, 262144, 128

@@ -191,3 +191,57 @@ def test_routed_stack_layers_s131072_sampled(fa):
         check_lse(np.array([l_h[b, h, i] for b, h, i in rows]), ref_lse, f"stack layer {l} lse")
     del qs, ks, vs, os_, ls
     torch.cuda.empty_cache()
+
+
+def test_routed_dispatch_reads_device_modes(fa):
+    """flux_attn_prefill_layers_routed: the router's device output selects each layer's mode with
+    no host round trip.  Layers forced dense / sparse through the router head bias; outputs must
+    equal the host-dispatched run bit for bit and match the oracle."""
+    B, S, Hq, Hkv, d = 1, 700, 8, 2, 128
+    L = 3
+    plan = np.array([1, 0, 1], np.int32)
+    say("routed dispatch", plan)
+    host = [synth.qkv_bf16(B, S, Hq, Hkv, d, seed=60 + l) for l in range(L)]
+    qs, ks, vs = ([synth.torch_bf16_from_bits(h[i]) for h in host] for i in range(3))
+    w = synth.router_weights(L, Hq * d, 64, seed=61)
+    w_enc, b_enc, w_head, b_head = (torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in w)
+    for l in range(L):
+        b_head[l, int(plan[l])] += 50.0
+    modes = torch.empty(L, dtype=torch.int32, device=DEV)
+    fa.flux_route_layers([x[0] for x in qs], w_enc, b_enc, w_head, b_head, modes, None, pool_tokens=100)
+    rp, ci = _csr_dev(fa, S, 128, 256)
+    o_r = [torch.empty((B, S, Hq, d), dtype=torch.float32, device=DEV) for _ in range(L)]
+    l_r = [torch.empty((B, Hq, S), dtype=torch.float32, device=DEV) for _ in range(L)]
+    fa.flux_attn_prefill_layers_routed(modes, qs, ks, vs, o_r, l_r, block=64, sink_tokens=128, window_tokens=256,
+                                       blk_row_ptr=rp, blk_col_idx=ci)
+    o_h = [torch.empty_like(x) for x in o_r]
+    l_h = [torch.empty_like(x) for x in l_r]
+    fa.flux_attn_prefill_layers(plan, qs, ks, vs, o_h, l_h, block=64, sink_tokens=128, window_tokens=256,
+                                blk_row_ptr=rp, blk_col_idx=ci)
+    torch.cuda.synchronize()
+    assert np.array_equal(modes.cpu().numpy(), plan)
+    for l in range(L):
+        assert torch.equal(o_r[l], o_h[l]) and torch.equal(l_r[l], l_h[l]), f"layer {l}"
+        q, k, v = host[l]
+        ref, ref_lse = oracle.attention(q, k, v, default_scale(d), causal=True, sparse=bool(plan[l]), block=64,
+                                        sink_tokens=128, window_tokens=256)
+        check_close(o_r[l].cpu().numpy(), ref, f"routed layer {l}")
+        check_lse(l_r[l].cpu().numpy(), np.transpose(ref_lse, (0, 2, 1)), f"routed layer {l} lse")
+
+
+def test_routed_dispatch_fp32_inputs(fa):
+    """The fp32-input kernel reads the device mode too."""
+    B, S, H, d = 1, 384, 2, 64
+    say("routed dispatch fp32")
+    q, k, v = synth.qkv_f32(B, S, H, H, d, seed=62)
+    qd, kd, vd = (torch.from_numpy(x).to(DEV) for x in (q, k, v))
+    rp, ci = _csr_dev(fa, S, 128, 128)
+    for mode in (0, 1):
+        modes = torch.tensor([mode], dtype=torch.int32, device=DEV)
+        o = torch.empty((B, S, H, d), dtype=torch.float32, device=DEV)
+        fa.flux_attn_prefill_layers_routed(modes, [qd], [kd], [vd], [o], None, block=64, sink_tokens=128,
+                                           window_tokens=128, blk_row_ptr=rp, blk_col_idx=ci)
+        torch.cuda.synchronize()
+        ref, _ = oracle.attention(q, k, v, 1.0 / 8, causal=True, sparse=bool(mode), block=64, sink_tokens=128,
+                                  window_tokens=128)
+        check_close(o.cpu().numpy(), ref, f"routed fp32 mode {mode}")
