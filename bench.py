@@ -232,7 +232,7 @@ def headline(args, fa, synth, torch, dev):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "algorithmic_bytes": algo_bytes,
-                     "kernel": "prefill_bf16_kernel<128, dense causal, bf16 out>",
+                     "kernel": "prefill_bf16_kernel<128, routed: dense causal, bf16 out>",
                      "kernel_ms": round(kern_ms, 4), "useful_flops_per_launch": useful},
     }
     del q, k, v, o
