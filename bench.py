@@ -76,6 +76,11 @@ class KernelTimer:
     def mean_ms(self):
         return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
 
+    def pct_ms(self):
+        """(p10, median, p90) of the recorded launch durations."""
+        d = np.array([s.elapsed_time(e) for s, e in self.pairs])
+        return tuple(round(float(np.percentile(d, q)), 4) for q in (10, 50, 90))
+
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_dense_causal_s8192_traffic.txt")
 PREFILL_SRC = os.path.join(ROOT, "long_context_attention_tiled_amd", "csrc", "prefill_bf16.hip")
@@ -117,8 +122,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="sparse,decode",
-                    help="comma list of secondary legs: sparse, dense64k, decode, stack (or 'none')")
+    ap.add_argument("--legs", default="sparse,decode,peaks",
+                    help="comma list of secondary legs: sparse, dense64k, decode, stack, peaks (or 'none')")
     ap.add_argument("--no-legs", dest="legs", action="store_const", const="none")
     ap.add_argument("--no-headline", dest="headline", action="store_false", default=True,
                     help="skip the headline step (profiling a single leg)")
@@ -233,7 +238,8 @@ def headline(args, fa, synth, torch, dev):
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "algorithmic_bytes": algo_bytes,
                      "kernel": "prefill_bf16_kernel<128, routed: dense causal, bf16 out>",
-                     "kernel_ms": round(kern_ms, 4), "useful_flops_per_launch": useful},
+                     "kernel_ms": round(kern_ms, 4), "kernel_ms_p10_p50_p90": timer.pct_ms(),
+                     "useful_flops_per_launch": useful},
     }
     del q, k, v, o
     torch.cuda.empty_cache()
@@ -299,7 +305,30 @@ def run_legs(fa, synth, torch, dev, sel, reps):
 
     if "stack" in sel:
         legs["stack_s131072"] = run_stack(fa, synth, torch, dev)
+    if "peaks" in sel:
+        legs["device_ceilings"] = run_peaks(torch, dev)
     return legs
+
+
+def run_peaks(torch, dev):
+    """Context for the roofline fractions: what vendor library kernels reach on this device with
+    the same kind of data (random N(0,1) bf16) -- a bf16 GEMM (hipBLASLt via torch.matmul) and a
+    device-to-device copy.  Not part of the attention path."""
+    log("leg: device ceilings")
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    gemm = lambda: torch.matmul(a, b)
+    ms_g = time_steps(gemm, 20, 3)
+    x = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    copy = lambda: y.copy_(x)
+    ms_c = time_steps(copy, 20, 3)
+    res = {"gemm_bf16_8192_TFLOP/s": round(2.0 * n ** 3 / ms_g / 1e9, 1),
+           "copy_2GiB_GB/s_read_plus_write": round(2.0 * x.numel() / ms_c / 1e6, 1)}
+    del a, b, x, y
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_stack(fa, synth, torch, dev):
