@@ -122,8 +122,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="sparse,decode,peaks",
-                    help="comma list of secondary legs: sparse, dense64k, decode, stack, peaks (or 'none')")
+    ap.add_argument("--legs", default="sparse,decode,decode_loop,peaks",
+                    help="comma list of secondary legs: sparse, dense64k, decode, decode_loop, stack, peaks "
+                         "(or 'none')")
     ap.add_argument("--no-legs", dest="legs", action="store_const", const="none")
     ap.add_argument("--no-headline", dest="headline", action="store_false", default=True,
                     help="skip the headline step (profiling a single leg)")
@@ -305,9 +306,58 @@ def run_legs(fa, synth, torch, dev, sel, reps):
 
     if "stack" in sel:
         legs["stack_s131072"] = run_stack(fa, synth, torch, dev)
+    if "decode_loop" in sel:
+        legs["decode_loop_36l_L262144"] = run_decode_loop(fa, synth, torch, dev)
     if "peaks" in sel:
         legs["device_ceilings"] = run_peaks(torch, dev)
     return legs
+
+
+def run_decode_loop(fa, synth, torch, dev, steps=5):
+    """One decode step of a 36-layer routed stack at position 262143 (batch 8, 32/8 heads, head_dim 128):
+    each layer appends its new token and attends from it (flux_decode_step_layers); the 12 dense layers
+    (seeded plan) stream a full 262144-row cache, the 24 sparse layers a 2176-row window cache.
+    Compared with the same step when every layer is dense.  The all-dense run reuses the 12 dense
+    caches three times each (36 distinct 8.6 GB caches would not fit in HBM); every layer call still
+    streams its whole cache from HBM."""
+    L, B, Hq, Hkv, d, S = 36, 8, 32, 8, 128, 262144
+    sink, window = 128, 2048
+    log("leg: routed decode loop, generating caches")
+    plan = synth.layer_mode_draw(L, 12, seed=1004)
+    wrows = fa.flux_window_cache_rows(64, sink, window)
+    dense_k = [synth.torch_normal((B, S, Hkv, d), 3000 + 2 * i, torch.bfloat16) for i in range(12)]
+    dense_v = [synth.torch_normal((B, S, Hkv, d), 3001 + 2 * i, torch.bfloat16) for i in range(12)]
+    win_k = [synth.torch_normal((B, wrows, Hkv, d), 3100 + 2 * i, torch.bfloat16) for i in range(24)]
+    win_v = [synth.torch_normal((B, wrows, Hkv, d), 3101 + 2 * i, torch.bfloat16) for i in range(24)]
+    qs = [synth.torch_normal((B, Hq, d), 3200 + l, torch.bfloat16) for l in range(L)]
+    kn = [synth.torch_normal((B, Hkv, d), 3300 + l, torch.bfloat16) for l in range(L)]
+    vn = [synth.torch_normal((B, Hkv, d), 3400 + l, torch.bfloat16) for l in range(L)]
+    os_ = [torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    ws = torch.empty(fa.flux_decode_workspace_size(B, Hq, Hkv, S, d, 0, 64, sink, window), dtype=torch.uint8,
+                     device=dev)
+    kc, vc, di, wi = [], [], 0, 0
+    for l in range(L):
+        if plan[l] == 0:
+            kc.append(dense_k[di]); vc.append(dense_v[di]); di += 1
+        else:
+            kc.append(win_k[wi]); vc.append(win_v[wi]); wi += 1
+    routed = lambda: fa.flux_decode_step_layers(plan, qs, kn, vn, kc, vc, os_, None, pos=S - 1, dense_cache_rows=S,
+                                                sink_tokens=sink, window_tokens=window, workspace=ws)
+    ms_r = time_steps(routed, steps, 1)
+    dense_kc = [dense_k[l % 12] for l in range(L)]
+    dense_vc = [dense_v[l % 12] for l in range(L)]
+    all_dense = lambda: fa.flux_decode_step_layers(np.zeros(L, np.int32), qs, kn, vn, dense_kc, dense_vc, os_, None,
+                                                   pos=S - 1, dense_cache_rows=S, sink_tokens=sink,
+                                                   window_tokens=window, workspace=ws)
+    ms_d = time_steps(all_dense, steps, 1)
+    bytes_r = int(12 * B * Hkv * S * d * 4 + 24 * B * Hkv * (sink + window) * d * 4)
+    res = {"routed_ms": round(ms_r, 3), "routed_tok/s": round(B / (ms_r * 1e-3), 1),
+           "all_dense_ms": round(ms_d, 3), "all_dense_tok/s": round(B / (ms_d * 1e-3), 1),
+           "speedup": round(ms_d / ms_r, 3), "dense_layers": int((plan == 0).sum()),
+           "routed_kv_GB/s": round(bytes_r / ms_r / 1e6, 1)}
+    del dense_k, dense_v, win_k, win_v, kc, vc, dense_kc, dense_vc
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_peaks(torch, dev):

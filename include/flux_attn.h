@@ -65,6 +65,12 @@ extern "C" {
 #define FLUX_MODE_DENSE 0  /* pi_FA: full (dense) attention   */
 #define FLUX_MODE_SPARSE 1 /* pi_SA: block-sparse attention   */
 
+/* ---- KV-cache layouts (decode) ----------------------------------------- */
+#define FLUX_KV_FULL 0   /* [batch, rows, hkv, head_dim]: token t at row t                       */
+#define FLUX_KV_WINDOW 1 /* [batch, sink+window, hkv, head_dim]: token t < sink at row t; a later  \
+                            token t at row sink + ((t/64) mod (window/64))*64 + t mod 64 (a ring  \
+                            of window blocks; a block's slot is reused once it has left the window) */
+
 /* Static text for a status code (never NULL). */
 const char* flux_status_string(int status);
 
@@ -208,6 +214,51 @@ int flux_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
                      int32_t num_splits, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * flux_window_cache_rows -- rows of a FLUX_KV_WINDOW cache: sink_tokens + window_tokens.
+ * Returns 0 if block != 64 or sink/window are not valid multiples of block (window >= block).
+ */
+int64_t flux_window_cache_rows(int32_t block, int32_t sink_tokens, int32_t window_tokens);
+
+/*
+ * flux_decode_step -- append one token to a layer's KV cache and attend from it.
+ *
+ * The decode loop of a routed model ([FA] architecture paragraph: a sparse layer loads only its sink
+ * and window KV; layer-granularity paragraph: one mode per layer).  For each sequence b the new token
+ * sits at position pos (all sequences of the batch advance together): its key/value k_new, v_new
+ * [batch, hkv, head_dim] bf16 are stored into the cache and the query q [batch, hq, head_dim] bf16
+ * attends to tokens 0..pos under `mode` exactly as flux_attn_decode with kv_len = pos + 1 (the new
+ * token is read from k_new / v_new by the same launch, so the store and the reads never race).
+ *   layout FLUX_KV_FULL:   k_cache/v_cache [batch, cache_rows, hkv, head_dim], cache_rows > pos, any mode;
+ *   layout FLUX_KV_WINDOW: cache_rows == flux_window_cache_rows(block, sink, window), mode SPARSE; the
+ *     tokens the sparse pattern can still reach (sink and last window blocks) are all the cache keeps.
+ * Earlier tokens must already be in the cache (written by earlier steps or by the caller).
+ * workspace: flux_decode_workspace_size(batch, hq, hkv, pos + 1, head_dim, mode, block, sink, window,
+ * num_splits) bytes.  out_dtype BF16 or F32; lse [batch, hq] fp32 or NULL.
+ */
+int flux_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                     void* v_cache, void* o, float* lse, int32_t out_dtype, int64_t batch, int64_t pos,
+                     int64_t cache_rows, int32_t layout, int32_t hq, int32_t hkv, int32_t head_dim,
+                     float scale, int32_t mode, int32_t block, int32_t sink_tokens,
+                     int32_t window_tokens, int32_t num_splits, void* workspace,
+                     size_t workspace_bytes, void* hip_stream);
+
+/*
+ * flux_decode_step_layers -- one decode step over a routed layer stack.
+ *
+ * Layer l runs flux_decode_step with mode modes_host[l] (the prefill-time router decision, host
+ * array): dense layers on FLUX_KV_FULL caches of dense_cache_rows rows, sparse layers on
+ * FLUX_KV_WINDOW caches.  One workspace, sized for the largest layer (the dense one), is reused by
+ * the layers in stream order.  All layers are validated before the first launch.
+ */
+int flux_decode_step_layers(int32_t n_layers, const int32_t* modes_host, const void* const* q,
+                            const void* const* k_new, const void* const* v_new,
+                            void* const* k_cache, void* const* v_cache, void* const* o,
+                            float* const* lse, int32_t out_dtype, int64_t batch, int64_t pos,
+                            int64_t dense_cache_rows, int32_t hq, int32_t hkv, int32_t head_dim,
+                            float scale, int32_t block, int32_t sink_tokens, int32_t window_tokens,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * flux_route_workspace_size -- bytes of workspace flux_route_layers needs:
  * the pooled features [n_layers, hq*head_dim] and the encoder activations
  * [n_layers, hidden], float32, each part 256-byte aligned.  0 if invalid.
@@ -229,8 +280,9 @@ size_t flux_route_workspace_size(int32_t n_layers, int32_t hq, int32_t head_dim,
  * w_head [n_layers, 2, hidden], b_head [n_layers, 2]: device float32.
  * logits_out [n_layers, 2] device float32 (may be NULL); modes_out
  * [n_layers] device int32.  workspace: device, 256-byte aligned, at least
- * flux_route_workspace_size(...) bytes.  Copying modes to the host is the
- * caller's one device-to-host synchronization per request.
+ * flux_route_workspace_size(...) bytes.  modes_out can feed
+ * flux_attn_prefill_layers_routed directly (no host round trip), or be copied to
+ * the host for flux_attn_prefill_layers / flux_decode_step_layers.
  * Supported: hq*head_dim a multiple of 8, pool_tokens >= 1.
  */
 int flux_route_layers(const void* const* q_layers, int32_t n_layers, int64_t seq, int32_t hq,

@@ -18,21 +18,24 @@ import numpy as np
 __all__ = [
     "FluxError", "lib", "status_string", "last_error_detail", "flux_version",
     "flux_build_block_mask", "flux_attn_prefill", "flux_attn_prefill_layers", "flux_attn_prefill_layers_routed",
-    "flux_decode_workspace_size", "flux_attn_decode", "flux_route_workspace_size", "flux_route_layers",
+    "flux_decode_workspace_size", "flux_attn_decode", "flux_window_cache_rows", "flux_decode_step",
+    "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers",
     "FLUX_OK", "FLUX_ERR_INVALID_ARG", "FLUX_ERR_UNSUPPORTED", "FLUX_ERR_CAPACITY", "FLUX_ERR_WORKSPACE",
-    "FLUX_ERR_HIP", "FLUX_DTYPE_BF16", "FLUX_DTYPE_F32", "FLUX_MODE_DENSE", "FLUX_MODE_SPARSE",
+    "FLUX_ERR_HIP", "FLUX_DTYPE_BF16", "FLUX_DTYPE_F32", "FLUX_MODE_DENSE", "FLUX_MODE_SPARSE", "FLUX_KV_FULL",
+    "FLUX_KV_WINDOW",
     "EXPORTED_SYMBOLS",
 ]
 
 FLUX_OK, FLUX_ERR_INVALID_ARG, FLUX_ERR_UNSUPPORTED, FLUX_ERR_CAPACITY, FLUX_ERR_WORKSPACE, FLUX_ERR_HIP = range(6)
 FLUX_DTYPE_BF16, FLUX_DTYPE_F32 = 0, 1
 FLUX_MODE_DENSE, FLUX_MODE_SPARSE = 0, 1
+FLUX_KV_FULL, FLUX_KV_WINDOW = 0, 1
 
 EXPORTED_SYMBOLS = (
     "flux_status_string", "flux_last_error_detail", "flux_version", "flux_build_block_mask",
     "flux_attn_prefill", "flux_attn_prefill_layers", "flux_attn_prefill_layers_routed",
-    "flux_decode_workspace_size", "flux_attn_decode",
-    "flux_route_workspace_size", "flux_route_layers",
+    "flux_decode_workspace_size", "flux_attn_decode", "flux_window_cache_rows", "flux_decode_step",
+    "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +73,14 @@ _lib.flux_decode_workspace_size.restype = _sz
 _lib.flux_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _f32,
                                   _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
 _lib.flux_attn_decode.restype = ctypes.c_int
+_lib.flux_window_cache_rows.argtypes = [_i32, _i32, _i32]
+_lib.flux_window_cache_rows.restype = _i64
+_lib.flux_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
+                                  _f32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+_lib.flux_decode_step.restype = ctypes.c_int
+_lib.flux_decode_step_layers.argtypes = [_i32, _vp, _pp, _pp, _pp, _pp, _pp, _pp, _pp, _i32, _i64, _i64, _i64, _i32,
+                                         _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz, _vp]
+_lib.flux_decode_step_layers.restype = ctypes.c_int
 _lib.flux_route_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.flux_route_workspace_size.restype = _sz
 _lib.flux_route_layers.argtypes = [_pp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
@@ -242,6 +253,46 @@ def flux_attn_decode(q, k_cache, v_cache, o, lse=None, *, kv_len: int | None = N
                                  _dtype_code(o), B, kv_len, cap, Hq, Hkv, d, scale, mode, block, sink_tokens,
                                  window_tokens, num_splits, _ptr(workspace), ws_bytes, _stream(stream)),
            "flux_attn_decode")
+
+
+def flux_window_cache_rows(block: int = 64, sink_tokens: int = 128, window_tokens: int = 2048) -> int:
+    return int(_lib.flux_window_cache_rows(block, sink_tokens, window_tokens))
+
+
+def flux_decode_step(q, k_new, v_new, k_cache, v_cache, o, lse=None, *, pos: int, layout: int = FLUX_KV_FULL,
+                     mode: int = FLUX_MODE_DENSE, block: int = 64, sink_tokens: int = 128, window_tokens: int = 2048,
+                     num_splits: int = 0, workspace=None, scale: float | None = None, stream=None):
+    """Append token `pos` (k_new/v_new [B,Hkv,d] bf16) to the cache [B,rows,Hkv,d] and attend from q [B,Hq,d]."""
+    _contig(q, k_new, v_new, k_cache, v_cache, o, lse)
+    B, Hq, d = q.shape
+    rows, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.flux_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
+                                 _dtype_code(o), B, pos, rows, layout, Hq, Hkv, d, scale, mode, block, sink_tokens,
+                                 window_tokens, num_splits, _ptr(workspace), ws_bytes, _stream(stream)),
+           "flux_decode_step")
+
+
+def flux_decode_step_layers(modes_host, qs, k_news, v_news, k_caches, v_caches, os_, lses=None, *, pos: int,
+                            dense_cache_rows: int, block: int = 64, sink_tokens: int = 128,
+                            window_tokens: int = 2048, workspace=None, scale: float | None = None, stream=None):
+    """One decode step over a routed stack: dense layers on full caches, sparse layers on window caches."""
+    L = len(qs)
+    modes = np.ascontiguousarray(np.asarray(modes_host, dtype=np.int32))
+    assert modes.shape == (L,)
+    B, Hq, d = qs[0].shape
+    Hkv = k_news[0].shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    arrs = [_ptr_array(x) for x in (qs, k_news, v_news, k_caches, v_caches, os_)]
+    pl, _e = _ptr_array(lses) if lses is not None else (None, None)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.flux_decode_step_layers(L, modes.ctypes.data_as(_vp), *[a[0] for a in arrs], pl, _dtype_code(os_[0]),
+                                        B, pos, dense_cache_rows, Hq, Hkv, d, scale, block, sink_tokens, window_tokens,
+                                        _ptr(workspace), ws_bytes, _stream(stream)),
+           "flux_decode_step_layers")
 
 
 def flux_route_workspace_size(n_layers, hq, head_dim, hidden) -> int:

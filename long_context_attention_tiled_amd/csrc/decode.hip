@@ -54,9 +54,16 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-__device__ __forceinline__ int64_t key_of(const DecodeArgs& a, int64_t idx) {
+// token position of active key idx
+__device__ __forceinline__ int64_t token_of(const DecodeArgs& a, int64_t idx) {
     return idx < a.r0_end ? idx : a.r1_begin + (idx - a.r0_end);
 }
+// cache row holding token t
+__device__ __forceinline__ int64_t row_of(const DecodeArgs& a, int64_t t) {
+    if (!a.ring || t < a.sink_rows) return t;
+    return a.sink_rows + ((t >> 6) % a.ring_blocks) * 64 + (t & 63);
+}
+__device__ __forceinline__ int64_t key_of(const DecodeArgs& a, int64_t idx) { return row_of(a, token_of(a, idx)); }
 
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
@@ -106,18 +113,32 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
     const float c2 = a.scale_log2;
 
+    // The new token (the last active key) comes from k_new / v_new; the first split's workgroups
+    // also store it into the cache.  No workgroup of this launch reads that cache row.
+    const int64_t new_idx = a.k_new ? a.n_active - 1 : -1;
+    const u16* kn = a.k_new ? reinterpret_cast<const u16*>(a.k_new) + ((int64_t)b * a.hkv + g) * D : nullptr;
+    const u16* vn = a.v_new ? reinterpret_cast<const u16*>(a.v_new) + ((int64_t)b * a.hkv + g) * D : nullptr;
+    if (a.k_new && split == 0 && tid < 2 * KCH) {
+        const int64_t row = row_of(a, a.kv_len - 1);
+        const bool is_v = tid >= KCH;
+        const int c = tid % KCH;
+        u16* dst = const_cast<u16*>(is_v ? vg : kg) + row * row_stride + c * 8;
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>((is_v ? vn : kn) + c * 8);
+    }
+
     // K and V of a 64-key step are loaded into registers one step ahead, so that a step's
     // arithmetic overlaps the next step's HBM reads.
     uint4 kcur[KPL], vcur[KPS];
     auto load_step = [&](int64_t t0, uint4* kr, uint4* vr) {
-        const int64_t kidx = t0 + sk;
-        const u16* krow = kg + key_of(a, min(kidx, a1 - 1)) * row_stride;
+        const int64_t kidx = min(t0 + sk, a1 - 1);
+        const u16* krow = kidx == new_idx ? kn : kg + key_of(a, kidx) * row_stride;
 #pragma unroll
         for (int i = 0; i < KPL; ++i) kr[i] = *reinterpret_cast<const uint4*>(krow + (part + 4 * i) * 8);
 #pragma unroll
         for (int i = 0; i < KPS; ++i) {
             const int64_t idx = min(t0 + kslot + i * KSLOTS, a1 - 1);
-            vr[i] = *reinterpret_cast<const uint4*>(vg + key_of(a, idx) * row_stride + dch * 8);
+            const u16* vrow = idx == new_idx ? vn : vg + key_of(a, idx) * row_stride;
+            vr[i] = *reinterpret_cast<const uint4*>(vrow + dch * 8);
         }
     };
     if (a0 < a1) load_step(a0, kcur, vcur);

@@ -225,6 +225,82 @@ int plan_decode(int64_t batch, int32_t hq, int32_t hkv, int64_t kv_len, int32_t 
 // ---------------------------------------------------------------- device attributes
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Validation and launch of one decode call.  k_new / v_new non-NULL: the token at kv_len-1 is taken
+// from them and stored into the cache by the same launch.  layout FLUX_KV_WINDOW: the cache holds the
+// sink rows and a ring of window blocks (see flux_attn.h).
+int run_decode(const void* q, const void* k_cache, const void* v_cache, const void* k_new, const void* v_new, void* o,
+               float* lse, int32_t in_dtype, int32_t out_dtype, int64_t batch, int64_t kv_len, int64_t cache_rows,
+               int32_t layout, int32_t hq, int32_t hkv, int32_t head_dim, float scale, int32_t mode, int32_t block,
+               int32_t sink_tokens, int32_t window_tokens, int32_t num_splits, void* workspace,
+               size_t workspace_bytes, void* hip_stream, bool launch = true) {
+    if (!q || !k_cache || !v_cache || !o) return fail(FLUX_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be non-NULL");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+        return fail(FLUX_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(FLUX_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(FLUX_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (in_dtype != FLUX_DTYPE_BF16 && in_dtype != FLUX_DTYPE_F32)
+        return fail(FLUX_ERR_INVALID_ARG, "in_dtype must be FLUX_DTYPE_BF16 or FLUX_DTYPE_F32");
+    if (out_dtype != FLUX_DTYPE_BF16 && out_dtype != FLUX_DTYPE_F32)
+        return fail(FLUX_ERR_INVALID_ARG, "out_dtype must be FLUX_DTYPE_BF16 or FLUX_DTYPE_F32");
+    DecodePlan p;
+    int st = plan_decode(batch, hq, hkv, kv_len, head_dim, mode, block, sink_tokens, window_tokens, num_splits, &p);
+    if (st != FLUX_OK) return st;
+    if (in_dtype != FLUX_DTYPE_BF16) return fail(FLUX_ERR_UNSUPPORTED, "decode supports bfloat16 inputs only");
+    if (!workspace || workspace_bytes < p.ws_bytes)
+        return fail(FLUX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(FLUX_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (!launch) return FLUX_OK;
+    flux::DecodeArgs a;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.o = o;
+    a.lse = lse;
+    size_t rows = (size_t)batch * hq * p.n_split;
+    a.part_o = reinterpret_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                          align256(rows * head_dim * sizeof(float)));
+    a.batch = batch;
+    a.kv_len = kv_len;
+    a.kv_cap = cache_rows;
+    a.hq = hq;
+    a.hkv = hkv;
+    a.head_dim = head_dim;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out_f32 = out_dtype == FLUX_DTYPE_F32;
+    a.r0_end = p.r0_end;
+    a.r1_begin = p.r1_begin;
+    a.n_active = p.n_active;
+    a.n_split = p.n_split;
+    a.split_len = p.split_len;
+    a.ring = layout == FLUX_KV_WINDOW;
+    a.sink_rows = sink_tokens;
+    a.ring_blocks = window_tokens / flux::kBlock;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    hipError_t e = flux::launch_decode(a, as_stream(hip_stream));
+    if (e == hipSuccess) e = hipGetLastError();
+    return hip_status(e, "decode launch");
+}
+
+int check_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, void* o,
+                      float* lse, int32_t out_dtype, int64_t batch, int64_t pos, int64_t cache_rows, int32_t layout,
+                      int32_t hq, int32_t hkv, int32_t head_dim, float scale, int32_t mode, int32_t block,
+                      int32_t sink_tokens, int32_t window_tokens, void* workspace, size_t workspace_bytes) {
+    if (!k_new || !v_new) return fail(FLUX_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
+    if (pos < 0) return fail(FLUX_ERR_INVALID_ARG, "pos must be >= 0");
+    if (layout == FLUX_KV_FULL && cache_rows <= pos)
+        return fail(FLUX_ERR_CAPACITY, "cache_rows %lld must exceed pos %lld", (long long)cache_rows, (long long)pos);
+    if (layout == FLUX_KV_WINDOW && cache_rows == 0)
+        return fail(FLUX_ERR_INVALID_ARG, "invalid block / sink / window for the window cache");
+    return run_decode(q, k_cache, v_cache, k_new, v_new, o, lse, FLUX_DTYPE_BF16, out_dtype, batch, pos + 1,
+                      cache_rows, layout, hq, hkv, head_dim, scale, mode, block, sink_tokens, window_tokens, 0,
+                      workspace, workspace_bytes, nullptr, false);
+}
+
 }  // namespace
 
 extern "C" {
@@ -366,53 +442,80 @@ int flux_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
                      int32_t head_dim, float scale, int32_t mode, int32_t block, int32_t sink_tokens,
                      int32_t window_tokens, int32_t num_splits, void* workspace, size_t workspace_bytes,
                      void* hip_stream) {
-    if (!q || !k_cache || !v_cache || !o) return fail(FLUX_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be non-NULL");
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
-        return fail(FLUX_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
-    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(FLUX_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-    if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(FLUX_ERR_INVALID_ARG, "scale must be finite and > 0");
-    if (in_dtype != FLUX_DTYPE_BF16 && in_dtype != FLUX_DTYPE_F32)
-        return fail(FLUX_ERR_INVALID_ARG, "in_dtype must be FLUX_DTYPE_BF16 or FLUX_DTYPE_F32");
-    if (out_dtype != FLUX_DTYPE_BF16 && out_dtype != FLUX_DTYPE_F32)
-        return fail(FLUX_ERR_INVALID_ARG, "out_dtype must be FLUX_DTYPE_BF16 or FLUX_DTYPE_F32");
     if (kv_capacity == 0) kv_capacity = kv_len;
     if (kv_capacity < kv_len) return fail(FLUX_ERR_INVALID_ARG, "kv_capacity must be 0 or >= kv_len");
-    DecodePlan p;
-    int st = plan_decode(batch, hq, hkv, kv_len, head_dim, mode, block, sink_tokens, window_tokens, num_splits, &p);
-    if (st != FLUX_OK) return st;
-    if (in_dtype != FLUX_DTYPE_BF16) return fail(FLUX_ERR_UNSUPPORTED, "decode supports bfloat16 inputs only");
-    if (!workspace || workspace_bytes < p.ws_bytes)
-        return fail(FLUX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
-                    workspace ? workspace_bytes : (size_t)0);
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-        return fail(FLUX_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    flux::DecodeArgs a;
-    a.q = q;
-    a.k = k_cache;
-    a.v = v_cache;
-    a.o = o;
-    a.lse = lse;
-    size_t rows = (size_t)batch * hq * p.n_split;
-    a.part_o = reinterpret_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                          align256(rows * head_dim * sizeof(float)));
-    a.batch = batch;
-    a.kv_len = kv_len;
-    a.kv_cap = kv_capacity;
-    a.hq = hq;
-    a.hkv = hkv;
-    a.head_dim = head_dim;
-    a.scale = scale;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    a.out_f32 = out_dtype == FLUX_DTYPE_F32;
-    a.r0_end = p.r0_end;
-    a.r1_begin = p.r1_begin;
-    a.n_active = p.n_active;
-    a.n_split = p.n_split;
-    a.split_len = p.split_len;
-    hipError_t e = flux::launch_decode(a, as_stream(hip_stream));
-    if (e == hipSuccess) e = hipGetLastError();
-    return hip_status(e, "decode launch");
+    return run_decode(q, k_cache, v_cache, nullptr, nullptr, o, lse, in_dtype, out_dtype, batch, kv_len, kv_capacity,
+                      FLUX_KV_FULL, hq, hkv, head_dim, scale, mode, block, sink_tokens, window_tokens, num_splits,
+                      workspace, workspace_bytes, hip_stream);
+}
+
+int64_t flux_window_cache_rows(int32_t block, int32_t sink_tokens, int32_t window_tokens) {
+    if (block != flux::kBlock || sink_tokens < 0 || window_tokens < block || sink_tokens % block ||
+        window_tokens % block)
+        return 0;
+    return (int64_t)sink_tokens + window_tokens;
+}
+
+int flux_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, void* o,
+                     float* lse, int32_t out_dtype, int64_t batch, int64_t pos, int64_t cache_rows, int32_t layout,
+                     int32_t hq, int32_t hkv, int32_t head_dim, float scale, int32_t mode, int32_t block,
+                     int32_t sink_tokens, int32_t window_tokens, int32_t num_splits, void* workspace,
+                     size_t workspace_bytes, void* hip_stream) {
+    if (!k_new || !v_new) return fail(FLUX_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(FLUX_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+    if (pos < 0) return fail(FLUX_ERR_INVALID_ARG, "pos must be >= 0");
+    if (layout == FLUX_KV_FULL) {
+        if (cache_rows <= pos) return fail(FLUX_ERR_CAPACITY, "cache_rows %lld must exceed pos %lld",
+                                           (long long)cache_rows, (long long)pos);
+    } else if (layout == FLUX_KV_WINDOW) {
+        if (mode != FLUX_MODE_SPARSE) return fail(FLUX_ERR_INVALID_ARG, "the window cache holds sparse layers only");
+        const int64_t rows = flux_window_cache_rows(block, sink_tokens, window_tokens);
+        if (rows == 0 || cache_rows != rows)
+            return fail(FLUX_ERR_INVALID_ARG, "window cache must have sink_tokens + window_tokens = %lld rows",
+                        (long long)rows);
+    } else {
+        return fail(FLUX_ERR_INVALID_ARG, "layout must be FLUX_KV_FULL or FLUX_KV_WINDOW");
+    }
+    return run_decode(q, k_cache, v_cache, k_new, v_new, o, lse, FLUX_DTYPE_BF16, out_dtype, batch, pos + 1,
+                      cache_rows, layout, hq, hkv, head_dim, scale, mode, block, sink_tokens, window_tokens,
+                      num_splits, workspace, workspace_bytes, hip_stream);
+}
+
+int flux_decode_step_layers(int32_t n_layers, const int32_t* modes_host, const void* const* q,
+                            const void* const* k_new, const void* const* v_new, void* const* k_cache,
+                            void* const* v_cache, void* const* o, float* const* lse, int32_t out_dtype, int64_t batch,
+                            int64_t pos, int64_t dense_cache_rows, int32_t hq, int32_t hkv, int32_t head_dim,
+                            float scale, int32_t block, int32_t sink_tokens, int32_t window_tokens, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+    if (n_layers < 1) return fail(FLUX_ERR_INVALID_ARG, "n_layers must be >= 1");
+    if (!modes_host || !q || !k_new || !v_new || !k_cache || !v_cache || !o)
+        return fail(FLUX_ERR_INVALID_ARG, "layer arrays must be non-NULL");
+    const int64_t wrows = flux_window_cache_rows(block, sink_tokens, window_tokens);
+    for (int pass = 0; pass < 2; ++pass) {   // pass 0 validates every layer, pass 1 launches
+        for (int32_t l = 0; l < n_layers; ++l) {
+            const int32_t m = modes_host[l];
+            if (m != FLUX_MODE_DENSE && m != FLUX_MODE_SPARSE)
+                return fail(FLUX_ERR_INVALID_ARG, "layer %d: mode %d is neither dense nor sparse", l, m);
+            const int32_t layout = m == FLUX_MODE_SPARSE ? FLUX_KV_WINDOW : FLUX_KV_FULL;
+            const int64_t rows = m == FLUX_MODE_SPARSE ? wrows : dense_cache_rows;
+            int st;
+            if (pass == 0) {
+                st = check_decode_step(q[l], k_new[l], v_new[l], k_cache[l], v_cache[l], o[l], lse ? lse[l] : nullptr,
+                                       out_dtype, batch, pos, rows, layout, hq, hkv, head_dim, scale, m, block,
+                                       sink_tokens, window_tokens, workspace, workspace_bytes);
+            } else {
+                st = flux_decode_step(q[l], k_new[l], v_new[l], k_cache[l], v_cache[l], o[l], lse ? lse[l] : nullptr,
+                                      out_dtype, batch, pos, rows, layout, hq, hkv, head_dim, scale, m, block,
+                                      sink_tokens, window_tokens, 0, workspace, workspace_bytes, hip_stream);
+            }
+            if (st != FLUX_OK) {
+                char tmp[512];
+                snprintf(tmp, sizeof tmp, "layer %d: %s", l, g_detail);
+                return fail(st, "%s", tmp);
+            }
+        }
+    }
+    return ok();
 }
 
 size_t flux_route_workspace_size(int32_t n_layers, int32_t hq, int32_t head_dim, int32_t hidden) {

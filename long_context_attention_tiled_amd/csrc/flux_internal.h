@@ -55,6 +55,14 @@ struct DecodeArgs {
     int64_t n_active;
     int n_split;
     int64_t split_len;     // active keys per split (multiple of 64)
+    // cache layout: ring == 0 -> token t at row t; ring == 1 (window cache) -> token t at row t when
+    // t < sink_rows, else at row sink_rows + ((t / 64) % ring_blocks) * 64 + t % 64
+    int ring;
+    int64_t sink_rows;
+    int ring_blocks;
+    // token kv_len-1 taken from k_new / v_new [B, Hkv, d] (and written into the cache), or nullptr
+    const void* k_new;
+    const void* v_new;
 };
 
 constexpr int kMaxRouteLayers = 64;

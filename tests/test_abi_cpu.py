@@ -185,6 +185,56 @@ def test_prefill_layers_routed_validation(fa):
     assert call(nnz=25) == E and "blk_nnz" in fa.last_error_detail()
 
 
+def test_window_cache_rows(fa):
+    assert fa.flux_window_cache_rows(64, 128, 2048) == 2176
+    assert fa.flux_window_cache_rows(64, 0, 64) == 64
+    assert fa.flux_window_cache_rows(32, 128, 2048) == 0
+    assert fa.flux_window_cache_rows(64, 100, 2048) == 0
+    assert fa.flux_window_cache_rows(64, 128, 0) == 0
+
+
+def _step(fa, **kw):
+    args = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, out_dtype=1, batch=2, pos=100,
+                rows=2176, layout=1, hq=8, hkv=2, d=128, scale=0.088, mode=1, block=64, sink=128, window=2048, ns=0,
+                ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    a = args
+    return fa.lib().flux_decode_step(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["o"], a["lse"], a["out_dtype"],
+                                     a["batch"], a["pos"], a["rows"], a["layout"], a["hq"], a["hkv"], a["d"],
+                                     a["scale"], a["mode"], a["block"], a["sink"], a["window"], a["ns"], a["ws"],
+                                     a["ws_bytes"], None)
+
+
+def test_decode_step_validation(fa):
+    E = fa.FLUX_ERR_INVALID_ARG
+    assert _step(fa, kn=None) == E
+    assert _step(fa, vn=FAKE + 4) == E                     # misaligned
+    assert _step(fa, pos=-1) == E
+    assert _step(fa, layout=2) == E
+    assert _step(fa, mode=0) == E                          # the window cache holds sparse layers only
+    assert _step(fa, rows=2175) == E and "2176" in fa.last_error_detail()
+    assert _step(fa, layout=0, mode=0, rows=100, pos=100) == fa.FLUX_ERR_CAPACITY
+    assert _step(fa, ws=None) == fa.FLUX_ERR_WORKSPACE
+    assert _step(fa, ws_bytes=16) == fa.FLUX_ERR_WORKSPACE
+    assert _step(fa, hq=6, hkv=4) == E                     # hq % hkv != 0
+    assert _step(fa, hq=6) == fa.FLUX_ERR_UNSUPPORTED       # group of 3
+
+
+def test_decode_step_layers_validation(fa):
+    L = 2
+    P = ctypes.POINTER(ctypes.c_void_p)
+    ptrs = (ctypes.c_void_p * L)(FAKE, FAKE)
+    pp = ctypes.cast(ptrs, P)
+
+    def call(modes, dense_rows=4096, pos=100):
+        m = np.array(modes, np.int32)
+        return fa.lib().flux_decode_step_layers(L, m.ctypes.data_as(ctypes.c_void_p), pp, pp, pp, pp, pp, pp, None,
+                                                1, 2, pos, dense_rows, 8, 2, 128, 0.088, 64, 128, 2048, FAKE, 1 << 30,
+                                                None)
+    assert call([0, 7]) == fa.FLUX_ERR_INVALID_ARG and "layer 1" in fa.last_error_detail()
+    assert call([1, 0], dense_rows=50) == fa.FLUX_ERR_CAPACITY and "layer 1" in fa.last_error_detail()
+
+
 # ---------------------------------------------------------------- decode validation / workspace
 def test_decode_workspace_size(fa):
     B, Hq, Hkv, L, d = 8, 32, 8, 262144, 128

@@ -182,3 +182,119 @@ def test_router_qwen_stack_shape(fa):
     _check_route(logits, modes, ref_logits, ref_modes, "router 36 layers")
     del xs_dev
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ decode loop: append + attend
+def _window_row(t, sink, window):
+    """Row of token t in a FLUX_KV_WINDOW cache (the layout documented in flux_attn.h)."""
+    return t if t < sink else sink + ((t // 64) % (window // 64)) * 64 + t % 64
+
+
+def test_decode_step_full_cache_appends_and_matches_oracle(fa):
+    """Full-cache layout: the new token is written at row pos and attended to in the same launch."""
+    B, Hq, Hkv, d, cap, pos = 2, 8, 2, 128, 1200, 777
+    say("decode step full cache")
+    k = synth.normal_bf16_bits((B, pos + 1, Hkv, d), 51, 0, synth.TENSOR_K)
+    v = synth.normal_bf16_bits((B, pos + 1, Hkv, d), 51, 0, synth.TENSOR_V)
+    q = synth.normal_bf16_bits((B, Hq, d), 51, 0, synth.TENSOR_Q)
+    for mode in (0, 1):
+        kc = torch.zeros((B, cap, Hkv, d), dtype=torch.bfloat16, device=DEV)
+        vc = torch.zeros_like(kc)
+        kc[:, :pos] = synth.torch_bf16_from_bits(np.ascontiguousarray(k[:, :pos]))
+        vc[:, :pos] = synth.torch_bf16_from_bits(np.ascontiguousarray(v[:, :pos]))
+        kn = synth.torch_bf16_from_bits(np.ascontiguousarray(k[:, pos]))
+        vn = synth.torch_bf16_from_bits(np.ascontiguousarray(v[:, pos]))
+        qd = synth.torch_bf16_from_bits(q)
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+        ws = torch.empty(fa.flux_decode_workspace_size(B, Hq, Hkv, pos + 1, d, mode, 64, 128, 256), dtype=torch.uint8,
+                         device=DEV)
+        fa.flux_decode_step(qd, kn, vn, kc, vc, o, lse, pos=pos, layout=fa.FLUX_KV_FULL, mode=mode, sink_tokens=128,
+                            window_tokens=256, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(dev_bits_to_host(kc[:, pos]), k[:, pos])
+        assert np.array_equal(dev_bits_to_host(vc[:, pos]), v[:, pos])
+        assert not dev_bits_to_host(kc[:, pos + 1:]).any()
+        ref, ref_lse = oracle.decode(q, k, v, default_scale(d), sparse=bool(mode), block=64, sink_tokens=128,
+                                     window_tokens=256)
+        check_close(o.cpu().numpy(), ref, f"decode step full mode {mode}")
+        check_lse(lse.cpu().numpy(), ref_lse, "decode step lse")
+
+
+def test_decode_loop_window_cache_ring(fa):
+    """Sparse layer on a window cache, token by token from position 0: the cache keeps only the sink
+    and a ring of window blocks, the ring wraps several times, and every step matches the oracle run
+    on the full history (sink 128 tokens, window 256 = 4 blocks; 700 steps)."""
+    B, Hq, Hkv, d, sink, window, n = 2, 4, 1, 128, 128, 256, 700
+    say("decode loop window cache")
+    rows = fa.flux_window_cache_rows(64, sink, window)
+    assert rows == sink + window
+    k = synth.normal_bf16_bits((B, n, Hkv, d), 52, 0, synth.TENSOR_K)
+    v = synth.normal_bf16_bits((B, n, Hkv, d), 52, 0, synth.TENSOR_V)
+    q = synth.normal_bf16_bits((n, B, Hq, d), 52, 0, synth.TENSOR_Q)
+    kd, vd, qd = (synth.torch_bf16_from_bits(x) for x in (k, v, q))
+    kc = torch.zeros((B, rows, Hkv, d), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    out = torch.empty((n, B, Hq, d), dtype=torch.float32, device=DEV)
+    ws = torch.empty(fa.flux_decode_workspace_size(B, Hq, Hkv, n, d, 1, 64, sink, window), dtype=torch.uint8,
+                     device=DEV)
+    kn_all = kd.transpose(0, 1).contiguous()   # [n, B, Hkv, d]
+    vn_all = vd.transpose(0, 1).contiguous()
+    for pos in range(n):
+        fa.flux_decode_step(qd[pos], kn_all[pos], vn_all[pos], kc, vc, out[pos], None, pos=pos,
+                            layout=fa.FLUX_KV_WINDOW, mode=fa.FLUX_MODE_SPARSE, sink_tokens=sink,
+                            window_tokens=window, workspace=ws)
+    torch.cuda.synchronize()
+    # the ring holds exactly the tokens the pattern can still reach at the last position
+    kc_h = dev_bits_to_host(kc)
+    last_blk = (n - 1) // 64
+    for t in list(range(sink)) + list(range(max(sink, (last_blk - window // 64 + 1) * 64), n)):
+        assert np.array_equal(kc_h[:, _window_row(t, sink, window)], k[:, t]), t
+    out_h = out.cpu().numpy()
+    for pos in sorted({0, 1, 63, 64, 127, 128, 129, 191, 192, 255, 256, 383, 384, 385, 447, 448, 511, 512, 575, 576,
+                       640, 641, n - 1} | set(range(5, n, 37))):
+        ref, _ = oracle.decode(q[pos], np.ascontiguousarray(k[:, :pos + 1]), np.ascontiguousarray(v[:, :pos + 1]),
+                               default_scale(d), sparse=True, block=64, sink_tokens=sink, window_tokens=window)
+        check_close(out_h[pos], ref, f"window decode pos {pos}")
+
+
+def test_decode_step_layers_routed_stack(fa):
+    """Three layers, modes [sparse, dense, sparse]: dense on a full cache, sparse on window caches."""
+    B, Hq, Hkv, d, sink, window, pos, cap = 2, 8, 2, 128, 128, 256, 900, 1024
+    say("decode step layers")
+    modes = [1, 0, 1]
+    L = len(modes)
+    wrows = fa.flux_window_cache_rows(64, sink, window)
+    ks = [synth.normal_bf16_bits((B, pos + 1, Hkv, d), 53, l, synth.TENSOR_K) for l in range(L)]
+    vs = [synth.normal_bf16_bits((B, pos + 1, Hkv, d), 53, l, synth.TENSOR_V) for l in range(L)]
+    qs = [synth.normal_bf16_bits((B, Hq, d), 53, l, synth.TENSOR_Q) for l in range(L)]
+    kcs, vcs = [], []
+    for l in range(L):
+        if modes[l] == 0:
+            kc = torch.zeros((B, cap, Hkv, d), dtype=torch.bfloat16, device=DEV)
+            vc = torch.zeros_like(kc)
+            kc[:, :pos] = synth.torch_bf16_from_bits(np.ascontiguousarray(ks[l][:, :pos]))
+            vc[:, :pos] = synth.torch_bf16_from_bits(np.ascontiguousarray(vs[l][:, :pos]))
+        else:   # fill the window cache with the tokens it holds before position pos
+            kh = np.zeros((B, wrows, Hkv, d), np.uint16)
+            vh = np.zeros_like(kh)
+            blk = pos // 64
+            for t in list(range(sink)) + list(range(max(sink, (blk - window // 64 + 1) * 64), pos)):
+                kh[:, _window_row(t, sink, window)] = ks[l][:, t]
+                vh[:, _window_row(t, sink, window)] = vs[l][:, t]
+            kc, vc = synth.torch_bf16_from_bits(kh), synth.torch_bf16_from_bits(vh)
+        kcs.append(kc)
+        vcs.append(vc)
+    kns = [synth.torch_bf16_from_bits(np.ascontiguousarray(x[:, pos])) for x in ks]
+    vns = [synth.torch_bf16_from_bits(np.ascontiguousarray(x[:, pos])) for x in vs]
+    qds = [synth.torch_bf16_from_bits(x) for x in qs]
+    os_ = [torch.empty((B, Hq, d), dtype=torch.float32, device=DEV) for _ in range(L)]
+    ws = torch.empty(fa.flux_decode_workspace_size(B, Hq, Hkv, pos + 1, d, 0, 64, sink, window), dtype=torch.uint8,
+                     device=DEV)
+    fa.flux_decode_step_layers(modes, qds, kns, vns, kcs, vcs, os_, None, pos=pos, dense_cache_rows=cap,
+                               sink_tokens=sink, window_tokens=window, workspace=ws)
+    torch.cuda.synchronize()
+    for l in range(L):
+        ref, _ = oracle.decode(qs[l], ks[l], vs[l], default_scale(d), sparse=bool(modes[l]), block=64,
+                               sink_tokens=sink, window_tokens=window)
+        check_close(os_[l].cpu().numpy(), ref, f"decode layers l={l}")
