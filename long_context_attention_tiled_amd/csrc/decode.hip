@@ -58,14 +58,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 __device__ __forceinline__ int64_t token_of(const DecodeArgs& a, int64_t idx) {
     return idx < a.r0_end ? idx : a.r1_begin + (idx - a.r0_end);
 }
-// cache row holding token t
+// cache row holding token t (RING: window-cache layout)
+template <bool RING>
 __device__ __forceinline__ int64_t row_of(const DecodeArgs& a, int64_t t) {
-    if (!a.ring || t < a.sink_rows) return t;
-    return a.sink_rows + ((t >> 6) % a.ring_blocks) * 64 + (t & 63);
+    if (!RING || t < a.sink_rows) return t;
+    const int slot = (int)(t >> 6) % a.ring_blocks;   // t < 2^37, so the block index fits 32 bits
+    return a.sink_rows + (int64_t)slot * 64 + (t & 63);
 }
-__device__ __forceinline__ int64_t key_of(const DecodeArgs& a, int64_t idx) { return row_of(a, token_of(a, idx)); }
 
-template <int D, int G>
+template <int D, int G, bool RING>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     constexpr int KCH = D / 8;            // 16-byte chunks per K/V row
     constexpr int KPL = KCH / 4;          // chunks per lane in the score step
@@ -113,32 +114,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
     const float c2 = a.scale_log2;
 
-    // The new token (the last active key) comes from k_new / v_new; the first split's workgroups
-    // also store it into the cache.  No workgroup of this launch reads that cache row.
-    const int64_t new_idx = a.k_new ? a.n_active - 1 : -1;
-    const u16* kn = a.k_new ? reinterpret_cast<const u16*>(a.k_new) + ((int64_t)b * a.hkv + g) * D : nullptr;
-    const u16* vn = a.v_new ? reinterpret_cast<const u16*>(a.v_new) + ((int64_t)b * a.hkv + g) * D : nullptr;
-    if (a.k_new && split == 0 && tid < 2 * KCH) {
-        const int64_t row = row_of(a, a.kv_len - 1);
-        const bool is_v = tid >= KCH;
-        const int c = tid % KCH;
-        u16* dst = const_cast<u16*>(is_v ? vg : kg) + row * row_stride + c * 8;
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>((is_v ? vn : kn) + c * 8);
-    }
-
     // K and V of a 64-key step are loaded into registers one step ahead, so that a step's
     // arithmetic overlaps the next step's HBM reads.
     uint4 kcur[KPL], vcur[KPS];
+    // A 64-key step never straddles a 64-token block (split starts, the end of the sink range and the
+    // start of the window range are all multiples of 64), so its keys sit in consecutive cache rows
+    // from a per-step base row.
     auto load_step = [&](int64_t t0, uint4* kr, uint4* vr) {
+        const int64_t base = row_of<RING>(a, token_of(a, t0));   // uniform
         const int64_t kidx = min(t0 + sk, a1 - 1);
-        const u16* krow = kidx == new_idx ? kn : kg + key_of(a, kidx) * row_stride;
+        const u16* krow = kg + (base + (kidx - t0)) * row_stride;
 #pragma unroll
         for (int i = 0; i < KPL; ++i) kr[i] = *reinterpret_cast<const uint4*>(krow + (part + 4 * i) * 8);
 #pragma unroll
         for (int i = 0; i < KPS; ++i) {
             const int64_t idx = min(t0 + kslot + i * KSLOTS, a1 - 1);
-            const u16* vrow = idx == new_idx ? vn : vg + key_of(a, idx) * row_stride;
-            vr[i] = *reinterpret_cast<const uint4*>(vrow + dch * 8);
+            vr[i] = *reinterpret_cast<const uint4*>(vg + (base + (idx - t0)) * row_stride + dch * 8);
         }
     };
     if (a0 < a1) load_step(a0, kcur, vcur);
@@ -252,6 +243,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
+// Stores the new token (position kv_len-1) of every (batch, kv head) into the cache: grid (hkv, B),
+// one 16-byte chunk of K or V per thread.  Runs before the split kernel on the same stream.
+template <int D, bool RING>
+__global__ __launch_bounds__(D / 4) void decode_append_kernel(DecodeArgs a) {
+    constexpr int KCH = D / 8;
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const bool is_v = tid >= KCH;
+    const int c = tid % KCH;
+    const int64_t row = row_of<RING>(a, a.kv_len - 1);
+    const u16* src = reinterpret_cast<const u16*>(is_v ? a.v_new : a.k_new) + ((int64_t)b * a.hkv + g) * D + c * 8;
+    u16* dst = reinterpret_cast<u16*>(const_cast<void*>(is_v ? a.v : a.k)) +
+               (((int64_t)b * a.kv_cap + row) * a.hkv + g) * D + c * 8;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+}
+
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     const int64_t row = blockIdx.x;  // b * hq + h
@@ -276,10 +282,21 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     if (a.lse && threadIdx.x == 0) a.lse[row] = wsum > 0.0f ? mx + __logf(wsum) : -INFINITY;
 }
 
+template <int D, int G, bool RING>
+hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
+    if (a.k_new) {
+        hipLaunchKernelGGL((decode_append_kernel<D, RING>), dim3(a.hkv, (unsigned)a.batch), dim3(D / 4), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((decode_split_kernel<D, G, RING>), dim3(a.n_split, a.hkv, (unsigned)a.batch), dim3(kThreads), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(a.n_split, a.hkv, (unsigned)a.batch), dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e = a.ring ? launch_split<D, G, true>(a, s) : launch_split<D, G, false>(a, s);
     if (e != hipSuccess) return e;
     const unsigned rows = (unsigned)(a.batch * a.hq);
     if (a.out_f32)

@@ -60,7 +60,7 @@ struct DecodeArgs {
     int ring;
     int64_t sink_rows;
     int ring_blocks;
-    // token kv_len-1 taken from k_new / v_new [B, Hkv, d] (and written into the cache), or nullptr
+    // token kv_len-1 [B, Hkv, d], stored into the cache by a launch that precedes the split kernel, or nullptr
     const void* k_new;
     const void* v_new;
 };
