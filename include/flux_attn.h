@@ -226,8 +226,8 @@ int64_t flux_window_cache_rows(int32_t block, int32_t sink_tokens, int32_t windo
  * and window KV; layer-granularity paragraph: one mode per layer).  For each sequence b the new token
  * sits at position pos (all sequences of the batch advance together): its key/value k_new, v_new
  * [batch, hkv, head_dim] bf16 are stored into the cache and the query q [batch, hq, head_dim] bf16
- * attends to tokens 0..pos under `mode` exactly as flux_attn_decode with kv_len = pos + 1 (the new
- * token is read from k_new / v_new by the same launch, so the store and the reads never race).
+ * attends to tokens 0..pos under `mode` exactly as flux_attn_decode with kv_len = pos + 1 (a small
+ * launch stores the new token before the attention launches, in stream order).
  *   layout FLUX_KV_FULL:   k_cache/v_cache [batch, cache_rows, hkv, head_dim], cache_rows > pos, any mode;
  *   layout FLUX_KV_WINDOW: cache_rows == flux_window_cache_rows(block, sink, window), mode SPARSE; the
  *     tokens the sparse pattern can still reach (sink and last window blocks) are all the cache keeps.
