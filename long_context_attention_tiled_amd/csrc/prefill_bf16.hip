@@ -158,17 +158,15 @@ struct TileWalk {
     int next_kb, last_kb, qb_base, nvalid;
     int p0, p1, p2, p3, e0, e1, e2, e3;   // CSR cursors and ends of the (up to 4) query blocks
     const int32_t* ci;
-    bool sparse;
+    static constexpr bool sparse = MODE == kSparse;
 
-    __device__ void init(int qb_base_, int nrows, int n_qblk, const int32_t* rp, const int32_t* ci_,
-                         const int32_t* mode_dev) {
+    __device__ void init(int qb_base_, int nrows, int n_qblk, const int32_t* rp, const int32_t* ci_) {
         qb_base = qb_base_;
         nvalid = max(0, min(nrows, n_qblk - qb_base));
         ci = ci_;
-        sparse = MODE == kSparse || (MODE == kRouted && mode_dev[0] != 0);
         next_kb = 0;
         last_kb = MODE == kDenseFull ? n_qblk - 1 : qb_base + nvalid - 1;
-        if (sparse) {
+        if constexpr (sparse) {
             p0 = p1 = p2 = p3 = e0 = e1 = e2 = e3 = 0;
             if (nvalid > 0) p0 = rp[qb_base], e0 = rp[qb_base + 1];
             if (nvalid > 1) p1 = rp[qb_base + 1], e1 = rp[qb_base + 2];
@@ -178,7 +176,7 @@ struct TileWalk {
     }
 
     __device__ bool next(int& kb, uint32_t& in) {
-        if (sparse) {
+        if constexpr (sparse) {
             const int big = 0x7fffffff;
             const int c0 = p0 < e0 ? ci[p0] : big;
             const int c1 = p1 < e1 ? ci[p1] : big;
@@ -235,12 +233,10 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ gbase, uint32
 }
 
 template <int D, int MODE, bool OUT_F32>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2))) void
-prefill_bf16_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     using L = Lay<D>;
     constexpr int NC = D / 16;   // 16-wide d chunks of the S^T contraction
     constexpr int NM = D / 32;   // 32-row d tiles of O^T
-    __shared__ __attribute__((aligned(1024))) char smem[L::SMEM_B];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -410,11 +406,15 @@ prefill_bf16_kernel(PrefillArgs a) {
         if (need_mask) {
             // key > lim is masked, lim = last allowed key of this lane's row minus the tile/lane base
             const int lim = (MODE != kDenseFull ? min(qpos, last_key) : last_key) - (kb * kBC + 4 * hh);
+            // one compare/select pair at a time: hoisting all 32 compares would hold 32 lane masks
+            // in scalar registers and push other scalars out to spill slots for the whole kernel
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
+                for (int r = 0; r < 16; ++r) {
                     if (32 * kh + 8 * (r >> 2) + (r & 3) > lim) sacc[kh][r] = -INFINITY;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
         }
         float mx = sacc[0][0];
 #pragma unroll
@@ -461,7 +461,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     constexpr BoolTag<true> kOn{};
     constexpr BoolTag<false> kOff{};
     TileWalk<MODE> walk;
-    walk.init(qb_base, nrows, a.n_qblk, a.row_ptr, a.col_idx, a.mode_dev);
+    walk.init(qb_base, nrows, a.n_qblk, a.row_ptr, a.col_idx);
     uint32_t in;
     int kb_p = 0, kb_c = 0, kb_n = 0;
     bool mine_p = false;
@@ -543,6 +543,22 @@ prefill_bf16_kernel(PrefillArgs a) {
     if (a.lse && hh == 0) {
         const float lse = l_tot > 0.0f ? (m_run * c2 + __log2f(l_tot)) * kLn2 : -INFINITY;
         a.lse[((int64_t)b * a.hq + h) * a.seq + qpos] = lse;
+    }
+}
+
+// kRouted: one launch whose workgroups read the layer's mode and run the dense-causal or the
+// block-sparse body (two complete code paths, so neither carries the other's state).
+template <int D, int MODE, bool OUT_F32>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2))) void
+prefill_bf16_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[Lay<D>::SMEM_B];
+    if constexpr (MODE == kRouted) {
+        if (a.mode_dev[0] != 0)
+            prefill_body<D, kSparse, OUT_F32>(a, smem);
+        else
+            prefill_body<D, kDenseCausal, OUT_F32>(a, smem);
+    } else {
+        prefill_body<D, MODE, OUT_F32>(a, smem);
     }
 }
 
