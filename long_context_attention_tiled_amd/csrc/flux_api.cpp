@@ -158,10 +158,27 @@ int check_prefill(const void* q, const void* k, const void* v, void* o, float* l
     a->row_ptr = ms.sparse ? rp : nullptr;
     a->col_idx = ms.sparse ? ci : nullptr;
     a->mode_dev = nullptr;
+    a->num_cu = 0;
     return FLUX_OK;
 }
 
-int launch_prefill(const flux::PrefillArgs& a, int32_t in_dtype, hipStream_t s) {
+// Compute units of the current device (cached per device id; 0 if the query fails, which makes the
+// prefill launch fall back to one workgroup per unit).
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cached[dev] = v;
+    }
+    return cached[dev];
+}
+
+int launch_prefill(const flux::PrefillArgs& args, int32_t in_dtype, hipStream_t s) {
+    flux::PrefillArgs a = args;
+    a.num_cu = device_cu_count();
     hipError_t e = in_dtype == FLUX_DTYPE_BF16 ? flux::launch_prefill_bf16(a, s) : flux::launch_prefill_f32(a, s);
     if (e == hipSuccess) e = hipGetLastError();
     return hip_status(e, "prefill launch");

@@ -30,6 +30,7 @@ struct PrefillArgs {
     const int32_t* col_idx;
     const int32_t* mode_dev;  // device-resident mode of this layer (0 dense causal, else sparse),
                               // read by the kernel; nullptr when the mode is fixed by `sparse`
+    int num_cu;               // compute units of the device (persistent grid size)
 };
 
 struct DecodeArgs {

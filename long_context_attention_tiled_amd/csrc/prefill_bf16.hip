@@ -246,50 +246,29 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     const int n = lane & 31;     // query column of this lane inside the wave's 32 rows
     const int hh = lane >> 5;    // which half of the k-slots / accumulator rows
 
-    // ---- work unit: (batch, kv head g, two slots of 128 query rows)
+    // ---- work units: (batch, kv head g, two slots of 128 query rows).  A unit's logical id comes
+    // from a virtual block index through xcd_remap, so the units of one kv head share an XCD.
     const int seq = (int)a.seq;          // the host guarantees seq * max(hq, hkv) * d < 2^31
     const int nqt = (seq + kBR - 1) / kBR;
     const int G = a.hq / a.hkv;
     const bool pair_heads = (G & 1) == 0;
     const int per_g = pair_heads ? (G / 2) * nqt : G * ((nqt + 1) / 2);
     const int total = (int)a.batch * a.hkv * per_g;
-    int lid = xcd_remap((int)blockIdx.x, total);
-    const int unit = lid % per_g;
-    lid /= per_g;
-    const int g = lid % a.hkv;
-    const int b = lid / a.hkv;
-    int h, qt, qb_base, my_r, nrows;
-    if (pair_heads) {                    // groups = query heads 2jp, 2jp+1 of g, same rows
-        const int jp = unit % (G / 2);
-        const int rank = unit / (G / 2);
-        qt = (MODE != kDenseFull) ? nqt - 1 - rank : rank;   // causal: longest first
-        h = g * G + 2 * jp + grp;
-        qb_base = 2 * qt;
-        my_r = wq >> 1;
-        nrows = 2;
-    } else {                             // groups = query tiles 2qp, 2qp+1 of one head
-        const int npq = (nqt + 1) / 2;
-        const int j = unit % G;
-        const int rank = unit / G;
-        const int qp = (MODE != kDenseFull) ? npq - 1 - rank : rank;
-        h = g * G + j;
-        qt = 2 * qp + grp;
-        qb_base = 4 * qp;
-        my_r = 2 * grp + (wq >> 1);
-        nrows = 4;
-    }
+    // Persistent schedule when the grid is smaller than the unit count (the grid is then a multiple
+    // of 8): workgroup w stays on XCD w % 8 and takes that XCD's units in snake order over rounds of
+    // gridDim/8 (longest-first units in even rounds, shortest-first in odd ones), which balances the
+    // causal triangle; otherwise one unit per workgroup.
+    const bool persistent = (int)gridDim.x < total;
+    const int xcd = (int)blockIdx.x & 7, wi = (int)blockIdx.x >> 3, nper = (int)gridDim.x >> 3;
+    auto vb_at = [&](int k) -> int {
+        if (!persistent) return k == 0 ? (int)blockIdx.x : total;
+        const int t = k * nper + ((k & 1) ? nper - 1 - wi : wi);
+        return t * 8 + xcd;
+    };
 
     const uint32_t q_row_stride = (uint32_t)(a.hq * D);
     const uint32_t kv_row_stride = (uint32_t)(a.hkv * D);
     const int last_key = seq - 1;
-    const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * D;
-    const u16* kg = reinterpret_cast<const u16*>(a.k) + ((int64_t)b * a.seq * a.hkv + g) * D;
-    const u16* vg = reinterpret_cast<const u16*>(a.v) + ((int64_t)b * a.seq * a.hkv + g) * D;
-
-    const int q0 = qt * kBR + wq * 32;       // first query row of this wave
-    const int qpos = q0 + n;                 // this lane's query row
-    const bool wave_live = q0 < seq;
-    const int my_qb = qb_base + my_r;
 
     // per-lane byte offsets of the direct loads inside a tile (tile-invariant)
     uint32_t koff[L::INSTS_PER_WAVE], voff[L::INSTS_PER_WAVE];
@@ -300,14 +279,67 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
         koff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz_k<D>(row)));   // bytes
         voff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz_v<D>(row)));
     }
+    const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
-    // Q rows as the B operand of S^T = K Q^T: lane holds Q[qpos][16c + 8hh .. +7]
-    bf16x8 qreg[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    // state of the current unit
+    int b = 0, h = 0, qb_base = 0, my_r = 0, my_qb = 0, qpos = 0;
+    bool wave_live = false;
+    const u16* kg = nullptr;
+    const u16* vg = nullptr;
+    bf16x8 qreg[NC];   // Q rows as the B operand of S^T = K Q^T: lane holds Q[qpos][16c + 8hh .. +7]
+    TileWalk<MODE> walk;
+    uint32_t in;
+    int kb_p = 0, kb_c = 0, kb_n = 0;
+    bool mine_p = false, mine_c = false, mine_n = false, have_any = false, have_n = false;
+
+    // Set up unit vb and issue its first loads (K of its first tile into K slot 0, its Q rows into
+    // registers).  Called before the first unit and, for the next unit, after the current unit's
+    // last S (Q and both K slots are free then).
+    auto begin_unit = [&](int vb) {
+        int lid = xcd_remap(vb, total);
+        const int unit = lid % per_g;
+        lid /= per_g;
+        const int g = lid % a.hkv;
+        b = lid / a.hkv;
+        int qt, nrows;
+        if (pair_heads) {                    // groups = query heads 2jp, 2jp+1 of g, same rows
+            const int jp = unit % (G / 2);
+            const int rank = unit / (G / 2);
+            qt = (MODE != kDenseFull) ? nqt - 1 - rank : rank;   // causal: longest first
+            h = g * G + 2 * jp + grp;
+            qb_base = 2 * qt;
+            my_r = wq >> 1;
+            nrows = 2;
+        } else {                             // groups = query tiles 2qp, 2qp+1 of one head
+            const int npq = (nqt + 1) / 2;
+            const int j = unit % G;
+            const int rank = unit / G;
+            const int qp = (MODE != kDenseFull) ? npq - 1 - rank : rank;
+            h = g * G + j;
+            qt = 2 * qp + grp;
+            qb_base = 4 * qp;
+            my_r = 2 * grp + (wq >> 1);
+            nrows = 4;
+        }
+        kg = reinterpret_cast<const u16*>(a.k) + ((int64_t)b * a.seq * a.hkv + g) * D;
+        vg = reinterpret_cast<const u16*>(a.v) + ((int64_t)b * a.seq * a.hkv + g) * D;
+        const int q0 = qt * kBR + wq * 32;   // first query row of this wave
+        qpos = q0 + n;                       // this lane's query row
+        wave_live = q0 < seq;
+        my_qb = qb_base + my_r;
+        walk.init(qb_base, nrows, a.n_qblk, a.row_ptr, a.col_idx);
+        have_any = walk.next(kb_c, in);      // uniform over the workgroup; true for every valid launch
+        mine_c = have_any && wave_live && ((in >> my_r) & 1);
+        have_n = have_any && walk.next(kb_n, in);
+        mine_n = have_n && wave_live && ((in >> my_r) & 1);
+        mine_p = false;
+        if (have_any) issue_tile<D, false>(kg, kv_row_stride, kb_c, last_key, smem_lds + L::K_BASE, wave, lane, koff);
+        const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * D;
         const uint32_t qrow = (uint32_t)min(qpos, last_key);
-        qreg[c] = *reinterpret_cast<const bf16x8*>(qg + qrow * q_row_stride + 16 * c + 8 * hh);
-    }
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            qreg[c] = *reinterpret_cast<const bf16x8*>(qg + qrow * q_row_stride + 16 * c + 8 * hh);
+    };
 
     // LDS byte offsets of this lane's operand reads (slot-relative)
     // K: row 32kh + n, logical chunk 2c + hh -> physical (2c + hh) ^ swz_k(32kh + n)
@@ -335,7 +367,6 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     bf16x8 pb[2][2];
     float m_run = kNegBig, l_run = 0.0f;
     const float c2 = a.scale_log2;
-    const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
     // ---- matrix work of one phase: O^T += V^T P^T for the previous tile (V slot vs), then
     // S^T = K Q^T for the current tile (K slot ks), as one sequence of up to 32 MFMAs whose
@@ -451,99 +482,105 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
         l_run += (lsum[0][0] + lsum[0][1]) + (lsum[1][0] + lsum[1][1]);
     };
 
+    // ---- epilogue of the current unit: O = O^T / l, lane holds O[qpos][32mt + 8(r/4) + 4hh + r%4]
+    auto finish_unit = [&]() {
+        const float l_tot = sum_halves(l_run);
+        if (!wave_live || qpos >= seq) return;
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        const int64_t orow = ((int64_t)b * seq + qpos) * a.hq + h;
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * mt + 8 * r4 + 4 * hh;
+                const float v0 = oacc[mt][4 * r4] * inv, v1 = oacc[mt][4 * r4 + 1] * inv;
+                const float v2 = oacc[mt][4 * r4 + 2] * inv, v3 = oacc[mt][4 * r4 + 3] * inv;
+                if constexpr (OUT_F32) {
+                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + orow * D + d) =
+                        make_float4(v0, v1, v2, v3);
+                } else {
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    bf16x4 pk = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                    *reinterpret_cast<bf16x4*>(reinterpret_cast<u16*>(a.o) + orow * D + d) = pk;
+                }
+            }
+        if (a.lse && hh == 0) {
+            const float lse = l_tot > 0.0f ? (m_run * c2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+            a.lse[((int64_t)b * a.hq + h) * a.seq + qpos] = lse;
+        }
+    };
+
     // ---- tile pipeline.  Tile t's K goes to K slot t&1, its V to V slot t&1.  Step u (one per
     // tile, plus a final one) issues the loads of K(u+1) and V(u), then runs two phases:
     //   phase A: group 0 matrix work (P.V of tile u-1, S of tile u) | group 1 softmax of tile u-1
     //   phase B: group 0 softmax of tile u | group 1 matrix work (P.V of tile u-1, S of tile u)
     // The first step has no P.V and the final step no S; every wave of a group issues the
     // same MFMAs (a wave whose rows skip a tile multiplies zero probabilities), so the
-    // loop body has a single form.
+    // loop body has a single form.  After the final step's S-free phase each group writes its
+    // outputs and starts the loads of its next unit.
     constexpr BoolTag<true> kOn{};
     constexpr BoolTag<false> kOff{};
-    TileWalk<MODE> walk;
-    walk.init(qb_base, nrows, a.n_qblk, a.row_ptr, a.col_idx);
-    uint32_t in;
-    int kb_p = 0, kb_c = 0, kb_n = 0;
-    bool mine_p = false;
-    const bool have_any = walk.next(kb_c, in);   // uniform over the workgroup; true for every valid launch
-    bool mine_c = have_any && wave_live && ((in >> my_r) & 1);
-    bool have_n = have_any && walk.next(kb_n, in);
-    bool mine_n = have_n && wave_live && ((in >> my_r) & 1);
-    if (have_any) issue_tile<D, false>(kg, kv_row_stride, kb_c, last_key, smem_lds + L::K_BASE, wave, lane, koff);
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): Q and K of tile 0 in place
-    __syncthreads();
+    begin_unit(vb_at(0));
     auto run = [&](auto group_tag) {
         constexpr bool kG1 = decltype(group_tag)::value;
-        if (!have_any) return;
-        // step 0
-        if (have_n)
-            issue_tile<D, false>(kg, kv_row_stride, kb_n, last_key, smem_lds + L::K_BASE + L::TILE_B, wave, lane,
-                                 koff);
-        issue_tile<D, true>(vg, kv_row_stride, kb_c, last_key, smem_lds + L::V_BASE, wave, lane, voff);
-        if constexpr (!kG1) mwork(kOff, kOn, 0, 0);
-        __syncthreads();
-        if constexpr (!kG1) vwork(mine_c, kb_c);
-        else mwork(kOff, kOn, 0, 0);
-        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of K(1), V(0) landed
-        __syncthreads();
-        // steps 1 .. T-1
-        int sl = 1;
-        while (have_n) {
-            kb_p = kb_c;
-            mine_p = mine_c;
-            kb_c = kb_n;
-            mine_c = mine_n;
-            have_n = walk.next(kb_n, in);
-            mine_n = have_n && wave_live && ((in >> my_r) & 1);
-            if (have_n)
-                issue_tile<D, false>(kg, kv_row_stride, kb_n, last_key,
-                                     smem_lds + L::K_BASE + (sl ^ 1) * L::TILE_B, wave, lane, koff);
-            issue_tile<D, true>(vg, kv_row_stride, kb_c, last_key, smem_lds + L::V_BASE + sl * L::TILE_B, wave,
-                                lane, voff);
-            if constexpr (!kG1) mwork(kOn, kOn, sl ^ 1, sl);
-            else vwork(mine_p, kb_p);
+        for (int k = 1;; ++k) {
+            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): Q and K of the unit's first tile in place
             __syncthreads();
-            if constexpr (!kG1) vwork(mine_c, kb_c);
-            else mwork(kOn, kOn, sl ^ 1, sl);
-            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of K(u+1), V(u) landed
-            __syncthreads();
-            sl ^= 1;
+            if (have_any) {
+                // step 0
+                if (have_n)
+                    issue_tile<D, false>(kg, kv_row_stride, kb_n, last_key, smem_lds + L::K_BASE + L::TILE_B, wave,
+                                         lane, koff);
+                issue_tile<D, true>(vg, kv_row_stride, kb_c, last_key, smem_lds + L::V_BASE, wave, lane, voff);
+                if constexpr (!kG1) mwork(kOff, kOn, 0, 0);
+                __syncthreads();
+                if constexpr (!kG1) vwork(mine_c, kb_c);
+                else mwork(kOff, kOn, 0, 0);
+                __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of K(1), V(0) landed
+                __syncthreads();
+                // steps 1 .. T-1
+                int sl = 1;
+                while (have_n) {
+                    kb_p = kb_c;
+                    mine_p = mine_c;
+                    kb_c = kb_n;
+                    mine_c = mine_n;
+                    have_n = walk.next(kb_n, in);
+                    mine_n = have_n && wave_live && ((in >> my_r) & 1);
+                    if (have_n)
+                        issue_tile<D, false>(kg, kv_row_stride, kb_n, last_key,
+                                             smem_lds + L::K_BASE + (sl ^ 1) * L::TILE_B, wave, lane, koff);
+                    issue_tile<D, true>(vg, kv_row_stride, kb_c, last_key, smem_lds + L::V_BASE + sl * L::TILE_B,
+                                        wave, lane, voff);
+                    if constexpr (!kG1) mwork(kOn, kOn, sl ^ 1, sl);
+                    else vwork(mine_p, kb_p);
+                    __syncthreads();
+                    if constexpr (!kG1) vwork(mine_c, kb_c);
+                    else mwork(kOn, kOn, sl ^ 1, sl);
+                    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of K(u+1), V(u) landed
+                    __syncthreads();
+                    sl ^= 1;
+                }
+                // final step: P.V of the last tile (its V is in slot sl ^ 1)
+                if constexpr (!kG1) mwork(kOn, kOff, sl ^ 1, 0);
+                else vwork(mine_c, kb_c);
+                __syncthreads();
+                if constexpr (kG1) mwork(kOn, kOff, sl ^ 1, 0);
+            }
+            finish_unit();
+            const int vb = vb_at(k);
+            if (vb >= total) break;
+#pragma unroll
+            for (int mt = 0; mt < NM; ++mt) oacc[mt] = f32x16{};
+            m_run = kNegBig;
+            l_run = 0.0f;
+            begin_unit(vb);
         }
-        // final step: P.V of the last tile (its V is in slot sl ^ 1)
-        if constexpr (!kG1) mwork(kOn, kOff, sl ^ 1, 0);
-        else vwork(mine_c, kb_c);
-        __syncthreads();
-        if constexpr (kG1) mwork(kOn, kOff, sl ^ 1, 0);
     };
     if (grp == 0)
         run(BoolTag<false>{});
     else
         run(BoolTag<true>{});
-
-    // ---- epilogue: O = O^T / l, lane holds O[qpos][32mt + 8(r/4) + 4hh + r%4]
-    const float l_tot = sum_halves(l_run);
-    if (!wave_live || qpos >= seq) return;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const int64_t orow = ((int64_t)b * seq + qpos) * a.hq + h;
-#pragma unroll
-    for (int mt = 0; mt < NM; ++mt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int d = 32 * mt + 8 * r4 + 4 * hh;
-            const float v0 = oacc[mt][4 * r4] * inv, v1 = oacc[mt][4 * r4 + 1] * inv;
-            const float v2 = oacc[mt][4 * r4 + 2] * inv, v3 = oacc[mt][4 * r4 + 3] * inv;
-            if constexpr (OUT_F32) {
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + orow * D + d) = make_float4(v0, v1, v2, v3);
-            } else {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                bf16x4 pk = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-                *reinterpret_cast<bf16x4*>(reinterpret_cast<u16*>(a.o) + orow * D + d) = pk;
-            }
-        }
-    if (a.lse && hh == 0) {
-        const float lse = l_tot > 0.0f ? (m_run * c2 + __log2f(l_tot)) * kLn2 : -INFINITY;
-        a.lse[((int64_t)b * a.hq + h) * a.seq + qpos] = lse;
-    }
 }
 
 // kRouted: one launch whose workgroups read the layer's mode and run the dense-causal or the
@@ -567,7 +604,10 @@ hipError_t launch_mode(const PrefillArgs& a, hipStream_t s) {
     const int64_t nqt = (a.seq + kBR - 1) / kBR;
     const int64_t G = a.hq / a.hkv;
     const int64_t per_g = (G % 2 == 0) ? (G / 2) * nqt : G * ((nqt + 1) / 2);
-    const int64_t grid = a.batch * a.hkv * per_g;
+    const int64_t total = a.batch * a.hkv * per_g;
+    // one resident workgroup per CU; persistent when there are at least two units per CU
+    const int64_t persist = (int64_t)(a.num_cu / 8) * 8;
+    const int64_t grid = (persist >= 8 && total >= 2 * persist) ? persist : total;
     if (a.out_f32)
         hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     else
