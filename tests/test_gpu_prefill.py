@@ -157,6 +157,18 @@ def test_llama_layer_dense_s8192_bf16_out(fa):
     _sampled_check(fa, 1, 8192, 32, 8, 128, 0, 128, 2048, seed=1012, n_random=200, out_dtype=torch.bfloat16)
 
 
+@pytest.mark.parametrize("B,S,Hq,Hkv,d,mode", [
+    (2, 8200, 16, 16, 64, 0),     # MHA (odd group: the two wave groups take two query tiles), ragged tail
+    (2, 8200, 16, 16, 64, 1),
+    (1, 16384, 8, 4, 128, 0),     # groups of 2 query heads
+    (1, 16384, 8, 4, 128, 1),
+])
+def test_persistent_schedule_shapes_sampled(fa, B, S, Hq, Hkv, d, mode):
+    """Shapes with at least two units per compute unit run on the persistent schedule; cover both
+    unit pairings and a ragged sequence end."""
+    _sampled_check(fa, B, S, Hq, Hkv, d, mode, 128, 2048, seed=1020 + S + Hq, n_random=120)
+
+
 def test_layer_sparse_s65536_sampled(fa):
     """Same layer at seq 65536, block-sparse: block 64, sink 128, window 2048 (32 blocks)."""
     _sampled_check(fa, 1, 65536, 32, 8, 128, 1, 128, 2048, seed=1003, n_random=400)
