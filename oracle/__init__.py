@@ -36,6 +36,10 @@ def _load():
     lib.oracle_attention_rows.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, i32, dbl, i32, i32, i32,
                                           i32, i32, vp, i64, i32, vp, vp]
     lib.oracle_attention_rows.restype = i32
+    lib.oracle_soft_weights.argtypes = [vp, vp, dbl, i32, vp]
+    lib.oracle_soft_weights.restype = i32
+    lib.oracle_mix.argtypes = [vp, vp, dbl, dbl, i64, vp]
+    lib.oracle_mix.restype = None
     lib.oracle_decode.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, i32, dbl, i32, i32, i32, i32, vp, i64,
                                   i32, vp, vp]
     lib.oracle_decode.restype = i32
@@ -161,3 +165,27 @@ def route(xq_layers, w_enc, b_enc, w_head, b_head, pool_tokens=100):
     if rc != 0:
         raise ValueError(f"oracle_route failed ({rc})")
     return pooled, logits, modes
+
+
+def soft_weights(logits, uniforms, tau):
+    """Gumbel-softmax routing weights [L,2] from logits [L,2] and uniforms [L,2] in (0,1)."""
+    logits = np.ascontiguousarray(logits, np.float64)
+    uniforms = np.ascontiguousarray(uniforms, np.float64)
+    L = logits.shape[0]
+    assert logits.shape == (L, 2) and uniforms.shape == (L, 2)
+    w = np.empty((L, 2), np.float64)
+    if _load().oracle_soft_weights(_ptr(logits), _ptr(uniforms), float(tau), L, _ptr(w)) != 0:
+        raise ValueError("oracle_soft_weights: bad argument")
+    return w
+
+
+def attention_soft(q, k, v, scale, weights, block=64, sink_tokens=0, window_tokens=0, rows=None, n_threads=0):
+    """Soft-routed layer output: weights[0] * full causal attention + weights[1] * block-sparse attention."""
+    o_full, _ = attention(q, k, v, scale, causal=True, sparse=False, rows=rows, n_threads=n_threads)
+    o_sparse, _ = attention(q, k, v, scale, causal=True, sparse=True, block=block, sink_tokens=sink_tokens,
+                            window_tokens=window_tokens, rows=rows, n_threads=n_threads)
+    o_full = np.ascontiguousarray(o_full, np.float64)
+    o_sparse = np.ascontiguousarray(o_sparse, np.float64)
+    out = np.empty_like(o_full)
+    _load().oracle_mix(_ptr(o_full), _ptr(o_sparse), float(weights[0]), float(weights[1]), o_full.size, _ptr(out))
+    return out

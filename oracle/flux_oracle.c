@@ -26,6 +26,10 @@
  *     last P tokens, an MLP context encoder, a two-logit router head and an
  *     argmax (ties to index 0 = full attention), from the router paragraphs of
  *     the Flux Attention page.
+ *   - soft routing (the training-time relaxation in the same router paragraph):
+ *     r = softmax((pi + g) / tau) over (pi_FA, pi_SA) with Gumbel noise
+ *     g = -ln(-ln u) drawn from uniforms u in (0, 1), and the layer output
+ *     r_FA * O_FA + r_SA * O_SA (full and sparse attention outputs).
  *
  * Inputs are read either as float32 or as bfloat16 bit patterns; both widen
  * to double exactly.
@@ -325,4 +329,34 @@ int oracle_route(const void* const* xq_layers, int kind, int n_layers, int64_t s
     free(pooled);
     free(z);
     return 0;
+}
+
+/*
+ * Soft-routing weights per layer (Flux Attention page, router paragraph: the
+ * Gumbel-Softmax relaxation used in training).  logits [L, 2] = (pi_FA, pi_SA),
+ * uniforms [L, 2] in (0, 1) -> Gumbel noise g = -ln(-ln u); weights [L, 2] =
+ * exp((pi_i + g_i) / tau) / sum_j exp((pi_j + g_j) / tau), computed with the
+ * larger exponent subtracted.  Returns 1 on a bad argument.
+ */
+int oracle_soft_weights(const double* logits, const double* uniforms, double tau, int n_layers,
+                        double* weights) {
+    if (n_layers <= 0 || !(tau > 0.0)) return 1;
+    for (int l = 0; l < n_layers; ++l) {
+        double x[2];
+        for (int c = 0; c < 2; ++c) {
+            double u = uniforms[2 * l + c];
+            if (!(u > 0.0 && u < 1.0)) return 1;
+            x[c] = (logits[2 * l + c] - log(-log(u))) / tau;
+        }
+        double m = x[0] > x[1] ? x[0] : x[1];
+        double e0 = exp(x[0] - m), e1 = exp(x[1] - m);
+        weights[2 * l] = e0 / (e0 + e1);
+        weights[2 * l + 1] = e1 / (e0 + e1);
+    }
+    return 0;
+}
+
+/* out[i] = w0 * o_full[i] + w1 * o_sparse[i]: the soft-routed layer output (same page). */
+void oracle_mix(const double* o_full, const double* o_sparse, double w0, double w1, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = w0 * o_full[i] + w1 * o_sparse[i];
 }
