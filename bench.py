@@ -122,8 +122,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="sparse,decode,decode_loop,peaks",
-                    help="comma list of secondary legs: sparse, dense64k, decode, decode_loop, stack, peaks "
+    ap.add_argument("--legs", default="sparse,decode,decode_loop,soft,peaks",
+                    help="comma list of secondary legs: sparse, dense64k, decode, decode_loop, soft, stack, peaks "
                          "(or 'none')")
     ap.add_argument("--no-legs", dest="legs", action="store_const", const="none")
     ap.add_argument("--no-headline", dest="headline", action="store_false", default=True,
@@ -306,11 +306,49 @@ def run_legs(fa, synth, torch, dev, sel, reps):
 
     if "stack" in sel:
         legs["stack_s131072"] = run_stack(fa, synth, torch, dev)
+    if "soft" in sel:
+        legs["soft_routed_prefill_s8192"] = run_soft(fa, synth, torch, dev, reps)
     if "decode_loop" in sel:
         legs["decode_loop_36l_L262144"] = run_decode_loop(fa, synth, torch, dev)
     if "peaks" in sel:
         legs["device_ceilings"] = run_peaks(torch, dev)
     return legs
+
+
+def run_soft(fa, synth, torch, dev, reps):
+    """Training-time soft routing at the headline layer shape (seq 8192, 32/8 heads, head_dim 128):
+    router logits -> Gumbel-softmax weights -> w_FA * dense + w_SA * sparse attention, timed against
+    the dense layer alone."""
+    B, S, Hq, Hkv, d = 1, 8192, 32, 8, 128
+    log("leg: soft-routed prefill")
+    q = synth.torch_normal((B, S, Hq, d), 1302, torch.bfloat16)
+    k = synth.torch_normal((B, S, Hkv, d), 1303, torch.bfloat16)
+    v = synth.torch_normal((B, S, Hkv, d), 1304, torch.bfloat16)
+    o = torch.empty((B, S, Hq, d), dtype=torch.bfloat16, device=dev)
+    w = synth.router_weights(1, Hq * d, 256, seed=1305)
+    w_enc, b_enc, w_head, b_head = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in w)
+    logits = torch.empty((1, 2), dtype=torch.float32, device=dev)
+    modes = torch.empty(1, dtype=torch.int32, device=dev)
+    u = torch.tensor([[0.37, 0.61]], dtype=torch.float32, device=dev)
+    weights = torch.empty((1, 2), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.flux_prefill_soft_workspace_size(B, S, Hq, d), dtype=torch.uint8, device=dev)
+    route_ws = torch.empty(fa.flux_route_workspace_size(1, Hq, d, 256), dtype=torch.uint8, device=dev)
+    rp, ci = fa.flux_build_block_mask(S, S, 64, 128, 2048, 1, fa.FLUX_MODE_SPARSE)
+    rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+
+    def soft():
+        fa.flux_route_layers([q[0]], w_enc, b_enc, w_head, b_head, modes, logits, workspace=route_ws,
+                             pool_tokens=100)
+        fa.flux_route_soft_weights(logits, u, 1.0, weights)
+        fa.flux_attn_prefill_soft(q, k, v, o, weights[0], blk_row_ptr=rpd, blk_col_idx=cid, workspace=ws)
+    ms = time_steps(soft, reps, 3)
+    dense = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_DENSE)
+    ms_d = time_steps(dense, reps, 3)
+    res = {"ms": round(ms, 4), "dense_only_ms": round(ms_d, 4), "overhead_vs_dense": round(ms / ms_d, 3),
+           "weights": [round(float(x), 4) for x in weights[0].cpu()]}
+    del q, k, v, o, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_decode_loop(fa, synth, torch, dev, steps=5):

@@ -176,6 +176,37 @@ int flux_attn_prefill_layers_routed(int32_t n_layers, const int32_t* modes_devic
                                     int64_t blk_nnz, void* hip_stream);
 
 /*
+ * flux_route_soft_weights -- Gumbel-softmax routing weights of the training-time
+ * relaxation ([FA] router paragraph): for each layer l,
+ *   g_i = -ln(-ln u[l][i]),  w[l][i] = exp((pi[l][i] + g_i) / tau) / sum_j exp((pi[l][j] + g_j) / tau)
+ * over i in {0 = FA, 1 = SA}.  logits [n_layers, 2] (e.g. flux_route_layers' logits_out), uniforms
+ * [n_layers, 2] in (0, 1) (the random draw, supplied by the caller) and weights_out [n_layers, 2]:
+ * device float32.  tau > 0 and finite.
+ */
+int flux_route_soft_weights(const float* logits, const float* uniforms, float tau, int32_t n_layers,
+                            float* weights_out, void* hip_stream);
+
+/* flux_prefill_soft_workspace_size -- bytes flux_attn_prefill_soft needs (an fp32 [B, S, Hq, d] buffer). */
+size_t flux_prefill_soft_workspace_size(int64_t batch, int64_t seq, int32_t hq, int32_t head_dim);
+
+/*
+ * flux_attn_prefill_soft -- soft-routed layer output for training ([FA] router paragraph: the full
+ * and sparse attention outputs weighted by the Gumbel-softmax probabilities):
+ *   o = w[0] * attention(dense causal) + w[1] * attention(block-sparse)
+ * with weights_device [2] device float32 (one row of flux_route_soft_weights' output).  The full
+ * attention goes to `workspace` in fp32; the sparse pass adds it in its epilogue (no extra launch).
+ * Inputs BF16; out_dtype BF16 or F32; CSR as for flux_attn_prefill in sparse mode.  No LSE (the
+ * output is a mixture of two softmaxes).
+ */
+int flux_attn_prefill_soft(const void* q, const void* k, const void* v, void* o, int32_t in_dtype,
+                           int32_t out_dtype, int64_t batch, int64_t seq, int32_t hq, int32_t hkv,
+                           int32_t head_dim, float scale, int32_t block, int32_t sink_tokens,
+                           int32_t window_tokens, const int32_t* blk_row_ptr,
+                           const int32_t* blk_col_idx, int64_t blk_nnz,
+                           const float* weights_device, void* workspace, size_t workspace_bytes,
+                           void* hip_stream);
+
+/*
  * flux_decode_workspace_size -- bytes of workspace flux_attn_decode needs.
  * Same meaning of arguments as flux_attn_decode (num_splits = 0: automatic;
  * the automatic split count depends on batch * hkv, so hkv is needed here).

@@ -19,7 +19,8 @@ __all__ = [
     "FluxError", "lib", "status_string", "last_error_detail", "flux_version",
     "flux_build_block_mask", "flux_attn_prefill", "flux_attn_prefill_layers", "flux_attn_prefill_layers_routed",
     "flux_decode_workspace_size", "flux_attn_decode", "flux_window_cache_rows", "flux_decode_step",
-    "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers",
+    "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers", "flux_route_soft_weights",
+    "flux_prefill_soft_workspace_size", "flux_attn_prefill_soft",
     "FLUX_OK", "FLUX_ERR_INVALID_ARG", "FLUX_ERR_UNSUPPORTED", "FLUX_ERR_CAPACITY", "FLUX_ERR_WORKSPACE",
     "FLUX_ERR_HIP", "FLUX_DTYPE_BF16", "FLUX_DTYPE_F32", "FLUX_MODE_DENSE", "FLUX_MODE_SPARSE", "FLUX_KV_FULL",
     "FLUX_KV_WINDOW",
@@ -35,7 +36,8 @@ EXPORTED_SYMBOLS = (
     "flux_status_string", "flux_last_error_detail", "flux_version", "flux_build_block_mask",
     "flux_attn_prefill", "flux_attn_prefill_layers", "flux_attn_prefill_layers_routed",
     "flux_decode_workspace_size", "flux_attn_decode", "flux_window_cache_rows", "flux_decode_step",
-    "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers",
+    "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers", "flux_route_soft_weights",
+    "flux_prefill_soft_workspace_size", "flux_attn_prefill_soft",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +83,13 @@ _lib.flux_decode_step.restype = ctypes.c_int
 _lib.flux_decode_step_layers.argtypes = [_i32, _vp, _pp, _pp, _pp, _pp, _pp, _pp, _pp, _i32, _i64, _i64, _i64, _i32,
                                          _i32, _i32, _f32, _i32, _i32, _i32, _vp, _sz, _vp]
 _lib.flux_decode_step_layers.restype = ctypes.c_int
+_lib.flux_route_soft_weights.argtypes = [_vp, _vp, _f32, _i32, _vp, _vp]
+_lib.flux_route_soft_weights.restype = ctypes.c_int
+_lib.flux_prefill_soft_workspace_size.argtypes = [_i64, _i64, _i32, _i32]
+_lib.flux_prefill_soft_workspace_size.restype = _sz
+_lib.flux_attn_prefill_soft.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _i32,
+                                        _i32, _vp, _vp, _i64, _vp, _vp, _sz, _vp]
+_lib.flux_attn_prefill_soft.restype = ctypes.c_int
 _lib.flux_route_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.flux_route_workspace_size.restype = _sz
 _lib.flux_route_layers.argtypes = [_pp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
@@ -315,3 +324,36 @@ def flux_route_layers(q_layers, w_enc, b_enc, w_head, b_head, modes_out, logits_
     _check(_lib.flux_route_layers(pq, L, S, Hq, d, _dtype_code(q_layers[0]), pool_tokens, _ptr(w_enc), _ptr(b_enc),
                                   hidden, _ptr(w_head), _ptr(b_head), _ptr(logits_out), _ptr(modes_out),
                                   _ptr(workspace), ws_bytes, _stream(stream)), "flux_route_layers")
+
+
+def flux_route_soft_weights(logits, uniforms, tau: float, weights_out, stream=None):
+    """Gumbel-softmax weights [L,2] (device float32) from logits [L,2] and uniforms [L,2] in (0,1)."""
+    _contig(logits, uniforms, weights_out)
+    L = logits.shape[0]
+    _check(_lib.flux_route_soft_weights(_ptr(logits), _ptr(uniforms), tau, L, _ptr(weights_out), _stream(stream)),
+           "flux_route_soft_weights")
+
+
+def flux_prefill_soft_workspace_size(batch, seq, hq, head_dim) -> int:
+    return int(_lib.flux_prefill_soft_workspace_size(batch, seq, hq, head_dim))
+
+
+def flux_attn_prefill_soft(q, k, v, o, weights_dev, *, block: int = 64, sink_tokens: int = 128,
+                           window_tokens: int = 2048, blk_row_ptr=None, blk_col_idx=None, workspace=None,
+                           scale: float | None = None, stream=None):
+    """o = w[0] * dense-causal attention + w[1] * block-sparse attention; weights_dev: device float32 [2]."""
+    _contig(q, k, v, o, weights_dev)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        import torch
+        workspace = torch.empty(flux_prefill_soft_workspace_size(B, S, Hq, d), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    nnz = int(blk_col_idx.numel()) if blk_col_idx is not None else 0
+    _check(_lib.flux_attn_prefill_soft(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), _dtype_code(o), B, S, Hq,
+                                       Hkv, d, scale, block, sink_tokens, window_tokens, _ptr(blk_row_ptr),
+                                       _ptr(blk_col_idx), nnz, _ptr(weights_dev), _ptr(workspace), ws_bytes,
+                                       _stream(stream)),
+           "flux_attn_prefill_soft")

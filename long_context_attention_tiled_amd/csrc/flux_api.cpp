@@ -159,6 +159,8 @@ int check_prefill(const void* q, const void* k, const void* v, void* o, float* l
     a->col_idx = ms.sparse ? ci : nullptr;
     a->mode_dev = nullptr;
     a->num_cu = 0;
+    a->mix_o = nullptr;
+    a->mix_w = nullptr;
     return FLUX_OK;
 }
 
@@ -442,6 +444,47 @@ int flux_attn_prefill_layers_routed(int32_t n_layers, const int32_t* modes_devic
         if (st != FLUX_OK) return st;
     }
     return ok();
+}
+
+size_t flux_prefill_soft_workspace_size(int64_t batch, int64_t seq, int32_t hq, int32_t head_dim) {
+    if (batch < 1 || seq < 1 || hq < 1 || head_dim < 1) return 0;
+    return (size_t)batch * seq * hq * head_dim * sizeof(float);
+}
+
+int flux_attn_prefill_soft(const void* q, const void* k, const void* v, void* o, int32_t in_dtype, int32_t out_dtype,
+                           int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                           int32_t block, int32_t sink_tokens, int32_t window_tokens, const int32_t* blk_row_ptr,
+                           const int32_t* blk_col_idx, int64_t blk_nnz, const float* weights_device,
+                           void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!weights_device || (reinterpret_cast<uintptr_t>(weights_device) & 3u))
+        return fail(FLUX_ERR_INVALID_ARG, "weights_device must be a 4-byte aligned device pointer");
+    if (in_dtype != FLUX_DTYPE_BF16) return fail(FLUX_ERR_UNSUPPORTED, "soft routing takes bfloat16 inputs");
+    flux::PrefillArgs full, sparse;
+    int st = check_prefill(q, k, v, workspace, nullptr, in_dtype, FLUX_DTYPE_F32, batch, seq, hq, hkv, head_dim, scale,
+                           1, FLUX_MODE_DENSE, block, sink_tokens, window_tokens, nullptr, nullptr, 0, &full);
+    if (st != FLUX_OK) return st;
+    st = check_prefill(q, k, v, o, nullptr, in_dtype, out_dtype, batch, seq, hq, hkv, head_dim, scale, 1,
+                       FLUX_MODE_SPARSE, block, sink_tokens, window_tokens, blk_row_ptr, blk_col_idx, blk_nnz, &sparse);
+    if (st != FLUX_OK) return st;
+    const size_t need = flux_prefill_soft_workspace_size(batch, seq, hq, head_dim);
+    if (workspace_bytes < need)
+        return fail(FLUX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (workspace == o) return fail(FLUX_ERR_INVALID_ARG, "workspace must not alias o");
+    st = launch_prefill(full, in_dtype, as_stream(hip_stream));       // full attention -> fp32 workspace
+    if (st != FLUX_OK) return st;
+    sparse.mix_o = reinterpret_cast<const float*>(workspace);          // sparse attention, mixed in its epilogue
+    sparse.mix_w = weights_device;
+    return launch_prefill(sparse, in_dtype, as_stream(hip_stream));
+}
+
+int flux_route_soft_weights(const float* logits, const float* uniforms, float tau, int32_t n_layers,
+                            float* weights_out, void* hip_stream) {
+    if (!logits || !uniforms || !weights_out) return fail(FLUX_ERR_INVALID_ARG, "pointers must be non-NULL");
+    if (n_layers < 1) return fail(FLUX_ERR_INVALID_ARG, "n_layers must be >= 1");
+    if (!(tau > 0.0f) || !std::isfinite(tau)) return fail(FLUX_ERR_INVALID_ARG, "tau must be finite and > 0");
+    hipError_t e = flux::launch_route_soft(logits, uniforms, tau, n_layers, weights_out, as_stream(hip_stream));
+    if (e == hipSuccess) e = hipGetLastError();
+    return hip_status(e, "soft routing launch");
 }
 
 size_t flux_decode_workspace_size(int64_t batch, int32_t hq, int32_t hkv, int64_t kv_len, int32_t head_dim,

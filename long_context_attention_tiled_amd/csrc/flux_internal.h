@@ -31,6 +31,8 @@ struct PrefillArgs {
     const int32_t* mode_dev;  // device-resident mode of this layer (0 dense causal, else sparse),
                               // read by the kernel; nullptr when the mode is fixed by `sparse`
     int num_cu;               // compute units of the device (persistent grid size)
+    const float* mix_o;       // soft routing: fp32 [B, S, Hq, d] output of the other mode, or nullptr
+    const float* mix_w;       // soft routing: device [2] weights (mix_o's, this launch's)
 };
 
 struct DecodeArgs {
@@ -91,5 +93,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_route_soft(const float* logits, const float* uniforms, float tau, int n_layers, float* weights,
+                             hipStream_t s);
 
 }  // namespace flux

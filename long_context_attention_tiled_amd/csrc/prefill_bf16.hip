@@ -493,8 +493,16 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int d = 32 * mt + 8 * r4 + 4 * hh;
-                const float v0 = oacc[mt][4 * r4] * inv, v1 = oacc[mt][4 * r4 + 1] * inv;
-                const float v2 = oacc[mt][4 * r4 + 2] * inv, v3 = oacc[mt][4 * r4 + 3] * inv;
+                float v0 = oacc[mt][4 * r4] * inv, v1 = oacc[mt][4 * r4 + 1] * inv;
+                float v2 = oacc[mt][4 * r4 + 2] * inv, v3 = oacc[mt][4 * r4 + 3] * inv;
+                if (a.mix_o) {   // soft routing: weighted sum with the other mode's output
+                    const float w0 = a.mix_w[0], w1 = a.mix_w[1];
+                    const float4 f = *reinterpret_cast<const float4*>(a.mix_o + orow * D + d);
+                    v0 = fmaf(w0, f.x, w1 * v0);
+                    v1 = fmaf(w0, f.y, w1 * v1);
+                    v2 = fmaf(w0, f.z, w1 * v2);
+                    v3 = fmaf(w0, f.w, w1 * v3);
+                }
                 if constexpr (OUT_F32) {
                     *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + orow * D + d) =
                         make_float4(v0, v1, v2, v3);

@@ -116,7 +116,29 @@ __global__ __launch_bounds__(64) void route_head_kernel(RouteArgs a) {
     }
 }
 
+// Gumbel-softmax routing weights (the training-time relaxation of the router head, router
+// paragraph of the Flux Attention page): w = softmax((pi + g) / tau), g = -ln(-ln u).
+__global__ __launch_bounds__(64) void route_soft_kernel(const float* logits, const float* uniforms, float tau,
+                                                        int n_layers, float* weights) {
+    const int l = blockIdx.x * 64 + threadIdx.x;
+    if (l >= n_layers) return;
+    const float x0 = (logits[2 * l] - logf(-logf(uniforms[2 * l]))) / tau;
+    const float x1 = (logits[2 * l + 1] - logf(-logf(uniforms[2 * l + 1]))) / tau;
+    const float m = fmaxf(x0, x1);
+    const float e0 = expf(x0 - m), e1 = expf(x1 - m);
+    const float inv = 1.0f / (e0 + e1);
+    weights[2 * l] = e0 * inv;
+    weights[2 * l + 1] = e1 * inv;
+}
+
 }  // namespace
+
+hipError_t launch_route_soft(const float* logits, const float* uniforms, float tau, int n_layers, float* weights,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(route_soft_kernel, dim3((n_layers + 63) / 64), dim3(64), 0, s, logits, uniforms, tau, n_layers,
+                       weights);
+    return hipGetLastError();
+}
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(route_pool_kernel, dim3(a.n_layers, (a.n_feat + kPoolFeat - 1) / kPoolFeat),

@@ -235,6 +235,32 @@ def test_decode_step_layers_validation(fa):
     assert call([1, 0], dense_rows=50) == fa.FLUX_ERR_CAPACITY and "layer 1" in fa.last_error_detail()
 
 
+def test_soft_routing_validation(fa):
+    E = fa.FLUX_ERR_INVALID_ARG
+    lib = fa.lib()
+    assert lib.flux_route_soft_weights(None, FAKE, 1.0, 2, FAKE, None) == E
+    assert lib.flux_route_soft_weights(FAKE, FAKE, 0.0, 2, FAKE, None) == E
+    assert lib.flux_route_soft_weights(FAKE, FAKE, float("nan"), 2, FAKE, None) == E
+    assert lib.flux_route_soft_weights(FAKE, FAKE, 1.0, 0, FAKE, None) == E
+    assert fa.flux_prefill_soft_workspace_size(2, 100, 4, 64) == 2 * 100 * 4 * 64 * 4
+    assert fa.flux_prefill_soft_workspace_size(0, 100, 4, 64) == 0
+
+    def soft(**kw):
+        a = dict(q=FAKE, o=FAKE + 4096, in_dtype=0, out_dtype=1, seq=512, rp=FAKE, ci=FAKE, nnz=26, w=FAKE,
+                 ws=FAKE + 8192, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.flux_attn_prefill_soft(a["q"], FAKE, FAKE, a["o"], a["in_dtype"], a["out_dtype"], 1, a["seq"], 4,
+                                          2, 128, 0.088, 64, 128, 128, a["rp"], a["ci"], a["nnz"], a["w"], a["ws"],
+                                          a["ws_bytes"], None)
+    assert soft(w=None) == E
+    assert soft(in_dtype=1) == fa.FLUX_ERR_UNSUPPORTED
+    assert soft(rp=None) == E
+    assert soft(nnz=25) == E
+    assert soft(ws_bytes=100) == fa.FLUX_ERR_WORKSPACE
+    assert soft(ws=FAKE + 4096) == E                       # aliases o
+    assert soft(ws=FAKE + 4100) == E                       # misaligned workspace
+
+
 # ---------------------------------------------------------------- decode validation / workspace
 def test_decode_workspace_size(fa):
     B, Hq, Hkv, L, d = 8, 32, 8, 262144, 128

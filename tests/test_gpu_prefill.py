@@ -257,3 +257,67 @@ def test_routed_dispatch_fp32_inputs(fa):
         ref, _ = oracle.attention(q, k, v, 1.0 / 8, causal=True, sparse=bool(mode), block=64, sink_tokens=128,
                                   window_tokens=128)
         check_close(o.cpu().numpy(), ref, f"routed fp32 mode {mode}")
+
+
+# ------------------------------------------------------------------ soft routing (training-time forward)
+def test_soft_weights_match_oracle(fa):
+    rng = np.random.default_rng(71)
+    L = 40
+    logits = rng.normal(size=(L, 2)).astype(np.float32) * 2
+    u = rng.uniform(0.001, 0.999, size=(L, 2)).astype(np.float32)
+    w = torch.empty((L, 2), dtype=torch.float32, device=DEV)
+    for tau in (5.0, 1.0, 0.1):
+        say("soft weights", tau)
+        fa.flux_route_soft_weights(torch.from_numpy(logits).to(DEV), torch.from_numpy(u).to(DEV), tau, w)
+        torch.cuda.synchronize()
+        ref = oracle.soft_weights(logits.astype(np.float64), u.astype(np.float64), tau)
+        assert np.abs(w.cpu().numpy() - ref).max() < 2e-5
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,d,sink,window,w0", [
+    (1, 700, 4, 2, 128, 128, 256, 0.3),
+    (2, 333, 8, 2, 64, 64, 128, 0.85),
+    (1, 512, 2, 2, 128, 128, 128, 1.0),
+    (1, 512, 2, 2, 128, 128, 128, 0.0),
+])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_soft_prefill_matches_oracle(fa, B, S, Hq, Hkv, d, sink, window, w0, out_dtype):
+    say("soft prefill", B, S, Hq, Hkv, d, sink, window, w0, out_dtype)
+    (q, k, v), (qd, kd, vd) = bf16_tensors(B, S, Hq, Hkv, d, seed=72 + S)
+    rp, ci = _csr_dev(fa, S, sink, window)
+    wd = torch.tensor([w0, 1.0 - w0], dtype=torch.float32, device=DEV)
+    o = torch.empty((B, S, Hq, d), dtype=out_dtype, device=DEV)
+    fa.flux_attn_prefill_soft(qd, kd, vd, o, wd, sink_tokens=sink, window_tokens=window, blk_row_ptr=rp,
+                              blk_col_idx=ci)
+    torch.cuda.synchronize()
+    ref = oracle.attention_soft(q, k, v, default_scale(d), (w0, 1.0 - w0), block=64, sink_tokens=sink,
+                                window_tokens=window)
+    check_close(o.float().cpu().numpy(), ref, "soft prefill", out_bf16=out_dtype == torch.bfloat16)
+
+
+def test_soft_prefill_router_pipeline_s8192_sampled(fa):
+    """Router logits -> Gumbel-softmax weights -> soft-routed layer at the Llama layer shape."""
+    B, S, Hq, Hkv, d = 1, 8192, 32, 8, 128
+    say("soft prefill S=8192")
+    qd = synth.torch_normal((B, S, Hq, d), 1040, torch.bfloat16)
+    kd = synth.torch_normal((B, S, Hkv, d), 1041, torch.bfloat16)
+    vd = synth.torch_normal((B, S, Hkv, d), 1042, torch.bfloat16)
+    w = synth.router_weights(1, Hq * d, 64, seed=1043)
+    w_enc, b_enc, w_head, b_head = (torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in w)
+    logits = torch.empty((1, 2), dtype=torch.float32, device=DEV)
+    modes = torch.empty(1, dtype=torch.int32, device=DEV)
+    fa.flux_route_layers([qd[0]], w_enc, b_enc, w_head, b_head, modes, logits, pool_tokens=100)
+    u = torch.tensor([[0.3, 0.6]], dtype=torch.float32, device=DEV)
+    weights = torch.empty((1, 2), dtype=torch.float32, device=DEV)
+    fa.flux_route_soft_weights(logits, u, 0.5, weights)
+    rp, ci = _csr_dev(fa, S, 128, 2048)
+    o = torch.empty((B, S, Hq, d), dtype=torch.float32, device=DEV)
+    fa.flux_attn_prefill_soft(qd, kd, vd, o, weights[0], blk_row_ptr=rp, blk_col_idx=ci)
+    torch.cuda.synchronize()
+    ref_w = oracle.soft_weights(logits.cpu().numpy().astype(np.float64), u.cpu().numpy().astype(np.float64), 0.5)
+    assert np.abs(weights.cpu().numpy() - ref_w).max() < 2e-5
+    rows = sample_rows(B, Hq, S, 100, seed=1044)
+    ref = oracle.attention_soft(dev_bits_to_host(qd), dev_bits_to_host(kd), dev_bits_to_host(vd), default_scale(d),
+                                ref_w[0], block=64, sink_tokens=128, window_tokens=2048, rows=rows)
+    o_h = o.cpu().numpy()
+    check_close(np.stack([o_h[b, i, h] for b, h, i in rows]), ref, "soft prefill S=8192")
