@@ -36,6 +36,9 @@ def _load():
     lib.oracle_attention_rows.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, i32, dbl, i32, i32, i32,
                                           i32, i32, vp, i64, i32, vp, vp]
     lib.oracle_attention_rows.restype = i32
+    lib.oracle_attention_backward.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, dbl, i32, i32, i32, i32,
+                                              i32, i32, vp, vp, vp]
+    lib.oracle_attention_backward.restype = i32
     lib.oracle_soft_weights.argtypes = [vp, vp, dbl, i32, vp]
     lib.oracle_soft_weights.restype = i32
     lib.oracle_mix.argtypes = [vp, vp, dbl, dbl, i64, vp]
@@ -189,3 +192,22 @@ def attention_soft(q, k, v, scale, weights, block=64, sink_tokens=0, window_toke
     out = np.empty_like(o_full)
     _load().oracle_mix(_ptr(o_full), _ptr(o_sparse), float(weights[0]), float(weights[1]), o_full.size, _ptr(out))
     return out
+
+
+def attention_backward(q, k, v, d_o, scale, causal=True, sparse=False, block=64, sink_tokens=0, window_tokens=0,
+                       n_threads=0):
+    """Gradients (dq [B,S,Hq,d], dk, dv [B,S,Hkv,d], float64) of O = attention(q, k, v) for output gradient d_o."""
+    q, k, v, d_o = (np.ascontiguousarray(x) for x in (q, k, v, d_o))
+    kind = _kind_of(q)
+    assert _kind_of(k) == kind and _kind_of(v) == kind and _kind_of(d_o) == kind
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    dq = np.empty((B, S, Hq, d), np.float64)
+    dk = np.empty((B, S, Hkv, d), np.float64)
+    dv = np.empty((B, S, Hkv, d), np.float64)
+    rc = _load().oracle_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(d_o), kind, B, S, Hq, Hkv, d, float(scale),
+                                           int(causal), int(sparse), int(block), int(sink_tokens), int(window_tokens),
+                                           int(n_threads), _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError(f"oracle_attention_backward failed ({rc})")
+    return dq, dk, dv

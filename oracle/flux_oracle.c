@@ -26,6 +26,12 @@
  *     last P tokens, an MLP context encoder, a two-logit router head and an
  *     argmax (ties to index 0 = full attention), from the router paragraphs of
  *     the Flux Attention page.
+ *   - the backward pass (gradients of the attention output with respect to Q,
+ *     K and V for a given output gradient dO), from the chain rule through the
+ *     same definition: dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P * dP)),
+ *     dQ = scale dS K, dK = scale dS^T Q -- the softmax Jacobian
+ *     diag(p) - p p^T applied row by row.  Needed to train the router over a
+ *     frozen backbone (Flux Attention page, router and architecture paragraphs).
  *   - soft routing (the training-time relaxation in the same router paragraph):
  *     r = softmax((pi + g) / tau) over (pi_FA, pi_SA) with Gumbel noise
  *     g = -ln(-ln u) drawn from uniforms u in (0, 1), and the layer output
@@ -359,4 +365,88 @@ int oracle_soft_weights(const double* logits, const double* uniforms, double tau
 /* out[i] = w0 * o_full[i] + w1 * o_sparse[i]: the soft-routed layer output (same page). */
 void oracle_mix(const double* o_full, const double* o_sparse, double w0, double w1, int64_t n, double* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = w0 * o_full[i] + w1 * o_sparse[i];
+}
+
+/*
+ * Backward pass.  q, d_o [B, S, Hq, d]; k, v [B, S, Hkv, d] (same element kind);
+ * outputs dq [B, S, Hq, d], dk, dv [B, S, Hkv, d] in double.  For each (b, h, i):
+ * the row's probabilities p_j (two-pass softmax over the allowed keys, as in
+ * attend_row), dp_j = <dO_i, v_j>, D = sum_j p_j dp_j, ds_j = p_j (dp_j - D);
+ * dq_i = scale sum_j ds_j k_j, dk_j += scale ds_j q_i, dv_j += p_j dO_i.  The
+ * query heads sharing a KV head accumulate into its dk/dv.  Parallel over
+ * (batch, kv head), so no two threads write the same dk/dv row.
+ */
+int oracle_attention_backward(const void* q, const void* k, const void* v, const void* d_o, int kind,
+                              int64_t batch, int64_t seq, int hq, int hkv, int d, double scale, int causal,
+                              int sparse, int block, int sink_tokens, int window_tokens, int n_threads,
+                              double* dq, double* dk, double* dv) {
+    if (check_shapes(batch, seq, hq, hkv, d)) return 1;
+    if (sparse && (!causal || block <= 0)) return 1;
+    const int G = hq / hkv;
+    const int64_t q_stride = (int64_t)hq * d, kv_stride = (int64_t)hkv * d;
+    memset(dk, 0, sizeof(double) * (size_t)(batch * seq * kv_stride));
+    memset(dv, 0, sizeof(double) * (size_t)(batch * seq * kv_stride));
+    const int64_t units = batch * hkv;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel
+#endif
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)seq);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)seq);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic)
+#endif
+        for (int64_t u = 0; u < units; ++u) {
+            const int64_t b = u / hkv;
+            const int g = (int)(u % hkv);
+            const int64_t kv_base = b * seq * kv_stride + (int64_t)g * d;
+            for (int hh = 0; hh < G; ++hh) {
+                const int h = g * G + hh;
+                for (int64_t i = 0; i < seq; ++i) {
+                    const int64_t q_off = (b * seq + i) * q_stride + (int64_t)h * d;
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < seq; ++j) {
+                        if (!key_allowed(i, j, seq, causal, sparse, block, sink_tokens, window_tokens)) continue;
+                        double s = 0.0;
+                        for (int t = 0; t < d; ++t)
+                            s += load_elem(q, kind, q_off + t) * load_elem(k, kind, kv_base + j * kv_stride + t);
+                        p[j] = s * scale;
+                        if (p[j] > m) m = p[j];
+                    }
+                    double l = 0.0;
+                    for (int64_t j = 0; j < seq; ++j) {
+                        if (!key_allowed(i, j, seq, causal, sparse, block, sink_tokens, window_tokens)) continue;
+                        p[j] = exp(p[j] - m);
+                        l += p[j];
+                    }
+                    double D = 0.0;
+                    for (int64_t j = 0; j < seq; ++j) {
+                        if (!key_allowed(i, j, seq, causal, sparse, block, sink_tokens, window_tokens)) continue;
+                        p[j] /= l;
+                        double a = 0.0;
+                        for (int t = 0; t < d; ++t)
+                            a += load_elem(d_o, kind, q_off + t) * load_elem(v, kind, kv_base + j * kv_stride + t);
+                        dp[j] = a;
+                        D += p[j] * a;
+                    }
+                    double* dq_row = dq + q_off;
+                    for (int t = 0; t < d; ++t) dq_row[t] = 0.0;
+                    for (int64_t j = 0; j < seq; ++j) {
+                        if (!key_allowed(i, j, seq, causal, sparse, block, sink_tokens, window_tokens)) continue;
+                        const double ds = p[j] * (dp[j] - D);
+                        const int64_t kv_off = kv_base + j * kv_stride;
+                        for (int t = 0; t < d; ++t) {
+                            dq_row[t] += scale * ds * load_elem(k, kind, kv_off + t);
+                            dk[kv_off + t] += scale * ds * load_elem(q, kind, q_off + t);
+                            dv[kv_off + t] += p[j] * load_elem(d_o, kind, q_off + t);
+                        }
+                    }
+                }
+            }
+        }
+        free(p);
+        free(dp);
+    }
+    return 0;
 }
