@@ -206,6 +206,45 @@ int flux_attn_prefill_soft(const void* q, const void* k, const void* v, void* o,
                            const float* weights_device, void* workspace, size_t workspace_bytes,
                            void* hip_stream);
 
+/* flux_attn_backward_workspace_size -- bytes flux_attn_backward needs for these sizes (0 if invalid):
+ * per-row statistics (fp32 [batch, hq, ceil(seq/64)*64, 2]), two counters and, when hq > hkv, two
+ * fp32 [batch, seq, hq, head_dim] per-query-head dK/dV buffers. */
+size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq, int32_t hkv,
+                                         int32_t head_dim);
+
+/*
+ * flux_attn_backward -- gradients of one layer of attention with respect to Q, K and V.
+ *
+ * For O = softmax(scale Q K^T + mask) V (the forward of flux_attn_prefill, same mask arguments)
+ * and an output gradient dO, per (batch, query head), with P the row probabilities:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O),
+ *   dQ = scale dS K,  dK = scale dS^T Q
+ * (chain rule through the softmax of the [NL] attention definition; the gradients the [FA]
+ * router training over a frozen backbone needs).  P is rebuilt tile by tile from Q, K and the
+ * forward pass's lse; inactive blocks of the sparse pattern are skipped and never read.  With
+ * grouped-query attention the query heads sharing a KV head add into its dK/dV (head order).
+ *   q, d_o    [batch, seq, hq,  head_dim]  device bf16 (d_o: dL/dO)
+ *   o         [batch, seq, hq,  head_dim]  device, o_dtype BF16 or F32: the forward output (only
+ *                                          D = rowsum(dO * O) reads it; an fp32 O keeps D exact
+ *                                          to fp32, a bf16 O perturbs D by its rounding)
+ *   k, v      [batch, seq, hkv, head_dim]  device bf16
+ *   lse       [batch, hq, seq]             device fp32, as written by flux_attn_prefill
+ *   dq        [batch, seq, hq,  head_dim]  device fp32 (written)
+ *   dk, dv    [batch, seq, hkv, head_dim]  device fp32 (written, not accumulated into)
+ * mode, causal, block, sink_tokens, window_tokens: as for flux_attn_prefill; the sparse key set
+ * is derived from (block, sink_tokens, window_tokens), the pattern flux_build_block_mask builds.
+ * workspace: device, >= flux_attn_backward_workspace_size(...) bytes, 16-byte aligned; its
+ * contents on entry do not matter.  Deterministic: no atomics on gradients, fixed summation order.
+ * P and dS enter the matrix products as bf16 (fp32 accumulation), as the forward's P does.
+ * Supported: in_dtype BF16, head_dim 128, block 64.
+ */
+int flux_attn_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                       const float* lse, float* dq, float* dk, float* dv, int32_t in_dtype,
+                       int32_t o_dtype, int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                       float scale, int32_t causal, int32_t mode, int32_t block,
+                       int32_t sink_tokens, int32_t window_tokens, void* workspace,
+                       size_t workspace_bytes, void* hip_stream);
+
 /*
  * flux_decode_workspace_size -- bytes of workspace flux_attn_decode needs.
  * Same meaning of arguments as flux_attn_decode (num_splits = 0: automatic;

@@ -20,7 +20,8 @@ __all__ = [
     "flux_build_block_mask", "flux_attn_prefill", "flux_attn_prefill_layers", "flux_attn_prefill_layers_routed",
     "flux_decode_workspace_size", "flux_attn_decode", "flux_window_cache_rows", "flux_decode_step",
     "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers", "flux_route_soft_weights",
-    "flux_prefill_soft_workspace_size", "flux_attn_prefill_soft",
+    "flux_prefill_soft_workspace_size", "flux_attn_prefill_soft", "flux_attn_backward_workspace_size",
+    "flux_attn_backward",
     "FLUX_OK", "FLUX_ERR_INVALID_ARG", "FLUX_ERR_UNSUPPORTED", "FLUX_ERR_CAPACITY", "FLUX_ERR_WORKSPACE",
     "FLUX_ERR_HIP", "FLUX_DTYPE_BF16", "FLUX_DTYPE_F32", "FLUX_MODE_DENSE", "FLUX_MODE_SPARSE", "FLUX_KV_FULL",
     "FLUX_KV_WINDOW",
@@ -37,7 +38,8 @@ EXPORTED_SYMBOLS = (
     "flux_attn_prefill", "flux_attn_prefill_layers", "flux_attn_prefill_layers_routed",
     "flux_decode_workspace_size", "flux_attn_decode", "flux_window_cache_rows", "flux_decode_step",
     "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers", "flux_route_soft_weights",
-    "flux_prefill_soft_workspace_size", "flux_attn_prefill_soft",
+    "flux_prefill_soft_workspace_size", "flux_attn_prefill_soft", "flux_attn_backward_workspace_size",
+    "flux_attn_backward",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -90,6 +92,11 @@ _lib.flux_prefill_soft_workspace_size.restype = _sz
 _lib.flux_attn_prefill_soft.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _i32,
                                         _i32, _vp, _vp, _i64, _vp, _vp, _sz, _vp]
 _lib.flux_attn_prefill_soft.restype = ctypes.c_int
+_lib.flux_attn_backward_workspace_size.argtypes = [_i64, _i64, _i32, _i32, _i32]
+_lib.flux_attn_backward_workspace_size.restype = _sz
+_lib.flux_attn_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32,
+                                    _f32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+_lib.flux_attn_backward.restype = ctypes.c_int
 _lib.flux_route_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.flux_route_workspace_size.restype = _sz
 _lib.flux_route_layers.argtypes = [_pp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
@@ -357,3 +364,27 @@ def flux_attn_prefill_soft(q, k, v, o, weights_dev, *, block: int = 64, sink_tok
                                        _ptr(blk_col_idx), nnz, _ptr(weights_dev), _ptr(workspace), ws_bytes,
                                        _stream(stream)),
            "flux_attn_prefill_soft")
+
+
+def flux_attn_backward_workspace_size(batch, seq, hq, hkv, head_dim) -> int:
+    return int(_lib.flux_attn_backward_workspace_size(batch, seq, hq, hkv, head_dim))
+
+
+def flux_attn_backward(q, k, v, o, d_o, lse, dq, dk, dv, *, causal: bool = True, mode: int = FLUX_MODE_DENSE,
+                       block: int = 64, sink_tokens: int = 0, window_tokens: int = 0, scale: float | None = None,
+                       workspace=None, stream=None):
+    """Gradients dq, dk, dv (fp32, written) of attention for output gradient d_o; lse from the forward pass."""
+    _contig(q, k, v, o, d_o, lse, dq, dk, dv)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(flux_attn_backward_workspace_size(B, S, Hq, Hkv, d), 1), dtype=torch.uint8,
+                                device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.flux_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), _dtype_code(q), _dtype_code(o), B, S, Hq, Hkv, d, scale, int(causal), mode, block,
+                                   sink_tokens, window_tokens, _ptr(workspace), ws_bytes, _stream(stream)),
+           "flux_attn_backward")

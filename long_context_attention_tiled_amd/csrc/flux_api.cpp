@@ -477,6 +477,107 @@ int flux_attn_prefill_soft(const void* q, const void* k, const void* v, void* o,
     return launch_prefill(sparse, in_dtype, as_stream(hip_stream));
 }
 
+// ---------------------------------------------------------------- backward
+namespace {
+
+struct BackwardLayout {
+    size_t stat, counters, part, total;   // byte offsets inside the workspace, and its size
+};
+
+BackwardLayout backward_layout(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim) {
+    BackwardLayout w;
+    const int64_t nqb = ceil_div(seq, 64);
+    w.stat = 0;
+    w.counters = align256((size_t)batch * hq * nqb * 128 * sizeof(float));
+    w.part = w.counters + 256;
+    const size_t part_bytes = hq != hkv ? (size_t)batch * seq * hq * head_dim * sizeof(float) : 0;
+    w.total = w.part + 2 * align256(part_bytes);
+    return w;
+}
+
+}  // namespace
+
+size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim) {
+    if (batch < 1 || seq < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || head_dim < 1) return 0;
+    return backward_layout(batch, seq, hq, hkv, head_dim).total;
+}
+
+int flux_attn_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+                       float* dq, float* dk, float* dv, int32_t in_dtype, int32_t o_dtype, int64_t batch,
+                       int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim, float scale, int32_t causal,
+                       int32_t mode, int32_t block, int32_t sink_tokens, int32_t window_tokens, void* workspace,
+                       size_t workspace_bytes, void* hip_stream) {
+    if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv)
+        return fail(FLUX_ERR_INVALID_ARG, "q, k, v, o, d_o, lse, dq, dk and dv must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv))
+        return fail(FLUX_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FLUX_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (batch < 1 || seq < 1) return fail(FLUX_ERR_INVALID_ARG, "batch and seq must be >= 1");
+    if (hq < 1 || hkv < 1 || hq % hkv != 0)
+        return fail(FLUX_ERR_INVALID_ARG, "hq (%d) must be a positive multiple of hkv (%d)", hq, hkv);
+    if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(FLUX_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (in_dtype != FLUX_DTYPE_BF16 && in_dtype != FLUX_DTYPE_F32)
+        return fail(FLUX_ERR_INVALID_ARG, "in_dtype must be FLUX_DTYPE_BF16 or FLUX_DTYPE_F32");
+    if (o_dtype != FLUX_DTYPE_BF16 && o_dtype != FLUX_DTYPE_F32)
+        return fail(FLUX_ERR_INVALID_ARG, "o_dtype must be FLUX_DTYPE_BF16 or FLUX_DTYPE_F32");
+    MaskSpec ms;
+    int st = check_mask_spec(seq, seq, block, sink_tokens, window_tokens, causal, mode, &ms);
+    if (st != FLUX_OK) return st;
+    if (in_dtype != FLUX_DTYPE_BF16) return fail(FLUX_ERR_UNSUPPORTED, "the backward pass takes bfloat16 inputs");
+    if (head_dim != 128) return fail(FLUX_ERR_UNSUPPORTED, "head_dim %d not supported by the backward pass (128)",
+                                     head_dim);
+    if (block != flux::kBlock) return fail(FLUX_ERR_UNSUPPORTED, "block %d not supported (64)", block);
+    if (batch * (int64_t)hq * ceil_div(seq, 64) * 64 > INT32_MAX)
+        return fail(FLUX_ERR_UNSUPPORTED, "batch * hq * seq exceeds the work-unit range");
+    if (seq * (int64_t)std::max(hq, hkv) * head_dim > INT32_MAX)
+        return fail(FLUX_ERR_UNSUPPORTED, "seq * max(hq, hkv) * head_dim must stay below 2^31 elements");
+    const BackwardLayout w = backward_layout(batch, seq, hq, hkv, head_dim);
+    if (!workspace || workspace_bytes < w.total)
+        return fail(FLUX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(FLUX_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (dk == dv || dq == dk || dq == dv) return fail(FLUX_ERR_INVALID_ARG, "dq, dk and dv must be distinct");
+    flux::BackwardArgs a;
+    char* ws = reinterpret_cast<char*>(workspace);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.d_o = d_o;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.stat = reinterpret_cast<float*>(ws + w.stat);
+    a.counters = reinterpret_cast<int*>(ws + w.counters);
+    if (hq != hkv) {
+        const size_t pb = align256((size_t)batch * seq * hq * head_dim * sizeof(float));
+        a.dk_part = reinterpret_cast<float*>(ws + w.part);
+        a.dv_part = reinterpret_cast<float*>(ws + w.part + pb);
+    } else {
+        a.dk_part = nullptr;
+        a.dv_part = nullptr;
+    }
+    a.batch = batch;
+    a.seq = seq;
+    a.hq = hq;
+    a.hkv = hkv;
+    a.head_dim = head_dim;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.causal = causal;
+    a.sparse = ms.sparse ? 1 : 0;
+    a.sink_blocks = (int)ms.sink_blocks;
+    a.window_blocks = (int)ms.window_blocks;
+    a.n_qblk = (int)ceil_div(seq, 64);
+    a.num_cu = device_cu_count();
+    a.o_f32 = o_dtype == FLUX_DTYPE_F32;
+    hipError_t e = flux::launch_backward(a, as_stream(hip_stream));
+    if (e == hipSuccess) e = hipGetLastError();
+    return hip_status(e, "backward launch");
+}
+
 int flux_route_soft_weights(const float* logits, const float* uniforms, float tau, int32_t n_layers,
                             float* weights_out, void* hip_stream) {
     if (!logits || !uniforms || !weights_out) return fail(FLUX_ERR_INVALID_ARG, "pointers must be non-NULL");

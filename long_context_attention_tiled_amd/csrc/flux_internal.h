@@ -89,11 +89,42 @@ struct RouteArgs {
     float* z;              // workspace [L_total, hidden]
 };
 
+struct BackwardArgs {
+    const void* q;         // [B, S, Hq, d] bf16
+    const void* k;         // [B, S, Hkv, d] bf16
+    const void* v;
+    const void* o;         // [B, S, Hq, d] forward output, bf16 or fp32 (o_f32)
+    const void* d_o;       // [B, S, Hq, d] bf16 output gradient
+    const float* lse;      // [B, Hq, S] natural-log row sum-exp of the scaled scores
+    float* dq;             // [B, S, Hq, d]
+    float* dk;             // [B, S, Hkv, d]
+    float* dv;
+    float* dk_part;        // workspace [B, S, Hq, d]: per-query-head dK when hq > hkv, else nullptr
+    float* dv_part;
+    float* stat;           // workspace [B, Hq, n_qblk, 2, 64]: -lse*log2(e), then rowsum(dO * O)
+    int* counters;         // workspace [2]: work-queue heads of the dK/dV and dQ kernels
+    int64_t batch;
+    int64_t seq;
+    int hq;
+    int hkv;
+    int head_dim;
+    float scale;
+    float scale_log2;
+    int causal;
+    int sparse;
+    int sink_blocks;
+    int window_blocks;
+    int n_qblk;            // ceil(seq / 64)
+    int num_cu;            // persistent grid size
+    int o_f32;
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_route_soft(const float* logits, const float* uniforms, float tau, int n_layers, float* weights,
                              hipStream_t s);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 
 }  // namespace flux

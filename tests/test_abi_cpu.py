@@ -261,6 +261,54 @@ def test_soft_routing_validation(fa):
     assert soft(ws=FAKE + 4100) == E                       # misaligned workspace
 
 
+def test_backward_workspace_size(fa):
+    align = lambda x: (x + 255) // 256 * 256
+    B, S, Hq, Hkv, d = 2, 1000, 8, 2, 128
+    nqb = (S + 63) // 64
+    stat = align(B * Hq * nqb * 128 * 4)
+    part = align(B * S * Hq * d * 4)
+    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d) == stat + 256 + 2 * part
+    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hq, d) == stat + 256          # no per-head buffers
+    assert fa.flux_attn_backward_workspace_size(B, S, Hq, 3, d) == 0                    # hq % hkv
+    assert fa.flux_attn_backward_workspace_size(0, S, Hq, Hkv, d) == 0
+
+
+def test_backward_validation(fa):
+    E, U = fa.FLUX_ERR_INVALID_ARG, fa.FLUX_ERR_UNSUPPORTED
+    lib = fa.lib()
+
+    def bwd(**kw):
+        a = dict(q=FAKE, lse=FAKE, dq=FAKE + 4096, dk=FAKE + 8192, dv=FAKE + 12288, in_dtype=0, o_dtype=0, seq=512, hq=4, hkv=2,
+                 d=128, scale=0.088, causal=1, mode=0, block=64, sink=128, window=128, ws=FAKE + 16384,
+                 ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.flux_attn_backward(a["q"], FAKE, FAKE, FAKE, FAKE, a["lse"], a["dq"], a["dk"], a["dv"],
+                                      a["in_dtype"], a["o_dtype"], 1, a["seq"], a["hq"], a["hkv"], a["d"], a["scale"], a["causal"],
+                                      a["mode"], a["block"], a["sink"], a["window"], a["ws"], a["ws_bytes"], None)
+    assert bwd(q=None) == E
+    assert bwd(lse=None) == E
+    assert bwd(dq=FAKE + 4100) == E                        # misaligned
+    assert bwd(lse=FAKE + 2) == E
+    assert bwd(seq=0) == E
+    assert bwd(hkv=3) == E
+    assert bwd(scale=0.0) == E
+    assert bwd(scale=float("inf")) == E
+    assert bwd(in_dtype=7) == E
+    assert bwd(causal=2) == E
+    assert bwd(mode=1, causal=0) == E                      # sparse needs causal
+    assert bwd(mode=1, sink=100) == E
+    assert bwd(mode=1, window=0) == E
+    assert bwd(o_dtype=2) == E
+    assert bwd(in_dtype=1) == U
+    assert bwd(d=64) == U
+    assert bwd(block=32) == U
+    assert bwd(ws_bytes=100) == fa.FLUX_ERR_WORKSPACE
+    assert bwd(ws=None) == fa.FLUX_ERR_WORKSPACE
+    assert bwd(ws=FAKE + 16388) == E                       # misaligned workspace
+    assert bwd(dk=FAKE + 4096) == E                        # dq aliases dk
+    assert "distinct" in fa.last_error_detail()
+
+
 # ---------------------------------------------------------------- decode validation / workspace
 def test_decode_workspace_size(fa):
     B, Hq, Hkv, L, d = 8, 32, 8, 262144, 128

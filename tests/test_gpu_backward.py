@@ -1,0 +1,191 @@
+"""GPU parity of the attention backward (dQ, dK, dV) vs the fp64 oracle.
+
+Every call goes through the C ABI (flux_attn_backward) via the thin binding.  Inputs: seeded iid
+N(0,1) Q, K, V and output gradient dO, rounded to bf16; the oracle reads the same bits.  The
+forward output O and row LSE handed to the backward come from the oracle's forward (fp64, rounded
+to fp32) unless a test says otherwise.  Bar: max-abs <= 1e-2 and mean-abs <= 1e-3 on the fp32
+gradients.  A bf16 O (one test) perturbs D = rowsum(dO * O) by its own rounding, which the kernel
+cannot undo; that case is held to max-abs 2e-2.  At the full layer shape (seq 8192, 32/8 heads) the
+oracle cannot run whole: there dQ rows of a causal prefix are compared (rows < T depend only on
+keys < T), and dK, dV are checked against identities that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu_helpers import check_close, default_scale, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+D = 128
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import long_context_attention_tiled_amd as fa
+    assert torch.cuda.is_available()
+    return fa
+
+
+def _inputs(B, S, Hq, Hkv, seed):
+    q, k, v = synth.qkv_bf16(B, S, Hq, Hkv, D, seed)
+    g = synth.normal_bf16_bits((B, S, Hq, D), seed, tensor_id=7)
+    return q, k, v, g
+
+
+def _oracle_forward(q, k, v, scale, causal, sparse, sink, window):
+    out, lse = oracle.attention(q, k, v, scale, causal=causal, sparse=sparse, block=64, sink_tokens=sink,
+                                window_tokens=window)
+    return out.astype(np.float32), np.ascontiguousarray(np.transpose(lse, (0, 2, 1))).astype(np.float32)
+
+
+def _gpu_forward(fa, qd, kd, vd, causal, mode, sink, window, o_dtype=torch.float32):
+    B, S, Hq, _ = qd.shape
+    o = torch.empty((B, S, Hq, D), dtype=o_dtype, device=DEV)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    rp = ci = None
+    if mode == fa.FLUX_MODE_SPARSE:
+        rp, ci = fa.flux_build_block_mask(S, S, 64, sink, window, 1, fa.FLUX_MODE_SPARSE)
+        rp, ci = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    fa.flux_attn_prefill(qd, kd, vd, o, lse, causal=int(causal), mode=mode, block=64, sink_tokens=sink,
+                         window_tokens=window, blk_row_ptr=rp, blk_col_idx=ci)
+    return o, lse
+
+
+def _backward(fa, qd, kd, vd, od, gd, lsed, causal, mode, sink, window):
+    B, S, Hq, _ = qd.shape
+    Hkv = kd.shape[2]
+    dq = torch.empty((B, S, Hq, D), dtype=torch.float32, device=DEV)
+    dk = torch.empty((B, S, Hkv, D), dtype=torch.float32, device=DEV)
+    dv = torch.empty((B, S, Hkv, D), dtype=torch.float32, device=DEV)
+    fa.flux_attn_backward(qd, kd, vd, od, gd, lsed, dq, dk, dv, causal=causal, mode=mode, block=64,
+                          sink_tokens=sink, window_tokens=window)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _run_case(fa, B, S, Hq, Hkv, seed, causal=True, mode=0, sink=0, window=0, gpu_forward=False, o_bf16=False,
+              max_abs=None):
+    say("backward", f"B={B} S={S} Hq={Hq} Hkv={Hkv} seed={seed} causal={causal} mode={mode} sink={sink} "
+        f"window={window} gpu_forward={gpu_forward} o_bf16={o_bf16}")
+    scale = default_scale(D)
+    sparse = mode == 1
+    q, k, v, g = _inputs(B, S, Hq, Hkv, seed)
+    qd, kd, vd, gd = (synth.torch_bf16_from_bits(x) for x in (q, k, v, g))
+    if gpu_forward:
+        od, lsed = _gpu_forward(fa, qd, kd, vd, causal, mode, sink, window,
+                                torch.bfloat16 if o_bf16 else torch.float32)
+    else:
+        o32, lse = _oracle_forward(q, k, v, scale, causal, sparse, sink, window)
+        od = synth.torch_bf16_from_bits(synth.f32_to_bf16_bits(o32)) if o_bf16 else torch.from_numpy(o32).to(DEV)
+        lsed = torch.from_numpy(lse).to(DEV)
+    dq, dk, dv = _backward(fa, qd, kd, vd, od, gd, lsed, causal, mode, sink, window)
+    rq, rk, rv = oracle.attention_backward(q, k, v, g, scale, causal=causal, sparse=sparse, block=64,
+                                           sink_tokens=sink, window_tokens=window)
+    tag = f"S={S} Hq={Hq} Hkv={Hkv} mode={mode}"
+    errs = [_close(t.cpu().numpy(), r, f"{name} {tag}", max_abs)
+            for name, t, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv))]
+    say("max/mean abs err", " ".join(f"{e[0]:.2e}/{e[1]:.1e}" for e in errs))
+
+
+def _close(gpu, ref, what, max_abs):
+    if max_abs is None:
+        return check_close(gpu, ref, what)
+    err = np.abs(np.asarray(gpu, np.float64) - ref)
+    assert np.all(np.isfinite(gpu)), what
+    assert err.max() <= max_abs, f"{what}: max-abs {err.max():.3e}"
+    assert err.mean() <= 1e-3, f"{what}: mean-abs {err.mean():.3e}"
+    return float(err.max()), float(err.mean())
+
+
+# ------------------------------------------------------------- dense
+@pytest.mark.parametrize("S", [1, 64, 65, 328])
+def test_dense_causal_mha(fa, S):
+    """Several key pairs and query pairs, a ragged last tile, and the one-row / one-tile edges."""
+    _run_case(fa, 1, S, 2, 2, seed=4101 + S)
+
+
+def test_dense_causal_gqa(fa):
+    """Grouped-query attention (4 query heads on 2 KV heads): per-head dK/dV summed in head order."""
+    _run_case(fa, 2, 256, 4, 2, seed=4201)
+
+
+def test_dense_noncausal(fa):
+    """All keys visible; the ragged last key tile is masked by position."""
+    _run_case(fa, 1, 200, 2, 1, causal=False, seed=4301)
+
+
+def test_dense_causal_longer(fa):
+    _run_case(fa, 1, 1100, 2, 1, seed=4401)
+
+
+# ------------------------------------------------------------- block-sparse
+def test_sparse_sink_window(fa):
+    """Sink 2 blocks, window 4 blocks over 16 query blocks: most blocks skipped, ragged end."""
+    _run_case(fa, 1, 1000, 2, 1, mode=1, sink=128, window=256, seed=4501)
+
+
+def test_sparse_odd_sink(fa):
+    """One sink block: the first key pair straddles the sink boundary."""
+    _run_case(fa, 1, 700, 2, 2, mode=1, sink=64, window=128, seed=4601)
+
+
+def test_sparse_no_sink_min_window(fa):
+    """No sink and a one-block window: only the diagonal blocks are visible."""
+    _run_case(fa, 1, 450, 2, 1, mode=1, sink=0, window=64, seed=4701)
+
+
+def test_bf16_output_input(fa):
+    """O handed over in bf16: D carries O's rounding (up to 2^-9 relative per element)."""
+    _run_case(fa, 1, 328, 2, 2, seed=4429, o_bf16=True, max_abs=2e-2)
+
+
+# ------------------------------------------------------------- end to end with the GPU forward
+@pytest.mark.parametrize("mode", [0, 1])
+def test_after_gpu_forward(fa, mode):
+    """O (fp32) and LSE from flux_attn_prefill, then the backward."""
+    _run_case(fa, 1, 512, 4, 1, mode=mode, sink=128, window=128, seed=4801 + mode, gpu_forward=True)
+
+
+# ------------------------------------------------------------- full layer shape
+@pytest.mark.parametrize("mode", [0, 1])
+def test_full_shape_prefix_and_identities(fa, mode):
+    """seq 8192, 32 query heads on 8 KV heads (the layer shape of the prefill workload).
+    dQ of the first T rows equals the backward of the length-T prefix (causal); dK, dV are checked
+    against sum_j dV_j = sum over the group's heads of sum_i dO_i (rows of P sum to one) and
+    sum_j dK_j = 0 (rows of dS sum to zero); a second run must be bit-identical."""
+    B, S, Hq, Hkv, T = 1, 8192, 32, 8, 384
+    sink, window = (128, 2048) if mode == 1 else (0, 0)
+    say("backward full shape", f"mode={mode}")
+    scale = default_scale(D)
+    q, k, v, g = _inputs(B, S, Hq, Hkv, seed=4901 + mode)
+    qd, kd, vd, gd = (synth.torch_bf16_from_bits(x) for x in (q, k, v, g))
+    od, lsed = _gpu_forward(fa, qd, kd, vd, True, mode, sink, window)
+    dq, dk, dv = _backward(fa, qd, kd, vd, od, gd, lsed, True, mode, sink, window)
+    dq2, dk2, dv2 = _backward(fa, qd, kd, vd, od, gd, lsed, True, mode, sink, window)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2), "not deterministic"
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+
+    # prefix rows of dQ
+    pq, pk, pv, pg = (np.ascontiguousarray(x[:, :T]) for x in (q, k, v, g))
+    rq, _, _ = oracle.attention_backward(pq, pk, pv, pg, scale, causal=True, sparse=bool(mode), block=64,
+                                         sink_tokens=sink, window_tokens=window)
+    check_close(dq[:, :T].cpu().numpy(), rq, f"dq prefix mode {mode}")
+
+    # identities over keys, per (batch, kv head, d)
+    G = Hq // Hkv
+    g64 = synth.bf16_bits_to_f32(g).astype(np.float64)                    # [B, S, Hq, d]
+    want_dv = g64.sum(axis=1).reshape(B, Hkv, G, D).sum(axis=2)         # [B, Hkv, d]
+    got_dv = dv.double().sum(dim=1).cpu().numpy()
+    got_dk = dk.double().sum(dim=1).cpu().numpy()
+    mag_v = float(np.abs(dv.cpu().numpy()).sum(axis=1).max())
+    mag_k = float(np.abs(dk.cpu().numpy()).sum(axis=1).max())
+    err_v = float(np.abs(got_dv - want_dv).max())
+    err_k = float(np.abs(got_dk).max())
+    say("identities", f"sum dV err {err_v:.3e} (scale {mag_v:.1f}), sum dK {err_k:.3e} (scale {mag_k:.1f})")
+    assert err_v <= 2e-3 * mag_v, err_v
+    assert err_k <= 2e-3 * mag_k, err_k
