@@ -14,7 +14,9 @@ whole step.
 
 Secondary legs (same JSON line, "legs"): block-sparse prefill at seq 65536,
 GQA decode over a 262144-token bf16 cache (dense and sparse; HBM GB/s and
-tok/s), and with --stack the 36-layer routed prefill stack at seq 131072.
+tok/s), the routed decode loop, soft-routed prefill, the attention backward
+(seq 8192 dense, seq 65536 sparse), and with --stack the 36-layer routed
+prefill stack at seq 131072.
 
 The roofline object is for the dominant kernel (dense prefill), timed with HIP
 events on the stream the kernel runs on.  cpu_baseline times the fp64 CPU
@@ -122,8 +124,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="sparse,decode,decode_loop,soft,peaks",
-                    help="comma list of secondary legs: sparse, dense64k, decode, decode_loop, soft, stack, peaks "
+    ap.add_argument("--legs", default="sparse,decode,decode_loop,soft,backward,peaks",
+                    help="comma list of secondary legs: sparse, dense64k, decode, decode_loop, soft, backward, stack, "
+                         "peaks "
                          "(or 'none')")
     ap.add_argument("--no-legs", dest="legs", action="store_const", const="none")
     ap.add_argument("--no-headline", dest="headline", action="store_false", default=True,
@@ -308,6 +311,8 @@ def run_legs(fa, synth, torch, dev, sel, reps):
         legs["stack_s131072"] = run_stack(fa, synth, torch, dev)
     if "soft" in sel:
         legs["soft_routed_prefill_s8192"] = run_soft(fa, synth, torch, dev, reps)
+    if "backward" in sel:
+        legs.update(run_backward(fa, synth, torch, dev, reps))
     if "decode_loop" in sel:
         legs["decode_loop_36l_L262144"] = run_decode_loop(fa, synth, torch, dev)
     if "peaks" in sel:
@@ -349,6 +354,47 @@ def run_soft(fa, synth, torch, dev, reps):
     del q, k, v, o, ws
     torch.cuda.empty_cache()
     return res
+
+
+def run_backward(fa, synth, torch, dev, reps):
+    """Attention backward (dQ, dK, dV in fp32) at the headline layer shape (seq 8192, 32/8 heads, head_dim 128,
+    dense causal) and at seq 65536 block-sparse (sink 128, window 2048).  O (bf16) and LSE come from one forward
+    launch outside the timed region.  Algorithmic FLOPs: the five products S, dP, dV, dK, dQ, 2*d each per
+    visible query-key pair and head (2.5x the forward's useful FLOPs)."""
+    out = {}
+    for S, mode, name in ((8192, fa.FLUX_MODE_DENSE, "backward_dense_s8192"),
+                          (65536, fa.FLUX_MODE_SPARSE, "backward_sparse_s65536")):
+        B, Hq, Hkv, d = 1, 32, 8, 128
+        sink, window = (128, 2048) if mode == fa.FLUX_MODE_SPARSE else (0, 0)
+        log(f"leg: backward S={S} mode={mode}")
+        q = synth.torch_normal((B, S, Hq, d), 1402, torch.bfloat16)
+        k = synth.torch_normal((B, S, Hkv, d), 1403, torch.bfloat16)
+        v = synth.torch_normal((B, S, Hkv, d), 1404, torch.bfloat16)
+        g = synth.torch_normal((B, S, Hq, d), 1405, torch.bfloat16)
+        o = torch.empty((B, S, Hq, d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+        rpd = cid = None
+        if mode == fa.FLUX_MODE_SPARSE:
+            rp, ci = fa.flux_build_block_mask(S, S, 64, sink, window, 1, fa.FLUX_MODE_SPARSE)
+            rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+            pairs = csr_pairs(rp, ci, S)
+        else:
+            pairs = causal_pairs(S)
+        fa.flux_attn_prefill(q, k, v, o, lse, causal=1, mode=mode, sink_tokens=sink, window_tokens=window,
+                             blk_row_ptr=rpd, blk_col_idx=cid)
+        dq = torch.empty((B, S, Hq, d), dtype=torch.float32, device=dev)
+        dk = torch.empty((B, S, Hkv, d), dtype=torch.float32, device=dev)
+        dv = torch.empty_like(dk)
+        ws = torch.empty(fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+        call = lambda: fa.flux_attn_backward(q, k, v, o, g, lse, dq, dk, dv, causal=True, mode=mode,
+                                             sink_tokens=sink, window_tokens=window, workspace=ws)
+        ms = time_steps(call, reps, 2)
+        flops = 10.0 * B * Hq * d * pairs
+        out[name] = {"ms": round(ms, 4), "algorithmic_flops": flops, "TFLOP/s": round(flops / ms / 1e9, 2),
+                     "frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v, g, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def run_decode_loop(fa, synth, torch, dev, steps=5):

@@ -25,9 +25,10 @@
 // Computing dQ apart from dK/dV rebuilds S and dP once more (7 matrix products instead of 5) but
 // needs no atomics: every gradient element is written once, summed in a fixed order.
 //
-// P and dS enter the gradient products as a bf16 pair hi + lo (hi = bf16(x), lo = bf16(x - hi)):
+// P and dS enter the gradient products as a bf16 pair hi + lo (hi = x truncated to bf16, lo =
+// bf16(x - hi)):
 // the sums over up to seq rows of bf16-rounded P or dS alone would carry a relative error of
-// 2^-9 per term, about 1e-2 absolute on gradients of size 5; the pair brings it near 2^-17 at the
+// 2^-9 per term, about 1e-2 absolute on gradients of size 5; the pair brings it near 2^-16 at the
 // cost of a second MFMA on the same A operand.
 //
 // Both main kernels are persistent (one workgroup per CU, 1 wave per SIMD) and take units from a
@@ -185,20 +186,46 @@ __global__ void __launch_bounds__(256) bwd_rowstat_kernel(BackwardArgs a) {
     }
 }
 
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): two bf16 MFMA operands whose products
-// sum to x * y with a relative error near 2^-17 instead of bf16's 2^-9.
-__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-    float r[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 h = (__bf16)x[e];
-        hi[e] = h;
-        r[e] = x[e] - (float)h;
-    }
-    lo = pack8(r);
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
 }
 
+// (x0, x1) = hi + lo per element, hi = x with its low 16 bits cleared (exact in bf16), lo = bf16(x - hi):
+// two bf16 MFMA operands whose products sum to x * y with a relative error near 2^-16 instead of
+// bf16's 2^-9.  Packed as bf16 pairs (element 2i in the low half of word i).
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    const float h0 = __uint_as_float(__float_as_uint(x0) & 0xffff0000u);
+    const float h1 = __uint_as_float(__float_as_uint(x1) & 0xffff0000u);
+    hi = pack2(h0, h1);
+    lo = pack2(x0 - h0, x1 - h1);
+}
+
+__device__ __forceinline__ bf16x8 as_op(const uint32_t* w) {
+    return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+}
+
+__device__ __forceinline__ float comp(const float4& v, int e) {
+    return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+#define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
+
 // ------------------------------------------------------------------ dK, dV
+//
+// One 64-query tile for a wave (32 keys) is 96 MFMAs: 32 for S and dP (16 rows at a time from the Q
+// and dO tiles, K and V rows in registers), then 16 groups of 4 for dV^T and dK^T (each group one
+// transposed dO operand and one transposed Q operand, times P hi, dS hi, P lo, dS lo).  The vector
+// work of the tile is spread over the MFMA steps once its inputs are complete (exp of S half 0
+// during S half 1, of half 1 during dP, dS during dP half 1 and the first gradient groups), and
+// every LDS operand is read a few MFMAs ahead; sched_barrier pins that order.
 __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BackwardArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSlots * kSlotB];
     __shared__ int qcell[2];
@@ -264,88 +291,120 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BackwardArgs a) {
             dv[mt] = f32x16{};
             dk[mt] = f32x16{};
         }
-        int slot = 0;
 
+        // One tile.  MASK: apply the per-element mask (C < lim, C = query - 64t - 4hh); tiles where no
+        // element of the workgroup can be masked skip it.
+        auto tile = [&](auto mask_tag, const char* qt, int lim) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            const char* dot = qt + kTileB;
+            const char* st = qt + 2 * kTileB;
+            f32x16 s[2], dp[2];
+            float pf[2][16], df[2][16];
+            uint32_t ph[4][4], pl[4][4], dh[4][4], dl[4][4];   // [k-step][word]: P and dS, hi and lo
+            float4 nl4[2][4], dd4[2][4];
+
+            auto E = [&](int hf, int r) {   // P element
+                float p = __builtin_amdgcn_exp2f(fmaf(s[hf][r], c2, comp(nl4[hf][r >> 2], r & 3)));
+                if (MASK) p = (32 * hf + 8 * (r >> 2) + (r & 3) < lim) ? 0.0f : p;
+                pf[hf][r] = p;
+            };
+            auto Dd = [&](int hf, int r) { df[hf][r] = pf[hf][r] * (dp[hf][r] - comp(dd4[hf][r >> 2], r & 3)); };
+            auto SP = [&](int hf, int pr) {   // pair pr of P half hf -> k-step 2hf + pr/4, word pr%4
+                split2(pf[hf][2 * pr], pf[hf][2 * pr + 1], ph[2 * hf + (pr >> 2)][pr & 3], pl[2 * hf + (pr >> 2)][pr & 3]);
+            };
+            auto SD = [&](int hf, int pr) {
+                split2(df[hf][2 * pr], df[hf][2 * pr + 1], dh[2 * hf + (pr >> 2)][pr & 3], dl[2 * hf + (pr >> 2)][pr & 3]);
+            };
+            auto rowA = [&](int j) -> bf16x8 { return L.row(j < 16 ? qt : dot, (j >> 3) & 1, j & 7); };
+            auto trop = [&](int gidx, int which) -> bf16x8 {   // group gidx = 4kk + mt; which 0: dO, 1: Q
+                return L.tr(which ? qt : dot, gidx >> 2, gidx & 3);
+            };
+
+            // ---- S (steps 0..15) and dP (16..31), operands read 4 steps ahead
+            bf16x8 ra[4];
+            bf16x8 rc[3][2];   // transposed operands of gradient groups, read 2 groups ahead
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ra[j] = rowA(j);
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const bf16x8 op = ra[j & 3];
+                if (j + 4 < 32) ra[j & 3] = rowA(j + 4);
+                if (j == 30 || j == 31) {
+                    rc[j - 30][0] = trop(j - 30, 0);
+                    rc[j - 30][1] = trop(j - 30, 1);
+                }
+                if (j < 16) {
+                    const int hf = j >> 3, c = j & 7;
+                    s[hf] = MFMA(op, kreg[c], c ? s[hf] : f32x16{});
+                } else {
+                    const int hf = (j - 16) >> 3, c = j & 7;
+                    dp[hf] = MFMA(op, vreg[c], c ? dp[hf] : f32x16{});
+                }
+                if (j < 8) {
+                    nl4[j >> 2][j & 3] = *reinterpret_cast<const float4*>(st + 4 * (32 * (j >> 2) + 8 * (j & 3) + 4 * hh));
+                    dd4[j >> 2][j & 3] =
+                        *reinterpret_cast<const float4*>(st + 256 + 4 * (32 * (j >> 2) + 8 * (j & 3) + 4 * hh));
+                } else if (j < 16) {
+                    E(0, 2 * (j - 8));
+                    E(0, 2 * (j - 8) + 1);
+                } else if (j < 24) {
+                    E(1, 2 * (j - 16));
+                    E(1, 2 * (j - 16) + 1);
+                    SP(0, j - 16);
+                } else {
+                    Dd(0, 2 * (j - 24));
+                    Dd(0, 2 * (j - 24) + 1);
+                    if (j >= 28) SD(0, j - 28);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+
+            // ---- dV^T += dO^T P and dK^T += Q^T dS: group gi = (kk, mt), operands 2 groups ahead
+#pragma unroll
+            for (int gi = 0; gi < 16; ++gi) {
+                const int kk = gi >> 2, mt = gi & 3;
+                const bf16x8 ado = rc[gi % 3][0], aq = rc[gi % 3][1];
+                if (gi + 2 < 16) {
+                    rc[(gi + 2) % 3][0] = trop(gi + 2, 0);
+                    rc[(gi + 2) % 3][1] = trop(gi + 2, 1);
+                }
+                dv[mt] = MFMA(ado, as_op(ph[kk]), dv[mt]);
+                dk[mt] = MFMA(aq, as_op(dh[kk]), dk[mt]);
+                dv[mt] = MFMA(ado, as_op(pl[kk]), dv[mt]);
+                dk[mt] = MFMA(aq, as_op(dl[kk]), dk[mt]);
+                if (gi < 4) {
+                    Dd(1, 4 * gi);
+                    Dd(1, 4 * gi + 1);
+                    Dd(1, 4 * gi + 2);
+                    Dd(1, 4 * gi + 3);
+                    SD(0, 4 + gi);
+                } else if (gi < 12) {
+                    SP(1, gi - 4);
+                    SD(1, gi - 4);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        int slot = 0;
         for (int i = 0; i < nt; ++i) {
             const int t = lo + i;
             __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's share of tile t landed
             __syncthreads();                       // tile t complete; every wave is done with tile t-1
             if (i + 1 < nt) issue(t + 1, slot ^ 1);
             const char* qt = smem + slot * kSlotB;
-            const char* dot = qt + kTileB;
-            const char* st = qt + 2 * kTileB;
-
-            // masked iff query < key; C below is (query - 64t - 4hh), so masked iff C < lim
+            // masked iff query < key, i.e. C < lim with C = query - 64t - 4hh
             int lim = key - 64 * t - 4 * hh;
             if (!a.causal) lim = -1000;
             else if (a.sparse && kb >= a.sink_blocks && t - kb >= a.window_blocks) lim = 1000;
-
-            // S = Q K^T and dP = dO V^T: lane holds key n, rows = queries 32hf + 8(r/4) + 4hh + r%4
-            f32x16 s[2], dp[2];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                s[hf] = f32x16{};
-#pragma unroll
-                for (int c = 0; c < kNC; ++c)
-                    s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(L.row(qt, hf, c), kreg[c], s[hf], 0, 0, 0);
-            }
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                dp[hf] = f32x16{};
-#pragma unroll
-                for (int c = 0; c < kNC; ++c)
-                    dp[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(L.row(dot, hf, c), vreg[c], dp[hf], 0, 0, 0);
-            }
-
-            // P = exp2(S * scale*log2(e) - LSE*log2(e)), dS = P (dP - D), both split into bf16 hi + lo;
-            // k-step kk = 2hf + aa takes registers 8aa .. 8aa+7 of half hf
-            bf16x8 ph[4], pl[4], dsh[4], dsl[4];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                float p[16], ds[16];
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const float4 nl = *reinterpret_cast<const float4*>(st + 4 * (32 * hf + 8 * g4 + 4 * hh));
-                    const float4 dd = *reinterpret_cast<const float4*>(st + 256 + 4 * (32 * hf + 8 * g4 + 4 * hh));
-                    const float nlv[4] = {nl.x, nl.y, nl.z, nl.w};
-                    const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * g4 + e;
-                        float pv = __builtin_amdgcn_exp2f(fmaf(s[hf][r], c2, nlv[e]));
-                        pv = (32 * hf + 8 * g4 + e < lim) ? 0.0f : pv;
-                        p[r] = pv;
-                        ds[r] = pv * (dp[hf][r] - ddv[e]);
-                    }
-                }
-                split8(p, ph[2 * hf], pl[2 * hf]);
-                split8(p + 8, ph[2 * hf + 1], pl[2 * hf + 1]);
-                split8(ds, dsh[2 * hf], dsl[2 * hf]);
-                split8(ds + 8, dsh[2 * hf + 1], dsl[2 * hf + 1]);
-            }
-
-            // dV^T += dO^T P and dK^T += Q^T dS (A operands: the tiles read transposed)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                bf16x8 ado[kNM], aq[kNM];
-#pragma unroll
-                for (int mt = 0; mt < kNM; ++mt) {
-                    ado[mt] = L.tr(dot, kk, mt);
-                    aq[mt] = L.tr(qt, kk, mt);
-                }
-#pragma unroll
-                for (int mt = 0; mt < kNM; ++mt)
-                    dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado[mt], ph[kk], dv[mt], 0, 0, 0);
-#pragma unroll
-                for (int mt = 0; mt < kNM; ++mt)
-                    dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[mt], dsh[kk], dk[mt], 0, 0, 0);
-#pragma unroll
-                for (int mt = 0; mt < kNM; ++mt)
-                    dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado[mt], pl[kk], dv[mt], 0, 0, 0);
-#pragma unroll
-                for (int mt = 0; mt < kNM; ++mt)
-                    dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[mt], dsl[kk], dk[mt], 0, 0, 0);
-            }
+            // some wave of the workgroup masks something: the diagonal tiles, or a tile the sparse
+            // pattern hides from one of the two key blocks
+            const bool any_mask = a.causal && (t < 2 * m + 2 ||
+                                               (a.sparse && ((2 * m >= a.sink_blocks && t - 2 * m >= a.window_blocks) ||
+                                                             (2 * m + 1 >= a.sink_blocks &&
+                                                              t - 2 * m - 1 >= a.window_blocks))));
+            if (any_mask) tile(Flag<true>{}, qt, lim);
+            else tile(Flag<false>{}, qt, lim);
             slot ^= 1;
         }
 
@@ -380,6 +439,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BackwardArgs a) {
 }
 
 // ------------------------------------------------------------------ dQ
+//
+// One 64-key tile for a wave (32 queries) is 64 MFMAs: 32 for S^T and dP^T (K and V rows from LDS,
+// Q and dO rows in registers), then 4 groups of 8 for dQ^T (four transposed K operands times dS hi,
+// then times dS lo).  The vector work is spread over the MFMA steps as in the dK/dV kernel.
 __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BackwardArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSlots * 2 * kTileB];
     __shared__ int qcell[2];
@@ -450,65 +513,93 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BackwardArgs a) {
         f32x16 dq[kNM];
 #pragma unroll
         for (int mt = 0; mt < kNM; ++mt) dq[mt] = f32x16{};
-        int slot = 0;
 
+        // One tile.  MASK: apply the per-element mask (C > lim, C = key - 64kb - 4hh).
+        auto tile = [&](auto mask_tag, const char* kt, int lim) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            const char* vt = kt + kTileB;
+            f32x16 s[2], dp[2];
+            float pf[2][16], df[2][16];
+            uint32_t dh[4][4], dl[4][4];
+
+            auto E = [&](int kh, int r) {
+                float p = __builtin_amdgcn_exp2f(fmaf(s[kh][r], c2, nl));
+                if (MASK) p = (32 * kh + 8 * (r >> 2) + (r & 3) > lim) ? 0.0f : p;
+                pf[kh][r] = p;
+            };
+            auto Dd = [&](int kh, int r) { df[kh][r] = pf[kh][r] * (dp[kh][r] - dd); };
+            auto SD = [&](int kh, int pr) {
+                split2(df[kh][2 * pr], df[kh][2 * pr + 1], dh[2 * kh + (pr >> 2)][pr & 3], dl[2 * kh + (pr >> 2)][pr & 3]);
+            };
+            auto rowA = [&](int j) -> bf16x8 { return L.row(j < 16 ? kt : vt, (j >> 3) & 1, j & 7); };
+
+            bf16x8 ra[4];
+            bf16x8 rc[2][kNM];   // transposed K operands of k-steps kk, kk + 1
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ra[j] = rowA(j);
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const bf16x8 op = ra[j & 3];
+                if (j + 4 < 32) ra[j & 3] = rowA(j + 4);
+                if (j >= 28) rc[0][j - 28] = L.tr(kt, 0, j - 28);
+                if (j < 16) {
+                    const int kh = j >> 3, c = j & 7;
+                    s[kh] = MFMA(op, qreg[c], c ? s[kh] : f32x16{});
+                } else {
+                    const int kh = (j - 16) >> 3, c = j & 7;
+                    dp[kh] = MFMA(op, doreg[c], c ? dp[kh] : f32x16{});
+                }
+                if (j >= 8 && j < 16) {
+                    E(0, 2 * (j - 8));
+                    E(0, 2 * (j - 8) + 1);
+                } else if (j >= 16 && j < 24) {
+                    E(1, 2 * (j - 16));
+                    E(1, 2 * (j - 16) + 1);
+                } else if (j >= 24) {
+                    Dd(0, 2 * (j - 24));
+                    Dd(0, 2 * (j - 24) + 1);
+                    if (j >= 28) SD(0, j - 28);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+
+            // ---- dQ^T += K^T dS^T, k-step kk: 4 operands, times dS hi then dS lo
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const int mt = x & 3;
+                    const bf16x8 ak = rc[kk & 1][mt];
+                    dq[mt] = MFMA(ak, as_op(x < 4 ? dh[kk] : dl[kk]), dq[mt]);
+                    if (x >= 4 && kk + 1 < 4) rc[(kk + 1) & 1][x - 4] = L.tr(kt, kk + 1, x - 4);
+                    if (kk == 0) {
+                        Dd(1, 2 * x);
+                        Dd(1, 2 * x + 1);
+                        if (x < 4) SD(0, 4 + x);
+                    } else if (kk == 1) {
+                        SD(1, x);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+
+        int slot = 0;
         for (int i = 0; i < nt; ++i) {
             const int kb = kb_of(i);
             __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
             __syncthreads();
             if (i + 1 < nt) issue(kb_of(i + 1), slot ^ 1);
             const char* kt = smem + slot * 2 * kTileB;
-            const char* vt = kt + kTileB;
-
-            // C below is (key - 64kb - 4hh); masked iff C > lim
+            // masked iff C > lim, C = key - 64kb - 4hh
             int lim = qpos - 64 * kb - 4 * hh;                                     // causal
             if (!a.causal) lim = seq - 1 - 64 * kb - 4 * hh;                       // keys past the end
             else if (a.sparse && kb >= a.sink_blocks && qb - kb >= a.window_blocks) lim = -1000;
-
-            // S^T = K Q^T and dP^T = V dO^T: lane holds query n, rows = keys 32kh + 8(r/4) + 4hh + r%4
-            f32x16 s[2], dp[2];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                s[kh] = f32x16{};
-#pragma unroll
-                for (int c = 0; c < kNC; ++c)
-                    s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(L.row(kt, kh, c), qreg[c], s[kh], 0, 0, 0);
-            }
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                dp[kh] = f32x16{};
-#pragma unroll
-                for (int c = 0; c < kNC; ++c)
-                    dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(L.row(vt, kh, c), doreg[c], dp[kh], 0, 0, 0);
-            }
-
-            bf16x8 dsh[4], dsl[4];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                float ds[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pv = __builtin_amdgcn_exp2f(fmaf(s[kh][r], c2, nl));
-                    pv = (32 * kh + 8 * (r >> 2) + (r & 3) > lim) ? 0.0f : pv;
-                    ds[r] = pv * (dp[kh][r] - dd);
-                }
-                split8(ds, dsh[2 * kh], dsl[2 * kh]);
-                split8(ds + 8, dsh[2 * kh + 1], dsl[2 * kh + 1]);
-            }
-
-            // dQ^T += K^T dS^T (A operand: the K tile read transposed)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                bf16x8 ak[kNM];
-#pragma unroll
-                for (int mt = 0; mt < kNM; ++mt) ak[mt] = L.tr(kt, kk, mt);
-#pragma unroll
-                for (int mt = 0; mt < kNM; ++mt)
-                    dq[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[mt], dsh[kk], dq[mt], 0, 0, 0);
-#pragma unroll
-                for (int mt = 0; mt < kNM; ++mt)
-                    dq[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[mt], dsl[kk], dq[mt], 0, 0, 0);
-            }
+            const bool any_mask = a.causal ? (kb >= 2 * tp || (a.sparse && kb >= a.sink_blocks &&
+                                                              2 * tp + 1 - kb >= a.window_blocks))
+                                           : 64 * (kb + 1) > seq;
+            if (any_mask) tile(Flag<true>{}, kt, lim);
+            else tile(Flag<false>{}, kt, lim);
             slot ^= 1;
         }
 
@@ -527,6 +618,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BackwardArgs a) {
         u = queue.next();
     }
 }
+
+#undef MFMA
 
 // ------------------------------------------------------------------ grouped-query sum
 // out[b, s, g, :] = sum over j < G of part[b, s, g*G + j, :], j ascending; blockIdx.y picks dK / dV.
