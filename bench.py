@@ -85,22 +85,30 @@ class KernelTimer:
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_dense_causal_s8192_traffic.txt")
-PREFILL_SRC = os.path.join(ROOT, "long_context_attention_tiled_amd", "csrc", "prefill_bf16.hip")
+PREFILL_SRCS = [os.path.join(ROOT, "long_context_attention_tiled_amd", "csrc", f)
+                for f in ("prefill_bf16.hip", "tile_common.h")]
+
+
+def prefill_source_hash() -> str:
+    """sha256 over the prefill kernel's sources (kernel file, then its tile helper header)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in PREFILL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per launch of the dense prefill kernel from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the summary was taken on
     another version of the kernel source."""
-    import hashlib
     try:
         kv = {}
         for line in open(TRAFFIC_FILE):
             if "=" in line and not line.lstrip().startswith("#"):
                 key, val = line.split("=", 1)
                 kv[key.strip()] = val.strip()
-        src_hash = hashlib.sha256(open(PREFILL_SRC, "rb").read()).hexdigest()
-        if kv.get("prefill_source_sha256") != src_hash:
+        if kv.get("prefill_source_sha256") != prefill_source_hash():
             return None
         return int(float(kv["hbm_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):
