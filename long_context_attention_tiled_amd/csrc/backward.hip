@@ -31,8 +31,8 @@
 // 2^-9 per term, about 1e-2 absolute on gradients of size 5; the pair brings it near 2^-16 at the
 // cost of a second MFMA on the same A operand.
 //
-// Both main kernels are persistent (one workgroup per CU, 1 wave per SIMD) and take units from a
-// device counter, longest first.  Two LDS slots: the tile in use and the next one in flight.
+// Both main kernels are persistent, run two waves per SIMD, and take units from a device counter,
+// longest first.  Two LDS slots: the tile in use and the next one in flight.
 #include "flux_internal.h"
 #include "tile_common.h"
 
@@ -189,11 +189,6 @@ __global__ void __launch_bounds__(256) bwd_rowstat_kernel(BackwardArgs a) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <bool B>
-struct Flag {
-    static constexpr bool value = B;
-};
-
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
 }
@@ -208,8 +203,16 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
     lo = pack2(x0 - h0, x1 - h1);
 }
 
-__device__ __forceinline__ bf16x8 as_op(const uint32_t* w) {
-    return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+// 16 accumulator values of one 32x32 block -> hi and lo operands of its two 16-wide k-steps
+__device__ __forceinline__ void split16(const float* x, bf16x8* hi, bf16x8* lo) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) split2(x[8 * q + 2 * w], x[8 * q + 2 * w + 1], h[w], l[w]);
+        hi[q] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+        lo[q] = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+    }
 }
 
 __device__ __forceinline__ float comp(const float4& v, int e) {
@@ -218,21 +221,71 @@ __device__ __forceinline__ float comp(const float4& v, int e) {
 
 #define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
 
+// NS MFMA steps whose A operands come from LDS: operand(i) is read kAhead steps before step(i, op)
+// uses it, and sched_barrier keeps that order (left alone, the scheduler reuses one register and
+// waits for each read right before its MFMA).
+constexpr int kAhead = 3;
+template <int NS, typename Operand, typename Step>
+__device__ __forceinline__ void mfma_seq(Operand operand, Step step) {
+    __builtin_amdgcn_s_setprio(1);   // the other wave of the SIMD fills the MFMA shadow with its vector work
+    bf16x8 ring[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i)
+        if (i < NS) ring[i] = operand(i);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const bf16x8 op = ring[i % kAhead];
+        if (i + kAhead < NS) ring[i % kAhead] = operand(i + kAhead);
+        step(i, op);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+}
+
+// acc[mt] += X^T[mt, k-steps kk0, kk0 + 1] * (hi + lo): the transposed operand of (kk, mt) is read
+// once and used by its hi and lo MFMAs; the next k-step's operand is read into the register its
+// last use frees.
+template <typename Lanes_>
+__device__ __forceinline__ void grad_product(const Lanes_& L, const char* xt, int kk0, const bf16x8* xh,
+                                             const bf16x8* xl, f32x16* acc) {
+    __builtin_amdgcn_s_setprio(1);
+    bf16x8 ax[kNM];
+#pragma unroll
+    for (int mt = 0; mt < kNM; ++mt) ax[mt] = L.tr(xt, kk0, mt);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int mt = 0; mt < kNM; ++mt) {
+            acc[mt] = MFMA(ax[mt], xh[q], acc[mt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int mt = 0; mt < kNM; ++mt) {
+            acc[mt] = MFMA(ax[mt], xl[q], acc[mt]);
+            if (q == 0) ax[mt] = L.tr(xt, kk0 + 1, mt);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // ------------------------------------------------------------------ dK, dV
 //
-// One 64-query tile for a wave (32 keys) is 96 MFMAs: 32 for S and dP (16 rows at a time from the Q
-// and dO tiles, K and V rows in registers), then 16 groups of 4 for dV^T and dK^T (each group one
-// transposed dO operand and one transposed Q operand, times P hi, dS hi, P lo, dS lo).  The vector
-// work of the tile is spread over the MFMA steps once its inputs are complete (exp of S half 0
-// during S half 1, of half 1 during dP, dS during dP half 1 and the first gradient groups), and
-// every LDS operand is read a few MFMAs ahead; sched_barrier pins that order.
-__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BackwardArgs a) {
+// 8 waves, two per SIMD, on 128 keys: waves w and w + 4 own the same 32 keys; wave w accumulates
+// dV^T (it needs S and P only), wave w + 4 accumulates dK^T (S, dP and dS).  Each takes a 64-query
+// tile in two 32-query halves: S (8 MFMAs; dP, 8 more, for dK), the vector work, then 16 MFMAs of
+// its gradient product.  That is 48 + 64 MFMAs per SIMD and tile, and each wave stays within 256
+// registers, so the two waves of a SIMD hide each other's vector work and LDS latency.
+constexpr int kKvWaves = 8;
+__global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSlots * kSlotB];
     __shared__ int qcell[2];
     Lanes L;
     L.init(threadIdx.x & 63);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = L.lane, n = L.n, hh = L.hh;
+    const int ks = wave & 3;          // 32-key group
+    const bool is_dk = wave >= 4;     // role: dK (true) or dV (false)
 
     const int seq = (int)a.seq, nqb = a.n_qblk, G = a.hq / a.hkv;
     const int bh_total = (int)a.batch * a.hq;
@@ -247,8 +300,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BackwardArgs a) {
         queue.prefetch();
         const int m = u / bh_total, bh = u % bh_total;   // key pair m: longest query range first
         const int b = bh / a.hq, h = bh % a.hq, g = h / G;
-        const int kb = 2 * m + (wave >> 1);               // this wave's key block
-        const int key = 128 * m + 32 * wave + n;          // this lane's key
+        const int kb = 2 * m + (ks >> 1);                 // this wave's key block
+        const int key = 128 * m + 32 * ks + n;            // this lane's key
         int lo = 0, hi = nqb - 1;
         if (a.causal) {
             lo = 2 * m;
@@ -259,10 +312,11 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BackwardArgs a) {
         const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * kD;
         const u16* dog = reinterpret_cast<const u16*>(a.d_o) + ((int64_t)b * a.seq * a.hq + h) * kD;
         const float* stg = a.stat + ((int64_t)b * a.hq + h) * nqb * 128;
+        // a tile is 32 loads of 1 KB (Q by waves 0-3, dO by waves 4-7) plus 2 of row statistics
         auto issue = [&](int t, int slot) {
             const uint32_t base = lds0 + slot * kSlotB;
-            load_tile(qg, q_stride, 64 * t, seq - 1, base, wave, lane);
-            load_tile(dog, q_stride, 64 * t, seq - 1, base + kTileB, wave, lane);
+            if (wave < 4) load_tile(qg, q_stride, 64 * t, seq - 1, base, wave, lane);
+            else load_tile(dog, q_stride, 64 * t, seq - 1, base + kTileB, wave - 4, lane);
             if (wave == 0) {
                 const u16* sp = uniform_ptr(reinterpret_cast<const u16*>(stg + t * 128));
                 load_lds_4(sp, 4u * lane, base + 2 * kTileB);
@@ -271,7 +325,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BackwardArgs a) {
         };
         issue(lo, 0);
 
-        // K and V rows of this lane's key as B operands (k-slots = d)
+        // K (both roles) and V (dK role) rows of this lane's key as B operands (k-slots = d)
         bf16x8 kreg[kNC], vreg[kNC];
         {
             const int kc = min(key, seq - 1);
@@ -279,110 +333,52 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BackwardArgs a) {
             const u16* kp = reinterpret_cast<const u16*>(a.k) + off;
             const u16* vp = reinterpret_cast<const u16*>(a.v) + off;
 #pragma unroll
-            for (int c = 0; c < kNC; ++c) {
-                kreg[c] = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
-                vreg[c] = *reinterpret_cast<const bf16x8*>(vp + 16 * c);
+            for (int c = 0; c < kNC; ++c) kreg[c] = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
+            if (is_dk) {
+#pragma unroll
+                for (int c = 0; c < kNC; ++c) vreg[c] = *reinterpret_cast<const bf16x8*>(vp + 16 * c);
             }
         }
 
-        f32x16 dv[kNM], dk[kNM];
+        f32x16 acc[kNM];   // dV^T or dK^T: lane = key, rows d = 32mt + 8(r/4) + 4hh + r%4
 #pragma unroll
-        for (int mt = 0; mt < kNM; ++mt) {
-            dv[mt] = f32x16{};
-            dk[mt] = f32x16{};
-        }
+        for (int mt = 0; mt < kNM; ++mt) acc[mt] = f32x16{};
 
-        // One tile.  MASK: apply the per-element mask (C < lim, C = query - 64t - 4hh); tiles where no
-        // element of the workgroup can be masked skip it.
-        auto tile = [&](auto mask_tag, const char* qt, int lim) {
-            constexpr bool MASK = decltype(mask_tag)::value;
+        // One tile: elements with C < lim are masked (C = query - 64t - 4hh).  Both roles run this one
+        // body, the role and the mask switching only short stretches (dP's MFMAs, dS, the mask):
+        // separate bodies per role or per masked/unmasked tile would cost about 30 registers more and spill.
+        auto tile = [&](const char* qt, int lim, bool need_mask) {
             const char* dot = qt + kTileB;
             const char* st = qt + 2 * kTileB;
-            f32x16 s[2], dp[2];
-            float pf[2][16], df[2][16];
-            uint32_t ph[4][4], pl[4][4], dh[4][4], dl[4][4];   // [k-step][word]: P and dS, hi and lo
-            float4 nl4[2][4], dd4[2][4];
-
-            auto E = [&](int hf, int r) {   // P element
-                float p = __builtin_amdgcn_exp2f(fmaf(s[hf][r], c2, comp(nl4[hf][r >> 2], r & 3)));
-                if (MASK) p = (32 * hf + 8 * (r >> 2) + (r & 3) < lim) ? 0.0f : p;
-                pf[hf][r] = p;
-            };
-            auto Dd = [&](int hf, int r) { df[hf][r] = pf[hf][r] * (dp[hf][r] - comp(dd4[hf][r >> 2], r & 3)); };
-            auto SP = [&](int hf, int pr) {   // pair pr of P half hf -> k-step 2hf + pr/4, word pr%4
-                split2(pf[hf][2 * pr], pf[hf][2 * pr + 1], ph[2 * hf + (pr >> 2)][pr & 3], pl[2 * hf + (pr >> 2)][pr & 3]);
-            };
-            auto SD = [&](int hf, int pr) {
-                split2(df[hf][2 * pr], df[hf][2 * pr + 1], dh[2 * hf + (pr >> 2)][pr & 3], dl[2 * hf + (pr >> 2)][pr & 3]);
-            };
-            auto rowA = [&](int j) -> bf16x8 { return L.row(j < 16 ? qt : dot, (j >> 3) & 1, j & 7); };
-            auto trop = [&](int gidx, int which) -> bf16x8 {   // group gidx = 4kk + mt; which 0: dO, 1: Q
-                return L.tr(which ? qt : dot, gidx >> 2, gidx & 3);
-            };
-
-            // ---- S (steps 0..15) and dP (16..31), operands read 4 steps ahead
-            bf16x8 ra[4];
-            bf16x8 rc[3][2];   // transposed operands of gradient groups, read 2 groups ahead
+            const char* xt = is_dk ? qt : dot;   // tile read transposed for the gradient product
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ra[j] = rowA(j);
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x16 s = f32x16{}, dp = f32x16{};
+                mfma_seq<8>([&](int i) { return L.row(qt, hf, i); }, [&](int i, bf16x8 op) { s = MFMA(op, kreg[i], s); });
+                if (is_dk)
+                    mfma_seq<8>([&](int i) { return L.row(dot, hf, i); }, [&](int i, bf16x8 op) { dp = MFMA(op, vreg[i], dp); });
+                float x[16];   // P, then dS = P (dP - D) for the dK role
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                const bf16x8 op = ra[j & 3];
-                if (j + 4 < 32) ra[j & 3] = rowA(j + 4);
-                if (j == 30 || j == 31) {
-                    rc[j - 30][0] = trop(j - 30, 0);
-                    rc[j - 30][1] = trop(j - 30, 1);
-                }
-                if (j < 16) {
-                    const int hf = j >> 3, c = j & 7;
-                    s[hf] = MFMA(op, kreg[c], c ? s[hf] : f32x16{});
-                } else {
-                    const int hf = (j - 16) >> 3, c = j & 7;
-                    dp[hf] = MFMA(op, vreg[c], c ? dp[hf] : f32x16{});
-                }
-                if (j < 8) {
-                    nl4[j >> 2][j & 3] = *reinterpret_cast<const float4*>(st + 4 * (32 * (j >> 2) + 8 * (j & 3) + 4 * hh));
-                    dd4[j >> 2][j & 3] =
-                        *reinterpret_cast<const float4*>(st + 256 + 4 * (32 * (j >> 2) + 8 * (j & 3) + 4 * hh));
-                } else if (j < 16) {
-                    E(0, 2 * (j - 8));
-                    E(0, 2 * (j - 8) + 1);
-                } else if (j < 24) {
-                    E(1, 2 * (j - 16));
-                    E(1, 2 * (j - 16) + 1);
-                    SP(0, j - 16);
-                } else {
-                    Dd(0, 2 * (j - 24));
-                    Dd(0, 2 * (j - 24) + 1);
-                    if (j >= 28) SD(0, j - 28);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-
-            // ---- dV^T += dO^T P and dK^T += Q^T dS: group gi = (kk, mt), operands 2 groups ahead
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const float4 nl = *reinterpret_cast<const float4*>(st + 4 * (32 * hf + 8 * g4 + 4 * hh));
 #pragma unroll
-            for (int gi = 0; gi < 16; ++gi) {
-                const int kk = gi >> 2, mt = gi & 3;
-                const bf16x8 ado = rc[gi % 3][0], aq = rc[gi % 3][1];
-                if (gi + 2 < 16) {
-                    rc[(gi + 2) % 3][0] = trop(gi + 2, 0);
-                    rc[(gi + 2) % 3][1] = trop(gi + 2, 1);
+                    for (int e = 0; e < 4; ++e) x[4 * g4 + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * g4 + e], c2, comp(nl, e)));
                 }
-                dv[mt] = MFMA(ado, as_op(ph[kk]), dv[mt]);
-                dk[mt] = MFMA(aq, as_op(dh[kk]), dk[mt]);
-                dv[mt] = MFMA(ado, as_op(pl[kk]), dv[mt]);
-                dk[mt] = MFMA(aq, as_op(dl[kk]), dk[mt]);
-                if (gi < 4) {
-                    Dd(1, 4 * gi);
-                    Dd(1, 4 * gi + 1);
-                    Dd(1, 4 * gi + 2);
-                    Dd(1, 4 * gi + 3);
-                    SD(0, 4 + gi);
-                } else if (gi < 12) {
-                    SP(1, gi - 4);
-                    SD(1, gi - 4);
+                if (need_mask) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x[r] = (32 * hf + 8 * (r >> 2) + (r & 3) < lim) ? 0.0f : x[r];
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                if (is_dk) {
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const float4 dd = *reinterpret_cast<const float4*>(st + 256 + 4 * (32 * hf + 8 * g4 + 4 * hh));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[4 * g4 + e] *= dp[4 * g4 + e] - comp(dd, e);
+                    }
+                }
+                bf16x8 xh[2], xl[2];
+                split16(x, xh, xl);
+                grad_product(L, xt, 2 * hf, xh, xl, acc);
             }
         };
 
@@ -397,41 +393,26 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BackwardArgs a) {
             int lim = key - 64 * t - 4 * hh;
             if (!a.causal) lim = -1000;
             else if (a.sparse && kb >= a.sink_blocks && t - kb >= a.window_blocks) lim = 1000;
-            // some wave of the workgroup masks something: the diagonal tiles, or a tile the sparse
-            // pattern hides from one of the two key blocks
-            const bool any_mask = a.causal && (t < 2 * m + 2 ||
-                                               (a.sparse && ((2 * m >= a.sink_blocks && t - 2 * m >= a.window_blocks) ||
-                                                             (2 * m + 1 >= a.sink_blocks &&
-                                                              t - 2 * m - 1 >= a.window_blocks))));
-            if (any_mask) tile(Flag<true>{}, qt, lim);
-            else tile(Flag<false>{}, qt, lim);
+            // this wave masks something only on its diagonal tile, on tiles before it, and on tiles the
+            // sparse pattern hides from its key block
+            const bool need_mask = a.causal && (t <= kb || lim == 1000);
+            tile(qt, lim, need_mask);
             slot ^= 1;
         }
 
         // lane holds column key, rows d = 32mt + 8(r/4) + 4hh + r%4
         if (key < seq) {
-            float* dkp;
-            float* dvp;
-            if (G == 1) {
-                const int64_t off = (((int64_t)b * a.seq + key) * a.hkv + g) * kD;
-                dkp = a.dk + off;
-                dvp = a.dv + off;
-            } else {
-                const int64_t off = (((int64_t)b * a.seq + key) * a.hq + h) * kD;
-                dkp = a.dk_part + off;
-                dvp = a.dv_part + off;
-            }
+            float* dst;
+            if (G == 1) dst = (is_dk ? a.dk : a.dv) + (((int64_t)b * a.seq + key) * a.hkv + g) * kD;
+            else dst = (is_dk ? a.dk_part : a.dv_part) + (((int64_t)b * a.seq + key) * a.hq + h) * kD;
+            const float f = is_dk ? a.scale : 1.0f;
 #pragma unroll
             for (int mt = 0; mt < kNM; ++mt)
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int d = 32 * mt + 8 * g4 + 4 * hh;
-                    *reinterpret_cast<float4*>(dkp + d) =
-                        float4{a.scale * dk[mt][4 * g4], a.scale * dk[mt][4 * g4 + 1], a.scale * dk[mt][4 * g4 + 2],
-                               a.scale * dk[mt][4 * g4 + 3]};
-                    *reinterpret_cast<float4*>(dvp + d) =
-                        float4{dv[mt][4 * g4], dv[mt][4 * g4 + 1], dv[mt][4 * g4 + 2], dv[mt][4 * g4 + 3]};
-                }
+                for (int g4 = 0; g4 < 4; ++g4)
+                    *reinterpret_cast<float4*>(dst + 32 * mt + 8 * g4 + 4 * hh) =
+                        float4{f * acc[mt][4 * g4], f * acc[mt][4 * g4 + 1], f * acc[mt][4 * g4 + 2],
+                               f * acc[mt][4 * g4 + 3]};
         }
         __syncthreads();   // every wave is done with the slots before the next unit loads into them
         u = queue.next();
@@ -440,10 +421,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BackwardArgs a) {
 
 // ------------------------------------------------------------------ dQ
 //
-// One 64-key tile for a wave (32 queries) is 64 MFMAs: 32 for S^T and dP^T (K and V rows from LDS,
-// Q and dO rows in registers), then 4 groups of 8 for dQ^T (four transposed K operands times dS hi,
-// then times dS lo).  The vector work is spread over the MFMA steps as in the dK/dV kernel.
-__global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BackwardArgs a) {
+// 4 waves of 32 queries, two workgroups per CU (two waves per SIMD).  A 64-key tile is taken in two
+// 32-key halves: S^T and dP^T (16 MFMAs, K and V rows from LDS, Q and dO rows in registers), the
+// vector work, then 16 MFMAs of dQ^T += K^T dS^T.
+__global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSlots * 2 * kTileB];
     __shared__ int qcell[2];
     Lanes L;
@@ -514,73 +495,30 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BackwardArgs a) {
 #pragma unroll
         for (int mt = 0; mt < kNM; ++mt) dq[mt] = f32x16{};
 
-        // One tile.  MASK: apply the per-element mask (C > lim, C = key - 64kb - 4hh).
-        auto tile = [&](auto mask_tag, const char* kt, int lim) {
-            constexpr bool MASK = decltype(mask_tag)::value;
+        // One tile: elements with C > lim are masked (C = key - 64kb - 4hh).  One body for masked and
+        // unmasked tiles (the mask is a short branch): two bodies would cost registers and spill.
+        auto tile = [&](const char* kt, int lim, bool need_mask) {
             const char* vt = kt + kTileB;
-            f32x16 s[2], dp[2];
-            float pf[2][16], df[2][16];
-            uint32_t dh[4][4], dl[4][4];
-
-            auto E = [&](int kh, int r) {
-                float p = __builtin_amdgcn_exp2f(fmaf(s[kh][r], c2, nl));
-                if (MASK) p = (32 * kh + 8 * (r >> 2) + (r & 3) > lim) ? 0.0f : p;
-                pf[kh][r] = p;
-            };
-            auto Dd = [&](int kh, int r) { df[kh][r] = pf[kh][r] * (dp[kh][r] - dd); };
-            auto SD = [&](int kh, int pr) {
-                split2(df[kh][2 * pr], df[kh][2 * pr + 1], dh[2 * kh + (pr >> 2)][pr & 3], dl[2 * kh + (pr >> 2)][pr & 3]);
-            };
-            auto rowA = [&](int j) -> bf16x8 { return L.row(j < 16 ? kt : vt, (j >> 3) & 1, j & 7); };
-
-            bf16x8 ra[4];
-            bf16x8 rc[2][kNM];   // transposed K operands of k-steps kk, kk + 1
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ra[j] = rowA(j);
+            for (int kh = 0; kh < 2; ++kh) {
+                // S^T = K Q^T, dP^T = V dO^T: lane = query n, registers = keys 32kh + 8(r/4) + 4hh + r%4
+                f32x16 s = f32x16{}, dp = f32x16{};
+                mfma_seq<16>([&](int i) { return L.row(i < 8 ? kt : vt, kh, i & 7); }, [&](int i, bf16x8 op) {
+                    if (i < 8) s = MFMA(op, qreg[i], s);
+                    else dp = MFMA(op, doreg[i & 7], dp);
+                });
+                float x[16];   // P, then dS = P (dP - D)
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                const bf16x8 op = ra[j & 3];
-                if (j + 4 < 32) ra[j & 3] = rowA(j + 4);
-                if (j >= 28) rc[0][j - 28] = L.tr(kt, 0, j - 28);
-                if (j < 16) {
-                    const int kh = j >> 3, c = j & 7;
-                    s[kh] = MFMA(op, qreg[c], c ? s[kh] : f32x16{});
-                } else {
-                    const int kh = (j - 16) >> 3, c = j & 7;
-                    dp[kh] = MFMA(op, doreg[c], c ? dp[kh] : f32x16{});
+                for (int r = 0; r < 16; ++r) x[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, nl));
+                if (need_mask) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x[r] = (32 * kh + 8 * (r >> 2) + (r & 3) > lim) ? 0.0f : x[r];
                 }
-                if (j >= 8 && j < 16) {
-                    E(0, 2 * (j - 8));
-                    E(0, 2 * (j - 8) + 1);
-                } else if (j >= 16 && j < 24) {
-                    E(1, 2 * (j - 16));
-                    E(1, 2 * (j - 16) + 1);
-                } else if (j >= 24) {
-                    Dd(0, 2 * (j - 24));
-                    Dd(0, 2 * (j - 24) + 1);
-                    if (j >= 28) SD(0, j - 28);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-
-            // ---- dQ^T += K^T dS^T, k-step kk: 4 operands, times dS hi then dS lo
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    const int mt = x & 3;
-                    const bf16x8 ak = rc[kk & 1][mt];
-                    dq[mt] = MFMA(ak, as_op(x < 4 ? dh[kk] : dl[kk]), dq[mt]);
-                    if (x >= 4 && kk + 1 < 4) rc[(kk + 1) & 1][x - 4] = L.tr(kt, kk + 1, x - 4);
-                    if (kk == 0) {
-                        Dd(1, 2 * x);
-                        Dd(1, 2 * x + 1);
-                        if (x < 4) SD(0, 4 + x);
-                    } else if (kk == 1) {
-                        SD(1, x);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                for (int r = 0; r < 16; ++r) x[r] *= dp[r] - dd;
+                bf16x8 xh[2], xl[2];
+                split16(x, xh, xl);
+                grad_product(L, kt, 2 * kh, xh, xl, dq);   // dQ^T += K^T dS^T
             }
         };
 
@@ -595,11 +533,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BackwardArgs a) {
             int lim = qpos - 64 * kb - 4 * hh;                                     // causal
             if (!a.causal) lim = seq - 1 - 64 * kb - 4 * hh;                       // keys past the end
             else if (a.sparse && kb >= a.sink_blocks && qb - kb >= a.window_blocks) lim = -1000;
-            const bool any_mask = a.causal ? (kb >= 2 * tp || (a.sparse && kb >= a.sink_blocks &&
-                                                              2 * tp + 1 - kb >= a.window_blocks))
-                                           : 64 * (kb + 1) > seq;
-            if (any_mask) tile(Flag<true>{}, kt, lim);
-            else tile(Flag<false>{}, kt, lim);
+            // this wave masks something only on its diagonal tile, on tiles after it, on tiles the
+            // sparse pattern hides from its query block, and (all keys visible) on a ragged last tile
+            const bool need_mask = a.causal ? (kb >= qb || lim == -1000) : 64 * (kb + 1) > seq;
+            tile(kt, lim, need_mask);
             slot ^= 1;
         }
 
@@ -620,6 +557,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BackwardArgs a) {
 }
 
 #undef MFMA
+
 
 // ------------------------------------------------------------------ grouped-query sum
 // out[b, s, g, :] = sum over j < G of part[b, s, g*G + j, :], j ascending; blockIdx.y picks dK / dV.
@@ -654,9 +592,10 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bwd_rowstat_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
     const int64_t units = ((a.n_qblk + 1) / 2) * a.batch * (int64_t)a.hq;
     const int cu = a.num_cu > 0 ? a.num_cu : 256;
-    const unsigned grid = (unsigned)(units < cu ? units : cu);
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(grid), dim3(kThreads), 0, s, a);
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+    const unsigned grid_kv = (unsigned)(units < cu ? units : cu);              // one 8-wave group per CU
+    const unsigned grid_q = (unsigned)(units < 2 * cu ? units : 2 * cu);      // two 4-wave groups per CU
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(grid_kv), dim3(64 * kKvWaves), 0, s, a);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid_q), dim3(kThreads), 0, s, a);
     if (a.hq != a.hkv) {
         const int64_t n4 = a.batch * a.seq * a.hkv * (kD / 4);
         hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((n4 + 255) / 256), 2), dim3(256), 0, s, a);
