@@ -127,6 +127,16 @@ def time_steps(step, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def call_percentiles(step, reps):
+    """(p10, median, p90) in ms of single calls, each bracketed by HIP events on the current stream."""
+    import torch
+    t = KernelTimer()
+    for _ in range(reps):
+        t.record(step)
+    torch.cuda.synchronize()
+    return t.pct_ms()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,7 +285,8 @@ def run_legs(fa, synth, torch, dev, sel, reps):
             call = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_SPARSE,
                                                 sink_tokens=128, window_tokens=2048, blk_row_ptr=rpd, blk_col_idx=cid)
             ms = time_steps(call, reps, 3)
-            legs["sparse_prefill_s65536"] = {"ms": round(ms, 4), "useful_flops": useful, "nnz_blocks": int(len(ci)),
+            legs["sparse_prefill_s65536"] = {"ms": round(ms, 4), "ms_p10_p50_p90": call_percentiles(call, reps),
+                                             "useful_flops": useful, "nnz_blocks": int(len(ci)),
                                              "TFLOP/s": round(useful / ms / 1e9, 2),
                                              "frac": round(useful / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
         if "dense64k" in sel:
@@ -308,7 +319,8 @@ def run_legs(fa, synth, torch, dev, sel, reps):
                                                workspace=ws)
             ms = time_steps(call, reps if mode == 0 else 5 * reps, 3)
             gbs = nbytes / ms / 1e6
-            legs[name] = {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
+            legs[name] = {"ms": round(ms, 4), "ms_p10_p50_p90": call_percentiles(call, reps), "bytes": nbytes,
+                          "GB/s": round(gbs, 1),
                           "frac": round(gbs / PEAK_HBM_GBS, 4), "tok/s": round(B / (ms * 1e-3), 1)}
         legs["decode_sparse_L262144"]["speedup_vs_dense"] = round(
             legs["decode_dense_L262144"]["ms"] / legs["decode_sparse_L262144"]["ms"], 2)
@@ -398,7 +410,7 @@ def run_backward(fa, synth, torch, dev, reps):
                                              sink_tokens=sink, window_tokens=window, workspace=ws)
         ms = time_steps(call, reps, 2)
         flops = 10.0 * B * Hq * d * pairs
-        out[name] = {"ms": round(ms, 4), "algorithmic_flops": flops, "TFLOP/s": round(flops / ms / 1e9, 2),
+        out[name] = {"ms": round(ms, 4), "ms_p10_p50_p90": call_percentiles(call, reps), "algorithmic_flops": flops, "TFLOP/s": round(flops / ms / 1e9, 2),
                      "frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
         del q, k, v, g, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
@@ -454,20 +466,24 @@ def run_decode_loop(fa, synth, torch, dev, steps=5):
 
 def run_peaks(torch, dev):
     """Context for the roofline fractions: what vendor library kernels reach on this device with
-    the same kind of data (random N(0,1) bf16) -- a bf16 GEMM (hipBLASLt via torch.matmul) and a
-    device-to-device copy.  Not part of the attention path."""
+    the same kind of data (random N(0,1) bf16) -- a bf16 GEMM (hipBLASLt via torch.matmul), a
+    device-to-device copy and a read-only reduction (torch.sum).  Not part of the attention path."""
     log("leg: device ceilings")
     n = 8192
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     gemm = lambda: torch.matmul(a, b)
     ms_g = time_steps(gemm, 20, 3)
-    x = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    x = torch.full((1 << 31,), 1, dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
     copy = lambda: y.copy_(x)
     ms_c = time_steps(copy, 20, 3)
+    xf = x.view(torch.float32)
+    read = lambda: torch.sum(xf)
+    ms_r = time_steps(read, 20, 3)
     res = {"gemm_bf16_8192_TFLOP/s": round(2.0 * n ** 3 / ms_g / 1e9, 1),
-           "copy_2GiB_GB/s_read_plus_write": round(2.0 * x.numel() / ms_c / 1e6, 1)}
+           "copy_2GiB_GB/s_read_plus_write": round(2.0 * x.numel() / ms_c / 1e6, 1),
+           "sum_2GiB_GB/s_read": round(x.numel() / ms_r / 1e6, 1)}
     del a, b, x, y
     torch.cuda.empty_cache()
     return res
