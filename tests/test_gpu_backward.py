@@ -113,6 +113,11 @@ def test_dense_causal_gqa(fa):
     _run_case(fa, 2, 256, 4, 2, seed=4201)
 
 
+def test_dense_causal_odd_group(fa):
+    """Three query heads per KV head (6 on 2)."""
+    _run_case(fa, 1, 300, 6, 2, seed=4251)
+
+
 def test_dense_noncausal(fa):
     """All keys visible; the ragged last key tile is masked by position."""
     _run_case(fa, 1, 200, 2, 1, causal=False, seed=4301)
@@ -136,6 +141,11 @@ def test_sparse_odd_sink(fa):
 def test_sparse_no_sink_min_window(fa):
     """No sink and a one-block window: only the diagonal blocks are visible."""
     _run_case(fa, 1, 450, 2, 1, mode=1, sink=0, window=64, seed=4701)
+
+
+def test_sparse_batch2_gqa(fa):
+    """Two sequences, 4 query heads on one KV head, sink 2 blocks, window 2 blocks, ragged end."""
+    _run_case(fa, 2, 500, 4, 1, mode=1, sink=128, window=128, seed=4751)
 
 
 def test_bf16_output_input(fa):
