@@ -236,7 +236,7 @@ size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq,
  * workspace: device, >= flux_attn_backward_workspace_size(...) bytes, 16-byte aligned; its
  * contents on entry do not matter.  Deterministic: no atomics on gradients, fixed summation order.
  * P and dS enter the matrix products as bf16 (fp32 accumulation), as the forward's P does.
- * Supported: in_dtype BF16, head_dim 128, block 64.
+ * Supported: in_dtype BF16, head_dim 64 or 128, block 64.
  */
 int flux_attn_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
                        const float* lse, float* dq, float* dk, float* dv, int32_t in_dtype,

@@ -1,4 +1,4 @@
-// backward.hip -- gradients of tiled attention on gfx950 (bf16 inputs, head_dim 128, fp32 gradients).
+// backward.hip -- gradients of tiled attention on gfx950 (bf16 inputs, head_dim 64 or 128, fp32 gradients).
 //
 // With P the probabilities of one attention row (rebuilt from Q, K and the row log-sum-exp the
 // forward pass keeps), the chain rule through the softmax gives, per (batch, query head):
@@ -41,22 +41,34 @@ namespace {
 
 using namespace tile;
 
-constexpr int kD = 128;
-constexpr int kNC = kD / 16;          // 16-wide d chunks: contraction steps of S and dP
-constexpr int kNM = kD / 32;          // 32-row d tiles of the transposed gradients
-constexpr int kRowB = kD * 2;         // bytes of one bf16 row
-constexpr int kTileB = 64 * kRowB;    // one 64-row tile
 constexpr int kStatB = 512;           // a tile's row statistics: 64 x -LSE*log2(e), then 64 x D
-constexpr int kSlotB = 2 * kTileB + kStatB;
-constexpr int kSlots = 2;            // the tile in use and the next one in flight
+constexpr int kSlots = 2;             // the tile in use and the next one in flight
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// One chunk swizzle for row reads (16 aligned rows at one logical chunk: 16 distinct physical
-// chunks) and transposing reads (4 aligned rows x 4 aligned chunks): swapping the two 2-bit halves
-// of row & 15 is a bijection on 16 rows and gives 4 aligned rows 4 distinct high halves.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// Tile geometry for head dimension D (64 or 128).
+template <int D>
+struct Geo {
+    static constexpr int NC = D / 16;                 // 16-wide d chunks: contraction steps of S and dP
+    static constexpr int NM = D / 32;                 // 32-row d tiles of the transposed gradients
+    static constexpr int ROW_B = 2 * D;               // bytes of one bf16 row
+    static constexpr int CH = ROW_B / 16;             // 16-byte chunks per row
+    static constexpr int TILE_B = 64 * ROW_B;         // one 64-row tile
+    static constexpr int SLOT_B = 2 * TILE_B + kStatB;
+    static constexpr int ROWS_PER_INST = 1024 / ROW_B;  // rows one 1 KB direct load fills
+    static constexpr int INSTS_PER_WAVE = TILE_B / 1024 / 4;   // a tile's loads, spread over 4 waves
+};
+
+// One chunk swizzle for row reads (16 aligned rows at one logical chunk: 16 distinct 16-byte bank
+// groups) and transposing reads (4 aligned rows x 4 aligned chunks).  D = 128 (16 chunks per row):
+// swap the two 2-bit halves of row & 15.  D = 64 (8 chunks, two rows per 256 bytes): rows of one
+// parity get the 8 values ((r >> 1) & 1) << 2 | ((r >> 2) & 3), and rows 4q, 4q + 2 differ in bit 2.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
 // 4-byte direct HBM -> LDS load (see load_lds_16): lane l's dword lands at lds_base + 4*l.
 __device__ __forceinline__ void load_lds_4(const void* sbase, uint32_t voff, uint32_t lds_base) {
@@ -64,25 +76,22 @@ __device__ __forceinline__ void load_lds_4(const void* sbase, uint32_t voff, uin
                  : "memory", "m0");
 }
 
-// 64 rows of kD bf16 (row r at base + r * row_stride elements, rows past last_row clamped to it)
-// into one LDS tile: row r at r * kRowB, 16-byte chunks swizzled.  16 loads of 1 KB (4 rows each),
-// 4 per wave.
+// 64 rows of D bf16 (row r at base + r * row_stride elements, rows past last_row clamped to it) into
+// one LDS tile: row r at r * ROW_B, 16-byte chunks swizzled.  TILE_B / 1 KB direct loads, a quarter of
+// them from each of the 4 waves `wave` indexes.
+template <int D>
 __device__ __forceinline__ void load_tile(const u16* base, uint32_t row_stride, int r0, int last_row, uint32_t lds,
                                           int wave, int lane) {
+    using Gm = Geo<D>;
     const u16* sb = uniform_ptr(base);
-    const int pch = lane & 15;
+    const int pch = lane % Gm::CH;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int inst = wave * 4 + i;
-        const int row = inst * 4 + (lane >> 4);
+    for (int i = 0; i < Gm::INSTS_PER_WAVE; ++i) {
+        const int inst = wave * Gm::INSTS_PER_WAVE + i;
+        const int row = inst * Gm::ROWS_PER_INST + lane / Gm::CH;
         const uint32_t grow = (uint32_t)min(r0 + row, last_row);
-        load_lds_16(sb, 2u * (grow * row_stride + 8u * (uint32_t)(pch ^ swz(row))), lds + inst * 1024);
+        load_lds_16(sb, 2u * (grow * row_stride + 8u * (uint32_t)(pch ^ swz<D>(row))), lds + inst * 1024);
     }
-}
-
-__device__ __forceinline__ bf16x8 pack8(const float* p) {
-    return bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
-                  (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -90,10 +99,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // Lane geometry of the MFMA operands (v_mfma_f32_32x32x16_bf16: lane l feeds row/column l % 32 with
 // k-slots 8(l/32) .. +7; the accumulator's register r of lane l is row 8(r/4) + 4(l/32) + r%4).
+template <int D>
 struct Lanes {
+    using Gm = Geo<D>;
     int lane, n, hh, jj, dh;
-    uint32_t rd[kNC];          // row read: row n, logical chunk 2c + hh (add 32 rows: + 32 * kRowB)
-    uint32_t trl[kNM], trh[kNM];  // transposing reads of k-step 0: rows 4hh + jj/4 (lo) and + 8 (hi)
+    uint32_t rd[Gm::NC];                // row read: row n, logical chunk 2c + hh (add 32 rows: + 32 * ROW_B)
+    uint32_t trl[Gm::NM], trh[Gm::NM];  // transposing reads of k-step 0: rows 4hh + jj/4 (lo) and + 8 (hi)
     __device__ __forceinline__ void init(int l) {
         lane = l;
         n = l & 31;
@@ -101,25 +112,25 @@ struct Lanes {
         jj = l & 15;
         dh = (l >> 4) & 1;
 #pragma unroll
-        for (int c = 0; c < kNC; ++c) rd[c] = n * kRowB + 16 * ((2 * c + hh) ^ swz(n));
+        for (int c = 0; c < Gm::NC; ++c) rd[c] = n * Gm::ROW_B + 16 * ((2 * c + hh) ^ swz<D>(n));
         const int rlo = 4 * hh + (jj >> 2), rhi = rlo + 8;
 #pragma unroll
-        for (int mt = 0; mt < kNM; ++mt) {
+        for (int mt = 0; mt < Gm::NM; ++mt) {
             const int lch = 4 * mt + 2 * dh + ((jj & 3) >> 1);
-            trl[mt] = rlo * kRowB + 16 * (lch ^ swz(rlo)) + 8 * (jj & 1);
-            trh[mt] = rhi * kRowB + 16 * (lch ^ swz(rhi)) + 8 * (jj & 1);
+            trl[mt] = rlo * Gm::ROW_B + 16 * (lch ^ swz<D>(rlo)) + 8 * (jj & 1);
+            trh[mt] = rhi * Gm::ROW_B + 16 * (lch ^ swz<D>(rhi)) + 8 * (jj & 1);
         }
     }
     // A operand X^T[32mt + l%32][16kk + k-slots] of a 64-row tile X (k-slot e of lane half hh is
     // row 16kk + 8(e/4) + 4hh + e%4, matching the accumulator layout of the B operand).
     __device__ __forceinline__ bf16x8 tr(const char* tile, int kk, int mt) const {
-        const i16x4 lo = read_tr16(tile + kk * 16 * kRowB + trl[mt]);
-        const i16x4 hi = read_tr16(tile + kk * 16 * kRowB + trh[mt]);
+        const i16x4 lo = read_tr16(tile + kk * 16 * Gm::ROW_B + trl[mt]);
+        const i16x4 hi = read_tr16(tile + kk * 16 * Gm::ROW_B + trh[mt]);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
     // A operand X[32half + l%32][16c + 8(l/32) .. +7] of a 64-row tile X
     __device__ __forceinline__ bf16x8 row(const char* tile, int half, int c) const {
-        return *reinterpret_cast<const bf16x8*>(tile + half * 32 * kRowB + rd[c]);
+        return *reinterpret_cast<const bf16x8*>(tile + half * 32 * Gm::ROW_B + rd[c]);
     }
 };
 
@@ -145,19 +156,22 @@ struct Queue {
 };
 
 // ------------------------------------------------------------------ row statistics
+template <int D>
 __global__ void __launch_bounds__(256) bwd_rowstat_kernel(BackwardArgs a) {
+    constexpr int LPR = D / 8;            // lanes per row, 8 elements (16 bytes) each
+    constexpr int RPB = 256 / LPR;        // rows per block
     if (blockIdx.x == 0 && threadIdx.x < 2) a.counters[threadIdx.x] = 0;
     const int padded = a.n_qblk * 64;
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int c = threadIdx.x & 15;
-    if (row >= a.batch * padded * a.hq) return;   // all 16 lanes of a row leave together
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int c = threadIdx.x % LPR;
+    if (row >= a.batch * padded * a.hq) return;   // all lanes of a row leave together
     const int h = (int)(row % a.hq);
     const int64_t rest = row / a.hq;
     const int i = (int)(rest % padded);
     const int64_t b = rest / padded;
     float acc = 0.0f;
     if (i < a.seq) {
-        const int64_t off = ((b * a.seq + i) * a.hq + h) * kD + 8 * c;
+        const int64_t off = ((b * a.seq + i) * a.hq + h) * D + 8 * c;
         const uint4 g4 = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(a.d_o) + off);
         float o[8];
         if (a.o_f32) {
@@ -174,10 +188,8 @@ __global__ void __launch_bounds__(256) bwd_rowstat_kernel(BackwardArgs a) {
         acc += o[4] * bf16_lo(g4.z) + o[5] * bf16_hi(g4.z);
         acc += o[6] * bf16_lo(g4.w) + o[7] * bf16_hi(g4.w);
     }
-    acc += __shfl_xor(acc, 8, 16);
-    acc += __shfl_xor(acc, 4, 16);
-    acc += __shfl_xor(acc, 2, 16);
-    acc += __shfl_xor(acc, 1, 16);
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, LPR);
     if (c == 0) {
         float* st = a.stat + ((b * a.hq + h) * a.n_qblk + i / 64) * 128 + i % 64;
         const bool live = i < a.seq;
@@ -245,9 +257,10 @@ __device__ __forceinline__ void mfma_seq(Operand operand, Step step) {
 // acc[mt] += X^T[mt, k-steps kk0, kk0 + 1] * (hi + lo): the transposed operand of (kk, mt) is read
 // once and used by its hi and lo MFMAs; the next k-step's operand is read into the register its
 // last use frees.
-template <typename Lanes_>
-__device__ __forceinline__ void grad_product(const Lanes_& L, const char* xt, int kk0, const bf16x8* xh,
+template <int D>
+__device__ __forceinline__ void grad_product(const Lanes<D>& L, const char* xt, int kk0, const bf16x8* xh,
                                              const bf16x8* xl, f32x16* acc) {
+    constexpr int kNM = Geo<D>::NM;
     __builtin_amdgcn_s_setprio(1);
     bf16x8 ax[kNM];
 #pragma unroll
@@ -277,10 +290,13 @@ __device__ __forceinline__ void grad_product(const Lanes_& L, const char* xt, in
 // its gradient product.  That is 48 + 64 MFMAs per SIMD and tile, and each wave stays within 256
 // registers, so the two waves of a SIMD hide each other's vector work and LDS latency.
 constexpr int kKvWaves = 8;
+template <int D>
 __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs a) {
+    using Gm = Geo<D>;
+    constexpr int kNC = Gm::NC, kNM = Gm::NM, kTileB = Gm::TILE_B, kSlotB = Gm::SLOT_B;
     __shared__ __attribute__((aligned(1024))) char smem[kSlots * kSlotB];
     __shared__ int qcell[2];
-    Lanes L;
+    Lanes<D> L;
     L.init(threadIdx.x & 63);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = L.lane, n = L.n, hh = L.hh;
@@ -290,7 +306,7 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
     const int seq = (int)a.seq, nqb = a.n_qblk, G = a.hq / a.hkv;
     const int bh_total = (int)a.batch * a.hq;
     const int total = ((nqb + 1) / 2) * bh_total;
-    const uint32_t q_stride = (uint32_t)a.hq * kD;
+    const uint32_t q_stride = (uint32_t)a.hq * D;
     const float c2 = a.scale_log2;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
@@ -309,14 +325,14 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
         }
         const int nt = hi - lo + 1;
 
-        const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * kD;
-        const u16* dog = reinterpret_cast<const u16*>(a.d_o) + ((int64_t)b * a.seq * a.hq + h) * kD;
+        const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * D;
+        const u16* dog = reinterpret_cast<const u16*>(a.d_o) + ((int64_t)b * a.seq * a.hq + h) * D;
         const float* stg = a.stat + ((int64_t)b * a.hq + h) * nqb * 128;
         // a tile is 32 loads of 1 KB (Q by waves 0-3, dO by waves 4-7) plus 2 of row statistics
         auto issue = [&](int t, int slot) {
             const uint32_t base = lds0 + slot * kSlotB;
-            if (wave < 4) load_tile(qg, q_stride, 64 * t, seq - 1, base, wave, lane);
-            else load_tile(dog, q_stride, 64 * t, seq - 1, base + kTileB, wave - 4, lane);
+            if (wave < 4) load_tile<D>(qg, q_stride, 64 * t, seq - 1, base, wave, lane);
+            else load_tile<D>(dog, q_stride, 64 * t, seq - 1, base + kTileB, wave - 4, lane);
             if (wave == 0) {
                 const u16* sp = uniform_ptr(reinterpret_cast<const u16*>(stg + t * 128));
                 load_lds_4(sp, 4u * lane, base + 2 * kTileB);
@@ -329,7 +345,7 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
         bf16x8 kreg[kNC], vreg[kNC];
         {
             const int kc = min(key, seq - 1);
-            const int64_t off = (((int64_t)b * a.seq + kc) * a.hkv + g) * kD + 8 * hh;
+            const int64_t off = (((int64_t)b * a.seq + kc) * a.hkv + g) * D + 8 * hh;
             const u16* kp = reinterpret_cast<const u16*>(a.k) + off;
             const u16* vp = reinterpret_cast<const u16*>(a.v) + off;
 #pragma unroll
@@ -354,9 +370,10 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 f32x16 s = f32x16{}, dp = f32x16{};
-                mfma_seq<8>([&](int i) { return L.row(qt, hf, i); }, [&](int i, bf16x8 op) { s = MFMA(op, kreg[i], s); });
+                mfma_seq<kNC>([&](int i) { return L.row(qt, hf, i); }, [&](int i, bf16x8 op) { s = MFMA(op, kreg[i], s); });
                 if (is_dk)
-                    mfma_seq<8>([&](int i) { return L.row(dot, hf, i); }, [&](int i, bf16x8 op) { dp = MFMA(op, vreg[i], dp); });
+                    mfma_seq<kNC>([&](int i) { return L.row(dot, hf, i); },
+                                  [&](int i, bf16x8 op) { dp = MFMA(op, vreg[i], dp); });
                 float x[16];   // P, then dS = P (dP - D) for the dK role
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
@@ -403,8 +420,8 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
         // lane holds column key, rows d = 32mt + 8(r/4) + 4hh + r%4
         if (key < seq) {
             float* dst;
-            if (G == 1) dst = (is_dk ? a.dk : a.dv) + (((int64_t)b * a.seq + key) * a.hkv + g) * kD;
-            else dst = (is_dk ? a.dk_part : a.dv_part) + (((int64_t)b * a.seq + key) * a.hq + h) * kD;
+            if (G == 1) dst = (is_dk ? a.dk : a.dv) + (((int64_t)b * a.seq + key) * a.hkv + g) * D;
+            else dst = (is_dk ? a.dk_part : a.dv_part) + (((int64_t)b * a.seq + key) * a.hq + h) * D;
             const float f = is_dk ? a.scale : 1.0f;
 #pragma unroll
             for (int mt = 0; mt < kNM; ++mt)
@@ -424,10 +441,13 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
 // 4 waves of 32 queries, two workgroups per CU (two waves per SIMD).  A 64-key tile is taken in two
 // 32-key halves: S^T and dP^T (16 MFMAs, K and V rows from LDS, Q and dO rows in registers), the
 // vector work, then 16 MFMAs of dQ^T += K^T dS^T.
+template <int D>
 __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
+    using Gm = Geo<D>;
+    constexpr int kNC = Gm::NC, kNM = Gm::NM, kTileB = Gm::TILE_B, kSlotB = Gm::SLOT_B;
     __shared__ __attribute__((aligned(1024))) char smem[kSlots * 2 * kTileB];
     __shared__ int qcell[2];
-    Lanes L;
+    Lanes<D> L;
     L.init(threadIdx.x & 63);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = L.lane, n = L.n, hh = L.hh;
@@ -436,7 +456,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
     const int npair = (nqb + 1) / 2;
     const int bh_total = (int)a.batch * a.hq;
     const int total = npair * bh_total;
-    const uint32_t kv_stride = (uint32_t)a.hkv * kD;
+    const uint32_t kv_stride = (uint32_t)a.hkv * D;
     const float c2 = a.scale_log2;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
@@ -461,13 +481,13 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
         }
         const int nt = e0 + (hi - w0 + 1);
 
-        const u16* kg = reinterpret_cast<const u16*>(a.k) + ((int64_t)b * a.seq * a.hkv + g) * kD;
-        const u16* vg = reinterpret_cast<const u16*>(a.v) + ((int64_t)b * a.seq * a.hkv + g) * kD;
+        const u16* kg = reinterpret_cast<const u16*>(a.k) + ((int64_t)b * a.seq * a.hkv + g) * D;
+        const u16* vg = reinterpret_cast<const u16*>(a.v) + ((int64_t)b * a.seq * a.hkv + g) * D;
         auto kb_of = [&](int i) { return i < e0 ? i : w0 + (i - e0); };
         auto issue = [&](int kb, int slot) {
             const uint32_t base = lds0 + slot * 2 * kTileB;
-            load_tile(kg, kv_stride, 64 * kb, seq - 1, base, wave, lane);
-            load_tile(vg, kv_stride, 64 * kb, seq - 1, base + kTileB, wave, lane);
+            load_tile<D>(kg, kv_stride, 64 * kb, seq - 1, base, wave, lane);
+            load_tile<D>(vg, kv_stride, 64 * kb, seq - 1, base + kTileB, wave, lane);
         };
         issue(kb_of(0), 0);
 
@@ -476,7 +496,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
         float nl = -INFINITY, dd = 0.0f;
         {
             const int qc = min(qpos, seq - 1);
-            const int64_t off = (((int64_t)b * a.seq + qc) * a.hq + h) * kD + 8 * hh;
+            const int64_t off = (((int64_t)b * a.seq + qc) * a.hq + h) * D + 8 * hh;
             const u16* qp = reinterpret_cast<const u16*>(a.q) + off;
             const u16* dop = reinterpret_cast<const u16*>(a.d_o) + off;
 #pragma unroll
@@ -503,9 +523,9 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
             for (int kh = 0; kh < 2; ++kh) {
                 // S^T = K Q^T, dP^T = V dO^T: lane = query n, registers = keys 32kh + 8(r/4) + 4hh + r%4
                 f32x16 s = f32x16{}, dp = f32x16{};
-                mfma_seq<16>([&](int i) { return L.row(i < 8 ? kt : vt, kh, i & 7); }, [&](int i, bf16x8 op) {
-                    if (i < 8) s = MFMA(op, qreg[i], s);
-                    else dp = MFMA(op, doreg[i & 7], dp);
+                mfma_seq<2 * kNC>([&](int i) { return L.row(i < kNC ? kt : vt, kh, i % kNC); }, [&](int i, bf16x8 op) {
+                    if (i < kNC) s = MFMA(op, qreg[i], s);
+                    else dp = MFMA(op, doreg[i - kNC], dp);
                 });
                 float x[16];   // P, then dS = P (dP - D)
 #pragma unroll
@@ -542,7 +562,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
 
         // lane holds column query, rows d = 32mt + 8(r/4) + 4hh + r%4
         if (qpos < seq) {
-            float* dqp = a.dq + (((int64_t)b * a.seq + qpos) * a.hq + h) * kD;
+            float* dqp = a.dq + (((int64_t)b * a.seq + qpos) * a.hq + h) * D;
 #pragma unroll
             for (int mt = 0; mt < kNM; ++mt)
 #pragma unroll
@@ -561,21 +581,22 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
 
 // ------------------------------------------------------------------ grouped-query sum
 // out[b, s, g, :] = sum over j < G of part[b, s, g*G + j, :], j ascending; blockIdx.y picks dK / dV.
+template <int D>
 __global__ void __launch_bounds__(256) bwd_group_sum_kernel(BackwardArgs a) {
     const int G = a.hq / a.hkv;
     const float* part = blockIdx.y == 0 ? a.dk_part : a.dv_part;
     float* out = blockIdx.y == 0 ? a.dk : a.dv;
-    const int64_t n4 = a.batch * a.seq * a.hkv * (kD / 4);
+    const int64_t n4 = a.batch * a.seq * a.hkv * (D / 4);
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n4) return;
-    const int d4 = (int)(i % (kD / 4));
-    const int64_t rg = i / (kD / 4);          // (b, s, g)
+    const int d4 = (int)(i % (D / 4));
+    const int64_t rg = i / (D / 4);          // (b, s, g)
     const int g = (int)(rg % a.hkv);
     const int64_t bs = rg / a.hkv;
-    const float4* src = reinterpret_cast<const float4*>(part + (bs * a.hq + (int64_t)g * G) * kD) + d4;
+    const float4* src = reinterpret_cast<const float4*>(part + (bs * a.hq + (int64_t)g * G) * D) + d4;
     float4 acc = src[0];
     for (int j = 1; j < G; ++j) {
-        const float4 x = src[j * (kD / 4)];
+        const float4 x = src[j * (D / 4)];
         acc.x += x.x;
         acc.y += x.y;
         acc.z += x.z;
@@ -586,21 +607,32 @@ __global__ void __launch_bounds__(256) bwd_group_sum_kernel(BackwardArgs a) {
 
 }  // namespace
 
-hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
-    if (a.head_dim != kD) return hipErrorInvalidValue;
+namespace {
+
+template <int D>
+hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     const int64_t rows = a.batch * (int64_t)a.n_qblk * 64 * a.hq;
-    hipLaunchKernelGGL(bwd_rowstat_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
+    constexpr int rpb = 256 / (D / 8);
+    hipLaunchKernelGGL(bwd_rowstat_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, a);
     const int64_t units = ((a.n_qblk + 1) / 2) * a.batch * (int64_t)a.hq;
     const int cu = a.num_cu > 0 ? a.num_cu : 256;
     const unsigned grid_kv = (unsigned)(units < cu ? units : cu);              // one 8-wave group per CU
     const unsigned grid_q = (unsigned)(units < 2 * cu ? units : 2 * cu);      // two 4-wave groups per CU
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(grid_kv), dim3(64 * kKvWaves), 0, s, a);
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid_q), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid_kv), dim3(64 * kKvWaves), 0, s, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid_q), dim3(kThreads), 0, s, a);
     if (a.hq != a.hkv) {
-        const int64_t n4 = a.batch * a.seq * a.hkv * (kD / 4);
-        hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((n4 + 255) / 256), 2), dim3(256), 0, s, a);
+        const int64_t n4 = a.batch * a.seq * a.hkv * (D / 4);
+        hipLaunchKernelGGL(bwd_group_sum_kernel<D>, dim3((unsigned)((n4 + 255) / 256), 2), dim3(256), 0, s, a);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
+    if (a.head_dim == 128) return launch_backward_d<128>(a, s);
+    if (a.head_dim == 64) return launch_backward_d<64>(a, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace flux

@@ -525,8 +525,8 @@ int flux_attn_backward(const void* q, const void* k, const void* v, const void* 
     int st = check_mask_spec(seq, seq, block, sink_tokens, window_tokens, causal, mode, &ms);
     if (st != FLUX_OK) return st;
     if (in_dtype != FLUX_DTYPE_BF16) return fail(FLUX_ERR_UNSUPPORTED, "the backward pass takes bfloat16 inputs");
-    if (head_dim != 128) return fail(FLUX_ERR_UNSUPPORTED, "head_dim %d not supported by the backward pass (128)",
-                                     head_dim);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FLUX_ERR_UNSUPPORTED, "head_dim %d not supported by the backward pass (64 or 128)", head_dim);
     if (block != flux::kBlock) return fail(FLUX_ERR_UNSUPPORTED, "block %d not supported (64)", block);
     if (batch * (int64_t)hq * ceil_div(seq, 64) * 64 > INT32_MAX)
         return fail(FLUX_ERR_UNSUPPORTED, "batch * hq * seq exceeds the work-unit range");

@@ -300,7 +300,7 @@ def test_backward_validation(fa):
     assert bwd(mode=1, window=0) == E
     assert bwd(o_dtype=2) == E
     assert bwd(in_dtype=1) == U
-    assert bwd(d=64) == U
+    assert bwd(d=96) == U
     assert bwd(block=32) == U
     assert bwd(ws_bytes=100) == fa.FLUX_ERR_WORKSPACE
     assert bwd(ws=None) == fa.FLUX_ERR_WORKSPACE

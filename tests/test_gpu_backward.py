@@ -30,9 +30,9 @@ def fa():
     return fa
 
 
-def _inputs(B, S, Hq, Hkv, seed):
-    q, k, v = synth.qkv_bf16(B, S, Hq, Hkv, D, seed)
-    g = synth.normal_bf16_bits((B, S, Hq, D), seed, tensor_id=7)
+def _inputs(B, S, Hq, Hkv, seed, d=D):
+    q, k, v = synth.qkv_bf16(B, S, Hq, Hkv, d, seed)
+    g = synth.normal_bf16_bits((B, S, Hq, d), seed, tensor_id=7)
     return q, k, v, g
 
 
@@ -43,8 +43,8 @@ def _oracle_forward(q, k, v, scale, causal, sparse, sink, window):
 
 
 def _gpu_forward(fa, qd, kd, vd, causal, mode, sink, window, o_dtype=torch.float32):
-    B, S, Hq, _ = qd.shape
-    o = torch.empty((B, S, Hq, D), dtype=o_dtype, device=DEV)
+    B, S, Hq, d = qd.shape
+    o = torch.empty((B, S, Hq, d), dtype=o_dtype, device=DEV)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
     rp = ci = None
     if mode == fa.FLUX_MODE_SPARSE:
@@ -56,11 +56,11 @@ def _gpu_forward(fa, qd, kd, vd, causal, mode, sink, window, o_dtype=torch.float
 
 
 def _backward(fa, qd, kd, vd, od, gd, lsed, causal, mode, sink, window):
-    B, S, Hq, _ = qd.shape
+    B, S, Hq, d = qd.shape
     Hkv = kd.shape[2]
-    dq = torch.empty((B, S, Hq, D), dtype=torch.float32, device=DEV)
-    dk = torch.empty((B, S, Hkv, D), dtype=torch.float32, device=DEV)
-    dv = torch.empty((B, S, Hkv, D), dtype=torch.float32, device=DEV)
+    dq = torch.empty((B, S, Hq, d), dtype=torch.float32, device=DEV)
+    dk = torch.empty((B, S, Hkv, d), dtype=torch.float32, device=DEV)
+    dv = torch.empty((B, S, Hkv, d), dtype=torch.float32, device=DEV)
     fa.flux_attn_backward(qd, kd, vd, od, gd, lsed, dq, dk, dv, causal=causal, mode=mode, block=64,
                           sink_tokens=sink, window_tokens=window)
     torch.cuda.synchronize()
@@ -68,12 +68,12 @@ def _backward(fa, qd, kd, vd, od, gd, lsed, causal, mode, sink, window):
 
 
 def _run_case(fa, B, S, Hq, Hkv, seed, causal=True, mode=0, sink=0, window=0, gpu_forward=False, o_bf16=False,
-              max_abs=None):
-    say("backward", f"B={B} S={S} Hq={Hq} Hkv={Hkv} seed={seed} causal={causal} mode={mode} sink={sink} "
+              max_abs=None, d=D):
+    say("backward", f"B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} seed={seed} causal={causal} mode={mode} sink={sink} "
         f"window={window} gpu_forward={gpu_forward} o_bf16={o_bf16}")
-    scale = default_scale(D)
+    scale = default_scale(d)
     sparse = mode == 1
-    q, k, v, g = _inputs(B, S, Hq, Hkv, seed)
+    q, k, v, g = _inputs(B, S, Hq, Hkv, seed, d)
     qd, kd, vd, gd = (synth.torch_bf16_from_bits(x) for x in (q, k, v, g))
     if gpu_forward:
         od, lsed = _gpu_forward(fa, qd, kd, vd, causal, mode, sink, window,
@@ -85,7 +85,7 @@ def _run_case(fa, B, S, Hq, Hkv, seed, causal=True, mode=0, sink=0, window=0, gp
     dq, dk, dv = _backward(fa, qd, kd, vd, od, gd, lsed, causal, mode, sink, window)
     rq, rk, rv = oracle.attention_backward(q, k, v, g, scale, causal=causal, sparse=sparse, block=64,
                                            sink_tokens=sink, window_tokens=window)
-    tag = f"S={S} Hq={Hq} Hkv={Hkv} mode={mode}"
+    tag = f"S={S} Hq={Hq} Hkv={Hkv} d={d} mode={mode}"
     errs = [_close(t.cpu().numpy(), r, f"{name} {tag}", max_abs)
             for name, t, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv))]
     say("max/mean abs err", " ".join(f"{e[0]:.2e}/{e[1]:.1e}" for e in errs))
@@ -125,6 +125,17 @@ def test_dense_noncausal(fa):
 
 def test_dense_causal_longer(fa):
     _run_case(fa, 1, 1100, 2, 1, seed=4401)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_head_dim_64(fa, causal):
+    """head_dim 64 (the tiny layer's width), GQA 4 on 2, ragged end."""
+    _run_case(fa, 1, 330, 4, 2, causal=causal, seed=4351, d=64)
+
+
+def test_head_dim_64_sparse(fa):
+    """head_dim 64, block-sparse with the tiny layer's pattern (sink 2 blocks, window 2 blocks)."""
+    _run_case(fa, 1, 512, 2, 2, mode=1, sink=128, window=128, seed=4361, d=64)
 
 
 # ------------------------------------------------------------- block-sparse
