@@ -13,10 +13,11 @@
 // Kernels, in stream order:
 //   bwd_rowstat_kernel    D and -LSE*log2(e) per query row, in 64-row tiles (rows past the end get
 //                         (-inf, 0), so they weigh nothing); clears the two work-queue heads.
-//   bwd_dkdv_kernel       one work unit = 128 keys (4 waves x 32) and one query head; walks the
-//                         64-query tiles that see those keys: S = Q K^T and dP = dO V^T with K, V
-//                         held in registers (keys in lanes), then dV^T += dO^T P and dK^T += Q^T dS
-//                         with the Q and dO tiles read transposed from LDS.
+//   bwd_dkdv_kernel       one work unit = 128 keys (4 groups of 32) and one query head, 8 waves: per
+//                         key group one wave accumulates dV, one dK; they walk the 64-query tiles
+//                         that see those keys: S = Q K^T (and dP = dO V^T) with K, V held in
+//                         registers (keys in lanes), then dV^T += dO^T P or dK^T += Q^T dS with the
+//                         dO or Q tile read transposed from LDS.
 //   bwd_dq_kernel         one work unit = 128 queries (4 waves x 32) of one query head; walks the
 //                         visible 64-key tiles: S^T = K Q^T and dP^T = V dO^T with Q, dO in
 //                         registers (queries in lanes), then dQ^T += K^T dS^T.
@@ -26,8 +27,7 @@
 // needs no atomics: every gradient element is written once, summed in a fixed order.
 //
 // P and dS enter the gradient products as a bf16 pair hi + lo (hi = x truncated to bf16, lo =
-// bf16(x - hi)):
-// the sums over up to seq rows of bf16-rounded P or dS alone would carry a relative error of
+// bf16(x - hi)): the sums over up to seq rows of bf16-rounded P or dS alone would carry a relative error of
 // 2^-9 per term, about 1e-2 absolute on gradients of size 5; the pair brings it near 2^-16 at the
 // cost of a second MFMA on the same A operand.
 //
@@ -286,9 +286,10 @@ __device__ __forceinline__ void grad_product(const Lanes<D>& L, const char* xt, 
 //
 // 8 waves, two per SIMD, on 128 keys: waves w and w + 4 own the same 32 keys; wave w accumulates
 // dV^T (it needs S and P only), wave w + 4 accumulates dK^T (S, dP and dS).  Each takes a 64-query
-// tile in two 32-query halves: S (8 MFMAs; dP, 8 more, for dK), the vector work, then 16 MFMAs of
-// its gradient product.  That is 48 + 64 MFMAs per SIMD and tile, and each wave stays within 256
-// registers, so the two waves of a SIMD hide each other's vector work and LDS latency.
+// tile in two 32-query halves: S (D/16 MFMAs; dP, as many more, for dK), the vector work, then
+// 4 * D/32 MFMAs of its gradient product.  At D = 128 that is 48 + 64 MFMAs per SIMD and tile, and
+// each wave stays within 256 registers, so the two waves of a SIMD hide each other's vector work
+// and LDS latency.
 constexpr int kKvWaves = 8;
 template <int D>
 __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs a) {
@@ -439,8 +440,8 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
 // ------------------------------------------------------------------ dQ
 //
 // 4 waves of 32 queries, two workgroups per CU (two waves per SIMD).  A 64-key tile is taken in two
-// 32-key halves: S^T and dP^T (16 MFMAs, K and V rows from LDS, Q and dO rows in registers), the
-// vector work, then 16 MFMAs of dQ^T += K^T dS^T.
+// 32-key halves: S^T and dP^T (D/8 MFMAs, K and V rows from LDS, Q and dO rows in registers), the
+// vector work, then 4 * D/32 MFMAs of dQ^T += K^T dS^T.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
     using Gm = Geo<D>;
