@@ -172,17 +172,18 @@ def test_after_gpu_forward(fa, mode):
 
 
 # ------------------------------------------------------------- full layer shape
-@pytest.mark.parametrize("mode", [0, 1])
-def test_full_shape_prefix_and_identities(fa, mode):
-    """seq 8192, 32 query heads on 8 KV heads (the layer shape of the prefill workload).
+@pytest.mark.parametrize("S,mode", [(8192, 0), (8192, 1), (65536, 1)])
+def test_full_shape_prefix_and_identities(fa, S, mode):
+    """seq 8192 (dense and sparse) and seq 65536 sparse, 32 query heads on 8 KV heads: the shapes the
+    benchmark times.
     dQ of the first T rows equals the backward of the length-T prefix (causal); dK, dV are checked
     against sum_j dV_j = sum over the group's heads of sum_i dO_i (rows of P sum to one) and
     sum_j dK_j = 0 (rows of dS sum to zero); a second run must be bit-identical."""
-    B, S, Hq, Hkv, T = 1, 8192, 32, 8, 384
+    B, Hq, Hkv, T = 1, 32, 8, 384
     sink, window = (128, 2048) if mode == 1 else (0, 0)
-    say("backward full shape", f"mode={mode}")
+    say("backward full shape", f"S={S} mode={mode}")
     scale = default_scale(D)
-    q, k, v, g = _inputs(B, S, Hq, Hkv, seed=4901 + mode)
+    q, k, v, g = _inputs(B, S, Hq, Hkv, seed=4901 + mode + S)
     qd, kd, vd, gd = (synth.torch_bf16_from_bits(x) for x in (q, k, v, g))
     od, lsed = _gpu_forward(fa, qd, kd, vd, True, mode, sink, window)
     dq, dk, dv = _backward(fa, qd, kd, vd, od, gd, lsed, True, mode, sink, window)
@@ -208,5 +209,7 @@ def test_full_shape_prefix_and_identities(fa, mode):
     err_v = float(np.abs(got_dv - want_dv).max())
     err_k = float(np.abs(got_dk).max())
     say("identities", f"sum dV err {err_v:.3e} (scale {mag_v:.1f}), sum dK {err_k:.3e} (scale {mag_k:.1f})")
-    assert err_v <= 2e-3 * mag_v, err_v
-    assert err_k <= 2e-3 * mag_k, err_k
+    # dV's identity is exact up to the rounding of the sums (measured ~1e-6 of the scale); dK's also carries
+    # the forward's rounding of O through D = rowsum(dO * O) (measured ~1e-4 of the scale)
+    assert err_v <= 2e-5 * mag_v, err_v
+    assert err_k <= 1e-3 * mag_k, err_k
