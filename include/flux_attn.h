@@ -223,11 +223,11 @@ size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq,
  * router training over a frozen backbone needs).  P is rebuilt tile by tile from Q, K and the
  * forward pass's lse; inactive blocks of the sparse pattern are skipped and never read.  With
  * grouped-query attention the query heads sharing a KV head add into its dK/dV (head order).
- *   q, d_o    [batch, seq, hq,  head_dim]  device bf16 (d_o: dL/dO)
+ *   q, d_o    [batch, seq, hq,  head_dim]  device, in_dtype (d_o: dL/dO)
  *   o         [batch, seq, hq,  head_dim]  device, o_dtype BF16 or F32: the forward output (only
  *                                          D = rowsum(dO * O) reads it; an fp32 O keeps D exact
  *                                          to fp32, a bf16 O perturbs D by its rounding)
- *   k, v      [batch, seq, hkv, head_dim]  device bf16
+ *   k, v      [batch, seq, hkv, head_dim]  device, in_dtype
  *   lse       [batch, hq, seq]             device fp32, as written by flux_attn_prefill
  *   dq        [batch, seq, hq,  head_dim]  device fp32 (written)
  *   dk, dv    [batch, seq, hkv, head_dim]  device fp32 (written, not accumulated into)
@@ -235,8 +235,10 @@ size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq,
  * is derived from (block, sink_tokens, window_tokens), the pattern flux_build_block_mask builds.
  * workspace: device, >= flux_attn_backward_workspace_size(...) bytes, 16-byte aligned; its
  * contents on entry do not matter.  Deterministic: no atomics on gradients, fixed summation order.
- * P and dS enter the matrix products as bf16 (fp32 accumulation), as the forward's P does.
- * Supported: in_dtype BF16, head_dim 64 or 128, block 64.
+ * in_dtype BF16: q, k, v, d_o bf16, matrix-core kernels; P and dS enter the matrix products as a
+ * bf16 hi + lo pair (fp32 accumulation).  in_dtype F32: q, k, v, d_o float32, vector-ALU kernels
+ * for small layers (as the float32 forward).
+ * Supported: head_dim 64 or 128, block 64.
  */
 int flux_attn_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
                        const float* lse, float* dq, float* dk, float* dv, int32_t in_dtype,

@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libflux_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["flux_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "router.hip", "backward.hip"]
+SOURCES = ["flux_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "router.hip", "backward.hip", "backward_f32.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]

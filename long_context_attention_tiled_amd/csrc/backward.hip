@@ -12,7 +12,8 @@
 //
 // Kernels, in stream order:
 //   bwd_rowstat_kernel    D and -LSE*log2(e) per query row, in 64-row tiles (rows past the end get
-//                         (-inf, 0), so they weigh nothing); clears the two work-queue heads.
+//                         (-inf, 0), so they weigh nothing); clears the two work-queue heads.  It also
+//                         serves the float32 kernels of backward_f32.hip.
 //   bwd_dkdv_kernel       one work unit = 128 keys (4 groups of 32) and one query head, 8 waves: per
 //                         key group one wave accumulates dV, one dK; they walk the 64-query tiles
 //                         that see those keys: S = Q K^T (and dP = dO V^T) with K, V held in
@@ -172,7 +173,16 @@ __global__ void __launch_bounds__(256) bwd_rowstat_kernel(BackwardArgs a) {
     float acc = 0.0f;
     if (i < a.seq) {
         const int64_t off = ((b * a.seq + i) * a.hq + h) * D + 8 * c;
-        const uint4 g4 = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(a.d_o) + off);
+        float gv[8];
+        if (a.in_f32) {
+            const float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.d_o) + off);
+            const float4 y = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.d_o) + off + 4);
+            gv[0] = x.x; gv[1] = x.y; gv[2] = x.z; gv[3] = x.w; gv[4] = y.x; gv[5] = y.y; gv[6] = y.z; gv[7] = y.w;
+        } else {
+            const uint4 x = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(a.d_o) + off);
+            gv[0] = bf16_lo(x.x); gv[1] = bf16_hi(x.x); gv[2] = bf16_lo(x.y); gv[3] = bf16_hi(x.y);
+            gv[4] = bf16_lo(x.z); gv[5] = bf16_hi(x.z); gv[6] = bf16_lo(x.w); gv[7] = bf16_hi(x.w);
+        }
         float o[8];
         if (a.o_f32) {
             const float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.o) + off);
@@ -183,10 +193,10 @@ __global__ void __launch_bounds__(256) bwd_rowstat_kernel(BackwardArgs a) {
             o[0] = bf16_lo(x.x); o[1] = bf16_hi(x.x); o[2] = bf16_lo(x.y); o[3] = bf16_hi(x.y);
             o[4] = bf16_lo(x.z); o[5] = bf16_hi(x.z); o[6] = bf16_lo(x.w); o[7] = bf16_hi(x.w);
         }
-        acc = o[0] * bf16_lo(g4.x) + o[1] * bf16_hi(g4.x);
-        acc += o[2] * bf16_lo(g4.y) + o[3] * bf16_hi(g4.y);
-        acc += o[4] * bf16_lo(g4.z) + o[5] * bf16_hi(g4.z);
-        acc += o[6] * bf16_lo(g4.w) + o[7] * bf16_hi(g4.w);
+        acc = o[0] * gv[0] + o[1] * gv[1];
+        acc += o[2] * gv[2] + o[3] * gv[3];
+        acc += o[4] * gv[4] + o[5] * gv[5];
+        acc += o[6] * gv[6] + o[7] * gv[7];
     }
 #pragma unroll
     for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, LPR);
@@ -445,7 +455,7 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
     using Gm = Geo<D>;
-    constexpr int kNC = Gm::NC, kNM = Gm::NM, kTileB = Gm::TILE_B, kSlotB = Gm::SLOT_B;
+    constexpr int kNC = Gm::NC, kNM = Gm::NM, kTileB = Gm::TILE_B;
     __shared__ __attribute__((aligned(1024))) char smem[kSlots * 2 * kTileB];
     __shared__ int qcell[2];
     Lanes<D> L;
@@ -615,6 +625,7 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     const int64_t rows = a.batch * (int64_t)a.n_qblk * 64 * a.hq;
     constexpr int rpb = 256 / (D / 8);
     hipLaunchKernelGGL(bwd_rowstat_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, a);
+    if (a.in_f32) return launch_backward_f32(a, s);   // float32 inputs: vector-ALU kernels
     const int64_t units = ((a.n_qblk + 1) / 2) * a.batch * (int64_t)a.hq;
     const int cu = a.num_cu > 0 ? a.num_cu : 256;
     const unsigned grid_kv = (unsigned)(units < cu ? units : cu);              // one 8-wave group per CU

@@ -524,7 +524,6 @@ int flux_attn_backward(const void* q, const void* k, const void* v, const void* 
     MaskSpec ms;
     int st = check_mask_spec(seq, seq, block, sink_tokens, window_tokens, causal, mode, &ms);
     if (st != FLUX_OK) return st;
-    if (in_dtype != FLUX_DTYPE_BF16) return fail(FLUX_ERR_UNSUPPORTED, "the backward pass takes bfloat16 inputs");
     if (head_dim != 64 && head_dim != 128)
         return fail(FLUX_ERR_UNSUPPORTED, "head_dim %d not supported by the backward pass (64 or 128)", head_dim);
     if (block != flux::kBlock) return fail(FLUX_ERR_UNSUPPORTED, "block %d not supported (64)", block);
@@ -573,6 +572,7 @@ int flux_attn_backward(const void* q, const void* k, const void* v, const void* 
     a.n_qblk = (int)ceil_div(seq, 64);
     a.num_cu = device_cu_count();
     a.o_f32 = o_dtype == FLUX_DTYPE_F32;
+    a.in_f32 = in_dtype == FLUX_DTYPE_F32;
     hipError_t e = flux::launch_backward(a, as_stream(hip_stream));
     if (e == hipSuccess) e = hipGetLastError();
     return hip_status(e, "backward launch");

@@ -117,6 +117,7 @@ struct BackwardArgs {
     int n_qblk;            // ceil(seq / 64)
     int num_cu;            // persistent grid size
     int o_f32;
+    int in_f32;            // q, k, v, d_o float32 (vector-ALU path) instead of bf16
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
@@ -126,5 +127,6 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_route_soft(const float* logits, const float* uniforms, float tau, int n_layers, float* weights,
                              hipStream_t s);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
+hipError_t launch_backward_f32(const BackwardArgs& a, hipStream_t s);
 
 }  // namespace flux

@@ -299,7 +299,6 @@ def test_backward_validation(fa):
     assert bwd(mode=1, sink=100) == E
     assert bwd(mode=1, window=0) == E
     assert bwd(o_dtype=2) == E
-    assert bwd(in_dtype=1) == U
     assert bwd(d=96) == U
     assert bwd(block=32) == U
     assert bwd(ws_bytes=100) == fa.FLUX_ERR_WORKSPACE

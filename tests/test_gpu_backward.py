@@ -164,6 +164,40 @@ def test_bf16_output_input(fa):
     _run_case(fa, 1, 328, 2, 2, seed=4429, o_bf16=True, max_abs=2e-2)
 
 
+# ------------------------------------------------------------- float32 inputs (vector-ALU kernels)
+def _run_case_f32(fa, B, S, Hq, Hkv, d, seed, causal=True, mode=0, sink=0, window=0):
+    say("backward f32", f"B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} seed={seed} causal={causal} mode={mode} sink={sink} "
+        f"window={window}")
+    scale = default_scale(d)
+    sparse = mode == 1
+    q, k, v = synth.qkv_f32(B, S, Hq, Hkv, d, seed)
+    g = synth.normal_f32((B, S, Hq, d), seed, tensor_id=7)
+    o32, lse = _oracle_forward(q, k, v, scale, causal, sparse, sink, window)
+    qd, kd, vd, gd, od = (torch.from_numpy(np.ascontiguousarray(x)).to(DEV) for x in (q, k, v, g, o32))
+    lsed = torch.from_numpy(lse).to(DEV)
+    dq, dk, dv = _backward(fa, qd, kd, vd, od, gd, lsed, causal, mode, sink, window)
+    rq, rk, rv = oracle.attention_backward(q, k, v, g, scale, causal=causal, sparse=sparse, block=64,
+                                           sink_tokens=sink, window_tokens=window)
+    tag = f"f32 S={S} Hq={Hq} Hkv={Hkv} d={d} mode={mode}"
+    for name, t, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        check_close(t.cpu().numpy(), r, f"{name} {tag}")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_f32_tiny_layer(fa, mode):
+    """The tiny float32 layer: batch 1, 2 heads, head_dim 64, seq 512; dense causal, then block-sparse
+    with sink 2 blocks and window 2 blocks."""
+    _run_case_f32(fa, 1, 512, 2, 2, 64, seed=5001, mode=mode, sink=128, window=128)
+
+
+def test_f32_gqa_noncausal_ragged(fa):
+    _run_case_f32(fa, 1, 330, 4, 2, 128, seed=5011, causal=False)
+
+
+def test_f32_gqa_causal_ragged(fa):
+    _run_case_f32(fa, 2, 200, 6, 2, 128, seed=5021)
+
+
 # ------------------------------------------------------------- end to end with the GPU forward
 @pytest.mark.parametrize("mode", [0, 1])
 def test_after_gpu_forward(fa, mode):
