@@ -465,9 +465,13 @@ def run_decode_loop(fa, synth, torch, dev, steps=5):
 
 
 def run_peaks(torch, dev):
-    """Context for the roofline fractions: what vendor library kernels reach on this device with
-    the same kind of data (random N(0,1) bf16) -- a bf16 GEMM (hipBLASLt via torch.matmul), a
-    device-to-device copy and a read-only reduction (torch.sum).  Not part of the attention path."""
+    """Context for the roofline fractions: what this device reaches outside the attention path.
+    Library kernels on random N(0,1) bf16 data -- a bf16 GEMM (hipBLASLt via torch.matmul), a
+    device-to-device copy, a read-only reduction (torch.sum) -- and the micro-benchmarks of
+    ceilings/ceilings.hip: a pure MFMA loop (operands N(0,1) bf16, then the constant 1.0), a
+    streaming read of 8 GiB, and the split-KV decode's own read pattern over its 2 x 4 GiB caches
+    (32 splits, the split count the decode picks at batch 8 x 8 KV heads); plus the CU count and
+    the peak engine clock the runtime reports."""
     log("leg: device ceilings")
     n = 8192
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
@@ -484,9 +488,56 @@ def run_peaks(torch, dev):
     res = {"gemm_bf16_8192_TFLOP/s": round(2.0 * n ** 3 / ms_g / 1e9, 1),
            "copy_2GiB_GB/s_read_plus_write": round(2.0 * x.numel() / ms_c / 1e6, 1),
            "sum_2GiB_GB/s_read": round(x.numel() / ms_r / 1e6, 1)}
-    del a, b, x, y
+    del a, b, x, y, xf
     torch.cuda.empty_cache()
+    try:
+        res.update(run_microbench(torch, dev))
+    except RuntimeError as e:   # library not built: the attention legs stand without this context
+        res["microbench_error"] = str(e)
     return res
+
+
+def run_microbench(torch, dev):
+    import ctypes
+
+    import ceilings
+    lib = ceilings.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cu, clk = ctypes.c_int(0), ctypes.c_int(0)
+    ceilings.check(lib.ceil_device_info(ctypes.byref(cu), ctypes.byref(clk)), "ceil_device_info")
+    out = {"compute_units": cu.value, "peak_clock_MHz": round(clk.value / 1e3)}
+
+    def median_ms(fn, reps=10, warm=2):
+        for _ in range(warm):
+            fn()
+        return call_percentiles(fn, reps)[1]
+
+    wgs, iters = 4 * cu.value, 2000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    flops = lib.ceil_mfma_loop_flops(wgs, iters)
+    for tag, ops in (("randn", torch.randn(1 << 18, device=dev).to(torch.bfloat16)),
+                     ("const", torch.ones(1 << 18, device=dev, dtype=torch.bfloat16))):
+        n_ops = ops.numel() // 8
+        call = lambda: ceilings.check(lib.ceil_mfma_loop(ops.data_ptr(), n_ops, sink.data_ptr(), sink.numel(), wgs,
+                                                         iters, stream), "ceil_mfma_loop")
+        out[f"mfma_loop_bf16_{tag}_TFLOP/s"] = round(flops / median_ms(call) / 1e9, 1)
+    del sink
+
+    sink = torch.empty(256, dtype=torch.float32, device=dev)
+    nbytes = 8 << 30
+    buf = torch.full((nbytes,), 1, dtype=torch.uint8, device=dev)
+    call = lambda: ceilings.check(lib.ceil_read_stream(buf.data_ptr(), nbytes, sink.data_ptr(), sink.numel(),
+                                                       16 * cu.value, stream), "ceil_read_stream")
+    out["read_stream_8GiB_GB/s"] = round(nbytes / median_ms(call) / 1e6, 1)
+    B, L, H = 8, 262144, 8
+    kc = buf[: nbytes // 2].view(torch.bfloat16).view(B, L, H, 128)
+    vc = buf[nbytes // 2:].view(torch.bfloat16).view(B, L, H, 128)
+    call = lambda: ceilings.check(lib.ceil_read_decode(kc.data_ptr(), vc.data_ptr(), B, L, H, 32, sink.data_ptr(),
+                                                       sink.numel(), stream), "ceil_read_decode")
+    out["read_decode_pattern_32_splits_GB/s"] = round(nbytes / median_ms(call) / 1e6, 1)
+    del buf, kc, vc
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_stack(fa, synth, torch, dev):

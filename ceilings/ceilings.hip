@@ -1,0 +1,148 @@
+// ceilings.hip -- device micro-benchmarks that put the attention kernels' roofline fractions in context.
+//
+// Not part of the attention path: bench.py loads this library (libceilings.so) to report, next to the
+// prefill's MFMA fraction and the decode's HBM fraction, what this very device reaches on
+//   * a pure matrix-core loop: back-to-back v_mfma_f32_32x32x16_bf16 with operands held in registers,
+//     fed from a caller buffer (random N(0,1) bf16 or a constant -- the chip's clock depends on the data);
+//   * a streaming read: every byte of a buffer read once with 16-byte loads, four in flight per lane;
+//   * the split-KV decode's read pattern: caches [B, L, H, 128] bf16, workgroup = (split, KV head, batch),
+//     64 rows of 256 B per step for K and for V.
+// Plus the CU count and peak engine clock the runtime reports.
+//
+// C ABI: every function returns a hipError_t value as int (0 = success, hipErrorInvalidValue for
+// arguments that do not fit the kernel), launches on the given stream and does not synchronise it.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kMfmaThreads = 256;
+constexpr int kReadThreads = 256;
+
+// Each lane loads four A and four B operand registers once, then issues iters x 32 MFMAs cycling over four
+// independent accumulators (a dependent MFMA is four issues later, so the chain never stalls the pipe).
+__global__ __launch_bounds__(kMfmaThreads) void mfma_loop_kernel(const bf16x8* __restrict__ ops, int64_t n_ops,
+                                                                 float* __restrict__ sink, int iters) {
+    const int64_t gid = (int64_t)blockIdx.x * kMfmaThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kMfmaThreads;
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        a[j] = ops[(gid + j * stride) % n_ops];
+        b[j] = ops[(gid + (j + 4) * stride) % n_ops];
+    }
+    f32x16 c[4] = {};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 32; ++s)
+            c[s & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 3], b[(s >> 2) & 3], c[s & 3], 0, 0, 0);
+    }
+    float r = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) r += c[j][i];
+    sink[gid] = r;
+}
+
+// Workgroup w reads vectors [w*per_wg, min((w+1)*per_wg, n_vec)) of the buffer.
+__global__ __launch_bounds__(kReadThreads) void read_stream_kernel(const uint4* __restrict__ p, int64_t n_vec,
+                                                                   int64_t per_wg, float* __restrict__ sink) {
+    const int64_t begin = (int64_t)blockIdx.x * per_wg;
+    const int64_t end = begin + per_wg < n_vec ? begin + per_wg : n_vec;
+    uint32_t acc = 0;
+    for (int64_t i = begin + threadIdx.x; i < end; i += 4 * kReadThreads) {
+        const uint4 x0 = p[i];
+        const uint4 x1 = i + kReadThreads < end ? p[i + kReadThreads] : make_uint4(0, 0, 0, 0);
+        const uint4 x2 = i + 2 * kReadThreads < end ? p[i + 2 * kReadThreads] : make_uint4(0, 0, 0, 0);
+        const uint4 x3 = i + 3 * kReadThreads < end ? p[i + 3 * kReadThreads] : make_uint4(0, 0, 0, 0);
+        acc ^= x0.x ^ x0.y ^ x0.z ^ x0.w ^ x1.x ^ x1.y ^ x1.z ^ x1.w;
+        acc ^= x2.x ^ x2.y ^ x2.z ^ x2.w ^ x3.x ^ x3.y ^ x3.z ^ x3.w;
+    }
+    if (acc == 0x9e3779b9u) sink[threadIdx.x] = 1.0f;   // keeps the loads; practically never taken
+}
+
+// Decode pattern: rows of 256 B (head_dim 128 bf16), 16 lanes per row, 16 rows per pass, 4 passes = one
+// 64-key step, K and V.  Workgroup (split, h, b) covers keys [split*len, (split+1)*len).
+__global__ __launch_bounds__(kReadThreads) void read_decode_kernel(const uint4* __restrict__ k,
+                                                                   const uint4* __restrict__ v, int64_t L, int H,
+                                                                   int64_t len, float* __restrict__ sink) {
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int row = threadIdx.x >> 4, ch = threadIdx.x & 15;
+    const int64_t k0 = (int64_t)split * len;
+    uint32_t acc = 0;
+    for (int64_t t = k0; t < k0 + len; t += 64) {
+        uint4 x[4], y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t off = (((int64_t)b * L + t + row + 16 * i) * H + h) * 16 + ch;
+            x[i] = k[off];
+            y[i] = v[off];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc ^= x[i].x ^ x[i].y ^ x[i].z ^ x[i].w ^ y[i].x ^ y[i].y ^ y[i].z ^ y[i].w;
+    }
+    if (acc == 0x9e3779b9u) sink[threadIdx.x] = 1.0f;
+}
+
+}  // namespace
+
+extern "C" {
+
+// CU count and peak engine clock (kHz) of the current device.
+int ceil_device_info(int* compute_units, int* clock_khz) {
+    if (!compute_units || !clock_khz) return (int)hipErrorInvalidValue;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(compute_units, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(clock_khz, hipDeviceAttributeClockRate, dev);
+    return (int)e;
+}
+
+// FLOPs of one ceil_mfma_loop call: workgroups * 4 waves * iters * 32 MFMAs * 32768.
+double ceil_mfma_loop_flops(int32_t workgroups, int32_t iters) {
+    return (double)workgroups * (kMfmaThreads / 64) * iters * 32.0 * 32768.0;
+}
+
+// ops: n_ops 16-byte vectors of 8 bf16 (device); sink: >= workgroups*256 floats (device).
+int ceil_mfma_loop(const void* ops, int64_t n_ops, float* sink, int64_t sink_elems, int32_t workgroups,
+                   int32_t iters, void* stream) {
+    if (!ops || !sink || n_ops < 1 || workgroups < 1 || iters < 1 || (reinterpret_cast<uintptr_t>(ops) & 15u) ||
+        sink_elems < (int64_t)workgroups * kMfmaThreads)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mfma_loop_kernel, dim3(workgroups), dim3(kMfmaThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const bf16x8*>(ops), n_ops, sink, iters);
+    return (int)hipGetLastError();
+}
+
+// buf: bytes (a multiple of 16) of device memory, read once; sink: >= 256 floats.
+int ceil_read_stream(const void* buf, int64_t bytes, float* sink, int64_t sink_elems, int32_t workgroups,
+                     void* stream) {
+    if (!buf || !sink || bytes < 16 || (bytes & 15) || (reinterpret_cast<uintptr_t>(buf) & 15u) || workgroups < 1 ||
+        sink_elems < kReadThreads)
+        return (int)hipErrorInvalidValue;
+    const int64_t n_vec = bytes / 16;
+    const int64_t per_wg = (n_vec + workgroups - 1) / workgroups;
+    hipLaunchKernelGGL(read_stream_kernel, dim3(workgroups), dim3(kReadThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const uint4*>(buf), n_vec, per_wg,
+                       sink);
+    return (int)hipGetLastError();
+}
+
+// k, v: [batch, L, hkv, 128] bf16 caches (device); L must be a multiple of 64 * splits.
+int ceil_read_decode(const void* k, const void* v, int64_t batch, int64_t L, int32_t hkv, int32_t splits,
+                     float* sink, int64_t sink_elems, void* stream) {
+    if (!k || !v || !sink || batch < 1 || batch > 65535 || hkv < 1 || hkv > 65535 || splits < 1 || L < 64 ||
+        L % (64 * (int64_t)splits) != 0 || ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15u) ||
+        sink_elems < kReadThreads)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(read_decode_kernel, dim3(splits, hkv, batch), dim3(kReadThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const uint4*>(k),
+                       reinterpret_cast<const uint4*>(v), L, hkv, L / splits, sink);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

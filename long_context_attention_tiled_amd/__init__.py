@@ -50,6 +50,10 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is not built; run `python long_context_attention_tiled_amd/build.py` "
         "(hipcc for gfx950).  There is no CPU fallback.")
 
+# torch first: its HIP runtime (same soname as the system one) is then the one this library binds to, so
+# tensors, streams and our launches share one runtime whichever module the caller imported first.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 _pp = ctypes.POINTER(ctypes.c_void_p)

@@ -1,0 +1,64 @@
+"""The device micro-benchmarks bench.py reports beside the roofline fractions (ceilings/ceilings.hip).
+
+CPU: the library loads, exports its entry points and rejects arguments that do not fit its kernels
+(validation runs before any device call).  GPU: each kernel runs at a small size; the MFMA loop on
+all-ones operands must leave exactly iters * 8 MFMAs * 16 (the contraction depth) in each of its
+accumulator elements, which pins the number of MFMAs it issues (and so the FLOPs bench.py divides).
+"""
+import ctypes
+import os
+
+import pytest
+
+import ceilings
+
+HIP_INVALID_VALUE = 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ceilings.LIB_PATH):
+        pytest.skip("libceilings.so not built")
+    return ceilings.load()
+
+
+def test_exports_and_flop_count(lib):
+    for name in ceilings.SIGNATURES:
+        assert hasattr(lib, name)
+    assert lib.ceil_mfma_loop_flops(1024, 2000) == 1024 * 4 * 2000 * 32 * 2 * 32 * 32 * 16
+
+
+def test_validation_before_launch(lib):
+    assert lib.ceil_device_info(None, None) == HIP_INVALID_VALUE
+    assert lib.ceil_mfma_loop(None, 1, None, 0, 1, 1, None) == HIP_INVALID_VALUE
+    assert lib.ceil_mfma_loop(16, 1, 16, 255, 1, 1, None) == HIP_INVALID_VALUE        # sink too small
+    assert lib.ceil_read_stream(16, 24, 16, 256, 1, None) == HIP_INVALID_VALUE        # not a multiple of 16
+    assert lib.ceil_read_decode(16, 16, 1, 192, 1, 2, 16, 256, None) == HIP_INVALID_VALUE   # L % (64 splits)
+
+
+@pytest.mark.gpu
+def test_kernels_run(lib):
+    import torch
+    dev = torch.device("cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    wgs, iters = 8, 10
+    ops = torch.ones(8 * 64, dtype=torch.bfloat16, device=dev)
+    sink = torch.zeros(wgs * 256, dtype=torch.float32, device=dev)
+    assert lib.ceil_mfma_loop(ops.data_ptr(), ops.numel() // 8, sink.data_ptr(), sink.numel(), wgs, iters,
+                              stream) == 0
+    torch.cuda.synchronize()
+    assert torch.all(sink == 4 * 16 * iters * 8 * 16).item()
+
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+    small = torch.zeros(256, dtype=torch.float32, device=dev)
+    assert lib.ceil_read_stream(buf.data_ptr(), buf.numel() - 48, small.data_ptr(), 256, 7, stream) == 0
+    B, L, H = 1, 256, 2
+    kv = torch.zeros(2 * B * L * H * 128, dtype=torch.bfloat16, device=dev)
+    half = B * L * H * 128
+    assert lib.ceil_read_decode(kv.data_ptr(), kv[half:].data_ptr(), B, L, H, 2, small.data_ptr(), 256,
+                                stream) == 0
+    torch.cuda.synchronize()
+    assert torch.all(small == 0).item()
+    cu, clk = ctypes.c_int(0), ctypes.c_int(0)
+    assert lib.ceil_device_info(ctypes.byref(cu), ctypes.byref(clk)) == 0
+    assert cu.value > 0 and clk.value > 0
