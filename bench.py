@@ -115,10 +115,17 @@ def measured_traffic():
         return None
 
 
-def time_steps(step, steps, warmup):
+def time_steps(step, steps, warmup, warm_ms=100.0):
+    """Wall-clock ms per call over `steps` calls, after `warmup` calls and then more until `warm_ms` of
+    warm-up have passed (kernel times settle over the first tens of ms on a freshly busy device)."""
     import torch
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < warm_ms:
         step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -141,7 +148,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--legs", default="sparse,decode,decode_loop,soft,backward,peaks",
                     help="comma list of secondary legs: sparse, dense64k, decode, decode_loop, soft, backward, stack, "
                          "peaks "
