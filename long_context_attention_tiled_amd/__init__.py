@@ -163,6 +163,70 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _dev(t, name, shape=None, dtypes=None, like=None):
+    """Check a tensor argument before its pointer crosses the C ABI, which cannot tell a host pointer or a
+    short buffer from a good one: a contiguous GPU tensor, on the same device as `like`, of the given
+    shape and dtype(s)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (it is on {t.device})")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, the other tensors on {like.device}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {tuple(str(x) for x in dtypes)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _float_types():
+    import torch
+    return (torch.bfloat16, torch.float32)
+
+
+def _check_csr(rp, ci, seq, block, like):
+    """Device CSR from flux_build_block_mask(seq, seq, block, ...): row_ptr int32 [ceil(seq/block)+1]."""
+    import torch
+    if rp is None or ci is None:
+        return
+    _dev(rp, "blk_row_ptr", (-(-seq // block) + 1,), (torch.int32,), like)
+    _dev(ci, "blk_col_idx", None, (torch.int32,), like)
+    if ci.dim() != 1:
+        raise ValueError("blk_col_idx must be one-dimensional")
+
+
+def _check_attention(q, k, v, o, lse, like=None):
+    """q [B,S,Hq,d], k/v [B,S,Hkv,d] of q's dtype, o [B,S,Hq,d] bf16/fp32, lse [B,Hq,S] fp32 or None."""
+    import torch
+    for name, t in (("q", q), ("k", k)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [batch, seq, heads, head_dim]")
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    like = q if like is None else like
+    _dev(q, "q", None, _float_types(), like)
+    _dev(k, "k", (B, S, Hkv, d), (q.dtype,), like)
+    _dev(v, "v", (B, S, Hkv, d), (q.dtype,), like)
+    _dev(o, "o", (B, S, Hq, d), _float_types(), like)
+    if lse is not None:
+        _dev(lse, "lse", (B, Hq, S), (torch.float32,), like)
+    return B, S, Hq, Hkv, d
+
+
+def _check_workspace(ws, like):
+    import torch
+    if ws is not None:
+        _dev(ws, "workspace", None, None, like)
+        if ws.dtype != torch.uint8:
+            raise TypeError("workspace must be a uint8 tensor")
+
+
 # ------------------------------------------------------------------ entry points
 def flux_build_block_mask(seq_q: int, seq_k: int, block: int = 64, sink_tokens: int = 128, window_tokens: int = 2048,
                           causal: int = 1, mode: int = FLUX_MODE_SPARSE):
@@ -185,9 +249,8 @@ def flux_attn_prefill(q, k, v, o, lse=None, *, causal: int = 1, mode: int = FLUX
     """q [B,S,Hq,d], k/v [B,S,Hkv,d], o [B,S,Hq,d] (device tensors); lse [B,Hq,S] float32 or None.
 
     blk_row_ptr / blk_col_idx: device int32 tensors from flux_build_block_mask (sparse mode)."""
-    _contig(q, k, v, o, lse)
-    B, S, Hq, d = q.shape
-    Hkv = k.shape[2]
+    B, S, Hq, Hkv, d = _check_attention(q, k, v, o, lse)
+    _check_csr(blk_row_ptr, blk_col_idx, S, block, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     nnz = int(blk_col_idx.numel()) if blk_col_idx is not None else 0
@@ -201,15 +264,29 @@ def _ptr_array(ts):
     return ctypes.cast(arr, _pp), arr
 
 
+def _check_layers(qs, ks, vs, os_, lses):
+    L = len(qs)
+    if L < 1 or not (len(ks) == len(vs) == len(os_) == L) or (lses is not None and len(lses) != L):
+        raise ValueError("qs, ks, vs, os_ (and lses) must hold one tensor per layer")
+    dims = _check_attention(qs[0], ks[0], vs[0], os_[0], None if lses is None else lses[0])
+    for l in range(1, L):
+        _check_attention(qs[l], ks[l], vs[l], os_[l], None if lses is None else lses[l], like=qs[0])
+        if tuple(qs[l].shape) != tuple(qs[0].shape) or tuple(ks[l].shape) != tuple(ks[0].shape) or \
+                qs[l].dtype != qs[0].dtype or os_[l].dtype != os_[0].dtype:
+            raise ValueError(f"layer {l} differs in shape or dtype from layer 0")
+    return dims
+
+
 def flux_attn_prefill_layers(modes_host, qs, ks, vs, os_, lses=None, *, block: int = 64, sink_tokens: int = 128,
                              window_tokens: int = 2048, blk_row_ptr=None, blk_col_idx=None,
                              scale: float | None = None, stream=None):
     """Per-layer dispatch: layer l runs dense or block-sparse prefill per modes_host[l] (host int32)."""
     L = len(qs)
     modes = np.ascontiguousarray(np.asarray(modes_host, dtype=np.int32))
-    assert modes.shape == (L,)
-    B, S, Hq, d = qs[0].shape
-    Hkv = ks[0].shape[2]
+    if modes.shape != (L,):
+        raise ValueError(f"modes_host must hold one mode per layer ({L})")
+    B, S, Hq, Hkv, d = _check_layers(qs, ks, vs, os_, lses)
+    _check_csr(blk_row_ptr, blk_col_idx, S, block, qs[0])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     pq, _a = _ptr_array(qs)
@@ -232,10 +309,11 @@ def flux_attn_prefill_layers_routed(modes_dev, qs, ks, vs, os_, lses=None, *, bl
     The block-sparse CSR is required."""
     L = len(qs)
     import torch
-    if modes_dev.dtype != torch.int32 or modes_dev.numel() != L or not modes_dev.is_contiguous():
+    B, S, Hq, Hkv, d = _check_layers(qs, ks, vs, os_, lses)
+    _dev(modes_dev, "modes_dev", None, (torch.int32,), qs[0])
+    if modes_dev.numel() != L:
         raise ValueError("modes_dev must be a contiguous int32 device tensor with one entry per layer")
-    B, S, Hq, d = qs[0].shape
-    Hkv = ks[0].shape[2]
+    _check_csr(blk_row_ptr, blk_col_idx, S, block, qs[0])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     pq, _a = _ptr_array(qs)
@@ -261,9 +339,18 @@ def flux_attn_decode(q, k_cache, v_cache, o, lse=None, *, kv_len: int | None = N
                      block: int = 64, sink_tokens: int = 128, window_tokens: int = 2048, num_splits: int = 0,
                      workspace=None, scale: float | None = None, stream=None):
     """q [B,Hq,d], caches [B,cap,Hkv,d] bf16, o [B,Hq,d]; workspace: a uint8 device tensor."""
-    _contig(q, k_cache, v_cache, o, lse)
+    import torch
+    _dev(q, "q", None, (torch.bfloat16,))
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [batch, q_heads, head_dim] and the caches [batch, rows, kv_heads, head_dim]")
     B, Hq, d = q.shape
     cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _dev(k_cache, "k_cache", (B, cap, Hkv, d), (torch.bfloat16,), q)
+    _dev(v_cache, "v_cache", (B, cap, Hkv, d), (torch.bfloat16,), q)
+    _dev(o, "o", (B, Hq, d), _float_types(), q)
+    if lse is not None:
+        _dev(lse, "lse", (B, Hq), (torch.float32,), q)
+    _check_workspace(workspace, q)
     if kv_len is None:
         kv_len = cap
     if scale is None:
@@ -279,13 +366,30 @@ def flux_window_cache_rows(block: int = 64, sink_tokens: int = 128, window_token
     return int(_lib.flux_window_cache_rows(block, sink_tokens, window_tokens))
 
 
+def _check_step_layer(q, k_new, v_new, k_cache, v_cache, o, lse, B, Hq, Hkv, d, rows, tag):
+    import torch
+    _dev(q, "q" + tag, (B, Hq, d), (torch.bfloat16,))
+    _dev(k_new, "k_new" + tag, (B, Hkv, d), (torch.bfloat16,), q)
+    _dev(v_new, "v_new" + tag, (B, Hkv, d), (torch.bfloat16,), q)
+    _dev(k_cache, "k_cache" + tag, (B, rows, Hkv, d), (torch.bfloat16,), q)
+    _dev(v_cache, "v_cache" + tag, (B, rows, Hkv, d), (torch.bfloat16,), q)
+    _dev(o, "o" + tag, (B, Hq, d), _float_types(), q)
+    if lse is not None:
+        _dev(lse, "lse" + tag, (B, Hq), (torch.float32,), q)
+
+
 def flux_decode_step(q, k_new, v_new, k_cache, v_cache, o, lse=None, *, pos: int, layout: int = FLUX_KV_FULL,
                      mode: int = FLUX_MODE_DENSE, block: int = 64, sink_tokens: int = 128, window_tokens: int = 2048,
                      num_splits: int = 0, workspace=None, scale: float | None = None, stream=None):
     """Append token `pos` (k_new/v_new [B,Hkv,d] bf16) to the cache [B,rows,Hkv,d] and attend from q [B,Hq,d]."""
-    _contig(q, k_new, v_new, k_cache, v_cache, o, lse)
+    import torch
+    _dev(q, "q", None, (torch.bfloat16,))
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [batch, q_heads, head_dim] and the caches [batch, rows, kv_heads, head_dim]")
     B, Hq, d = q.shape
     rows, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check_step_layer(q, k_new, v_new, k_cache, v_cache, o, lse, B, Hq, Hkv, d, rows, "")
+    _check_workspace(workspace, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -301,9 +405,23 @@ def flux_decode_step_layers(modes_host, qs, k_news, v_news, k_caches, v_caches, 
     """One decode step over a routed stack: dense layers on full caches, sparse layers on window caches."""
     L = len(qs)
     modes = np.ascontiguousarray(np.asarray(modes_host, dtype=np.int32))
-    assert modes.shape == (L,)
+    if modes.shape != (L,):
+        raise ValueError(f"modes_host must hold one mode per layer ({L})")
+    if not (len(k_news) == len(v_news) == len(k_caches) == len(v_caches) == len(os_) == L) or \
+            (lses is not None and len(lses) != L):
+        raise ValueError("every per-layer list must hold one tensor per layer")
+    if qs[0].dim() != 3 or k_news[0].dim() != 3:
+        raise ValueError("q must be [batch, q_heads, head_dim] and k_new [batch, kv_heads, head_dim]")
     B, Hq, d = qs[0].shape
     Hkv = k_news[0].shape[1]
+    win_rows = flux_window_cache_rows(block, sink_tokens, window_tokens)
+    for l in range(L):
+        rows = dense_cache_rows if modes[l] == FLUX_MODE_DENSE else win_rows
+        _check_step_layer(qs[l], k_news[l], v_news[l], k_caches[l], v_caches[l], os_[l],
+                          None if lses is None else lses[l], B, Hq, Hkv, d, rows, f"[{l}]")
+        if qs[l].device != qs[0].device:
+            raise ValueError("all layers must be on one device")
+    _check_workspace(workspace, qs[0])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     arrs = [_ptr_array(x) for x in (qs, k_news, v_news, k_caches, v_caches, os_)]
@@ -323,9 +441,25 @@ def flux_route_layers(q_layers, w_enc, b_enc, w_head, b_head, modes_out, logits_
                       pool_tokens: int = 100, stream=None):
     """q_layers: list of device tensors [S,Hq,d]; weights device float32; modes_out device int32 [L];
     workspace: uint8 device tensor of flux_route_workspace_size(...) bytes (allocated here if None)."""
+    import torch
     L = len(q_layers)
+    if L < 1 or q_layers[0].dim() != 3:
+        raise ValueError("q_layers must be a non-empty list of [seq, q_heads, head_dim] tensors")
     S, Hq, d = q_layers[0].shape
+    for l, x in enumerate(q_layers):
+        _dev(x, f"q_layers[{l}]", (S, Hq, d), (q_layers[0].dtype,) if l else _float_types(), q_layers[0])
+    if w_enc.dim() != 3:
+        raise ValueError("w_enc must be [n_layers, hidden, q_heads * head_dim]")
     hidden = w_enc.shape[1]
+    f32 = (torch.float32,)
+    _dev(w_enc, "w_enc", (L, hidden, Hq * d), f32, q_layers[0])
+    _dev(b_enc, "b_enc", (L, hidden), f32, q_layers[0])
+    _dev(w_head, "w_head", (L, 2, hidden), f32, q_layers[0])
+    _dev(b_head, "b_head", (L, 2), f32, q_layers[0])
+    _dev(modes_out, "modes_out", (L,), (torch.int32,), q_layers[0])
+    if logits_out is not None:
+        _dev(logits_out, "logits_out", (L, 2), f32, q_layers[0])
+    _check_workspace(workspace, q_layers[0])
     if workspace is None:
         import torch
         workspace = torch.empty(flux_route_workspace_size(L, Hq, d, hidden), dtype=torch.uint8,
@@ -339,8 +473,14 @@ def flux_route_layers(q_layers, w_enc, b_enc, w_head, b_head, modes_out, logits_
 
 def flux_route_soft_weights(logits, uniforms, tau: float, weights_out, stream=None):
     """Gumbel-softmax weights [L,2] (device float32) from logits [L,2] and uniforms [L,2] in (0,1)."""
-    _contig(logits, uniforms, weights_out)
+    import torch
+    if logits.dim() != 2 or logits.shape[1] != 2:
+        raise ValueError("logits must be [n_layers, 2]")
     L = logits.shape[0]
+    f32 = (torch.float32,)
+    _dev(logits, "logits", (L, 2), f32)
+    _dev(uniforms, "uniforms", (L, 2), f32, logits)
+    _dev(weights_out, "weights_out", (L, 2), f32, logits)
     _check(_lib.flux_route_soft_weights(_ptr(logits), _ptr(uniforms), tau, L, _ptr(weights_out), _stream(stream)),
            "flux_route_soft_weights")
 
@@ -353,13 +493,14 @@ def flux_attn_prefill_soft(q, k, v, o, weights_dev, *, block: int = 64, sink_tok
                            window_tokens: int = 2048, blk_row_ptr=None, blk_col_idx=None, workspace=None,
                            scale: float | None = None, stream=None):
     """o = w[0] * dense-causal attention + w[1] * block-sparse attention; weights_dev: device float32 [2]."""
-    _contig(q, k, v, o, weights_dev)
-    B, S, Hq, d = q.shape
-    Hkv = k.shape[2]
+    import torch
+    B, S, Hq, Hkv, d = _check_attention(q, k, v, o, None)
+    _dev(weights_dev, "weights_dev", (2,), (torch.float32,), q)
+    _check_csr(blk_row_ptr, blk_col_idx, S, block, q)
+    _check_workspace(workspace, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        import torch
         workspace = torch.empty(flux_prefill_soft_workspace_size(B, S, Hq, d), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     nnz = int(blk_col_idx.numel()) if blk_col_idx is not None else 0
@@ -378,13 +519,19 @@ def flux_attn_backward(q, k, v, o, d_o, lse, dq, dk, dv, *, causal: bool = True,
                        block: int = 64, sink_tokens: int = 0, window_tokens: int = 0, scale: float | None = None,
                        workspace=None, stream=None):
     """Gradients dq, dk, dv (fp32, written) of attention for output gradient d_o; lse from the forward pass."""
-    _contig(q, k, v, o, d_o, lse, dq, dk, dv)
-    B, S, Hq, d = q.shape
-    Hkv = k.shape[2]
+    import torch
+    B, S, Hq, Hkv, d = _check_attention(q, k, v, o, lse)
+    if lse is None:
+        raise ValueError("lse (from the forward pass) is required")
+    _dev(d_o, "d_o", (B, S, Hq, d), (q.dtype,), q)
+    f32 = (torch.float32,)
+    _dev(dq, "dq", (B, S, Hq, d), f32, q)
+    _dev(dk, "dk", (B, S, Hkv, d), f32, q)
+    _dev(dv, "dv", (B, S, Hkv, d), f32, q)
+    _check_workspace(workspace, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        import torch
         workspace = torch.empty(max(flux_attn_backward_workspace_size(B, S, Hq, Hkv, d), 1), dtype=torch.uint8,
                                 device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()

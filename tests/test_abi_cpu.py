@@ -379,3 +379,35 @@ def test_route_validation(fa):
     assert call(1000, 32, 128, 0, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, FAKE, 100) == fa.FLUX_ERR_WORKSPACE
     assert call(1000, 32, 128, 0, 100, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, FAKE + 16, big) == \
         fa.FLUX_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ the Python binding's own checks
+def test_binding_refuses_host_tensors(fa):
+    """The C ABI cannot tell a host pointer from a device pointer; the binding refuses tensors that are
+    not on a GPU before any pointer crosses it (the kernels would otherwise fault on them)."""
+    import torch
+    B, S, Hq, Hkv, d = 1, 64, 2, 1, 64
+    q = torch.zeros((B, S, Hq, d), dtype=torch.bfloat16)
+    k = torch.zeros((B, S, Hkv, d), dtype=torch.bfloat16)
+    o = torch.zeros((B, S, Hq, d), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.flux_attn_prefill(q, k, k, o)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.flux_attn_decode(q[:, 0], k, k, o[:, 0])
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.flux_attn_backward(q, k, k, o, q, torch.zeros((B, Hq, S)), o, o[:, :, :1].contiguous(),
+                              o[:, :, :1].contiguous())
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.flux_route_soft_weights(torch.zeros((1, 2)), torch.zeros((1, 2)), 1.0, torch.zeros((1, 2)))
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        fa.flux_attn_prefill(np.zeros((B, S, Hq, d), np.float32), k, k, o)
+
+
+def test_binding_shape_checks_order(fa):
+    """Shape and rank errors are reported as such (ValueError) for malformed inputs."""
+    import torch
+    with pytest.raises(ValueError, match="batch, seq, heads, head_dim"):
+        fa.flux_attn_prefill(torch.zeros((64, 2, 64)), torch.zeros((64, 2, 64)), torch.zeros((64, 2, 64)),
+                             torch.zeros((64, 2, 64)))
+    with pytest.raises(ValueError, match="one mode per layer"):
+        fa.flux_attn_prefill_layers([0, 1], [torch.zeros((1, 64, 2, 64))], [None], [None], [None])
