@@ -333,7 +333,9 @@ int flux_decode_step_layers(int32_t n_layers, const int32_t* modes_host, const v
 /*
  * flux_route_workspace_size -- bytes of workspace flux_route_layers needs:
  * the pooled features [n_layers, hq*head_dim] and the encoder activations
- * [n_layers, hidden], float32, each part 256-byte aligned.  0 if invalid.
+ * [n_layers, hidden], float32, then one int32 arrival counter per layer (set by
+ * the call itself: the workspace needs no clearing), each part 256-byte aligned.
+ * 0 if invalid.  Calls that share a workspace must be ordered (one stream).
  */
 size_t flux_route_workspace_size(int32_t n_layers, int32_t hq, int32_t head_dim, int32_t hidden);
 

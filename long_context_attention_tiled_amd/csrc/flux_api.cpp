@@ -682,7 +682,8 @@ int flux_decode_step_layers(int32_t n_layers, const int32_t* modes_host, const v
 size_t flux_route_workspace_size(int32_t n_layers, int32_t hq, int32_t head_dim, int32_t hidden) {
     if (n_layers < 1 || hq < 1 || head_dim < 1 || hidden < 1) return 0;
     const size_t nf = (size_t)hq * head_dim;
-    return align256((size_t)n_layers * nf * sizeof(float)) + align256((size_t)n_layers * hidden * sizeof(float));
+    return align256((size_t)n_layers * nf * sizeof(float)) + align256((size_t)n_layers * hidden * sizeof(float)) +
+           align256((size_t)n_layers * sizeof(int32_t));
 }
 
 int flux_route_layers(const void* const* q_layers, int32_t n_layers, int64_t seq, int32_t hq, int32_t head_dim,
@@ -712,6 +713,8 @@ int flux_route_layers(const void* const* q_layers, int32_t n_layers, int64_t seq
     float* pooled = reinterpret_cast<float*>(workspace);
     float* z = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                         align256((size_t)n_layers * nf * sizeof(float)));
+    int32_t* counters = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(z) +
+                                                   align256((size_t)n_layers * hidden * sizeof(float)));
     for (int32_t l0 = 0; l0 < n_layers; l0 += flux::kMaxRouteLayers) {
         flux::RouteArgs a;
         a.n_layers = std::min(n_layers - l0, flux::kMaxRouteLayers);
@@ -730,6 +733,7 @@ int flux_route_layers(const void* const* q_layers, int32_t n_layers, int64_t seq
         a.modes = modes_out;
         a.pooled = pooled;
         a.z = z;
+        a.counters = counters;
         hipError_t e = flux::launch_route(a, as_stream(hip_stream));
         if (e == hipSuccess) e = hipGetLastError();
         if (e != hipSuccess) return hip_status(e, "router launch");

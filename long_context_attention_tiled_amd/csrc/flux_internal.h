@@ -87,6 +87,7 @@ struct RouteArgs {
     int32_t* modes;
     float* pooled;         // workspace [L_total, n_feat]
     float* z;              // workspace [L_total, hidden]
+    int32_t* counters;     // workspace [L_total]: encoder workgroups done (reset by the pool kernel)
 };
 
 struct BackwardArgs {

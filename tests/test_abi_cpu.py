@@ -356,7 +356,7 @@ def test_decode_validation(fa):
 
 def test_route_workspace_size(fa):
     align = lambda x: (x + 255) // 256 * 256
-    assert fa.flux_route_workspace_size(36, 32, 128, 256) == align(36 * 4096 * 4) + align(36 * 256 * 4)
+    assert fa.flux_route_workspace_size(36, 32, 128, 256) == align(36 * 4096 * 4) + align(36 * 256 * 4) + align(36 * 4)
     assert fa.flux_route_workspace_size(0, 32, 128, 256) == 0
 
 
