@@ -16,9 +16,10 @@
 //                         serves the float32 kernels of backward_f32.hip.
 //   bwd_dkdv_kernel       one work unit = 128 keys (4 groups of 32) and one query head, 8 waves: per
 //                         key group one wave accumulates dV, one dK; they walk the 64-query tiles
-//                         that see those keys: S = Q K^T (and dP = dO V^T) with K, V held in
-//                         registers (keys in lanes), then dV^T += dO^T P or dK^T += Q^T dS with the
-//                         dO or Q tile read transposed from LDS.
+//                         that see those keys: S = Q K^T (dV wave, K in registers, keys in lanes;
+//                         P goes to the dK wave through LDS) and dP = dO V^T (dK wave, V in
+//                         registers), then dV^T += dO^T P or dK^T += Q^T dS with the dO or Q tile
+//                         read transposed from LDS.
 //   bwd_dq_kernel         one work unit = 128 queries (4 waves x 32) of one query head; walks the
 //                         visible 64-key tiles: S^T = K Q^T and dP^T = V dO^T with Q, dO in
 //                         registers (queries in lanes), then dQ^T += K^T dS^T.
@@ -295,17 +296,20 @@ __device__ __forceinline__ void grad_product(const Lanes<D>& L, const char* xt, 
 // ------------------------------------------------------------------ dK, dV
 //
 // 8 waves, two per SIMD, on 128 keys: waves w and w + 4 own the same 32 keys; wave w accumulates
-// dV^T (it needs S and P only), wave w + 4 accumulates dK^T (S, dP and dS).  Each takes a 64-query
-// tile in two 32-query halves: S (D/16 MFMAs; dP, as many more, for dK), the vector work, then
-// 4 * D/32 MFMAs of its gradient product.  At D = 128 that is 48 + 64 MFMAs per SIMD and tile, and
-// each wave stays within 256 registers, so the two waves of a SIMD hide each other's vector work
-// and LDS latency.
+// dV^T, wave w + 4 dK^T.  Each takes a 64-query tile in two 32-query halves: wave w computes S (D/16
+// MFMAs) and P and hands P to wave w + 4 through LDS, which meanwhile computes dP (as many MFMAs) and
+// then dS; each then runs the 4 * D/32 MFMAs of its gradient product.  At D = 128 that is 48 + 48
+// MFMAs per SIMD and tile, S is computed once per key group, and each wave stays within 256
+// registers, so the two waves of a SIMD hide each other's vector work and LDS latency.
 constexpr int kKvWaves = 8;
 template <int D>
 __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs a) {
     using Gm = Geo<D>;
     constexpr int kNC = Gm::NC, kNM = Gm::NM, kTileB = Gm::TILE_B, kSlotB = Gm::SLOT_B;
     __shared__ __attribute__((aligned(1024))) char smem[kSlots * kSlotB];
+    // P of one 32-query half, handed from the dV wave to the dK wave of each key group: two halves in
+    // flight, [parity][key group][accumulator quad][lane] (lane-contiguous float4: conflict-free)
+    __shared__ float4 pbuf[2][4][4][64];
     __shared__ int qcell[2];
     Lanes<D> L;
     L.init(threadIdx.x & 63);
@@ -313,6 +317,7 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
     const int lane = L.lane, n = L.n, hh = L.hh;
     const int ks = wave & 3;          // 32-key group
     const bool is_dk = wave >= 4;     // role: dK (true) or dV (false)
+    int par = 0;                      // parity of the P buffer of the next half
 
     const int seq = (int)a.seq, nqb = a.n_qblk, G = a.hq / a.hkv;
     const int bh_total = (int)a.batch * a.hq;
@@ -352,58 +357,64 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
         };
         issue(lo, 0);
 
-        // K (both roles) and V (dK role) rows of this lane's key as B operands (k-slots = d)
-        bf16x8 kreg[kNC], vreg[kNC];
+        // this lane's key row as the B operand (k-slots = d): K for the dV wave (S = Q K^T), V for the
+        // dK wave (dP = dO V^T)
+        bf16x8 breg[kNC];
         {
             const int kc = min(key, seq - 1);
             const int64_t off = (((int64_t)b * a.seq + kc) * a.hkv + g) * D + 8 * hh;
-            const u16* kp = reinterpret_cast<const u16*>(a.k) + off;
-            const u16* vp = reinterpret_cast<const u16*>(a.v) + off;
+            const u16* bp = reinterpret_cast<const u16*>(is_dk ? a.v : a.k) + off;
 #pragma unroll
-            for (int c = 0; c < kNC; ++c) kreg[c] = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
-            if (is_dk) {
-#pragma unroll
-                for (int c = 0; c < kNC; ++c) vreg[c] = *reinterpret_cast<const bf16x8*>(vp + 16 * c);
-            }
+            for (int c = 0; c < kNC; ++c) breg[c] = *reinterpret_cast<const bf16x8*>(bp + 16 * c);
         }
 
         f32x16 acc[kNM];   // dV^T or dK^T: lane = key, rows d = 32mt + 8(r/4) + 4hh + r%4
 #pragma unroll
         for (int mt = 0; mt < kNM; ++mt) acc[mt] = f32x16{};
 
-        // One tile: elements with C < lim are masked (C = query - 64t - 4hh).  Both roles run this one
-        // body, the role and the mask switching only short stretches (dP's MFMAs, dS, the mask):
-        // separate bodies per role or per masked/unmasked tile would cost about 30 registers more and spill.
+        // One tile, in two 32-query halves.  The dV wave computes S, P (exp2 of the scaled score minus
+        // the row's LSE, zero where masked) and publishes P in LDS; the dK wave computes dP meanwhile,
+        // and after the barrier forms dS = P (dP - D) from the published P.  Then each runs its gradient
+        // product.  Elements with C < lim are masked (C = query - 64t - 4hh).  S is computed once per
+        // key group (48 + 48 MFMAs per SIMD and tile at D = 128), and the barrier staggers the two waves
+        // of a SIMD: one runs its gradient product's MFMAs while the other does its vector work.
         auto tile = [&](const char* qt, int lim, bool need_mask) {
             const char* dot = qt + kTileB;
             const char* st = qt + 2 * kTileB;
             const char* xt = is_dk ? qt : dot;   // tile read transposed for the gradient product
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                f32x16 s = f32x16{}, dp = f32x16{};
-                mfma_seq<kNC>([&](int i) { return L.row(qt, hf, i); }, [&](int i, bf16x8 op) { s = MFMA(op, kreg[i], s); });
-                if (is_dk)
-                    mfma_seq<kNC>([&](int i) { return L.row(dot, hf, i); },
-                                  [&](int i, bf16x8 op) { dp = MFMA(op, vreg[i], dp); });
-                float x[16];   // P, then dS = P (dP - D) for the dK role
+                f32x16 sd = f32x16{};   // S (dV wave) or dP (dK wave)
+                mfma_seq<kNC>([&](int i) { return L.row(is_dk ? dot : qt, hf, i); },
+                              [&](int i, bf16x8 op) { sd = MFMA(op, breg[i], sd); });
+                float x[16];   // P, then dS = P (dP - D) for the dK wave
+                if (!is_dk) {
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const float4 nl = *reinterpret_cast<const float4*>(st + 4 * (32 * hf + 8 * g4 + 4 * hh));
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const float4 nl = *reinterpret_cast<const float4*>(st + 4 * (32 * hf + 8 * g4 + 4 * hh));
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[4 * g4 + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * g4 + e], c2, comp(nl, e)));
+                        for (int e = 0; e < 4; ++e)
+                            x[4 * g4 + e] = __builtin_amdgcn_exp2f(fmaf(sd[4 * g4 + e], c2, comp(nl, e)));
+                    }
+                    if (need_mask) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) x[r] = (32 * hf + 8 * (r >> 2) + (r & 3) < lim) ? 0.0f : x[r];
+                    }
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        pbuf[par][ks][g4][lane] = float4{x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]};
                 }
-                if (need_mask) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) x[r] = (32 * hf + 8 * (r >> 2) + (r & 3) < lim) ? 0.0f : x[r];
-                }
+                __syncthreads();   // P of this half published
                 if (is_dk) {
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
+                        const float4 p = pbuf[par][ks][g4][lane];
                         const float4 dd = *reinterpret_cast<const float4*>(st + 256 + 4 * (32 * hf + 8 * g4 + 4 * hh));
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) x[4 * g4 + e] *= dp[4 * g4 + e] - comp(dd, e);
+                        for (int e = 0; e < 4; ++e) x[4 * g4 + e] = comp(p, e) * (sd[4 * g4 + e] - comp(dd, e));
                     }
                 }
+                par ^= 1;
                 bf16x8 xh[2], xl[2];
                 split16(x, xh, xl);
                 grad_product(L, xt, 2 * hf, xh, xl, acc);
