@@ -186,17 +186,21 @@ int flux_attn_prefill_layers_routed(int32_t n_layers, const int32_t* modes_devic
 int flux_route_soft_weights(const float* logits, const float* uniforms, float tau, int32_t n_layers,
                             float* weights_out, void* hip_stream);
 
-/* flux_prefill_soft_workspace_size -- bytes flux_attn_prefill_soft needs (an fp32 [B, S, Hq, d] buffer). */
+/* flux_prefill_soft_workspace_size -- bytes flux_attn_prefill_soft needs (an fp32 [B, S, Hq, d] buffer,
+ * 16-byte aligned). */
 size_t flux_prefill_soft_workspace_size(int64_t batch, int64_t seq, int32_t hq, int32_t head_dim);
 
 /*
  * flux_attn_prefill_soft -- soft-routed layer output for training ([FA] router paragraph: the full
  * and sparse attention outputs weighted by the Gumbel-softmax probabilities):
  *   o = w[0] * attention(dense causal) + w[1] * attention(block-sparse)
- * with weights_device [2] device float32 (one row of flux_route_soft_weights' output).  The full
- * attention goes to `workspace` in fp32; the sparse pass adds it in its epilogue (no extra launch).
- * Inputs BF16; out_dtype BF16 or F32; CSR as for flux_attn_prefill in sparse mode.  No LSE (the
- * output is a mixture of two softmaxes).
+ * with weights_device [2] device float32 (one row of flux_route_soft_weights' output).  One launch:
+ * the dense-causal pass visits each row's sink and window blocks first, takes the row's block-sparse
+ * output there (into `workspace`, fp32) and mixes both at the end, so the blocks the two modes share
+ * are computed once.  Inputs BF16; out_dtype BF16 or F32.  The block pattern is the one of
+ * flux_build_block_mask(seq, seq, block, sink_tokens, window_tokens, 1, FLUX_MODE_SPARSE); the CSR
+ * arguments may be NULL (with blk_nnz ignored) or that CSR, which is then checked as for
+ * flux_attn_prefill in sparse mode.  No LSE (the output is a mixture of two softmaxes).
  */
 int flux_attn_prefill_soft(const void* q, const void* k, const void* v, void* o, int32_t in_dtype,
                            int32_t out_dtype, int64_t batch, int64_t seq, int32_t hq, int32_t hkv,

@@ -161,6 +161,9 @@ int check_prefill(const void* q, const void* k, const void* v, void* o, float* l
     a->num_cu = 0;
     a->mix_o = nullptr;
     a->mix_w = nullptr;
+    a->soft_ws = nullptr;
+    a->sink_blocks = ms.sparse ? (int)(sink / block) : 0;
+    a->window_blocks = ms.sparse ? (int)(window / block) : 0;
     return FLUX_OK;
 }
 
@@ -459,22 +462,36 @@ int flux_attn_prefill_soft(const void* q, const void* k, const void* v, void* o,
     if (!weights_device || (reinterpret_cast<uintptr_t>(weights_device) & 3u))
         return fail(FLUX_ERR_INVALID_ARG, "weights_device must be a 4-byte aligned device pointer");
     if (in_dtype != FLUX_DTYPE_BF16) return fail(FLUX_ERR_UNSUPPORTED, "soft routing takes bfloat16 inputs");
-    flux::PrefillArgs full, sparse;
-    int st = check_prefill(q, k, v, workspace, nullptr, in_dtype, FLUX_DTYPE_F32, batch, seq, hq, hkv, head_dim, scale,
-                           1, FLUX_MODE_DENSE, block, sink_tokens, window_tokens, nullptr, nullptr, 0, &full);
-    if (st != FLUX_OK) return st;
-    st = check_prefill(q, k, v, o, nullptr, in_dtype, out_dtype, batch, seq, hq, hkv, head_dim, scale, 1,
-                       FLUX_MODE_SPARSE, block, sink_tokens, window_tokens, blk_row_ptr, blk_col_idx, blk_nnz, &sparse);
+    if (!workspace || !aligned16(workspace)) return fail(FLUX_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    // the CSR is optional here (the fused kernel walks the pattern from sink and window); when given it is
+    // checked as in sparse mode
+    flux::PrefillArgs a;
+    int st;
+    if (blk_row_ptr || blk_col_idx) {
+        st = check_prefill(q, k, v, o, nullptr, in_dtype, out_dtype, batch, seq, hq, hkv, head_dim, scale, 1,
+                           FLUX_MODE_SPARSE, block, sink_tokens, window_tokens, blk_row_ptr, blk_col_idx, blk_nnz, &a);
+    } else {
+        MaskSpec ms;
+        st = check_mask_spec(seq, seq, block, sink_tokens, window_tokens, 1, FLUX_MODE_SPARSE, &ms);
+        if (st == FLUX_OK)
+            st = check_prefill(q, k, v, o, nullptr, in_dtype, out_dtype, batch, seq, hq, hkv, head_dim, scale, 1,
+                               FLUX_MODE_DENSE, block, 0, 0, nullptr, nullptr, 0, &a);
+        a.sink_blocks = sink_tokens / block;
+        a.window_blocks = window_tokens / block;
+    }
     if (st != FLUX_OK) return st;
     const size_t need = flux_prefill_soft_workspace_size(batch, seq, hq, head_dim);
     if (workspace_bytes < need)
         return fail(FLUX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
     if (workspace == o) return fail(FLUX_ERR_INVALID_ARG, "workspace must not alias o");
-    st = launch_prefill(full, in_dtype, as_stream(hip_stream));       // full attention -> fp32 workspace
-    if (st != FLUX_OK) return st;
-    sparse.mix_o = reinterpret_cast<const float*>(workspace);          // sparse attention, mixed in its epilogue
-    sparse.mix_w = weights_device;
-    return launch_prefill(sparse, in_dtype, as_stream(hip_stream));
+    // one launch: dense-causal walk ordered sink, window (descending), then the other blocks; each row's
+    // block-sparse output is taken when its window ends, the mixture written at the end
+    a.sparse = 0;
+    a.row_ptr = nullptr;
+    a.col_idx = nullptr;
+    a.soft_ws = reinterpret_cast<float*>(workspace);
+    a.mix_w = weights_device;
+    return launch_prefill(a, in_dtype, as_stream(hip_stream));
 }
 
 // ---------------------------------------------------------------- backward

@@ -77,8 +77,11 @@ struct Lay {
     static_assert(INSTS_PER_WAVE * kWaves * 1024 == TILE_B, "tile split over the waves");
 };
 
-// kRouted: causal, dense or sparse as the layer's device-resident mode says (read at start)
-enum Mode { kDenseCausal = 0, kDenseFull = 1, kSparse = 2, kRouted = 3 };
+// kRouted: causal, dense or sparse as the layer's device-resident mode says (read at start).
+// kSoft: dense causal with the key tiles ordered sink, window (descending), then the rest, so that every
+// row's block-sparse set is a prefix of its walk: the row's sparse output is taken where its window
+// ends and both outputs come from one pass (soft routing).
+enum Mode { kDenseCausal = 0, kDenseFull = 1, kSparse = 2, kRouted = 3, kSoft = 4 };
 
 template <bool B>
 struct BoolTag {
@@ -93,15 +96,23 @@ template <int MODE>
 struct TileWalk {
     int next_kb, last_kb, qb_base, nvalid;
     int p0, p1, p2, p3, e0, e1, e2, e3;   // CSR cursors and ends of the (up to 4) query blocks
+    int n_sink, desc_lo, sink_b;          // kSoft: sink tiles, lowest window tile, sink blocks
     const int32_t* ci;
     static constexpr bool sparse = MODE == kSparse;
 
-    __device__ void init(int qb_base_, int nrows, int n_qblk, const int32_t* rp, const int32_t* ci_) {
+    __device__ void init(int qb_base_, int nrows, int n_qblk, const int32_t* rp, const int32_t* ci_, int sb = 0,
+                         int wb = 0) {
         qb_base = qb_base_;
         nvalid = max(0, min(nrows, n_qblk - qb_base));
         ci = ci_;
         next_kb = 0;
         last_kb = MODE == kDenseFull ? n_qblk - 1 : qb_base + nvalid - 1;
+        if constexpr (MODE == kSoft) {
+            // walk: sink [0, n_sink), window [desc_lo, last_kb] from the top down, then [sb, desc_lo)
+            sink_b = sb;
+            n_sink = min(sb, last_kb + 1);
+            desc_lo = max(sb, qb_base - wb + 1);
+        }
         if constexpr (sparse) {
             p0 = p1 = p2 = p3 = e0 = e1 = e2 = e3 = 0;
             if (nvalid > 0) p0 = rp[qb_base], e0 = rp[qb_base + 1];
@@ -128,8 +139,18 @@ struct TileWalk {
             in = (uint32_t)h0 | ((uint32_t)h1 << 1) | ((uint32_t)h2 << 2) | ((uint32_t)h3 << 3);
             return true;
         } else {
-            if (next_kb > last_kb) return false;
-            kb = next_kb++;
+            if constexpr (MODE == kSoft) {
+                const int i = next_kb;   // position in the walk
+                const int n_desc = max(0, last_kb - desc_lo + 1);
+                if (i < n_sink) kb = i;
+                else if (i < n_sink + n_desc) kb = last_kb - (i - n_sink);
+                else kb = sink_b + (i - n_sink - n_desc);
+                if (i >= n_sink + n_desc && kb >= min(desc_lo, last_kb + 1)) return false;
+                ++next_kb;
+            } else {
+                if (next_kb > last_kb) return false;
+                kb = next_kb++;
+            }
             in = 0;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -263,7 +284,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
         qpos = q0 + n;                       // this lane's query row
         wave_live = q0 < seq;
         my_qb = qb_base + my_r;
-        walk.init(qb_base, nrows, a.n_qblk, a.row_ptr, a.col_idx);
+        walk.init(qb_base, nrows, a.n_qblk, a.row_ptr, a.col_idx, a.sink_blocks, a.window_blocks);
         have_any = walk.next(kb_c, in);      // uniform over the workgroup; true for every valid launch
         mine_c = have_any && wave_live && ((in >> my_r) & 1);
         have_n = have_any && walk.next(kb_n, in);
@@ -303,6 +324,23 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     bf16x8 pb[2][2];
     float m_run = kNegBig, l_run = 0.0f;
     const float c2 = a.scale_log2;
+    bool snapped = false;   // kSoft: this wave's block-sparse output has been written to soft_ws
+
+    // kSoft: the rows' block-sparse output O / l over the tiles accumulated so far (the row's sink and
+    // window tiles), to soft_ws in fp32.  Wave-uniform call (the half-row sums are exchanged).
+    auto snapshot = [&]() {
+        const float l_tot = sum_halves(l_run);
+        if (!wave_live || qpos >= seq) return;
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        float* dst = a.soft_ws + (((int64_t)b * seq + qpos) * a.hq + h) * D;
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                *reinterpret_cast<float4*>(dst + 32 * mt + 8 * r4 + 4 * hh) =
+                    make_float4(oacc[mt][4 * r4] * inv, oacc[mt][4 * r4 + 1] * inv, oacc[mt][4 * r4 + 2] * inv,
+                                oacc[mt][4 * r4 + 3] * inv);
+    };
 
     // ---- matrix work of one phase: O^T += V^T P^T for the previous tile (V slot vs), then
     // S^T = K Q^T for the current tile (K slot ks), as one sequence of up to 32 MFMAs whose
@@ -362,6 +400,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     // ---- vector work: online softmax of the scores of key tile kb -> P (bf16) in pb.
     // Lane holds S[qpos][key], key = kb*64 + 32kh + 8(r/4) + 4hh + (r%4).
     auto vwork = [&](bool mine, int kb) {
+        if constexpr (MODE == kSoft) {
+            // first tile of this wave's rows outside their sink and window: every earlier P.V is in O
+            // (the matrix phase before this one added the previous tile), l counts exactly those tiles
+            if (mine && !snapped && kb >= a.sink_blocks && my_qb - kb >= a.window_blocks) {
+                snapshot();
+                snapped = true;
+            }
+        }
         if (!mine) {   // tile not used by this wave's rows: its P.V adds exact zeros
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
@@ -431,7 +477,22 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
                 const int d = 32 * mt + 8 * r4 + 4 * hh;
                 float v0 = oacc[mt][4 * r4] * inv, v1 = oacc[mt][4 * r4 + 1] * inv;
                 float v2 = oacc[mt][4 * r4 + 2] * inv, v3 = oacc[mt][4 * r4 + 3] * inv;
-                if (a.mix_o) {   // soft routing: weighted sum with the other mode's output
+                if constexpr (MODE == kSoft) {   // w_FA * dense + w_SA * block-sparse
+                    const float w0 = a.mix_w[0], w1 = a.mix_w[1];
+                    if (snapped) {
+                        const float4 f = *reinterpret_cast<const float4*>(a.soft_ws + orow * D + d);
+                        v0 = fmaf(w1, f.x, w0 * v0);
+                        v1 = fmaf(w1, f.y, w0 * v1);
+                        v2 = fmaf(w1, f.z, w0 * v2);
+                        v3 = fmaf(w1, f.w, w0 * v3);
+                    } else {   // the row's sparse set is all of its keys
+                        const float w = w0 + w1;
+                        v0 *= w;
+                        v1 *= w;
+                        v2 *= w;
+                        v3 *= w;
+                    }
+                } else if (a.mix_o) {   // soft routing: weighted sum with the other mode's output
                     const float w0 = a.mix_w[0], w1 = a.mix_w[1];
                     const float4 f = *reinterpret_cast<const float4*>(a.mix_o + orow * D + d);
                     v0 = fmaf(w0, f.x, w1 * v0);
@@ -518,6 +579,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
             for (int mt = 0; mt < NM; ++mt) oacc[mt] = f32x16{};
             m_run = kNegBig;
             l_run = 0.0f;
+            snapped = false;
             begin_unit(vb);
         }
     };
@@ -561,6 +623,7 @@ hipError_t launch_mode(const PrefillArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_dim(const PrefillArgs& a, hipStream_t s) {
+    if (a.soft_ws) return launch_mode<D, kSoft>(a, s);
     if (a.mode_dev) return launch_mode<D, kRouted>(a, s);
     if (a.sparse) return launch_mode<D, kSparse>(a, s);
     if (a.causal) return launch_mode<D, kDenseCausal>(a, s);

@@ -254,7 +254,9 @@ def test_soft_routing_validation(fa):
                                           a["ws_bytes"], None)
     assert soft(w=None) == E
     assert soft(in_dtype=1) == fa.FLUX_ERR_UNSUPPORTED
-    assert soft(rp=None) == E
+    assert soft(rp=None) == E                              # half a CSR
+    assert soft(rp=None, ci=None, ws_bytes=100) == fa.FLUX_ERR_WORKSPACE   # no CSR: pattern from sink/window
+    assert soft(rp=None, ci=None, seq=0) == E
     assert soft(nnz=25) == E
     assert soft(ws_bytes=100) == fa.FLUX_ERR_WORKSPACE
     assert soft(ws=FAKE + 4096) == E                       # aliases o

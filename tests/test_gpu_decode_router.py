@@ -169,6 +169,27 @@ def test_router_small(fa, S, Hq, d, L):
     _check_route(logits, modes, ref_logits, ref_modes, "router small")
 
 
+@pytest.mark.parametrize("hidden", [5, 37])
+def test_router_odd_hidden_ragged_features_reused_workspace(fa, hidden):
+    """A hidden width that is not a multiple of the encoder's 4 units per workgroup, 192 features (one
+    and a half pooling blocks), and three calls on one workspace: each call resets the layers' arrival
+    counters itself, so the last-arriving encoder workgroup runs the head every time."""
+    S, Hq, d, L = 300, 3, 64, 2
+    say("router odd hidden", hidden)
+    xs = [synth.normal_bf16_bits((S, Hq, d), 4100 + hidden, l, 0) for l in range(L)]
+    xs_dev = [synth.torch_bf16_from_bits(x) for x in xs]
+    w = synth.router_weights(L, Hq * d, hidden, seed=4003)
+    wd = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in w]
+    ws = torch.full((fa.flux_route_workspace_size(L, Hq, d, hidden),), 0x5A, dtype=torch.uint8, device=DEV)
+    _, ref_logits, ref_modes = oracle.route(xs, *w)
+    for rep in range(3):
+        modes = torch.full((L,), -7, dtype=torch.int32, device=DEV)
+        logits = torch.full((L, 2), float("nan"), dtype=torch.float32, device=DEV)
+        fa.flux_route_layers(xs_dev, *wd, modes, logits, workspace=ws, pool_tokens=100)
+        torch.cuda.synchronize()
+        _check_route(logits.cpu().numpy(), modes.cpu().numpy(), ref_logits, ref_modes, f"router call {rep}")
+
+
 def test_router_qwen_stack_shape(fa):
     """36 layers, seq 131072, 32 heads x 128: the pooled rows are the first and last 100 tokens."""
     S, Hq, d, L = 131072, 32, 128, 36

@@ -274,17 +274,22 @@ def test_soft_weights_match_oracle(fa):
         assert np.abs(w.cpu().numpy() - ref).max() < 2e-5
 
 
-@pytest.mark.parametrize("B,S,Hq,Hkv,d,sink,window,w0", [
-    (1, 700, 4, 2, 128, 128, 256, 0.3),
-    (2, 333, 8, 2, 64, 64, 128, 0.85),
-    (1, 512, 2, 2, 128, 128, 128, 1.0),
-    (1, 512, 2, 2, 128, 128, 128, 0.0),
+@pytest.mark.parametrize("B,S,Hq,Hkv,d,sink,window,w0,csr", [
+    (1, 700, 4, 2, 128, 128, 256, 0.3, True),
+    (2, 333, 8, 2, 64, 64, 128, 0.85, True),
+    (1, 512, 2, 2, 128, 128, 128, 1.0, True),
+    (1, 512, 2, 2, 128, 128, 128, 0.0, True),
+    (1, 650, 3, 1, 128, 0, 64, 0.4, False),      # odd group (4 query blocks per unit), no sink, 1-block window
+    (1, 1000, 6, 2, 128, 64, 192, 0.7, False),   # odd group, 1 sink block, 3-block window, ragged end
+    (1, 100, 2, 2, 64, 128, 128, 0.5, False),    # every row inside its sink: both outputs equal
 ])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_soft_prefill_matches_oracle(fa, B, S, Hq, Hkv, d, sink, window, w0, out_dtype):
-    say("soft prefill", B, S, Hq, Hkv, d, sink, window, w0, out_dtype)
+def test_soft_prefill_matches_oracle(fa, B, S, Hq, Hkv, d, sink, window, w0, csr, out_dtype):
+    """The fused soft pass (sink and window blocks first, each row's block-sparse output taken where its
+    window ends) against w0 * dense + (1 - w0) * block-sparse from the oracle; with and without the CSR."""
+    say("soft prefill", B, S, Hq, Hkv, d, sink, window, w0, csr, out_dtype)
     (q, k, v), (qd, kd, vd) = bf16_tensors(B, S, Hq, Hkv, d, seed=72 + S)
-    rp, ci = _csr_dev(fa, S, sink, window)
+    rp, ci = _csr_dev(fa, S, sink, window) if csr else (None, None)
     wd = torch.tensor([w0, 1.0 - w0], dtype=torch.float32, device=DEV)
     o = torch.empty((B, S, Hq, d), dtype=out_dtype, device=DEV)
     fa.flux_attn_prefill_soft(qd, kd, vd, o, wd, sink_tokens=sink, window_tokens=window, blk_row_ptr=rp,
