@@ -159,7 +159,6 @@ int check_prefill(const void* q, const void* k, const void* v, void* o, float* l
     a->col_idx = ms.sparse ? ci : nullptr;
     a->mode_dev = nullptr;
     a->num_cu = 0;
-    a->mix_o = nullptr;
     a->mix_w = nullptr;
     a->soft_ws = nullptr;
     a->sink_blocks = ms.sparse ? (int)(sink / block) : 0;

@@ -31,7 +31,6 @@ struct PrefillArgs {
     const int32_t* mode_dev;  // device-resident mode of this layer (0 dense causal, else sparse),
                               // read by the kernel; nullptr when the mode is fixed by `sparse`
     int num_cu;               // compute units of the device (persistent grid size)
-    const float* mix_o;       // soft routing: fp32 [B, S, Hq, d] output of the other mode, or nullptr
     const float* mix_w;       // soft routing: device [2] weights (w_FA, w_SA)
     float* soft_ws;           // fused soft routing: fp32 [B, S, Hq, d] scratch for the sparse output, or nullptr
     int sink_blocks;          // fused soft routing: the block-sparse pattern (sink and window in blocks)

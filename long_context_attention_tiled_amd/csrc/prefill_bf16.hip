@@ -492,13 +492,6 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
                         v2 *= w;
                         v3 *= w;
                     }
-                } else if (a.mix_o) {   // soft routing: weighted sum with the other mode's output
-                    const float w0 = a.mix_w[0], w1 = a.mix_w[1];
-                    const float4 f = *reinterpret_cast<const float4*>(a.mix_o + orow * D + d);
-                    v0 = fmaf(w0, f.x, w1 * v0);
-                    v1 = fmaf(w0, f.y, w1 * v1);
-                    v2 = fmaf(w0, f.z, w1 * v2);
-                    v3 = fmaf(w0, f.w, w1 * v3);
                 }
                 if constexpr (OUT_F32) {
                     *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + orow * D + d) =
