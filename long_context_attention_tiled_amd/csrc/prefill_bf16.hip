@@ -48,6 +48,11 @@
 //   * workgroup order: kv-head groups are kept on one XCD (blockIdx % 8 picks the
 //     XCD) so the query heads sharing K/V hit the same L2, and query tiles are
 //     issued longest-first for causal masks.
+//   * soft routing (the Flux Attention page's training-time mix of both modes) is
+//     one dense-causal pass whose walk visits each row's sink and window tiles
+//     first: where a row's window ends its running O / l is exactly the
+//     block-sparse output, which goes to an fp32 scratch buffer; the epilogue
+//     writes w_FA * dense + w_SA * sparse.
 #include "flux_internal.h"
 #include "tile_common.h"
 
