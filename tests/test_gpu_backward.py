@@ -247,3 +247,26 @@ def test_full_shape_prefix_and_identities(fa, S, mode):
     # the forward's rounding of O through D = rowsum(dO * O) (measured ~1e-4 of the scale)
     assert err_v <= 2e-5 * mag_v, err_v
     assert err_k <= 1e-3 * mag_k, err_k
+
+
+# ------------------------------------------------------------- scores far from N(0,1)
+@pytest.mark.parametrize("mode", [0, 1])
+def test_sharp_scores(fa, mode):
+    """Q, K scaled by 4 (scores of std ~16): P is nearly one-hot per row, exp2(S * scale * log2e - LSE *
+    log2e) spans the whole fp32 range and underflows for most keys."""
+    B, S, Hq, Hkv, d = 1, 400, 4, 2, 128
+    say("backward sharp", mode)
+    scale = default_scale(d)
+    q, k, v = (synth.bf16_bits_to_f32(x) for x in synth.qkv_bf16(B, S, Hq, Hkv, d, 4951))
+    q, k = (synth.f32_to_bf16_bits(np.ascontiguousarray(4.0 * x)) for x in (q, k))
+    v = synth.f32_to_bf16_bits(v)
+    g = synth.normal_bf16_bits((B, S, Hq, d), 4951, tensor_id=7)
+    sink, window = (64, 128) if mode else (0, 0)
+    qd, kd, vd, gd = (synth.torch_bf16_from_bits(x) for x in (q, k, v, g))
+    o32, lse = _oracle_forward(q, k, v, scale, True, bool(mode), sink, window)
+    dq, dk, dv = _backward(fa, qd, kd, vd, torch.from_numpy(o32).to(DEV), gd, torch.from_numpy(lse).to(DEV), True,
+                           mode, sink, window)
+    rq, rk, rv = oracle.attention_backward(q, k, v, g, scale, causal=True, sparse=bool(mode), block=64,
+                                           sink_tokens=sink, window_tokens=window)
+    for name, t, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _close(t.cpu().numpy(), r, f"sharp {name} mode {mode}", None)

@@ -319,3 +319,26 @@ def test_decode_step_layers_routed_stack(fa):
         ref, _ = oracle.decode(qs[l], ks[l], vs[l], default_scale(d), sparse=bool(modes[l]), block=64,
                                sink_tokens=sink, window_tokens=window)
         check_close(os_[l].cpu().numpy(), ref, f"decode layers l={l}")
+
+
+# ------------------------------------------------------------------ scores far from N(0,1)
+@pytest.mark.parametrize("mode,ns", [(0, 0), (0, 5), (1, 0)])
+def test_decode_rising_scores(fa, mode, ns):
+    """Scores that grow along the cache (q and k share a direction along which k grows with the
+    position, ~6 per 64 keys): every step raises the running max, and the splits' LSEs differ by
+    hundreds, so the combine weights of the early splits underflow to zero."""
+    B, L, Hq, Hkv, d = 2, 3000, 8, 2, 128
+    say("decode rising scores", mode, ns)
+    q = synth.bf16_bits_to_f32(synth.normal_bf16_bits((B, Hq, d), 3500, 0, synth.TENSOR_Q))
+    k = synth.bf16_bits_to_f32(synth.normal_bf16_bits((B, L, Hkv, d), 3500, 0, synth.TENSOR_K))
+    v = synth.normal_bf16_bits((B, L, Hkv, d), 3500, 0, synth.TENSOR_V)
+    u = np.full(d, 1.0 / np.sqrt(d), np.float32)
+    q = 0.5 * q + 6.0 * u
+    k = 0.5 * k + (np.arange(L, dtype=np.float32) / 64.0 * np.sqrt(d))[None, :, None, None] * u
+    q, k = (synth.f32_to_bf16_bits(np.ascontiguousarray(x, dtype=np.float32)) for x in (q, k))
+    qd, kd, vd = (synth.torch_bf16_from_bits(x) for x in (q, k, v))
+    o, lse = _decode(fa, qd, kd, vd, torch.float32, mode, sink=128, window=1024, num_splits=ns)
+    ref, ref_lse = oracle.decode(q, k, v, default_scale(d), sparse=bool(mode), block=64, sink_tokens=128,
+                                 window_tokens=1024)
+    check_close(o.cpu().numpy(), ref, "decode rising")
+    check_lse(lse.cpu().numpy(), ref_lse, "decode rising lse")

@@ -326,3 +326,34 @@ def test_soft_prefill_router_pipeline_s8192_sampled(fa):
                                 ref_w[0], block=64, sink_tokens=128, window_tokens=2048, rows=rows)
     o_h = o.cpu().numpy()
     check_close(np.stack([o_h[b, i, h] for b, h, i in rows]), ref, "soft prefill S=8192")
+
+
+# ------------------------------------------------------------- scores far from N(0,1): the rescale path
+def _large_score_inputs(pattern, B, S, Hq, Hkv, d, seed):
+    """'sharp': Q, K scaled by 4 (scores of std ~16), so a row's running max jumps past the kernel's
+    lazy-rescale slack many times; 'rising': Q and K share a direction along which K grows with the key
+    position (about 6 score units per 64-key tile), so every tile raises every row's max."""
+    q, k, v = (synth.bf16_bits_to_f32(x) for x in synth.qkv_bf16(B, S, Hq, Hkv, d, seed))
+    if pattern == "sharp":
+        q, k = 4.0 * q, 4.0 * k
+    else:
+        u = np.full(d, 1.0 / np.sqrt(d), np.float32)
+        pos = (np.arange(S, dtype=np.float32) / 64.0 * 6.0 * np.sqrt(d) / 6.0)[None, :, None, None]
+        q = 0.5 * q + 6.0 * u
+        k = 0.5 * k + pos * u
+    q, k, v = (synth.f32_to_bf16_bits(np.ascontiguousarray(x, dtype=np.float32)) for x in (q, k, v))
+    return (q, k, v), tuple(synth.torch_bf16_from_bits(x) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("pattern", ["sharp", "rising"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_large_scores_rescale_path(fa, pattern, mode):
+    """Output and LSE against the oracle when the online softmax must rescale O on most tiles."""
+    B, S, Hq, Hkv, d = 1, 700, 4, 2, 128
+    say("large scores", pattern, "mode", mode)
+    (q, k, v), (qd, kd, vd) = _large_score_inputs(pattern, B, S, Hq, Hkv, d, seed=2601)
+    o, lse = _run_prefill(fa, qd, kd, vd, torch.float32, mode, sink=64, window=128)
+    ref, ref_lse = oracle.attention(q, k, v, default_scale(d), causal=True, sparse=bool(mode), block=64,
+                                    sink_tokens=64, window_tokens=128)
+    check_close(o.cpu().numpy(), ref, f"large scores {pattern}")
+    check_lse(lse.cpu().numpy(), np.transpose(ref_lse, (0, 2, 1)), f"large scores {pattern} lse")
