@@ -475,7 +475,8 @@ def run_peaks(torch, dev):
     """Context for the roofline fractions: what this device reaches outside the attention path.
     Library kernels on random N(0,1) bf16 data -- a bf16 GEMM (hipBLASLt via torch.matmul), a
     device-to-device copy, a read-only reduction (torch.sum) -- and the micro-benchmarks of
-    ceilings/ceilings.hip: a pure MFMA loop (operands N(0,1) bf16, then the constant 1.0), a
+    ceilings/ceilings.hip: a pure MFMA loop, 32x32x16 and 16x16x32 (operands N(0,1) bf16, then the
+    constant 1.0), a
     streaming read of 8 GiB, and the split-KV decode's own read pattern over its 2 x 4 GiB caches
     (32 splits, the split count the decode picks at batch 8 x 8 KV heads); plus the CU count and
     the peak engine clock the runtime reports."""
@@ -522,12 +523,13 @@ def run_microbench(torch, dev):
     wgs, iters = 4 * cu.value, 2000
     sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
     flops = lib.ceil_mfma_loop_flops(wgs, iters)
-    for tag, ops in (("randn", torch.randn(1 << 18, device=dev).to(torch.bfloat16)),
-                     ("const", torch.ones(1 << 18, device=dev, dtype=torch.bfloat16))):
-        n_ops = ops.numel() // 8
-        call = lambda: ceilings.check(lib.ceil_mfma_loop(ops.data_ptr(), n_ops, sink.data_ptr(), sink.numel(), wgs,
-                                                         iters, stream), "ceil_mfma_loop")
-        out[f"mfma_loop_bf16_{tag}_TFLOP/s"] = round(flops / median_ms(call) / 1e9, 1)
+    for shape, sname in ((0, ""), (1, "16x16x32_")):
+        for tag, ops in (("randn", torch.randn(1 << 18, device=dev).to(torch.bfloat16)),
+                         ("const", torch.ones(1 << 18, device=dev, dtype=torch.bfloat16))):
+            n_ops = ops.numel() // 8
+            call = lambda: ceilings.check(lib.ceil_mfma_loop(ops.data_ptr(), n_ops, sink.data_ptr(), sink.numel(),
+                                                             wgs, iters, shape, stream), "ceil_mfma_loop")
+            out[f"mfma_loop_bf16_{sname}{tag}_TFLOP/s"] = round(flops / median_ms(call) / 1e9, 1)
     del sink
 
     sink = torch.empty(256, dtype=torch.float32, device=dev)

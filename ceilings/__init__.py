@@ -14,7 +14,7 @@ _i32, _i64, _p, _f32p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.
 SIGNATURES = {
     "ceil_device_info": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]),
     "ceil_mfma_loop_flops": (ctypes.c_double, [_i32, _i32]),
-    "ceil_mfma_loop": (ctypes.c_int, [_p, _i64, _p, _i64, _i32, _i32, _p]),
+    "ceil_mfma_loop": (ctypes.c_int, [_p, _i64, _p, _i64, _i32, _i32, _i32, _p]),
     "ceil_read_stream": (ctypes.c_int, [_p, _i64, _p, _i64, _i32, _p]),
     "ceil_read_decode": (ctypes.c_int, [_p, _p, _i64, _i64, _i32, _i32, _p, _i64, _p]),
 }

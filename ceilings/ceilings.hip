@@ -2,8 +2,9 @@
 //
 // Not part of the attention path: bench.py loads this library (libceilings.so) to report, next to the
 // prefill's MFMA fraction and the decode's HBM fraction, what this very device reaches on
-//   * a pure matrix-core loop: back-to-back v_mfma_f32_32x32x16_bf16 with operands held in registers,
-//     fed from a caller buffer (random N(0,1) bf16 or a constant -- the chip's clock depends on the data);
+//   * a pure matrix-core loop: back-to-back v_mfma_f32_32x32x16_bf16 (or 16x16x32) with operands held in
+//     registers, fed from a caller buffer (random N(0,1) bf16 or a constant -- the chip's clock depends on
+//     the data);
 //   * a streaming read: every byte of a buffer read once with 16-byte loads, four in flight per lane;
 //   * the split-KV decode's read pattern: caches [B, L, H, 128] bf16, workgroup = (split, KV head, batch),
 //     64 rows of 256 B per step for K and for V.
@@ -21,6 +22,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMfmaThreads = 256;
 constexpr int kReadThreads = 256;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Each lane loads four A and four B operand registers once, then issues iters x 32 MFMAs cycling over four
 // independent accumulators (a dependent MFMA is four issues later, so the chain never stalls the pipe).
@@ -45,6 +48,32 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_loop_kernel(const bf16x8* _
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 16; ++i) r += c[j][i];
+    sink[gid] = r;
+}
+
+// The same FLOPs with v_mfma_f32_16x16x32_bf16 (half the FLOPs per instruction): iters x 64 MFMAs over
+// eight accumulators, A and B changing at the same pace as in mfma_loop_kernel.
+__global__ __launch_bounds__(kMfmaThreads) void mfma16_loop_kernel(const bf16x8* __restrict__ ops, int64_t n_ops,
+                                                                   float* __restrict__ sink, int iters) {
+    const int64_t gid = (int64_t)blockIdx.x * kMfmaThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kMfmaThreads;
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        a[j] = ops[(gid + j * stride) % n_ops];
+        b[j] = ops[(gid + (j + 4) * stride) % n_ops];
+    }
+    f32x4 c[8] = {};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 64; ++s)
+            c[s & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s & 3], b[(s >> 3) & 3], c[s & 7], 0, 0, 0);
+    }
+    float r = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r += c[j][i];
     sink[gid] = r;
 }
 
@@ -102,19 +131,26 @@ int ceil_device_info(int* compute_units, int* clock_khz) {
     return (int)e;
 }
 
-// FLOPs of one ceil_mfma_loop call: workgroups * 4 waves * iters * 32 MFMAs * 32768.
+// FLOPs of one ceil_mfma_loop call (either shape): workgroups * 4 waves * iters * 32 * 32768.
 double ceil_mfma_loop_flops(int32_t workgroups, int32_t iters) {
     return (double)workgroups * (kMfmaThreads / 64) * iters * 32.0 * 32768.0;
 }
 
 // ops: n_ops 16-byte vectors of 8 bf16 (device); sink: >= workgroups*256 floats (device).
+// shape 0: v_mfma_f32_32x32x16_bf16, 1: v_mfma_f32_16x16x32_bf16.
 int ceil_mfma_loop(const void* ops, int64_t n_ops, float* sink, int64_t sink_elems, int32_t workgroups,
-                   int32_t iters, void* stream) {
+                   int32_t iters, int32_t shape, void* stream) {
     if (!ops || !sink || n_ops < 1 || workgroups < 1 || iters < 1 || (reinterpret_cast<uintptr_t>(ops) & 15u) ||
-        sink_elems < (int64_t)workgroups * kMfmaThreads)
+        sink_elems < (int64_t)workgroups * kMfmaThreads || (shape != 0 && shape != 1))
         return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(mfma_loop_kernel, dim3(workgroups), dim3(kMfmaThreads), 0,
-                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const bf16x8*>(ops), n_ops, sink, iters);
+    if (shape == 0)
+        hipLaunchKernelGGL(mfma_loop_kernel, dim3(workgroups), dim3(kMfmaThreads), 0,
+                           reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const bf16x8*>(ops), n_ops, sink,
+                           iters);
+    else
+        hipLaunchKernelGGL(mfma16_loop_kernel, dim3(workgroups), dim3(kMfmaThreads), 0,
+                           reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const bf16x8*>(ops), n_ops, sink,
+                           iters);
     return (int)hipGetLastError();
 }
 

@@ -1,9 +1,9 @@
 """The device micro-benchmarks bench.py reports beside the roofline fractions (ceilings/ceilings.hip).
 
 CPU: the library loads, exports its entry points and rejects arguments that do not fit its kernels
-(validation runs before any device call).  GPU: each kernel runs at a small size; the MFMA loop on
-all-ones operands must leave exactly iters * 8 MFMAs * 16 (the contraction depth) in each of its
-accumulator elements, which pins the number of MFMAs it issues (and so the FLOPs bench.py divides).
+(validation runs before any device call).  GPU: each kernel runs at a small size; the MFMA loops on
+all-ones operands must leave exactly iters * 8 MFMAs * the contraction depth (16 or 32) in each of their
+accumulator elements, which pins the number of MFMAs they issue (and so the FLOPs bench.py divides).
 """
 import ctypes
 import os
@@ -30,8 +30,9 @@ def test_exports_and_flop_count(lib):
 
 def test_validation_before_launch(lib):
     assert lib.ceil_device_info(None, None) == HIP_INVALID_VALUE
-    assert lib.ceil_mfma_loop(None, 1, None, 0, 1, 1, None) == HIP_INVALID_VALUE
-    assert lib.ceil_mfma_loop(16, 1, 16, 255, 1, 1, None) == HIP_INVALID_VALUE        # sink too small
+    assert lib.ceil_mfma_loop(None, 1, None, 0, 1, 1, 0, None) == HIP_INVALID_VALUE
+    assert lib.ceil_mfma_loop(16, 1, 16, 256, 1, 1, 2, None) == HIP_INVALID_VALUE        # unknown shape
+    assert lib.ceil_mfma_loop(16, 1, 16, 255, 1, 1, 0, None) == HIP_INVALID_VALUE     # sink too small
     assert lib.ceil_read_stream(16, 24, 16, 256, 1, None) == HIP_INVALID_VALUE        # not a multiple of 16
     assert lib.ceil_read_decode(16, 16, 1, 192, 1, 2, 16, 256, None) == HIP_INVALID_VALUE   # L % (64 splits)
 
@@ -44,10 +45,16 @@ def test_kernels_run(lib):
     wgs, iters = 8, 10
     ops = torch.ones(8 * 64, dtype=torch.bfloat16, device=dev)
     sink = torch.zeros(wgs * 256, dtype=torch.float32, device=dev)
-    assert lib.ceil_mfma_loop(ops.data_ptr(), ops.numel() // 8, sink.data_ptr(), sink.numel(), wgs, iters,
+    assert lib.ceil_mfma_loop(ops.data_ptr(), ops.numel() // 8, sink.data_ptr(), sink.numel(), wgs, iters, 0,
                               stream) == 0
     torch.cuda.synchronize()
     assert torch.all(sink == 4 * 16 * iters * 8 * 16).item()
+    # 16x16x32: 8 accumulators of 4, each updated 8 times per iteration, 32 products per element
+    sink.zero_()
+    assert lib.ceil_mfma_loop(ops.data_ptr(), ops.numel() // 8, sink.data_ptr(), sink.numel(), wgs, iters, 1,
+                              stream) == 0
+    torch.cuda.synchronize()
+    assert torch.all(sink == 8 * 4 * iters * 8 * 32).item()
 
     buf = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
     small = torch.zeros(256, dtype=torch.float32, device=dev)
