@@ -428,7 +428,8 @@ def run_decode_loop(fa, synth, torch, dev, steps=5):
     """One decode step of a 36-layer routed stack at position 262143 (batch 8, 32/8 heads, head_dim 128):
     each layer appends its new token and attends from it (flux_decode_step_layers); the 12 dense layers
     (seeded plan) stream a full 262144-row cache, the 24 sparse layers a 2176-row window cache.
-    Compared with the same step when every layer is dense.  The all-dense run reuses the 12 dense
+    Compared with the same step when every layer is dense, and also timed as one HIP-graph replay of
+    the routed step (the 108 launches captured once).  The all-dense run reuses the 12 dense
     caches three times each (36 distinct 8.6 GB caches would not fit in HBM); every layer call still
     streams its whole cache from HBM."""
     L, B, Hq, Hkv, d, S = 36, 8, 32, 8, 128, 262144
@@ -455,6 +456,18 @@ def run_decode_loop(fa, synth, torch, dev, steps=5):
     routed = lambda: fa.flux_decode_step_layers(plan, qs, kn, vn, kc, vc, os_, None, pos=S - 1, dense_cache_rows=S,
                                                 sink_tokens=sink, window_tokens=window, workspace=ws)
     ms_r = time_steps(routed, steps, 1)
+    # the same step captured once in a HIP graph and replayed (no per-launch host work)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        routed()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        routed()
+    ms_g = time_steps(graph.replay, steps, 1)
+    del graph
     dense_kc = [dense_k[l % 12] for l in range(L)]
     dense_vc = [dense_v[l % 12] for l in range(L)]
     all_dense = lambda: fa.flux_decode_step_layers(np.zeros(L, np.int32), qs, kn, vn, dense_kc, dense_vc, os_, None,
@@ -463,6 +476,7 @@ def run_decode_loop(fa, synth, torch, dev, steps=5):
     ms_d = time_steps(all_dense, steps, 1)
     bytes_r = int(12 * B * Hkv * S * d * 4 + 24 * B * Hkv * (sink + window) * d * 4)
     res = {"routed_ms": round(ms_r, 3), "routed_tok/s": round(B / (ms_r * 1e-3), 1),
+           "routed_graph_ms": round(ms_g, 3), "routed_graph_tok/s": round(B / (ms_g * 1e-3), 1),
            "all_dense_ms": round(ms_d, 3), "all_dense_tok/s": round(B / (ms_d * 1e-3), 1),
            "speedup": round(ms_d / ms_r, 3), "dense_layers": int((plan == 0).sum()),
            "routed_kv_GB/s": round(bytes_r / ms_r / 1e6, 1)}

@@ -342,3 +342,49 @@ def test_decode_rising_scores(fa, mode, ns):
                                  window_tokens=1024)
     check_close(o.cpu().numpy(), ref, "decode rising")
     check_lse(lse.cpu().numpy(), ref_lse, "decode rising lse")
+
+
+# ------------------------------------------------------------------ graph capture of a decode step
+def test_decode_step_layers_graph_replay(fa):
+    """The routed decode step of a small stack captured in a HIP graph (the launch-bound loop a serving
+    engine replays): every replay, with eager work between replays, reproduces the eager outputs bit
+    for bit (the step allocates nothing and issues no memset)."""
+    B, Hq, Hkv, d, sink, window, pos, cap = 2, 8, 2, 128, 128, 256, 900, 1024
+    say("decode step layers, graph replay")
+    modes = [1, 0, 1, 0]
+    L = len(modes)
+    wrows = fa.flux_window_cache_rows(64, sink, window)
+    qds = [synth.torch_normal((B, Hq, d), 61 + l, torch.bfloat16) for l in range(L)]
+    kns = [synth.torch_normal((B, Hkv, d), 71 + l, torch.bfloat16) for l in range(L)]
+    vns = [synth.torch_normal((B, Hkv, d), 81 + l, torch.bfloat16) for l in range(L)]
+    kcs = [synth.torch_normal((B, cap if m == 0 else wrows, Hkv, d), 91 + l, torch.bfloat16) for l, m in enumerate(modes)]
+    vcs = [synth.torch_normal((B, cap if m == 0 else wrows, Hkv, d), 101 + l, torch.bfloat16) for l, m in enumerate(modes)]
+    os_ = [torch.empty((B, Hq, d), dtype=torch.float32, device=DEV) for _ in range(L)]
+    ws = torch.empty(fa.flux_decode_workspace_size(B, Hq, Hkv, pos + 1, d, 0, 64, sink, window), dtype=torch.uint8,
+                     device=DEV)
+
+    def step():
+        fa.flux_decode_step_layers(modes, qds, kns, vns, kcs, vcs, os_, None, pos=pos, dense_cache_rows=cap,
+                                   sink_tokens=sink, window_tokens=window, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in os_]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for o in os_:
+            o.fill_(float("nan"))   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert torch.equal(os_[l], eager[l]), f"replay {rep} layer {l}"
+    del g
