@@ -158,6 +158,9 @@ def main():
                     help="skip the headline step (profiling a single leg)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run one plain device-to-device copy of MIB MiB (HBM counter calibration)")
+    ap.add_argument("--sustain", nargs=2, metavar=("DATA", "SECONDS"), default=None,
+                    help="only run the seq-65536 dense-causal prefill back to back for SECONDS with DATA = randn "
+                         "(N(0,1) inputs) or const (constant inputs), for reading clocks with rocm-smi meanwhile")
     ap.add_argument("--stack", action="store_true", help="also time the 36-layer routed stack at seq 131072")
     ap.add_argument("--steps-leg", type=int, default=20, help="timed repetitions per secondary leg")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false", default=True)
@@ -183,6 +186,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes": n}), flush=True)
         return
+    if args.sustain:
+        run_sustain(fa, synth, torch, args.sustain[0], float(args.sustain[1]))
+        return
     legs_sel = set() if args.legs == "none" else set(x for x in args.legs.split(",") if x)
     if args.stack:
         legs_sel.add("stack")
@@ -198,6 +204,31 @@ def main():
     if args.cpu_baseline and args.headline:
         result["cpu_baseline"] = cpu_baseline(synth)
     print(json.dumps(result), flush=True)
+
+
+def run_sustain(fa, synth, torch, data, seconds):
+    """The seq-65536 dense-causal prefill (32/8 heads, d 128) back to back for `seconds`; N(0,1) or constant
+    inputs.  Prints the mean time per call (the clock the chip settles at depends on the data)."""
+    B, S, Hq, Hkv, d = 1, 65536, 32, 8, 128
+    q = synth.torch_normal((B, S, Hq, d), 1102, torch.bfloat16)
+    k = synth.torch_normal((B, S, Hkv, d), 1103, torch.bfloat16)
+    v = synth.torch_normal((B, S, Hkv, d), 1104, torch.bfloat16)
+    if data == "const":
+        q.fill_(0.01)
+        k.fill_(0.02)
+        v.fill_(0.5)
+    o = torch.empty_like(q)
+    log(f"sustained prefill, {data} inputs, {seconds} s")
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_DENSE)
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    print(json.dumps({"sustain": data, "calls": n, "seconds": round(dt, 2), "ms_per_call": round(dt / n * 1e3, 3)}),
+          flush=True)
 
 
 def headline(args, fa, synth, torch, dev):
