@@ -357,3 +357,53 @@ def test_large_scores_rescale_path(fa, pattern, mode):
                                     sink_tokens=64, window_tokens=128)
     check_close(o.cpu().numpy(), ref, f"large scores {pattern}")
     check_lse(lse.cpu().numpy(), np.transpose(ref_lse, (0, 2, 1)), f"large scores {pattern} lse")
+
+
+# ------------------------------------------------------------- graph capture of the routed step
+def test_routed_step_graph_replay(fa):
+    """Router + routed prefill of two layers (one routed dense, one sparse by the head bias) captured in a
+    HIP graph: each replay, with eager work between replays, reproduces the eager outputs and modes bit
+    for bit (the router resets its own counters with a kernel; nothing in the step issues a memset)."""
+    B, S, Hq, Hkv, d, L = 1, 700, 4, 2, 128, 2
+    say("routed step graph replay")
+    qs = [synth.torch_normal((B, S, Hq, d), 801 + l, torch.bfloat16) for l in range(L)]
+    ks = [synth.torch_normal((B, S, Hkv, d), 811 + l, torch.bfloat16) for l in range(L)]
+    vs = [synth.torch_normal((B, S, Hkv, d), 821 + l, torch.bfloat16) for l in range(L)]
+    os_ = [torch.empty((B, S, Hq, d), dtype=torch.float32, device=DEV) for _ in range(L)]
+    w = synth.router_weights(L, Hq * d, 64, seed=831)
+    w[3][0, 0] += 8.0    # layer 0 dense
+    w[3][1, 1] += 8.0    # layer 1 sparse
+    wd = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in w]
+    modes = torch.empty(L, dtype=torch.int32, device=DEV)
+    ws = torch.empty(fa.flux_route_workspace_size(L, Hq, d, 64), dtype=torch.uint8, device=DEV)
+    rp, ci = _csr_dev(fa, S, 128, 256)
+
+    def step():
+        fa.flux_route_layers([q[0] for q in qs], *wd, modes, None, workspace=ws, pool_tokens=100)
+        fa.flux_attn_prefill_layers_routed(modes, qs, ks, vs, os_, None, sink_tokens=128, window_tokens=256,
+                                           blk_row_ptr=rp, blk_col_idx=ci)
+
+    step()
+    torch.cuda.synchronize()
+    assert modes.cpu().tolist() == [0, 1]
+    eager = [o.clone() for o in os_]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        modes.fill_(-1)
+        for o in os_:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert modes.cpu().tolist() == [0, 1], f"replay {rep} modes"
+        for l in range(L):
+            assert torch.equal(os_[l], eager[l]), f"replay {rep} layer {l}"
+    del g
