@@ -136,8 +136,10 @@ struct Lanes {
     }
 };
 
-// Work queue: thread 0 takes the next unit; two LDS cells alternate so that the value read at the
-// end of one unit is not overwritten before every thread has read it.
+// Work queue: thread 0 takes the next unit during the current unit's last step (taking it earlier would
+// fix each workgroup's next unit at the start of the current one and undo the balancing of a dynamic
+// queue when units are few and long); two LDS cells alternate so that the value read at the end of one
+// unit is not overwritten before every thread has read it.
 struct Queue {
     int* counter;
     int* cell;   // LDS [2]
@@ -293,6 +295,17 @@ __device__ __forceinline__ void grad_product(const Lanes<D>& L, const char* xt, 
     __builtin_amdgcn_s_setprio(0);
 }
 
+// Key pairs (128 keys) that hold sink blocks when the pattern is block-sparse and query heads are grouped:
+// every query sees them, so they are split by query head (one unit per head, partial dK/dV summed by
+// bwd_group_sum_kernel) rather than taking a KV head's G heads in one unit, which would make them the
+// longest units by a factor of G.
+__host__ __device__ __forceinline__ int dkdv_sink_pairs(const BackwardArgs& a) {
+    if (!a.sparse || !a.causal || a.hq == a.hkv) return 0;
+    const int npk = (a.n_qblk + 1) / 2;
+    const int sp = (a.sink_blocks + 1) / 2;
+    return sp < npk ? sp : npk;
+}
+
 // ------------------------------------------------------------------ dK, dV
 //
 // 8 waves, two per SIMD, on 128 keys: waves w and w + 4 own the same 32 keys; wave w accumulates
@@ -320,8 +333,10 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
     int par = 0;                      // parity of the P buffer of the next half
 
     const int seq = (int)a.seq, nqb = a.n_qblk, G = a.hq / a.hkv;
-    const int bh_total = (int)a.batch * a.hq;
-    const int total = ((nqb + 1) / 2) * bh_total;
+    const int bh_total = (int)a.batch * a.hq, bg_total = (int)a.batch * a.hkv;
+    const int n_sp = dkdv_sink_pairs(a);
+    const int ph_units = n_sp * bh_total;
+    const int total = ph_units + ((nqb + 1) / 2 - n_sp) * bg_total;
     const uint32_t q_stride = (uint32_t)a.hq * D;
     const float c2 = a.scale_log2;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
@@ -329,9 +344,26 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
     Queue queue{a.counters + 0, qcell, 0};
     int u = queue.first();
     while (u < total) {
-        queue.prefetch();
-        const int m = u / bh_total, bh = u % bh_total;   // key pair m: longest query range first
-        const int b = bh / a.hq, h = bh % a.hq, g = h / G;
+        // Units, longest query range first: a key pair holding sink blocks (every query sees it) with one
+        // query head, its dK/dV going to per-head partials; any other key pair with all G query heads of
+        // one KV head in turn, summed in registers in head order and written to dK/dV directly.
+        int m, b, h0, nh;
+        if (u < ph_units) {
+            m = u / bh_total;
+            const int bh = u % bh_total;
+            b = bh / a.hq;
+            h0 = bh % a.hq;
+            nh = 1;
+        } else {
+            const int v = u - ph_units;
+            m = n_sp + v / bg_total;
+            const int bg = v % bg_total;
+            b = bg / a.hkv;
+            h0 = (bg % a.hkv) * G;
+            nh = G;
+        }
+        const bool partial = nh < G;
+        const int g = h0 / G;
         const int kb = 2 * m + (ks >> 1);                 // this wave's key block
         const int key = 128 * m + 32 * ks + n;            // this lane's key
         int lo = 0, hi = nqb - 1;
@@ -340,12 +372,13 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
             if (a.sparse && 2 * m >= a.sink_blocks) hi = min(hi, 2 * m + a.window_blocks);
         }
         const int nt = hi - lo + 1;
+        const int nsteps = nh * nt;   // the unit's steps: its heads in order, each over tiles lo .. hi
 
-        const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * D;
-        const u16* dog = reinterpret_cast<const u16*>(a.d_o) + ((int64_t)b * a.seq * a.hq + h) * D;
-        const float* stg = a.stat + ((int64_t)b * a.hq + h) * nqb * 128;
         // a tile is 32 loads of 1 KB (Q by waves 0-3, dO by waves 4-7) plus 2 of row statistics
-        auto issue = [&](int t, int slot) {
+        auto issue = [&](int h, int t, int slot) {
+            const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * D;
+            const u16* dog = reinterpret_cast<const u16*>(a.d_o) + ((int64_t)b * a.seq * a.hq + h) * D;
+            const float* stg = a.stat + ((int64_t)b * a.hq + h) * nqb * 128;
             const uint32_t base = lds0 + slot * kSlotB;
             if (wave < 4) load_tile<D>(qg, q_stride, 64 * t, seq - 1, base, wave, lane);
             else load_tile<D>(dog, q_stride, 64 * t, seq - 1, base + kTileB, wave - 4, lane);
@@ -355,7 +388,7 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
                 load_lds_4(sp, 256u + 4u * lane, base + 2 * kTileB + 256);
             }
         };
-        issue(lo, 0);
+        issue(h0, lo, 0);
 
         // this lane's key row as the B operand (k-slots = d): K for the dV wave (S = Q K^T), V for the
         // dK wave (dP = dO V^T)
@@ -421,12 +454,13 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
             }
         };
 
-        int slot = 0;
-        for (int i = 0; i < nt; ++i) {
-            const int t = lo + i;
+        int slot = 0, t = lo, h = h0;
+        for (int i = 0; i < nsteps; ++i) {
+            const int t_next = t < hi ? t + 1 : lo, h_next = t < hi ? h : h + 1;
             __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's share of tile t landed
             __syncthreads();                       // tile t complete; every wave is done with tile t-1
-            if (i + 1 < nt) issue(t + 1, slot ^ 1);
+            if (i + 1 < nsteps) issue(h_next, t_next, slot ^ 1);
+            else queue.prefetch();   // the next unit is taken when this one ends (keeps the queue dynamic)
             const char* qt = smem + slot * kSlotB;
             // masked iff query < key, i.e. C < lim with C = query - 64t - 4hh
             int lim = key - 64 * t - 4 * hh;
@@ -437,13 +471,15 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
             const bool need_mask = a.causal && (t <= kb || lim == 1000);
             tile(qt, lim, need_mask);
             slot ^= 1;
+            t = t_next;
+            h = h_next;
         }
 
         // lane holds column key, rows d = 32mt + 8(r/4) + 4hh + r%4
         if (key < seq) {
             float* dst;
-            if (G == 1) dst = (is_dk ? a.dk : a.dv) + (((int64_t)b * a.seq + key) * a.hkv + g) * D;
-            else dst = (is_dk ? a.dk_part : a.dv_part) + (((int64_t)b * a.seq + key) * a.hq + h) * D;
+            if (!partial) dst = (is_dk ? a.dk : a.dv) + (((int64_t)b * a.seq + key) * a.hkv + g) * D;
+            else dst = (is_dk ? a.dk_part : a.dv_part) + (((int64_t)b * a.seq + key) * a.hq + h0) * D;
             const float f = is_dk ? a.scale : 1.0f;
 #pragma unroll
             for (int mt = 0; mt < kNM; ++mt)
@@ -485,7 +521,6 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
     Queue queue{a.counters + 1, qcell, 0};
     int u = queue.first();
     while (u < total) {
-        queue.prefetch();
         const int rank = u / bh_total, bh = u % bh_total;
         const int tp = a.causal ? npair - 1 - rank : rank;   // query-tile pair: causal longest first
         const int b = bh / a.hq, h = bh % a.hq, g = h / G;
@@ -570,6 +605,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
             __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
             __syncthreads();
             if (i + 1 < nt) issue(kb_of(i + 1), slot ^ 1);
+            else queue.prefetch();   // the next unit is taken when this one ends (keeps the queue dynamic)
             const char* kt = smem + slot * 2 * kTileB;
             // masked iff C > lim, C = key - 64kb - 4hh
             int lim = qpos - 64 * kb - 4 * hh;                                     // causal
@@ -602,19 +638,21 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
 
 
 // ------------------------------------------------------------------ grouped-query sum
-// out[b, s, g, :] = sum over j < G of part[b, s, g*G + j, :], j ascending; blockIdx.y picks dK / dV.
+// out[b, s, g, :] = sum over j < G of part[b, s, g*G + j, :], j ascending, for the keys s < nkeys of the
+// per-head units (the sink key pairs); blockIdx.y picks dK / dV.
 template <int D>
-__global__ void __launch_bounds__(256) bwd_group_sum_kernel(BackwardArgs a) {
+__global__ void __launch_bounds__(256) bwd_group_sum_kernel(BackwardArgs a, int64_t nkeys) {
     const int G = a.hq / a.hkv;
     const float* part = blockIdx.y == 0 ? a.dk_part : a.dv_part;
     float* out = blockIdx.y == 0 ? a.dk : a.dv;
-    const int64_t n4 = a.batch * a.seq * a.hkv * (D / 4);
+    const int64_t n4 = a.batch * nkeys * a.hkv * (D / 4);
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n4) return;
     const int d4 = (int)(i % (D / 4));
-    const int64_t rg = i / (D / 4);          // (b, s, g)
+    const int64_t rg = i / (D / 4);          // (b, s, g), s < nkeys
     const int g = (int)(rg % a.hkv);
-    const int64_t bs = rg / a.hkv;
+    const int64_t bk = rg / a.hkv;
+    const int64_t bs = (bk / nkeys) * a.seq + bk % nkeys;
     const float4* src = reinterpret_cast<const float4*>(part + (bs * a.hq + (int64_t)g * G) * D) + d4;
     float4 acc = src[0];
     for (int j = 1; j < G; ++j) {
@@ -624,7 +662,7 @@ __global__ void __launch_bounds__(256) bwd_group_sum_kernel(BackwardArgs a) {
         acc.z += x.z;
         acc.w += x.w;
     }
-    reinterpret_cast<float4*>(out)[i] = acc;
+    reinterpret_cast<float4*>(out + (bs * a.hkv + g) * D)[d4] = acc;
 }
 
 }  // namespace
@@ -637,15 +675,20 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     constexpr int rpb = 256 / (D / 8);
     hipLaunchKernelGGL(bwd_rowstat_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, a);
     if (a.in_f32) return launch_backward_f32(a, s);   // float32 inputs: vector-ALU kernels
-    const int64_t units = ((a.n_qblk + 1) / 2) * a.batch * (int64_t)a.hq;
+    const int64_t npk = (a.n_qblk + 1) / 2;
+    const int64_t n_sp = dkdv_sink_pairs(a);
+    const int64_t units_kv = n_sp * a.batch * a.hq + (npk - n_sp) * a.batch * a.hkv;
+    const int64_t units_q = npk * a.batch * (int64_t)a.hq;
     const int cu = a.num_cu > 0 ? a.num_cu : 256;
-    const unsigned grid_kv = (unsigned)(units < cu ? units : cu);              // one 8-wave group per CU
-    const unsigned grid_q = (unsigned)(units < 2 * cu ? units : 2 * cu);      // two 4-wave groups per CU
+    const unsigned grid_kv = (unsigned)(units_kv < cu ? units_kv : cu);          // one 8-wave group per CU
+    const unsigned grid_q = (unsigned)(units_q < 2 * cu ? units_q : 2 * cu);     // two 4-wave groups per CU
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid_kv), dim3(64 * kKvWaves), 0, s, a);
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid_q), dim3(kThreads), 0, s, a);
-    if (a.hq != a.hkv) {
-        const int64_t n4 = a.batch * a.seq * a.hkv * (D / 4);
-        hipLaunchKernelGGL(bwd_group_sum_kernel<D>, dim3((unsigned)((n4 + 255) / 256), 2), dim3(256), 0, s, a);
+    if (n_sp > 0) {
+        const int64_t nkeys = 128 * n_sp < a.seq ? 128 * n_sp : a.seq;
+        const int64_t n4 = a.batch * nkeys * a.hkv * (D / 4);
+        hipLaunchKernelGGL(bwd_group_sum_kernel<D>, dim3((unsigned)((n4 + 255) / 256), 2), dim3(256), 0, s, a,
+                           nkeys);
     }
     return hipGetLastError();
 }
