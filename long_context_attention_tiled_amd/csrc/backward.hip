@@ -14,17 +14,18 @@
 //   bwd_rowstat_kernel    D and -LSE*log2(e) per query row, in 64-row tiles (rows past the end get
 //                         (-inf, 0), so they weigh nothing); clears the two work-queue heads.  It also
 //                         serves the float32 kernels of backward_f32.hip.
-//   bwd_dkdv_kernel       one work unit = 128 keys (4 groups of 32) and one query head, 8 waves: per
-//                         key group one wave accumulates dV, one dK; they walk the 64-query tiles
-//                         that see those keys: S = Q K^T (dV wave, K in registers, keys in lanes;
+//   bwd_dkdv_kernel       one work unit = 128 keys (4 groups of 32) of one KV head with its query heads
+//                         taken in turn (a single query head for the sink key pairs of block-sparse
+//                         GQA), 8 waves: per key group one wave accumulates dV, one dK; they walk the
+//                         64-query tiles that see those keys: S = Q K^T (dV wave, K in registers, keys in lanes;
 //                         P goes to the dK wave through LDS) and dP = dO V^T (dK wave, V in
 //                         registers), then dV^T += dO^T P or dK^T += Q^T dS with the dO or Q tile
 //                         read transposed from LDS.
 //   bwd_dq_kernel         one work unit = 128 queries (4 waves x 32) of one query head; walks the
 //                         visible 64-key tiles: S^T = K Q^T and dP^T = V dO^T with Q, dO in
 //                         registers (queries in lanes), then dQ^T += K^T dS^T.
-//   bwd_group_sum_kernel  grouped-query attention: adds the per-query-head dK/dV of each group, in
-//                         head order, into dK/dV.
+//   bwd_group_sum_kernel  block-sparse grouped-query attention: adds the per-query-head dK/dV of the
+//                         sink keys, in head order, into dK/dV.
 // Computing dQ apart from dK/dV rebuilds S and dP once more (7 matrix products instead of 5) but
 // needs no atomics: every gradient element is written once, summed in a fixed order.
 //

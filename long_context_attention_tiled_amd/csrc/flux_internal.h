@@ -102,7 +102,7 @@ struct BackwardArgs {
     float* dq;             // [B, S, Hq, d]
     float* dk;             // [B, S, Hkv, d]
     float* dv;
-    float* dk_part;        // workspace [B, S, Hq, d]: per-query-head dK when hq > hkv, else nullptr
+    float* dk_part;        // workspace [B, S, Hq, d]: per-query-head dK of the sink keys (sparse GQA), else unused
     float* dv_part;
     float* stat;           // workspace [B, Hq, n_qblk, 2, 64]: -lse*log2(e), then rowsum(dO * O)
     int* counters;         // workspace [2]: work-queue heads of the dK/dV and dQ kernels
