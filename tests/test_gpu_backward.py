@@ -159,6 +159,13 @@ def test_sparse_batch2_gqa(fa):
     _run_case(fa, 2, 500, 4, 1, mode=1, sink=128, window=128, seed=4751)
 
 
+def test_sparse_odd_group_two_sink_pairs(fa):
+    """Three query heads per KV head, a 3-block sink (two key pairs hold sink blocks, so they run per query
+    head and are summed over the group afterwards; the other pairs take the group's heads in one unit),
+    two sequences, ragged end."""
+    _run_case(fa, 2, 700, 6, 2, mode=1, sink=192, window=128, seed=4771)
+
+
 def test_bf16_output_input(fa):
     """O handed over in bf16: D carries O's rounding (up to 2^-9 relative per element)."""
     _run_case(fa, 1, 328, 2, 2, seed=4429, o_bf16=True, max_abs=2e-2)
