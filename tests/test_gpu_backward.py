@@ -277,3 +277,47 @@ def test_sharp_scores(fa, mode):
                                            sink_tokens=sink, window_tokens=window)
     for name, t, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         _close(t.cpu().numpy(), r, f"sharp {name} mode {mode}", None)
+
+
+# ------------------------------------------------------------- graph capture
+def test_backward_graph_replay(fa):
+    """The backward (row statistics, dK/dV, dQ, sink-key GQA sum) captured in a HIP graph: its work queues
+    are reset by its own first kernel, so every replay, with eager work between replays, reproduces the
+    eager gradients bit for bit."""
+    B, S, Hq, Hkv, d, mode, sink, window = 1, 600, 4, 2, 128, 1, 128, 128
+    say("backward graph replay")
+    scale = default_scale(d)
+    q, k, v, g = _inputs(B, S, Hq, Hkv, seed=4991)
+    qd, kd, vd, gd = (synth.torch_bf16_from_bits(x) for x in (q, k, v, g))
+    o32, lse = _oracle_forward(q, k, v, scale, True, True, sink, window)
+    od, lsed = torch.from_numpy(o32).to(DEV), torch.from_numpy(lse).to(DEV)
+    dq = torch.empty((B, S, Hq, d), dtype=torch.float32, device=DEV)
+    dk = torch.empty((B, S, Hkv, d), dtype=torch.float32, device=DEV)
+    dv = torch.empty_like(dk)
+    ws = torch.empty(fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d), dtype=torch.uint8, device=DEV)
+
+    def step():
+        fa.flux_attn_backward(qd, kd, vd, od, gd, lsed, dq, dk, dv, causal=True, mode=mode, block=64,
+                              sink_tokens=sink, window_tokens=window, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (dq, dk, dv)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in (dq, dk, dv):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t, e in zip(("dq", "dk", "dv"), (dq, dk, dv), eager):
+            assert torch.equal(t, e), f"replay {rep} {name}"
+    del graph
