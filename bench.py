@@ -509,7 +509,8 @@ def run_decode_loop(fa, synth, torch, dev, steps=5):
     res = {"routed_ms": round(ms_r, 3), "routed_tok/s": round(B / (ms_r * 1e-3), 1),
            "routed_graph_ms": round(ms_g, 3), "routed_graph_tok/s": round(B / (ms_g * 1e-3), 1),
            "all_dense_ms": round(ms_d, 3), "all_dense_tok/s": round(B / (ms_d * 1e-3), 1),
-           "speedup": round(ms_d / ms_r, 3), "dense_layers": int((plan == 0).sum()),
+           "speedup": round(ms_d / ms_r, 3), "speedup_graph": round(ms_d / ms_g, 3),
+           "dense_layers": int((plan == 0).sum()),
            "routed_kv_GB/s": round(bytes_r / ms_r / 1e6, 1)}
     del dense_k, dense_v, win_k, win_v, kc, vc, dense_kc, dense_vc
     torch.cuda.empty_cache()
