@@ -443,7 +443,8 @@ def run_backward(fa, synth, torch, dev, reps):
         dq = torch.empty((B, S, Hq, d), dtype=torch.float32, device=dev)
         dk = torch.empty((B, S, Hkv, d), dtype=torch.float32, device=dev)
         dv = torch.empty_like(dk)
-        ws = torch.empty(fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+        ws = torch.empty(fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d, mode, 64, sink), dtype=torch.uint8,
+                         device=dev)
         call = lambda: fa.flux_attn_backward(q, k, v, o, g, lse, dq, dk, dv, causal=True, mode=mode,
                                              sink_tokens=sink, window_tokens=window, workspace=ws)
         ms = time_steps(call, reps, 2)

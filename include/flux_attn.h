@@ -210,11 +210,14 @@ int flux_attn_prefill_soft(const void* q, const void* k, const void* v, void* o,
                            const float* weights_device, void* workspace, size_t workspace_bytes,
                            void* hip_stream);
 
-/* flux_attn_backward_workspace_size -- bytes flux_attn_backward needs for these sizes (0 if invalid):
- * per-row statistics (fp32 [batch, hq, ceil(seq/64)*64, 2]), two counters and, when hq > hkv, two
- * fp32 [batch, seq, hq, head_dim] per-query-head dK/dV buffers. */
+/* flux_attn_backward_workspace_size -- bytes flux_attn_backward needs for these sizes and this mask
+ * (0 if invalid): per-row statistics (fp32 [batch, hq, ceil(seq/64)*64, 2]), two counters and, with
+ * grouped-query attention in block-sparse mode, two fp32 [batch, K, hq, head_dim] per-query-head dK/dV
+ * buffers for the K = min(seq, 128 * ceil(sink_blocks / 2)) keys of the key pairs holding sink blocks
+ * (every query sees them, so they are not grouped by KV head).  mode, block and sink_tokens as passed
+ * to flux_attn_backward. */
 size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq, int32_t hkv,
-                                         int32_t head_dim);
+                                         int32_t head_dim, int32_t mode, int32_t block, int32_t sink_tokens);
 
 /*
  * flux_attn_backward -- gradients of one layer of attention with respect to Q, K and V.

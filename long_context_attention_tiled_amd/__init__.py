@@ -96,7 +96,7 @@ _lib.flux_prefill_soft_workspace_size.restype = _sz
 _lib.flux_attn_prefill_soft.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _i32,
                                         _i32, _vp, _vp, _i64, _vp, _vp, _sz, _vp]
 _lib.flux_attn_prefill_soft.restype = ctypes.c_int
-_lib.flux_attn_backward_workspace_size.argtypes = [_i64, _i64, _i32, _i32, _i32]
+_lib.flux_attn_backward_workspace_size.argtypes = [_i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32]
 _lib.flux_attn_backward_workspace_size.restype = _sz
 _lib.flux_attn_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32,
                                     _f32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
@@ -511,8 +511,9 @@ def flux_attn_prefill_soft(q, k, v, o, weights_dev, *, block: int = 64, sink_tok
            "flux_attn_prefill_soft")
 
 
-def flux_attn_backward_workspace_size(batch, seq, hq, hkv, head_dim) -> int:
-    return int(_lib.flux_attn_backward_workspace_size(batch, seq, hq, hkv, head_dim))
+def flux_attn_backward_workspace_size(batch, seq, hq, hkv, head_dim, mode=FLUX_MODE_DENSE, block=64,
+                                      sink_tokens=0) -> int:
+    return int(_lib.flux_attn_backward_workspace_size(batch, seq, hq, hkv, head_dim, mode, block, sink_tokens))
 
 
 def flux_attn_backward(q, k, v, o, d_o, lse, dq, dk, dv, *, causal: bool = True, mode: int = FLUX_MODE_DENSE,
@@ -532,7 +533,8 @@ def flux_attn_backward(q, k, v, o, d_o, lse, dq, dk, dv, *, causal: bool = True,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        workspace = torch.empty(max(flux_attn_backward_workspace_size(B, S, Hq, Hkv, d), 1), dtype=torch.uint8,
+        workspace = torch.empty(max(flux_attn_backward_workspace_size(B, S, Hq, Hkv, d, mode, block, sink_tokens), 1),
+                                dtype=torch.uint8,
                                 device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.flux_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),

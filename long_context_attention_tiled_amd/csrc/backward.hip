@@ -480,7 +480,7 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
         if (key < seq) {
             float* dst;
             if (!partial) dst = (is_dk ? a.dk : a.dv) + (((int64_t)b * a.seq + key) * a.hkv + g) * D;
-            else dst = (is_dk ? a.dk_part : a.dv_part) + (((int64_t)b * a.seq + key) * a.hq + h0) * D;
+            else dst = (is_dk ? a.dk_part : a.dv_part) + (((int64_t)b * a.part_keys + key) * a.hq + h0) * D;
             const float f = is_dk ? a.scale : 1.0f;
 #pragma unroll
             for (int mt = 0; mt < kNM; ++mt)
@@ -639,11 +639,12 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
 
 
 // ------------------------------------------------------------------ grouped-query sum
-// out[b, s, g, :] = sum over j < G of part[b, s, g*G + j, :], j ascending, for the keys s < nkeys of the
-// per-head units (the sink key pairs); blockIdx.y picks dK / dV.
+// out[b, s, g, :] = sum over j < G of part[b, s, g*G + j, :], j ascending, for the keys s < part_keys of
+// the per-head units (the sink key pairs); blockIdx.y picks dK / dV.
 template <int D>
-__global__ void __launch_bounds__(256) bwd_group_sum_kernel(BackwardArgs a, int64_t nkeys) {
+__global__ void __launch_bounds__(256) bwd_group_sum_kernel(BackwardArgs a) {
     const int G = a.hq / a.hkv;
+    const int64_t nkeys = a.part_keys;
     const float* part = blockIdx.y == 0 ? a.dk_part : a.dv_part;
     float* out = blockIdx.y == 0 ? a.dk : a.dv;
     const int64_t n4 = a.batch * nkeys * a.hkv * (D / 4);
@@ -652,9 +653,9 @@ __global__ void __launch_bounds__(256) bwd_group_sum_kernel(BackwardArgs a, int6
     const int d4 = (int)(i % (D / 4));
     const int64_t rg = i / (D / 4);          // (b, s, g), s < nkeys
     const int g = (int)(rg % a.hkv);
-    const int64_t bk = rg / a.hkv;
+    const int64_t bk = rg / a.hkv;           // b * nkeys + s
     const int64_t bs = (bk / nkeys) * a.seq + bk % nkeys;
-    const float4* src = reinterpret_cast<const float4*>(part + (bs * a.hq + (int64_t)g * G) * D) + d4;
+    const float4* src = reinterpret_cast<const float4*>(part + (bk * a.hq + (int64_t)g * G) * D) + d4;
     float4 acc = src[0];
     for (int j = 1; j < G; ++j) {
         const float4 x = src[j * (D / 4)];
@@ -672,12 +673,16 @@ namespace {
 
 template <int D>
 hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
+    const int64_t npk = (a.n_qblk + 1) / 2;
+    const int64_t n_sp = dkdv_sink_pairs(a);
+    // the per-head partial buffers must hold exactly the sink key pairs' keys (checked before any launch)
+    if (!a.in_f32 && n_sp > 0 &&
+        (a.part_keys != (128 * n_sp < a.seq ? 128 * n_sp : a.seq) || !a.dk_part || !a.dv_part))
+        return hipErrorInvalidValue;
     const int64_t rows = a.batch * (int64_t)a.n_qblk * 64 * a.hq;
     constexpr int rpb = 256 / (D / 8);
     hipLaunchKernelGGL(bwd_rowstat_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, a);
     if (a.in_f32) return launch_backward_f32(a, s);   // float32 inputs: vector-ALU kernels
-    const int64_t npk = (a.n_qblk + 1) / 2;
-    const int64_t n_sp = dkdv_sink_pairs(a);
     const int64_t units_kv = n_sp * a.batch * a.hq + (npk - n_sp) * a.batch * a.hkv;
     const int64_t units_q = npk * a.batch * (int64_t)a.hq;
     const int cu = a.num_cu > 0 ? a.num_cu : 256;
@@ -686,10 +691,8 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid_kv), dim3(64 * kKvWaves), 0, s, a);
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid_q), dim3(kThreads), 0, s, a);
     if (n_sp > 0) {
-        const int64_t nkeys = 128 * n_sp < a.seq ? 128 * n_sp : a.seq;
-        const int64_t n4 = a.batch * nkeys * a.hkv * (D / 4);
-        hipLaunchKernelGGL(bwd_group_sum_kernel<D>, dim3((unsigned)((n4 + 255) / 256), 2), dim3(256), 0, s, a,
-                           nkeys);
+        const int64_t n4 = a.batch * a.part_keys * a.hkv * (D / 4);
+        hipLaunchKernelGGL(bwd_group_sum_kernel<D>, dim3((unsigned)((n4 + 255) / 256), 2), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -500,22 +500,34 @@ struct BackwardLayout {
     size_t stat, counters, part, total;   // byte offsets inside the workspace, and its size
 };
 
-BackwardLayout backward_layout(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim) {
+// Keys whose dK/dV the dK/dV kernel writes per query head (summed over the group afterwards): with
+// grouped-query attention in block-sparse mode, the 128-key pairs holding sink blocks.
+int64_t backward_part_keys(int64_t seq, int32_t hq, int32_t hkv, bool sparse, int64_t sink_blocks) {
+    if (!sparse || hq == hkv || sink_blocks <= 0) return 0;
+    const int64_t pairs = std::min(ceil_div(sink_blocks, 2), ceil_div(ceil_div(seq, 64), 2));
+    return std::min(128 * pairs, seq);
+}
+
+BackwardLayout backward_layout(int64_t batch, int64_t seq, int32_t hq, int32_t head_dim, int64_t part_keys) {
     BackwardLayout w;
     const int64_t nqb = ceil_div(seq, 64);
     w.stat = 0;
     w.counters = align256((size_t)batch * hq * nqb * 128 * sizeof(float));
     w.part = w.counters + 256;
-    const size_t part_bytes = hq != hkv ? (size_t)batch * seq * hq * head_dim * sizeof(float) : 0;
+    const size_t part_bytes = (size_t)batch * part_keys * hq * head_dim * sizeof(float);
     w.total = w.part + 2 * align256(part_bytes);
     return w;
 }
 
 }  // namespace
 
-size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim) {
+size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                                         int32_t mode, int32_t block, int32_t sink_tokens) {
     if (batch < 1 || seq < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || head_dim < 1) return 0;
-    return backward_layout(batch, seq, hq, hkv, head_dim).total;
+    if (mode != FLUX_MODE_DENSE && mode != FLUX_MODE_SPARSE) return 0;
+    if (block < 1 || sink_tokens < 0 || sink_tokens % block != 0) return 0;
+    const int64_t pk = backward_part_keys(seq, hq, hkv, mode == FLUX_MODE_SPARSE, sink_tokens / block);
+    return backward_layout(batch, seq, hq, head_dim, pk).total;
 }
 
 int flux_attn_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
@@ -547,7 +559,8 @@ int flux_attn_backward(const void* q, const void* k, const void* v, const void* 
         return fail(FLUX_ERR_UNSUPPORTED, "batch * hq * seq exceeds the work-unit range");
     if (seq * (int64_t)std::max(hq, hkv) * head_dim > INT32_MAX)
         return fail(FLUX_ERR_UNSUPPORTED, "seq * max(hq, hkv) * head_dim must stay below 2^31 elements");
-    const BackwardLayout w = backward_layout(batch, seq, hq, hkv, head_dim);
+    const int64_t part_keys = backward_part_keys(seq, hq, hkv, ms.sparse && causal, ms.sink_blocks);
+    const BackwardLayout w = backward_layout(batch, seq, hq, head_dim, part_keys);
     if (!workspace || workspace_bytes < w.total)
         return fail(FLUX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
                     workspace ? workspace_bytes : (size_t)0);
@@ -566,14 +579,15 @@ int flux_attn_backward(const void* q, const void* k, const void* v, const void* 
     a.dv = dv;
     a.stat = reinterpret_cast<float*>(ws + w.stat);
     a.counters = reinterpret_cast<int*>(ws + w.counters);
-    if (hq != hkv) {
-        const size_t pb = align256((size_t)batch * seq * hq * head_dim * sizeof(float));
+    if (part_keys > 0) {
+        const size_t pb = align256((size_t)batch * part_keys * hq * head_dim * sizeof(float));
         a.dk_part = reinterpret_cast<float*>(ws + w.part);
         a.dv_part = reinterpret_cast<float*>(ws + w.part + pb);
     } else {
         a.dk_part = nullptr;
         a.dv_part = nullptr;
     }
+    a.part_keys = part_keys;
     a.batch = batch;
     a.seq = seq;
     a.hq = hq;

@@ -102,8 +102,9 @@ struct BackwardArgs {
     float* dq;             // [B, S, Hq, d]
     float* dk;             // [B, S, Hkv, d]
     float* dv;
-    float* dk_part;        // workspace [B, S, Hq, d]: per-query-head dK of the sink keys (sparse GQA), else unused
+    float* dk_part;        // workspace [B, part_keys, Hq, d]: per-query-head dK of the sink keys (sparse GQA)
     float* dv_part;
+    int64_t part_keys;     // keys held by dk_part / dv_part (the sink key pairs' keys), 0 if none
     float* stat;           // workspace [B, Hq, n_qblk, 2, 64]: -lse*log2(e), then rowsum(dO * O)
     int* counters;         // workspace [2]: work-queue heads of the dK/dV and dQ kernels
     int64_t batch;

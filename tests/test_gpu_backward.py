@@ -294,7 +294,8 @@ def test_backward_graph_replay(fa):
     dq = torch.empty((B, S, Hq, d), dtype=torch.float32, device=DEV)
     dk = torch.empty((B, S, Hkv, d), dtype=torch.float32, device=DEV)
     dv = torch.empty_like(dk)
-    ws = torch.empty(fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d, mode, 64, sink), dtype=torch.uint8,
+                     device=DEV)
 
     def step():
         fa.flux_attn_backward(qd, kd, vd, od, gd, lsed, dq, dk, dv, causal=True, mode=mode, block=64,
