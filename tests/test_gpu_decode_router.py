@@ -45,6 +45,9 @@ SMALL = [
     (1, 10000, 8, 2, 128, 1, 128, 1024, 3),     # ragged L, sparse
     (2, 200, 8, 2, 128, 1, 128, 128, 0),         # window overlaps the sink
     (1, 90, 4, 1, 128, 1, 128, 2048, 0),         # L shorter than the sink
+    (2, 6000, 8, 1, 64, 1, 0, 64, 0),            # no sink, one-block window, 8 query heads per KV head
+    (1, 7777, 2, 2, 128, 1, 192, 320, 5),        # MHA, sink of 3 blocks, ragged L, forced splits
+    (4, 65, 16, 8, 64, 1, 64, 64, 0),            # one key past the first block
 ]
 
 

@@ -76,6 +76,10 @@ SMALL = [
     (2, 517, 8, 2, 64, 1, 1, 64, 192),
     (1, 640, 2, 1, 128, 1, 1, 0, 64),          # no sink, window of one block
     (1, 100, 2, 1, 128, 1, 1, 128, 128),       # shorter than the sink
+    (1, 700, 8, 1, 128, 1, 1, 128, 320),       # 8 query heads per KV head, window of 5 blocks, ragged
+    (1, 450, 3, 1, 64, 1, 1, 192, 128),        # odd group (two query tiles per workgroup), sink of 3 blocks
+    (1, 333, 6, 2, 128, 0, 1, 128, 2048),      # odd group, dense causal, ragged
+    (3, 200, 2, 1, 128, 1, 1, 64, 64),         # batch 3, one-block sink and window
 ]
 
 
