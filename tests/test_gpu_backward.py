@@ -166,6 +166,17 @@ def test_sparse_odd_group_two_sink_pairs(fa):
     _run_case(fa, 2, 700, 6, 2, mode=1, sink=192, window=128, seed=4771)
 
 
+def test_sparse_group_of_eight_no_sink(fa):
+    """Eight query heads per KV head on the block-sparse path with no sink (every key pair is a grouped
+    unit) and a 3-block window, ragged end."""
+    _run_case(fa, 1, 600, 8, 1, mode=1, sink=0, window=192, seed=4791)
+
+
+def test_dense_causal_group_of_eight_batch2(fa):
+    """Two sequences, eight query heads per KV head, dense causal, ragged end."""
+    _run_case(fa, 2, 390, 16, 2, seed=4793)
+
+
 def test_bf16_output_input(fa):
     """O handed over in bf16: D carries O's rounding (up to 2^-9 relative per element)."""
     _run_case(fa, 1, 328, 2, 2, seed=4429, o_bf16=True, max_abs=2e-2)
