@@ -73,10 +73,19 @@ __device__ __forceinline__ int swz(int row) {
     else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-// 4-byte direct HBM -> LDS load (see load_lds_16): lane l's dword lands at lds_base + 4*l.
+// 4-byte direct HBM -> LDS load (see load_lds_16, same M0 handling): lane l's dword lands
+// at lds_base + 4*l.
 __device__ __forceinline__ void load_lds_4(const void* sbase, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
-                 : "memory", "m0");
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(voff), "s"(sbase), "s"(lds_base)
+        : "memory");
 }
 
 // 64 rows of D bf16 (row r at base + r * row_stride elements, rows past last_row clamped to it) into

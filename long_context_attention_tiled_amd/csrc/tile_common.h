@@ -29,16 +29,27 @@ __device__ __forceinline__ int swz_v(int row) {
     else return 4 * ((row >> 1) & 1);
 }
 
-// 16-byte direct HBM -> LDS load from sbase + voff (sbase wave-uniform, in SGPRs; voff a
-// per-lane byte offset): lane l's 16 bytes land at LDS byte lds_base + 16*l (lds_base is
-// wave-uniform and goes through M0).  Written as inline asm on purpose: the instruction
-// has no destination register, and hiding it from the compiler's wait-count pass stops
-// that pass from assuming the in-flight write may alias every later LDS read of the
-// other slots (it would then wait for the whole prefetch before the operand reads).
-// The kernel itself waits for vmcnt(0) before the barrier that publishes a tile.
+// 16-byte direct HBM -> LDS load (global_load_lds_dwordx4) from sbase + voff: sbase is
+// wave-uniform (SGPRs), voff a per-lane byte offset; lane l's 16 bytes land at LDS byte
+// lds_base + 16*l.  The instruction takes lds_base from M0, so the asm saves M0, sets it,
+// waits the one cycle an M0 write needs before an LDS DMA reads it, issues the load and
+// restores M0: the compiler's M0 is never changed behind its back.  Written as inline asm
+// on purpose: with the compiler builtin the wait-count pass assumes the in-flight LDS
+// write may alias every later LDS read (a transposing read of another slot among them)
+// and waits for the whole prefetch before the operand reads, and the release fence of
+// the mid-step barrier waits for it as well.  The kernels wait for vmcnt(0) themselves
+// before the barrier that publishes a tile.
 __device__ __forceinline__ void load_lds_16(const void* sbase, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
-                 : "memory", "m0");
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(voff), "s"(sbase), "s"(lds_base)
+        : "memory");
 }
 
 // The same pointer value taken from the first active lane, so that it lives in SGPRs.
