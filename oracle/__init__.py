@@ -39,6 +39,9 @@ def _load():
     lib.oracle_attention_backward.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, dbl, i32, i32, i32, i32,
                                               i32, i32, vp, vp, vp]
     lib.oracle_attention_backward.restype = i32
+    lib.oracle_attention_backward_keys.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, dbl, i32, i32,
+                                                   i32, i32, i32, vp, i64, i32, vp, vp]
+    lib.oracle_attention_backward_keys.restype = i32
     lib.oracle_soft_weights.argtypes = [vp, vp, dbl, i32, vp]
     lib.oracle_soft_weights.restype = i32
     lib.oracle_mix.argtypes = [vp, vp, dbl, dbl, i64, vp]
@@ -211,3 +214,25 @@ def attention_backward(q, k, v, d_o, scale, causal=True, sparse=False, block=64,
     if rc != 0:
         raise ValueError(f"oracle_attention_backward failed ({rc})")
     return dq, dk, dv
+
+
+def attention_backward_keys(q, k, v, d_o, scale, keys, causal=True, sparse=False, block=64, sink_tokens=0,
+                            window_tokens=0, n_threads=0):
+    """dK, dV ([n, d] float64 each) of the requested keys only: keys is an int array [n, 3] of
+    (b, kv head g, key position j).  Same gradients as attention_backward at those rows."""
+    q, k, v, d_o = (np.ascontiguousarray(x) for x in (q, k, v, d_o))
+    kind = _kind_of(q)
+    assert _kind_of(k) == kind and _kind_of(v) == kind and _kind_of(d_o) == kind
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    keys = np.ascontiguousarray(np.asarray(keys, dtype=np.int64).reshape(-1, 3))
+    n = keys.shape[0]
+    dk = np.empty((n, d), np.float64)
+    dv = np.empty((n, d), np.float64)
+    rc = _load().oracle_attention_backward_keys(_ptr(q), _ptr(k), _ptr(v), _ptr(d_o), kind, B, S, Hq, Hkv, d,
+                                                float(scale), int(causal), int(sparse), int(block),
+                                                int(sink_tokens), int(window_tokens), _ptr(keys), n,
+                                                int(n_threads), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError(f"oracle_attention_backward_keys failed ({rc})")
+    return dk, dv

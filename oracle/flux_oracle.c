@@ -450,3 +450,133 @@ int oracle_attention_backward(const void* q, const void* k, const void* v, const
     }
     return 0;
 }
+
+/*
+ * dK and dV of selected keys only (same definition as oracle_attention_backward, restricted to
+ * the requested key rows), for checking gradients at sizes where the full backward is too slow.
+ * keys: n_keys triples (b, g, j) = (batch, KV head, key position); dk, dv: [n_keys, d] doubles.
+ * For a requested key j of KV head g:
+ *   dv_j = sum over query heads h of the group and rows i that may attend to j of p_ij dO_i
+ *   dk_j = sum over the same (h, i) of scale * p_ij (dp_ij - D_i) q_i
+ * with p_ij the row's softmax probability, dp_ij = <dO_i, v_j> and D_i = sum_j' p_ij' dp_ij' over
+ * the row's allowed keys.  Step 1 marks the rows that see a requested key; step 2 computes those
+ * rows' statistics (max m, sum l, D) with the two-pass softmax; step 3 sums each requested key's
+ * gradient over its rows.  Returns 0, 1 on bad arguments, 2 if out of memory.
+ */
+int oracle_attention_backward_keys(const void* q, const void* k, const void* v, const void* d_o, int kind,
+                                   int64_t batch, int64_t seq, int hq, int hkv, int d, double scale, int causal,
+                                   int sparse, int block, int sink_tokens, int window_tokens,
+                                   const int64_t* keys, int64_t n_keys, int n_threads, double* dk, double* dv) {
+    if (check_shapes(batch, seq, hq, hkv, d)) return 1;
+    if (sparse && (!causal || block <= 0)) return 1;
+    for (int64_t r = 0; r < n_keys; ++r)
+        if (keys[3 * r] < 0 || keys[3 * r] >= batch || keys[3 * r + 1] < 0 || keys[3 * r + 1] >= hkv ||
+            keys[3 * r + 2] < 0 || keys[3 * r + 2] >= seq)
+            return 1;
+    const int G = hq / hkv;
+    const int64_t q_stride = (int64_t)hq * d, kv_stride = (int64_t)hkv * d;
+    const int64_t n_rows = batch * hq * seq;   /* row index (b * hq + h) * seq + i */
+    unsigned char* need = (unsigned char*)calloc((size_t)n_rows, 1);
+    double* m_row = (double*)malloc(sizeof(double) * (size_t)n_rows);
+    double* l_row = (double*)malloc(sizeof(double) * (size_t)n_rows);
+    double* D_row = (double*)malloc(sizeof(double) * (size_t)n_rows);
+    if (!need || !m_row || !l_row || !D_row) {
+        free(need);
+        free(m_row);
+        free(l_row);
+        free(D_row);
+        return 2;
+    }
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#endif
+    /* step 1: rows that may attend to at least one requested key of their KV head */
+#pragma omp parallel for schedule(dynamic, 256)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t b = r / ((int64_t)hq * seq), h = (r / seq) % hq, i = r % seq;
+        for (int64_t t = 0; t < n_keys; ++t)
+            if (keys[3 * t] == b && keys[3 * t + 1] == h / G &&
+                key_allowed(i, keys[3 * t + 2], seq, causal, sparse, block, sink_tokens, window_tokens)) {
+                need[r] = 1;
+                break;
+            }
+    }
+    /* step 2: statistics of those rows: m = max_j s_j, l = sum_j exp(s_j - m), D = sum_j p_j dp_j */
+    int err = 0;
+#pragma omp parallel
+    {
+        double* s_buf = (double*)malloc(sizeof(double) * (size_t)seq);
+        if (!s_buf) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                if (!need[r]) continue;
+                const int64_t b = r / ((int64_t)hq * seq), h = (r / seq) % hq, i = r % seq;
+                const int64_t q_off = (b * seq + i) * q_stride + h * d;
+                const int64_t kv_base = b * seq * kv_stride + (h / G) * d;
+                double m = -INFINITY;
+                for (int64_t j = 0; j < seq; ++j) {
+                    if (!key_allowed(i, j, seq, causal, sparse, block, sink_tokens, window_tokens)) continue;
+                    double s = 0.0;
+                    for (int t = 0; t < d; ++t)
+                        s += load_elem(q, kind, q_off + t) * load_elem(k, kind, kv_base + j * kv_stride + t);
+                    s_buf[j] = s * scale;
+                    if (s_buf[j] > m) m = s_buf[j];
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j < seq; ++j)
+                    if (key_allowed(i, j, seq, causal, sparse, block, sink_tokens, window_tokens))
+                        l += exp(s_buf[j] - m);
+                double D = 0.0;
+                for (int64_t j = 0; j < seq; ++j) {
+                    if (!key_allowed(i, j, seq, causal, sparse, block, sink_tokens, window_tokens)) continue;
+                    double a = 0.0;
+                    for (int t = 0; t < d; ++t)
+                        a += load_elem(d_o, kind, q_off + t) * load_elem(v, kind, kv_base + j * kv_stride + t);
+                    D += exp(s_buf[j] - m) / l * a;
+                }
+                m_row[r] = m;
+                l_row[r] = l;
+                D_row[r] = D;
+            }
+        }
+        free(s_buf);
+    }
+    /* step 3: each requested key's dk, dv over the rows that see it */
+    if (!err) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t t = 0; t < n_keys; ++t) {
+            const int64_t b = keys[3 * t], g = keys[3 * t + 1], j = keys[3 * t + 2];
+            const int64_t kv_off = b * seq * kv_stride + j * kv_stride + g * d;
+            double* dk_t = dk + t * d;
+            double* dv_t = dv + t * d;
+            for (int c = 0; c < d; ++c) dk_t[c] = dv_t[c] = 0.0;
+            for (int hh = 0; hh < G; ++hh) {
+                const int64_t h = g * G + hh;
+                for (int64_t i = 0; i < seq; ++i) {
+                    if (!key_allowed(i, j, seq, causal, sparse, block, sink_tokens, window_tokens)) continue;
+                    const int64_t r = (b * hq + h) * seq + i;
+                    const int64_t q_off = (b * seq + i) * q_stride + h * d;
+                    double s = 0.0, dp = 0.0;
+                    for (int c = 0; c < d; ++c) {
+                        s += load_elem(q, kind, q_off + c) * load_elem(k, kind, kv_off + c);
+                        dp += load_elem(d_o, kind, q_off + c) * load_elem(v, kind, kv_off + c);
+                    }
+                    const double p = exp(s * scale - m_row[r]) / l_row[r];
+                    const double ds = p * (dp - D_row[r]);
+                    for (int c = 0; c < d; ++c) {
+                        dv_t[c] += p * load_elem(d_o, kind, q_off + c);
+                        dk_t[c] += scale * ds * load_elem(q, kind, q_off + c);
+                    }
+                }
+            }
+        }
+    }
+    free(need);
+    free(m_row);
+    free(l_row);
+    free(D_row);
+    return err;
+}

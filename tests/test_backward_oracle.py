@@ -108,3 +108,39 @@ def test_sparse_full_window_equals_dense_causal():
                                   window_tokens=48)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+KEY_CASES = [
+    # B, S, Hq, Hkv, d, causal, sparse, block, sink, window
+    (1, 40, 2, 1, 8, True, False, 8, 0, 0),
+    (2, 37, 4, 2, 8, False, False, 8, 0, 0),
+    (2, 70, 6, 2, 4, True, True, 8, 16, 16),   # ragged, sink 2 blocks, window 2 blocks, odd group
+    (1, 64, 8, 1, 8, True, True, 8, 0, 8),      # no sink, diagonal blocks only
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,d,causal,sparse,block,sink,window", KEY_CASES)
+def test_backward_keys_equals_full_backward(B, S, Hq, Hkv, d, causal, sparse, block, sink, window):
+    """dK/dV of a key subset equal the full backward's rows for those keys (every key, then a random
+    subset in shuffled order, so a key written to another's slot fails)."""
+    q, k, v = synth.qkv_bf16(B, S, Hq, Hkv, d, seed=S + Hq)
+    g = synth.normal_bf16_bits((B, S, Hq, d), seed=S + Hq, tensor_id=7)
+    scale = 1.0 / math.sqrt(d)
+    kw = dict(causal=causal, sparse=sparse, block=block, sink_tokens=sink, window_tokens=window)
+    _, dk, dv = oracle.attention_backward(q, k, v, g, scale, **kw)
+    all_keys = np.array([(b, h, j) for b in range(B) for h in range(Hkv) for j in range(S)], np.int64)
+    rng = np.random.default_rng(S)
+    for keys in (all_keys, rng.permutation(all_keys)[: max(3, len(all_keys) // 5)]):
+        gk, gv = oracle.attention_backward_keys(q, k, v, g, scale, keys, **kw)
+        want_k = np.stack([dk[b, j, h] for b, h, j in keys])
+        want_v = np.stack([dv[b, j, h] for b, h, j in keys])
+        np.testing.assert_allclose(gk, want_k, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(gv, want_v, rtol=1e-11, atol=1e-12)
+
+
+def test_backward_keys_rejects_bad_keys():
+    q, k, v = synth.qkv_bf16(1, 16, 2, 1, 4, seed=3)
+    g = synth.normal_bf16_bits((1, 16, 2, 4), seed=3, tensor_id=7)
+    for bad in ((0, 1, 0), (1, 0, 0), (0, 0, 16), (0, 0, -1)):
+        with pytest.raises(ValueError):
+            oracle.attention_backward_keys(q, k, v, g, 0.5, np.array([bad]))

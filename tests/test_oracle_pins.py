@@ -250,15 +250,37 @@ def test_zero_keys_give_mean_of_allowed_values():
         np.testing.assert_allclose(sp[0, i], vv[keys].mean(axis=0), rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("L", [333, 320])
 @pytest.mark.parametrize("sparse", [False, True])
-def test_decode_equals_last_prefill_row(sparse):
-    L, Hq, Hkv, d = 333, 4, 2, 16
+def test_decode_equals_last_prefill_row(sparse, L):
+    """L = 320 is a block multiple: there a decode from position L instead of L-1 would see another
+    window (blocks 8..10 instead of 7..9) and fail."""
+    Hq, Hkv, d = 4, 2, 16
     q, k, v = synth.qkv_f32(2, L, Hq, Hkv, d, seed=4)
     kw = dict(sparse=sparse, block=32, sink_tokens=64, window_tokens=96)
     pre, plse = oracle.attention(q, k, v, 0.25, causal=True, **kw)
     dec, dlse = oracle.decode(np.ascontiguousarray(q[:, -1]), k, v, 0.25, **kw)
     np.testing.assert_array_equal(dec, pre[:, -1])
     np.testing.assert_array_equal(dlse, plse[:, -1])
+
+
+@pytest.mark.parametrize("L", [256, 2304])
+def test_decode_sparse_is_sink_plus_last_window_tokens(L):
+    """With the cache length a multiple of the block, the sparse decode row attends to exactly the sink
+    tokens and the last `window` tokens (the decode workload's own wording: sink 128 plus the last 2048
+    tokens); checked against scipy's softmax over that explicit token set."""
+    from scipy.special import softmax as scipy_softmax
+    block, sink, window = (32, 64, 96) if L == 256 else (64, 128, 2048)
+    Hq, Hkv, d = 2, 1, 16
+    q, k, v = synth.qkv_f32(1, L, Hq, Hkv, d, seed=L)
+    qd = np.ascontiguousarray(q[:, -1])
+    dec, dlse = oracle.decode(qd, k, v, 0.25, sparse=True, block=block, sink_tokens=sink, window_tokens=window)
+    keys = np.r_[0:sink, L - window:L]
+    k64, v64 = k[0, keys, 0].astype(np.float64), v[0, keys, 0].astype(np.float64)
+    for h in range(Hq):
+        s = 0.25 * (k64 @ qd[0, h].astype(np.float64))
+        np.testing.assert_allclose(dec[0, h], scipy_softmax(s) @ v64, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dlse[0, h], np.log(np.sum(np.exp(s))), rtol=1e-14)
 
 
 def test_rows_subset_matches_full():
