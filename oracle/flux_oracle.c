@@ -67,17 +67,39 @@ static double load_elem(const void* base, int kind, int64_t idx) {
  *   sparse (always causal): j <= i and (key block is a sink block, or the key
  *   block lies within the last `window` blocks ending at the query's block).
  * window_tokens == 0 in dense mode means "no window".
+ *
+ * The block tests are restated as two key thresholds that depend on i only:
+ * j/block < sink_blocks  <=>  j < sink_blocks * block, and
+ * i/block - j/block < window_blocks  <=>  j >= (i/block - window_blocks + 1) * block
+ * (floor division, j >= 0), so a scan over the keys of one row does no division.
  */
+typedef struct {
+    int64_t last;           /* last key position the row may see: i when causal or sparse, else seq_k - 1 */
+    int64_t sink_end;       /* sparse: keys before this are sink keys */
+    int64_t window_start;   /* sparse: keys from here on lie in the row's window */
+    int sparse;
+} key_rule;
+
+static key_rule row_rule(int64_t i, int64_t seq_k, int causal, int sparse, int64_t block, int64_t sink_tokens,
+                         int64_t window_tokens) {
+    key_rule r;
+    r.last = (causal || sparse) && i < seq_k - 1 ? i : seq_k - 1;
+    r.sparse = sparse;
+    r.sink_end = sparse ? (sink_tokens / block) * block : 0;
+    r.window_start = sparse ? (i / block - window_tokens / block + 1) * block : 0;
+    return r;
+}
+
+static int rule_allows(const key_rule* r, int64_t j) {
+    if (j < 0 || j > r->last) return 0;
+    if (r->sparse && !(j < r->sink_end || j >= r->window_start)) return 0;
+    return 1;
+}
+
 static int key_allowed(int64_t i, int64_t j, int64_t seq_k, int causal, int sparse,
                        int64_t block, int64_t sink_tokens, int64_t window_tokens) {
-    if (j < 0 || j >= seq_k) return 0;
-    if ((causal || sparse) && j > i) return 0;
-    if (sparse) {
-        int64_t ib = i / block, jb = j / block;
-        int64_t sink_blocks = sink_tokens / block, window_blocks = window_tokens / block;
-        if (!(jb < sink_blocks || ib - jb < window_blocks)) return 0;
-    }
-    return 1;
+    const key_rule r = row_rule(i, seq_k, causal, sparse, block, sink_tokens, window_tokens);
+    return rule_allows(&r, j);
 }
 
 /*
@@ -90,10 +112,11 @@ static void attend_row(const void* q, int64_t q_off, const void* k, const void* 
                        int64_t kv_base, int64_t kv_row_stride, int64_t seq_k, int d, double scale,
                        int64_t i, int causal, int sparse, int64_t block, int64_t sink, int64_t window,
                        double* s_buf, double* acc, double* out, double* lse) {
+    const key_rule rule = row_rule(i, seq_k, causal, sparse, block, sink, window);
     double m = -INFINITY;
     int64_t n_allowed = 0;
     for (int64_t j = 0; j < seq_k; ++j) {
-        if (!key_allowed(i, j, seq_k, causal, sparse, block, sink, window)) continue;
+        if (!rule_allows(&rule, j)) continue;
         double s = 0.0;
         for (int t = 0; t < d; ++t)
             s += load_elem(q, kind, q_off + t) * load_elem(k, kind, kv_base + j * kv_row_stride + t);
@@ -110,7 +133,7 @@ static void attend_row(const void* q, int64_t q_off, const void* k, const void* 
     }
     double l = 0.0;
     for (int64_t j = 0; j < seq_k; ++j) {
-        if (!key_allowed(i, j, seq_k, causal, sparse, block, sink, window)) continue;
+        if (!rule_allows(&rule, j)) continue;
         double p = exp(s_buf[j] - m);
         l += p;
         for (int t = 0; t < d; ++t) acc[t] += p * load_elem(v, kind, kv_base + j * kv_row_stride + t);
@@ -501,12 +524,14 @@ int oracle_attention_backward_keys(const void* q, const void* k, const void* v, 
                 break;
             }
     }
-    /* step 2: statistics of those rows: m = max_j s_j, l = sum_j exp(s_j - m), D = sum_j p_j dp_j */
+    /* step 2: statistics of those rows: m = max_j s_j, l = sum_j exp(s_j - m), D = sum_j p_j dp_j, over
+     * the row's allowed keys (listed once, in ascending order, by the first pass) */
     int err = 0;
 #pragma omp parallel
     {
         double* s_buf = (double*)malloc(sizeof(double) * (size_t)seq);
-        if (!s_buf) {
+        int64_t* allowed = (int64_t*)malloc(sizeof(int64_t) * (size_t)seq);
+        if (!s_buf || !allowed) {
 #pragma omp atomic write
             err = 2;
         } else {
@@ -516,26 +541,27 @@ int oracle_attention_backward_keys(const void* q, const void* k, const void* v, 
                 const int64_t b = r / ((int64_t)hq * seq), h = (r / seq) % hq, i = r % seq;
                 const int64_t q_off = (b * seq + i) * q_stride + h * d;
                 const int64_t kv_base = b * seq * kv_stride + (h / G) * d;
+                const key_rule rule = row_rule(i, seq, causal, sparse, block, sink_tokens, window_tokens);
+                int64_t n_allowed = 0;
                 double m = -INFINITY;
                 for (int64_t j = 0; j < seq; ++j) {
-                    if (!key_allowed(i, j, seq, causal, sparse, block, sink_tokens, window_tokens)) continue;
+                    if (!rule_allows(&rule, j)) continue;
                     double s = 0.0;
                     for (int t = 0; t < d; ++t)
                         s += load_elem(q, kind, q_off + t) * load_elem(k, kind, kv_base + j * kv_stride + t);
-                    s_buf[j] = s * scale;
-                    if (s_buf[j] > m) m = s_buf[j];
+                    s_buf[n_allowed] = s * scale;
+                    allowed[n_allowed++] = j;
+                    if (s * scale > m) m = s * scale;
                 }
                 double l = 0.0;
-                for (int64_t j = 0; j < seq; ++j)
-                    if (key_allowed(i, j, seq, causal, sparse, block, sink_tokens, window_tokens))
-                        l += exp(s_buf[j] - m);
+                for (int64_t a = 0; a < n_allowed; ++a) l += exp(s_buf[a] - m);
                 double D = 0.0;
-                for (int64_t j = 0; j < seq; ++j) {
-                    if (!key_allowed(i, j, seq, causal, sparse, block, sink_tokens, window_tokens)) continue;
-                    double a = 0.0;
+                for (int64_t a = 0; a < n_allowed; ++a) {
+                    const int64_t j = allowed[a];
+                    double dp = 0.0;
                     for (int t = 0; t < d; ++t)
-                        a += load_elem(d_o, kind, q_off + t) * load_elem(v, kind, kv_base + j * kv_stride + t);
-                    D += exp(s_buf[j] - m) / l * a;
+                        dp += load_elem(d_o, kind, q_off + t) * load_elem(v, kind, kv_base + j * kv_stride + t);
+                    D += exp(s_buf[a] - m) / l * dp;
                 }
                 m_row[r] = m;
                 l_row[r] = l;
@@ -543,6 +569,7 @@ int oracle_attention_backward_keys(const void* q, const void* k, const void* v, 
             }
         }
         free(s_buf);
+        free(allowed);
     }
     /* step 3: each requested key's dk, dv over the rows that see it */
     if (!err) {

@@ -7,7 +7,8 @@ to fp32) unless a test says otherwise.  Bar: max-abs <= 1e-2 and mean-abs <= 1e-
 gradients.  A bf16 O (one test) perturbs D = rowsum(dO * O) by its own rounding, which the kernel
 cannot undo; that case is held to max-abs 2e-2.  At the full layer shape (seq 8192, 32/8 heads) the
 oracle cannot run whole: there dQ rows of a causal prefix are compared (rows < T depend only on
-keys < T), and dK, dV are checked against identities that hold at any size.
+keys < T), dK, dV are checked against identities that hold at any size and element-wise on four
+sampled key blocks against the oracle's gradients of those keys only.
 """
 import numpy as np
 import pytest
@@ -58,9 +59,9 @@ def _gpu_forward(fa, qd, kd, vd, causal, mode, sink, window, o_dtype=torch.float
 def _backward(fa, qd, kd, vd, od, gd, lsed, causal, mode, sink, window):
     B, S, Hq, d = qd.shape
     Hkv = kd.shape[2]
-    dq = torch.empty((B, S, Hq, d), dtype=torch.float32, device=DEV)
-    dk = torch.empty((B, S, Hkv, d), dtype=torch.float32, device=DEV)
-    dv = torch.empty((B, S, Hkv, d), dtype=torch.float32, device=DEV)
+    dq = torch.full((B, S, Hq, d), float("nan"), dtype=torch.float32, device=DEV)   # unwritten elements fail
+    dk = torch.full((B, S, Hkv, d), float("nan"), dtype=torch.float32, device=DEV)
+    dv = torch.full((B, S, Hkv, d), float("nan"), dtype=torch.float32, device=DEV)
     fa.flux_attn_backward(qd, kd, vd, od, gd, lsed, dq, dk, dv, causal=causal, mode=mode, block=64,
                           sink_tokens=sink, window_tokens=window)
     torch.cuda.synchronize()
@@ -230,7 +231,9 @@ def test_full_shape_prefix_and_identities(fa, S, mode):
     benchmark times.
     dQ of the first T rows equals the backward of the length-T prefix (causal); dK, dV are checked
     against sum_j dV_j = sum over the group's heads of sum_i dO_i (rows of P sum to one) and
-    sum_j dK_j = 0 (rows of dS sum to zero); a second run must be bit-identical."""
+    sum_j dK_j = 0 (rows of dS sum to zero), and element-wise on four 64-key blocks (sink, window
+    width, middle, last) against the oracle's gradients for those keys; every element written (NaN
+    fill); a second run must be bit-identical."""
     B, Hq, Hkv, T = 1, 32, 8, 384
     sink, window = (128, 2048) if mode == 1 else (0, 0)
     say("backward full shape", f"S={S} mode={mode}")
@@ -265,6 +268,21 @@ def test_full_shape_prefix_and_identities(fa, S, mode):
     # the forward's rounding of O through D = rowsum(dO * O) (measured ~1e-4 of the scale)
     assert err_v <= 2e-5 * mag_v, err_v
     assert err_k <= 1e-3 * mag_k, err_k
+
+    # element-wise dK/dV of four key blocks, each on its own KV head: the first sink block, the block at the
+    # window's width, a middle block and the last block (a key written to another block's rows fails here,
+    # unlike the sums above)
+    nb = S // 64
+    picks = [(0, 0), (32, 3), (nb // 2 + 5, 5), (nb - 1, Hkv - 1)]
+    keys = np.array([(0, kvh, 64 * blk + j) for blk, kvh in picks for j in range(64)], np.int64)
+    say("dK/dV key blocks", picks)
+    rk, rv = oracle.attention_backward_keys(q, k, v, g, scale, keys, causal=True, sparse=bool(mode), block=64,
+                                            sink_tokens=sink, window_tokens=window)
+    dk_h, dv_h = dk.cpu().numpy(), dv.cpu().numpy()
+    for (blk, gh), sl in zip(picks, range(0, len(keys), 64)):
+        rows = keys[sl:sl + 64]
+        check_close(dk_h[rows[:, 0], rows[:, 2], rows[:, 1]], rk[sl:sl + 64], f"dK block {blk} kv head {gh}")
+        check_close(dv_h[rows[:, 0], rows[:, 2], rows[:, 1]], rv[sl:sl + 64], f"dV block {blk} kv head {gh}")
 
 
 # ------------------------------------------------------------- scores far from N(0,1)

@@ -25,8 +25,8 @@ def _decode(fa, qd, kd, vd, out_dtype, mode, kv_len=None, sink=128, window=2048,
     kv_len = cap if kv_len is None else kv_len
     ws_bytes = fa.flux_decode_workspace_size(B, Hq, Hkv, kv_len, d, mode, 64, sink, window, num_splits)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
-    o = torch.empty((B, Hq, d), dtype=out_dtype, device=DEV)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    o = torch.full((B, Hq, d), float("nan"), dtype=out_dtype, device=DEV)      # unwritten elements fail
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
     fa.flux_attn_decode(qd, kd, vd, o, lse, kv_len=kv_len, mode=mode, block=64, sink_tokens=sink,
                         window_tokens=window, num_splits=num_splits, workspace=ws)
     torch.cuda.synchronize()
@@ -114,26 +114,26 @@ def test_decode_equals_prefill_last_row(fa):
 
 
 def test_decode_full_size_dense_and_sparse(fa):
-    """GQA decode: batch 8, KV length 262144, 32 query heads, 8 KV heads, head_dim 128, bf16 cache."""
+    """GQA decode: batch 8, KV length 262144, 32 query heads, 8 KV heads, head_dim 128, bf16 cache, dense
+    and block-sparse (sink 128 + last 2048 tokens): every (sequence, head) output and LSE against the oracle,
+    outputs NaN-filled before the call."""
     B, L, Hq, Hkv, d = 8, 262144, 32, 8, 128
     say("decode full size")
     qd = synth.torch_normal((B, Hq, d), 1005, torch.bfloat16)
     kd = synth.torch_normal((B, L, Hkv, d), 1006, torch.bfloat16)
     vd = synth.torch_normal((B, L, Hkv, d), 1007, torch.bfloat16)
     q = dev_bits_to_host(qd)
-    for mode in (0, 1):
-        o, lse = _decode(fa, qd, kd, vd, torch.float32, mode)
-        o_h, l_h = o.cpu().numpy(), lse.cpu().numpy()
-        for b in (0, 5):
-            kb = dev_bits_to_host(kd[b:b + 1])
-            vb = dev_bits_to_host(vd[b:b + 1])
-            groups = [1, 6] if mode == 0 else list(range(Hkv))
-            rows = np.array([(0, h) for g in groups for h in range(g * 4, g * 4 + 4)], np.int64)
+    outs = {mode: _decode(fa, qd, kd, vd, torch.float32, mode) for mode in (0, 1)}
+    for mode, (o, lse) in outs.items():
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all(), f"mode {mode}: unwritten output"
+    for b in range(B):
+        kb = dev_bits_to_host(kd[b:b + 1])
+        vb = dev_bits_to_host(vd[b:b + 1])
+        for mode, (o, lse) in outs.items():
             ref, ref_lse = oracle.decode(np.ascontiguousarray(q[b:b + 1]), kb, vb, default_scale(d),
-                                         sparse=bool(mode), block=64, sink_tokens=128, window_tokens=2048, rows=rows)
-            got = np.stack([o_h[b, h] for _, h in rows])
-            check_close(got, ref, f"decode full mode {mode} b {b}")
-            check_lse(np.array([l_h[b, h] for _, h in rows]), ref_lse, "decode full lse")
+                                         sparse=bool(mode), block=64, sink_tokens=128, window_tokens=2048)
+            check_close(o[b:b + 1].cpu().numpy(), ref, f"decode full mode {mode} b {b}")
+            check_lse(lse[b:b + 1].cpu().numpy(), ref_lse, f"decode full lse mode {mode} b {b}")
     del qd, kd, vd
     torch.cuda.empty_cache()
 
@@ -142,8 +142,8 @@ def test_decode_full_size_dense_and_sparse(fa):
 def _route_gpu(fa, xs_dev, w):
     L = len(xs_dev)
     wd = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in w]
-    modes = torch.empty(L, dtype=torch.int32, device=DEV)
-    logits = torch.empty((L, 2), dtype=torch.float32, device=DEV)
+    modes = torch.full((L,), -7, dtype=torch.int32, device=DEV)
+    logits = torch.full((L, 2), float("nan"), dtype=torch.float32, device=DEV)
     fa.flux_route_layers(xs_dev, *wd, modes, logits, pool_tokens=100)
     torch.cuda.synchronize()
     return logits.cpu().numpy(), modes.cpu().numpy()
@@ -229,8 +229,8 @@ def test_decode_step_full_cache_appends_and_matches_oracle(fa):
         kn = synth.torch_bf16_from_bits(np.ascontiguousarray(k[:, pos]))
         vn = synth.torch_bf16_from_bits(np.ascontiguousarray(v[:, pos]))
         qd = synth.torch_bf16_from_bits(q)
-        o = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+        o = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+        lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
         ws = torch.empty(fa.flux_decode_workspace_size(B, Hq, Hkv, pos + 1, d, mode, 64, 128, 256), dtype=torch.uint8,
                          device=DEV)
         fa.flux_decode_step(qd, kn, vn, kc, vc, o, lse, pos=pos, layout=fa.FLUX_KV_FULL, mode=mode, sink_tokens=128,
@@ -259,7 +259,7 @@ def test_decode_loop_window_cache_ring(fa):
     kd, vd, qd = (synth.torch_bf16_from_bits(x) for x in (k, v, q))
     kc = torch.zeros((B, rows, Hkv, d), dtype=torch.bfloat16, device=DEV)
     vc = torch.zeros_like(kc)
-    out = torch.empty((n, B, Hq, d), dtype=torch.float32, device=DEV)
+    out = torch.full((n, B, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
     ws = torch.empty(fa.flux_decode_workspace_size(B, Hq, Hkv, n, d, 1, 64, sink, window), dtype=torch.uint8,
                      device=DEV)
     kn_all = kd.transpose(0, 1).contiguous()   # [n, B, Hkv, d]
@@ -312,7 +312,7 @@ def test_decode_step_layers_routed_stack(fa):
     kns = [synth.torch_bf16_from_bits(np.ascontiguousarray(x[:, pos])) for x in ks]
     vns = [synth.torch_bf16_from_bits(np.ascontiguousarray(x[:, pos])) for x in vs]
     qds = [synth.torch_bf16_from_bits(x) for x in qs]
-    os_ = [torch.empty((B, Hq, d), dtype=torch.float32, device=DEV) for _ in range(L)]
+    os_ = [torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=DEV) for _ in range(L)]
     ws = torch.empty(fa.flux_decode_workspace_size(B, Hq, Hkv, pos + 1, d, 0, 64, sink, window), dtype=torch.uint8,
                      device=DEV)
     fa.flux_decode_step_layers(modes, qds, kns, vns, kcs, vcs, os_, None, pos=pos, dense_cache_rows=cap,
@@ -362,7 +362,7 @@ def test_decode_step_layers_graph_replay(fa):
     vns = [synth.torch_normal((B, Hkv, d), 81 + l, torch.bfloat16) for l in range(L)]
     kcs = [synth.torch_normal((B, cap if m == 0 else wrows, Hkv, d), 91 + l, torch.bfloat16) for l, m in enumerate(modes)]
     vcs = [synth.torch_normal((B, cap if m == 0 else wrows, Hkv, d), 101 + l, torch.bfloat16) for l, m in enumerate(modes)]
-    os_ = [torch.empty((B, Hq, d), dtype=torch.float32, device=DEV) for _ in range(L)]
+    os_ = [torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=DEV) for _ in range(L)]
     ws = torch.empty(fa.flux_decode_workspace_size(B, Hq, Hkv, pos + 1, d, 0, 64, sink, window), dtype=torch.uint8,
                      device=DEV)
 

@@ -3,7 +3,11 @@
 Every call goes through the C ABI (libflux_attn.so) via the thin binding.
 Inputs: seeded iid N(0,1), rounded to bf16 (the fp32 case keeps float32); the
 oracle reads exactly the same bits.  Bar: max-abs <= 1e-2 and mean-abs <= 1e-3
-with fp32 outputs; bf16 outputs may differ by a further half bf16 ulp.
+with fp32 outputs; bf16 outputs may differ by a further half bf16 ulp.  Output
+buffers are NaN-filled before each call, so an element the kernels never write
+fails.  At seq 8192 every row is compared; at seq 65536 and 131072 one seeded
+row of every 32-row wave segment of every head (1024-row segments for the dense
+seq-131072 layer), plus every element checked written.
 """
 import numpy as np
 import pytest
@@ -11,8 +15,7 @@ import torch
 
 import oracle
 import synth
-from _gpu_helpers import (bf16_tensors, check_close, check_lse, default_scale, dev_bits_to_host,
-                          sample_rows, say)
+from _gpu_helpers import bf16_tensors, check_close, check_lse, default_scale, dev_bits_to_host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -33,8 +36,9 @@ def _csr_dev(fa, S, sink, window):
 
 def _run_prefill(fa, qd, kd, vd, out_dtype, mode, causal=1, sink=128, window=2048, with_lse=True):
     B, S, Hq, d = qd.shape
-    o = torch.empty((B, S, Hq, d), dtype=out_dtype, device=DEV)
-    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV) if with_lse else None
+    # NaN-filled, so an output element the kernels never write fails the comparison
+    o = torch.full((B, S, Hq, d), float("nan"), dtype=out_dtype, device=DEV)
+    lse = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=DEV) if with_lse else None
     rp = ci = None
     if mode == fa.FLUX_MODE_SPARSE:
         rp, ci = _csr_dev(fa, S, sink, window)
@@ -127,38 +131,98 @@ def test_gqa_matches_repeated_kv(fa):
         assert torch.equal(a, b)
 
 
-# ------------------------------------------------------------- full-size layers, sampled rows
-def _sampled_check(fa, B, S, Hq, Hkv, d, mode, sink, window, seed, n_random, out_dtype=torch.float32):
-    say("full size", B, S, Hq, Hkv, d, "mode", mode, "out", out_dtype)
-    qd = synth.torch_normal((B, S, Hq, d), seed, torch.bfloat16)
-    kd = synth.torch_normal((B, S, Hkv, d), seed + 1, torch.bfloat16)
-    vd = synth.torch_normal((B, S, Hkv, d), seed + 2, torch.bfloat16)
-    o, lse = _run_prefill(fa, qd, kd, vd, out_dtype, mode, sink=sink, window=window)
-    rows = sample_rows(B, Hq, S, n_random, seed)
-    q = dev_bits_to_host(qd)
-    k = dev_bits_to_host(kd)
-    v = dev_bits_to_host(vd)
-    ref, ref_lse = oracle.attention(q, k, v, default_scale(d), causal=True, sparse=bool(mode), block=64,
-                                    sink_tokens=sink, window_tokens=window, rows=rows)
+# ------------------------------------------------------------- full-size layers
+def _wave_rows(B, Hq, S, stride, seed):
+    """(b, h, i) rows: for every batch and head, one seeded row in each `stride`-row segment (so every
+    32-row wave segment of every unit is sampled when stride <= 32), plus the block-edge positions."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    edges = [0, 1, 63, 64, 127, 128, 2047, 2048, 2049, S // 2, S - 65, S - 64, S - 2, S - 1]
+    for b in range(B):
+        for h in range(Hq):
+            for i in edges:
+                if 0 <= i < S:
+                    rows.add((b, h, i))
+            starts = np.arange(0, S, stride)
+            offs = rng.integers(0, stride, len(starts))
+            for i in np.minimum(starts + offs, S - 1):
+                rows.add((b, h, int(i)))
+    return np.array(sorted(rows), np.int64)
+
+
+def _check_rows(o, lse, rows, ref, ref_lse, what, out_bf16):
     o_h = o.float().cpu().numpy()
-    l_h = lse.cpu().numpy()
-    got = np.stack([o_h[b, i, h] for b, h, i in rows])
-    got_lse = np.array([l_h[b, h, i] for b, h, i in rows])
-    check_close(got, ref, f"S={S} mode {mode}", out_bf16=out_dtype == torch.bfloat16)
-    check_lse(got_lse, ref_lse, f"S={S} lse")
-    # every output finite (no row left unnormalised)
-    assert torch.isfinite(o).all()
-    del qd, kd, vd, o, lse
-    torch.cuda.empty_cache()
+    got = o_h[rows[:, 0], rows[:, 2], rows[:, 1]]
+    check_close(got, ref, what, out_bf16=out_bf16)
+    if lse is not None:
+        l_h = lse.cpu().numpy()
+        check_lse(l_h[rows[:, 0], rows[:, 1], rows[:, 2]], ref_lse, what + " lse")
 
 
-def test_llama_layer_dense_s8192_sampled(fa):
-    """One Llama-3.1-8B-shaped layer: batch 1, seq 8192, 32 query heads, 8 KV heads, head_dim 128."""
-    _sampled_check(fa, 1, 8192, 32, 8, 128, 0, 128, 2048, seed=1002, n_random=400)
+def _assert_all_written(*ts):
+    for t in ts:
+        if t is not None:
+            assert torch.isfinite(t).all(), "an output element was not written (NaN fill survived)"
 
 
-def test_llama_layer_dense_s8192_bf16_out(fa):
-    _sampled_check(fa, 1, 8192, 32, 8, 128, 0, 128, 2048, seed=1012, n_random=200, out_dtype=torch.bfloat16)
+@pytest.fixture(scope="module")
+def llama_layer(fa):
+    """One Llama-3.1-8B-shaped layer: batch 1, seq 8192, 32 query heads, 8 KV heads, head_dim 128, with the
+    fp64 oracle for EVERY row (about 10 s on 16 host threads)."""
+    B, S, Hq, Hkv, d = 1, 8192, 32, 8, 128
+    say("llama layer S=8192: inputs and full oracle")
+    qd = synth.torch_normal((B, S, Hq, d), 1002, torch.bfloat16)
+    kd = synth.torch_normal((B, S, Hkv, d), 1003, torch.bfloat16)
+    vd = synth.torch_normal((B, S, Hkv, d), 1004, torch.bfloat16)
+    q, k, v = (dev_bits_to_host(x) for x in (qd, kd, vd))
+    ref, ref_lse = oracle.attention(q, k, v, default_scale(d), causal=True)
+    return dict(qd=qd, kd=kd, vd=vd, q=q, ref=ref, ref_lse=np.transpose(ref_lse, (0, 2, 1)))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_llama_layer_dense_s8192_every_row(fa, llama_layer, out_dtype):
+    """Dense causal prefill at seq 8192 (persistent schedule), every output row against the oracle."""
+    L = llama_layer
+    say("llama layer S=8192 every row", out_dtype)
+    o, lse = _run_prefill(fa, L["qd"], L["kd"], L["vd"], out_dtype, 0)
+    _assert_all_written(o, lse)
+    check_close(o.float().cpu().numpy(), L["ref"], "S=8192 dense", out_bf16=out_dtype == torch.bfloat16)
+    check_lse(lse.cpu().numpy(), L["ref_lse"], "S=8192 dense lse")
+
+
+def test_headline_routed_layer_s8192_every_row(fa, llama_layer):
+    """The benchmarked instance: router on the layer's queries (head bias +8 on the dense index) -> device
+    mode -> flux_attn_prefill_layers_routed with bf16 output, i.e. prefill_bf16_kernel<128, kRouted> on the
+    persistent schedule.  Bit-equal to host-mode dispatch and to the plain dense call; every row against the
+    oracle (bf16 output bound)."""
+    L = llama_layer
+    qd, kd, vd = L["qd"], L["kd"], L["vd"]
+    B, S, Hq, d = qd.shape
+    say("headline routed layer S=8192")
+    w = synth.router_weights(1, Hq * d, 256, seed=1005)
+    w_enc, b_enc, w_head, b_head = (torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in w)
+    b_head[0, 0] += 8.0
+    modes = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    rp, ci = _csr_dev(fa, S, 128, 2048)
+    fa.flux_route_layers([qd[0]], w_enc, b_enc, w_head, b_head, modes, None, pool_tokens=100)
+    outs = []
+    for routed in (True, False):
+        o = torch.full((B, S, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=DEV)
+        if routed:
+            fa.flux_attn_prefill_layers_routed(modes, [qd], [kd], [vd], [o], [lse], block=64, sink_tokens=128,
+                                               window_tokens=2048, blk_row_ptr=rp, blk_col_idx=ci)
+        else:
+            fa.flux_attn_prefill_layers([0], [qd], [kd], [vd], [o], [lse], block=64, sink_tokens=128,
+                                        window_tokens=2048, blk_row_ptr=rp, blk_col_idx=ci)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert int(modes.cpu()[0]) == fa.FLUX_MODE_DENSE
+    (o_r, l_r), (o_h, l_h) = outs
+    _assert_all_written(o_r, l_r)
+    assert torch.equal(o_r, o_h) and torch.equal(l_r, l_h), "routed != host-mode dispatch"
+    check_close(o_r.float().cpu().numpy(), L["ref"], "headline routed S=8192", out_bf16=True)
+    check_lse(l_r.cpu().numpy(), L["ref_lse"], "headline routed S=8192 lse")
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,d,mode", [
@@ -167,45 +231,91 @@ def test_llama_layer_dense_s8192_bf16_out(fa):
     (1, 16384, 8, 4, 128, 0),     # groups of 2 query heads
     (1, 16384, 8, 4, 128, 1),
 ])
-def test_persistent_schedule_shapes_sampled(fa, B, S, Hq, Hkv, d, mode):
-    """Shapes with at least two units per compute unit run on the persistent schedule; cover both
-    unit pairings and a ragged sequence end."""
-    _sampled_check(fa, B, S, Hq, Hkv, d, mode, 128, 2048, seed=1020 + S + Hq, n_random=120)
+def test_persistent_schedule_shapes(fa, B, S, Hq, Hkv, d, mode):
+    """Shapes with at least two units per compute unit run on the persistent schedule; cover both unit
+    pairings and a ragged sequence end.  NaN-filled outputs must all be written; one row of every 32-row
+    wave segment of every head (block-sparse) or of every 256 rows (dense) against the oracle."""
+    seed = 1020 + S + Hq
+    say("persistent schedule", B, S, Hq, Hkv, d, "mode", mode)
+    qd = synth.torch_normal((B, S, Hq, d), seed, torch.bfloat16)
+    kd = synth.torch_normal((B, S, Hkv, d), seed + 1, torch.bfloat16)
+    vd = synth.torch_normal((B, S, Hkv, d), seed + 2, torch.bfloat16)
+    o, lse = _run_prefill(fa, qd, kd, vd, torch.float32, mode)
+    _assert_all_written(o, lse)
+    rows = _wave_rows(B, Hq, S, 32 if mode else 256, seed)
+    ref, ref_lse = oracle.attention(dev_bits_to_host(qd), dev_bits_to_host(kd), dev_bits_to_host(vd),
+                                    default_scale(d), causal=True, sparse=bool(mode), block=64, sink_tokens=128,
+                                    window_tokens=2048, rows=rows)
+    _check_rows(o, lse, rows, ref, ref_lse, f"persistent S={S} mode {mode}", False)
 
 
-def test_layer_sparse_s65536_sampled(fa):
-    """Same layer at seq 65536, block-sparse: block 64, sink 128, window 2048 (32 blocks)."""
-    _sampled_check(fa, 1, 65536, 32, 8, 128, 1, 128, 2048, seed=1003, n_random=400)
+def test_layer_sparse_s65536(fa):
+    """Same layer at seq 65536, block-sparse: block 64, sink 128, window 2048 (32 blocks).  Every output
+    written (NaN fill); one seeded row of every 32-row wave segment of every head (65,536 rows) against
+    the oracle."""
+    B, S, Hq, Hkv, d = 1, 65536, 32, 8, 128
+    say("sparse layer S=65536")
+    qd = synth.torch_normal((B, S, Hq, d), 1003, torch.bfloat16)
+    kd = synth.torch_normal((B, S, Hkv, d), 1004, torch.bfloat16)
+    vd = synth.torch_normal((B, S, Hkv, d), 1005, torch.bfloat16)
+    o, lse = _run_prefill(fa, qd, kd, vd, torch.float32, 1)
+    _assert_all_written(o, lse)
+    rows = _wave_rows(B, Hq, S, 32, 1003)
+    ref, ref_lse = oracle.attention(dev_bits_to_host(qd), dev_bits_to_host(kd), dev_bits_to_host(vd),
+                                    default_scale(d), causal=True, sparse=True, block=64, sink_tokens=128,
+                                    window_tokens=2048, rows=rows)
+    _check_rows(o, lse, rows, ref, ref_lse, "S=65536 sparse", False)
+    del qd, kd, vd, o, lse
+    torch.cuda.empty_cache()
 
 
-def test_routed_stack_layers_s131072_sampled(fa):
-    """Qwen3-8B-shaped stack at seq 131072 through the per-layer dispatcher: one dense and one
-    sparse layer (the dispatcher is what runs all 36 layers in the benchmark)."""
+def test_routed_stack_layers_s131072(fa):
+    """Qwen3-8B-shaped stack at seq 131072: one dense and one sparse layer whose modes come from the router
+    (head bias) and stay on the device, run by flux_attn_prefill_layers_routed with bf16 outputs as in the
+    36-layer benchmark, and again by host-mode dispatch: bit-equal, every element written (NaN fill), and
+    rows against the oracle -- one row of every 32-row wave segment of every head for the sparse layer, of
+    every 1024 rows for the dense one."""
     S, Hq, Hkv, d = 131072, 32, 8, 128
     say("routed stack S=131072")
-    modes = np.array([0, 1], np.int32)
-    qs, ks, vs, os_, ls = [], [], [], [], []
+    plan = np.array([0, 1], np.int32)
+    qs, ks, vs = [], [], []
     for l in range(2):
         qs.append(synth.torch_normal((1, S, Hq, d), 1004 + 10 * l, torch.bfloat16))
         ks.append(synth.torch_normal((1, S, Hkv, d), 1005 + 10 * l, torch.bfloat16))
         vs.append(synth.torch_normal((1, S, Hkv, d), 1006 + 10 * l, torch.bfloat16))
-        os_.append(torch.empty((1, S, Hq, d), dtype=torch.float32, device=DEV))
-        ls.append(torch.empty((1, Hq, S), dtype=torch.float32, device=DEV))
-    rp, ci = _csr_dev(fa, S, 128, 2048)
-    fa.flux_attn_prefill_layers(modes, qs, ks, vs, os_, ls, block=64, sink_tokens=128, window_tokens=2048,
-                                blk_row_ptr=rp, blk_col_idx=ci)
-    torch.cuda.synchronize()
+    w = synth.router_weights(2, Hq * d, 256, seed=1006)
+    w_enc, b_enc, w_head, b_head = (torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in w)
     for l in range(2):
-        rows = sample_rows(1, Hq, S, 64, seed=77 + l)
-        rows = rows[np.isin(rows[:, 2], [0, 1, 64, 2048, 2049, S // 2, S - 65, S - 1]) | (np.arange(len(rows)) % 7 == 0)]
+        b_head[l, int(plan[l])] += 8.0
+    modes = torch.full((2,), -1, dtype=torch.int32, device=DEV)
+    fa.flux_route_layers([x[0] for x in qs], w_enc, b_enc, w_head, b_head, modes, None, pool_tokens=100)
+    rp, ci = _csr_dev(fa, S, 128, 2048)
+    res = {}
+    for routed in (True, False):
+        os_ = [torch.full((1, S, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+        ls = [torch.full((1, Hq, S), float("nan"), dtype=torch.float32, device=DEV) for _ in range(2)]
+        if routed:
+            fa.flux_attn_prefill_layers_routed(modes, qs, ks, vs, os_, ls, block=64, sink_tokens=128,
+                                               window_tokens=2048, blk_row_ptr=rp, blk_col_idx=ci)
+        else:
+            fa.flux_attn_prefill_layers(plan, qs, ks, vs, os_, ls, block=64, sink_tokens=128, window_tokens=2048,
+                                        blk_row_ptr=rp, blk_col_idx=ci)
+        res[routed] = (os_, ls)
+    torch.cuda.synchronize()
+    assert np.array_equal(modes.cpu().numpy(), plan)
+    for l in range(2):
+        o_r, l_r = res[True][0][l], res[True][1][l]
+        _assert_all_written(o_r, l_r)
+        assert torch.equal(o_r, res[False][0][l]) and torch.equal(l_r, res[False][1][l]), f"layer {l}"
+    del res[False]
+    for l in range(2):
+        say("stack layer", l, "oracle rows")
+        rows = _wave_rows(1, Hq, S, 32 if plan[l] else 1024, 77 + l)
         ref, ref_lse = oracle.attention(dev_bits_to_host(qs[l]), dev_bits_to_host(ks[l]), dev_bits_to_host(vs[l]),
-                                        default_scale(d), causal=True, sparse=bool(modes[l]), block=64,
+                                        default_scale(d), causal=True, sparse=bool(plan[l]), block=64,
                                         sink_tokens=128, window_tokens=2048, rows=rows)
-        o_h = os_[l].cpu().numpy()
-        l_h = ls[l].cpu().numpy()
-        check_close(np.stack([o_h[b, i, h] for b, h, i in rows]), ref, f"stack layer {l}")
-        check_lse(np.array([l_h[b, h, i] for b, h, i in rows]), ref_lse, f"stack layer {l} lse")
-    del qs, ks, vs, os_, ls
+        _check_rows(res[True][0][l], res[True][1][l], rows, ref, ref_lse, f"stack layer {l}", True)
+    del qs, ks, vs, res
     torch.cuda.empty_cache()
 
 
@@ -295,7 +405,7 @@ def test_soft_prefill_matches_oracle(fa, B, S, Hq, Hkv, d, sink, window, w0, csr
     (q, k, v), (qd, kd, vd) = bf16_tensors(B, S, Hq, Hkv, d, seed=72 + S)
     rp, ci = _csr_dev(fa, S, sink, window) if csr else (None, None)
     wd = torch.tensor([w0, 1.0 - w0], dtype=torch.float32, device=DEV)
-    o = torch.empty((B, S, Hq, d), dtype=out_dtype, device=DEV)
+    o = torch.full((B, S, Hq, d), float("nan"), dtype=out_dtype, device=DEV)
     fa.flux_attn_prefill_soft(qd, kd, vd, o, wd, sink_tokens=sink, window_tokens=window, blk_row_ptr=rp,
                               blk_col_idx=ci)
     torch.cuda.synchronize()
@@ -320,12 +430,13 @@ def test_soft_prefill_router_pipeline_s8192_sampled(fa):
     weights = torch.empty((1, 2), dtype=torch.float32, device=DEV)
     fa.flux_route_soft_weights(logits, u, 0.5, weights)
     rp, ci = _csr_dev(fa, S, 128, 2048)
-    o = torch.empty((B, S, Hq, d), dtype=torch.float32, device=DEV)
+    o = torch.full((B, S, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
     fa.flux_attn_prefill_soft(qd, kd, vd, o, weights[0], blk_row_ptr=rp, blk_col_idx=ci)
     torch.cuda.synchronize()
+    _assert_all_written(o)
     ref_w = oracle.soft_weights(logits.cpu().numpy().astype(np.float64), u.cpu().numpy().astype(np.float64), 0.5)
     assert np.abs(weights.cpu().numpy() - ref_w).max() < 2e-5
-    rows = sample_rows(B, Hq, S, 100, seed=1044)
+    rows = _wave_rows(B, Hq, S, 32, 1044)
     ref = oracle.attention_soft(dev_bits_to_host(qd), dev_bits_to_host(kd), dev_bits_to_host(vd), default_scale(d),
                                 ref_w[0], block=64, sink_tokens=128, window_tokens=2048, rows=rows)
     o_h = o.cpu().numpy()
