@@ -1,26 +1,32 @@
 """Benchmark of the tiled-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs] [--stack] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs LIST] [--no-cpu-baseline]
 
-Headline workload (one step): one Llama-3.1-8B-shaped attention layer at seq 8192
-(batch 1, 32 query heads, 8 KV heads, head_dim 128, bf16, Q/K/V iid N(0,1)):
-the layer router reads the layer's queries (first/last 100 tokens -> MLP ->
-argmax) and leaves the mode on the device, and the routed dispatcher's prefill
-kernel reads it and runs the selected attention -- dense causal, which the
-router's head bias selects
-for this layer because the workload is defined as dense causal.
+Headline workload (one step): a Qwen3-8B-shaped 36-layer attention stack prefill
+at seq 131072 (batch 1, 32 query heads, 8 KV heads, head_dim 128, bf16, per-layer
+Q/K/V iid N(0,1)).  The layer router reads every layer's queries (first/last 100
+tokens -> MLP -> argmax) and leaves the 36 modes on the device; each layer's
+routed prefill kernel reads its own mode and runs dense causal attention or
+64x64 block-sparse attention (sink 128 tokens, causal window 2048 tokens).  The
+seeded plan (12 dense layers, 24 sparse) is encoded in the router's head bias, so
+the router's argmax reproduces it while all router arithmetic still runs.
 `value` = useful prefill TFLOP/s (4*B*Hq*d per allowed query-key pair) of the
-whole step.
+whole step.  The same 36 layers run all dense beside it, for the ratio the
+Flux Attention pages quote as "up to 2.8x prefill at 256K context" (hardware not
+stated there).
 
-Secondary legs (same JSON line, "legs"): block-sparse prefill at seq 65536,
-GQA decode over a 262144-token bf16 cache (dense and sparse; HBM GB/s and
-tok/s), the routed decode loop, soft-routed prefill, the attention backward
-(seq 8192 dense, seq 65536 sparse), and with --stack the 36-layer routed
-prefill stack at seq 131072.
+The roofline object is for the dominant kernel, the routed prefill kernel (every
+layer's launch), timed with HIP events on the stream it runs on, with the dense
+and sparse launches also given separately.  cpu_baseline times the fp64 CPU
+oracle on a bounded sample of the same workload (rank 0, N=1 only), extrapolated
+to the whole stack by allowed-pair counts, plus oracle samples of the other
+configurations.
 
-The roofline object is for the dominant kernel (dense prefill), timed with HIP
-events on the stream the kernel runs on.  cpu_baseline times the fp64 CPU
-oracle on a bounded sample of the same workload (rank 0, N=1 only).
+Secondary legs (same JSON line, "legs"): the routed Llama-3.1-8B layer at seq
+8192 (router + dense-causal prefill), block-sparse prefill at seq 65536, GQA
+decode over a 262144-token bf16 cache (dense and sparse; HBM GB/s and tok/s), the
+routed decode loop, soft-routed prefill, the attention backward (seq 8192 dense,
+seq 65536 sparse) and device ceilings.
 """
 from __future__ import annotations
 
@@ -85,6 +91,7 @@ class KernelTimer:
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_dense_causal_s8192_traffic.txt")
+STACK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_routed_stack_s131072_traffic.txt")
 PREFILL_SRCS = [os.path.join(ROOT, "long_context_attention_tiled_amd", "csrc", f)
                 for f in ("prefill_bf16.hip", "tile_common.h")]
 
@@ -98,13 +105,13 @@ def prefill_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dense prefill kernel from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the summary was taken on
-    another version of the kernel source."""
+def measured_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per launch of a prefill kernel from a committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the summary was taken on another
+    version of the kernel source."""
     try:
         kv = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(path):
             if "=" in line and not line.lstrip().startswith("#"):
                 key, val = line.split("=", 1)
                 kv[key.strip()] = val.strip()
@@ -147,12 +154,11 @@ def call_percentiles(step, reps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--legs", default="sparse,decode,decode_loop,soft,backward,peaks",
-                    help="comma list of secondary legs: sparse, dense64k, decode, decode_loop, soft, backward, stack, "
-                         "peaks "
-                         "(or 'none')")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="layer8k,sparse,decode,decode_loop,soft,backward,peaks",
+                    help="comma list of secondary legs: layer8k, sparse, dense64k, decode, decode_loop, soft, backward, "
+                         "peaks (or 'none')")
     ap.add_argument("--no-legs", dest="legs", action="store_const", const="none")
     ap.add_argument("--no-headline", dest="headline", action="store_false", default=True,
                     help="skip the headline step (profiling a single leg)")
@@ -161,7 +167,8 @@ def main():
     ap.add_argument("--sustain", nargs=2, metavar=("DATA", "SECONDS"), default=None,
                     help="only run the seq-65536 dense-causal prefill back to back for SECONDS with DATA = randn "
                          "(N(0,1) inputs) or const (constant inputs), for reading clocks with rocm-smi meanwhile")
-    ap.add_argument("--stack", action="store_true", help="also time the 36-layer routed stack at seq 131072")
+    ap.add_argument("--dense-steps", type=int, default=2,
+                    help="timed steps of the all-dense 36-layer comparison (0 skips it)")
     ap.add_argument("--steps-leg", type=int, default=20, help="timed repetitions per secondary leg")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false", default=True)
     args = ap.parse_args()
@@ -190,19 +197,18 @@ def main():
         run_sustain(fa, synth, torch, args.sustain[0], float(args.sustain[1]))
         return
     legs_sel = set() if args.legs == "none" else set(x for x in args.legs.split(",") if x)
-    if args.stack:
-        legs_sel.add("stack")
     result = {}
     if args.headline:
         result = headline(args, fa, synth, torch, dev)
-    legs = run_legs(fa, synth, torch, dev, legs_sel, args.steps_leg)
+    legs = run_legs(fa, synth, torch, dev, legs_sel, args.steps_leg, args.warmup)
     if legs:
         result["legs"] = legs
         if "decode_dense_L262144" in legs:
             dd = legs["decode_dense_L262144"]
             result["decode"] = {"GB/s": dd["GB/s"], "tok/s": dd["tok/s"], "frac_hbm": dd["frac"]}
     if args.cpu_baseline and args.headline:
-        result["cpu_baseline"] = cpu_baseline(synth)
+        result["cpu_baseline"] = cpu_baseline(synth, result.pop("_oracle_inputs"))
+    result.pop("_oracle_inputs", None)
     print(json.dumps(result), flush=True)
 
 
@@ -231,39 +237,59 @@ def run_sustain(fa, synth, torch, data, seconds):
           flush=True)
 
 
+def host_bits(t) -> np.ndarray:
+    """Device bf16 tensor -> host uint16 bit pattern (exact copy)."""
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def sparse_row_pairs(i: int, block: int = 64, sink: int = 128, window: int = 2048) -> int:
+    """Keys the block-sparse causal rule allows to query position i: the row's window blocks up to i, plus the
+    sink keys before the window."""
+    w0 = max(0, (i // block - window // block + 1) * block)
+    return (i - w0 + 1) + min((sink // block) * block, w0)
+
+
 def headline(args, fa, synth, torch, dev):
 
-    # ---------------------------------------------------------------- headline: routed dense layer, S=8192
-    B, S, Hq, Hkv, d = 1, 8192, 32, 8, 128
-    scale = 1.0 / math.sqrt(d)
-    log("generating headline inputs")
-    q = synth.torch_normal((B, S, Hq, d), 1002, torch.bfloat16)
-    k = synth.torch_normal((B, S, Hkv, d), 1003, torch.bfloat16)
-    v = synth.torch_normal((B, S, Hkv, d), 1004, torch.bfloat16)
-    o = torch.empty((B, S, Hq, d), dtype=torch.bfloat16, device=dev)
-    w = synth.router_weights(1, Hq * d, 256, seed=1005)
+    # ---------------------------------------------------------------- headline: 36-layer routed stack, S=131072
+    L, S, Hq, Hkv, d = 36, 131072, 32, 8, 128
+    sink, window = 128, 2048
+    log("generating headline inputs (36 layers, seq 131072)")
+    plan = synth.layer_mode_draw(L, 12, seed=1004)
+    qs = [synth.torch_normal((1, S, Hq, d), 2000 + 3 * l, torch.bfloat16) for l in range(L)]
+    ks = [synth.torch_normal((1, S, Hkv, d), 2001 + 3 * l, torch.bfloat16) for l in range(L)]
+    vs = [synth.torch_normal((1, S, Hkv, d), 2002 + 3 * l, torch.bfloat16) for l in range(L)]
+    o = torch.empty((1, S, Hq, d), dtype=torch.bfloat16, device=dev)   # one output buffer reused by every layer
+    w = synth.router_weights(L, Hq * d, 256, seed=1006)
     w_enc, b_enc, w_head, b_head = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in w)
-    b_head[0, 0] += 8.0   # the workload is dense causal: the head bias makes the router select index 0
-    modes_dev = torch.empty(1, dtype=torch.int32, device=dev)
-    route_ws = torch.empty(fa.flux_route_workspace_size(1, Hq, d, 256), dtype=torch.uint8, device=dev)
-    timer = KernelTimer()
-    useful = 4.0 * B * Hq * d * causal_pairs(S)
-    algo_bytes = 2 * B * S * (2 * Hq + 2 * Hkv) * d   # Q, K, V read once and O written once, bf16
-
-    rp, ci = fa.flux_build_block_mask(S, S, 64, 128, 2048, 1, fa.FLUX_MODE_SPARSE)
+    for l in range(L):
+        b_head[l, int(plan[l])] += 8.0   # the seeded plan, reproduced by the router's own argmax
+    rp, ci = fa.flux_build_block_mask(S, S, 64, sink, window, 1, fa.FLUX_MODE_SPARSE)
     rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+    modes_dev = torch.empty(L, dtype=torch.int32, device=dev)
+    route_ws = torch.empty(fa.flux_route_workspace_size(L, Hq, d, 256), dtype=torch.uint8, device=dev)
+    flops_dense = 4.0 * Hq * d * causal_pairs(S)
+    flops_sparse = 4.0 * Hq * d * csr_pairs(rp, ci, S)
+    layer_flops = [flops_dense if plan[l] == 0 else flops_sparse for l in range(L)]
+    useful = float(sum(layer_flops))
+    useful_all_dense = L * flops_dense
+    algo_bytes = 2 * S * (2 * Hq + 2 * Hkv) * d   # per layer launch: Q, K, V read once and O written once, bf16
+    timers = [KernelTimer() for _ in range(L)]
+
+    def layer_call(l):
+        fa.flux_attn_prefill_layers_routed(modes_dev[l:l + 1], [qs[l]], [ks[l]], [vs[l]], [o], None, block=64,
+                                           sink_tokens=sink, window_tokens=window, blk_row_ptr=rpd, blk_col_idx=cid)
 
     def step(record=False):
-        # router -> device mode -> prefill kernels that read the mode themselves: no host round trip
-        fa.flux_route_layers([q[0]], w_enc, b_enc, w_head, b_head, modes_dev, None, workspace=route_ws,
+        # router -> 36 device modes -> each layer's prefill kernel reads its own mode: no host round trip
+        fa.flux_route_layers([x[0] for x in qs], w_enc, b_enc, w_head, b_head, modes_dev, None, workspace=route_ws,
                              pool_tokens=100)
-        call = lambda: fa.flux_attn_prefill_layers_routed(modes_dev, [q], [k], [v], [o], None, block=64,
-                                                          sink_tokens=128, window_tokens=2048, blk_row_ptr=rpd,
-                                                          blk_col_idx=cid)
-        if record:
-            timer.record(call)
-        else:
-            call()
+        for l in range(L):
+            if record:
+                timers[l].record(lambda l=l: layer_call(l))
+            else:
+                layer_call(l)
 
     log("timing headline")
     for _ in range(args.warmup):
@@ -274,10 +300,35 @@ def headline(args, fa, synth, torch, dev):
         step(record=True)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    assert int(modes_dev.cpu()[0]) == fa.FLUX_MODE_DENSE
-    kern_ms = timer.mean_ms()
+    assert np.array_equal(modes_dev.cpu().numpy(), plan), "router modes differ from the plan"
+    layer_ms = [t.mean_ms() for t in timers]
+    dense_ms = float(np.mean([layer_ms[l] for l in range(L) if plan[l] == 0]))
+    sparse_ms = float(np.mean([layer_ms[l] for l in range(L) if plan[l] == 1]))
+    kern_ms_total = float(np.sum(layer_ms))
+    achieved = useful / (kern_ms_total * 1e-3) / 1e12
     value = useful / (ms_per_step * 1e-3) / 1e12
-    achieved = useful / (kern_ms * 1e-3) / 1e12
+
+    # the same 36 layers, every one dense causal (host-mode dispatch): the pages' "versus full attention"
+    dense_cmp = None
+    if args.dense_steps > 0:
+        log("timing the all-dense stack")
+        all_dense = lambda: fa.flux_attn_prefill_layers(np.zeros(L, np.int32), qs, ks, vs, [o] * L, None, block=64,
+                                                        sink_tokens=sink, window_tokens=window, blk_row_ptr=rpd,
+                                                        blk_col_idx=cid)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.dense_steps):
+            all_dense()
+        torch.cuda.synchronize()
+        ms_dense = (time.perf_counter() - t0) * 1e3 / args.dense_steps
+        dense_cmp = {"routed_ms_per_step": round(ms_per_step, 2), "all_dense_ms_per_step": round(ms_dense, 2),
+                     "all_dense_TFLOP/s": round(useful_all_dense / ms_dense / 1e9, 2),
+                     "speedup": round(ms_dense / ms_per_step, 3),
+                     "useful_flop_ratio": round(useful_all_dense / useful, 3), "steps": args.dense_steps,
+                     "pages_context": "Flux Attention page (aitrends.kr), speed paragraph: up to 2.8x prefill and "
+                                      "2.0x decode speedup versus full attention at 256K context; hardware not "
+                                      "stated there"}
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -285,29 +336,100 @@ def headline(args, fa, synth, torch, dev):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic iid N(0,1) Q/K/V rounded to bf16; seeded random router weights",
-        "config": {"workload": "llama3.1-8b-layer routed dense-causal prefill", "batch": B, "seq_len": S,
-                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "block": 64, "out_dtype": "bf16",
-                   "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+        "data": "synthetic: per-layer iid N(0,1) Q/K/V rounded to bf16; seeded random router weights whose head "
+                "bias encodes a seeded 12-dense / 24-sparse plan",
+        "config": {"workload": "qwen3-8b-shaped 36-layer routed attention stack prefill (router + 12 dense-causal "
+                               "+ 24 block-sparse layers)",
+                   "batch": 1, "seq_len": S, "layers": L, "dense_layers": int((plan == 0).sum()), "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": d, "block": 64, "sink_tokens": sink, "window_tokens": window,
+                   "out_dtype": "bf16", "useful_flops_per_step": useful, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(STACK_TRAFFIC_FILE),
                      "algorithmic_bytes": algo_bytes,
-                     "kernel": "prefill_bf16_kernel<128, routed: dense causal, bf16 out>",
-                     "kernel_ms": round(kern_ms, 4), "kernel_ms_p10_p50_p90": timer.pct_ms(),
-                     "useful_flops_per_launch": useful},
+                     "kernel": "prefill_bf16_kernel<128, routed, bf16 out>: all 36 layer launches of a step",
+                     "kernel_ms_mean": round(kern_ms_total / L, 4),
+                     "useful_flops_per_launch_mean": useful / L,
+                     "dense_layer": {"ms": round(dense_ms, 3), "TFLOP/s": round(flops_dense / dense_ms / 1e9, 2),
+                                     "frac": round(flops_dense / dense_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                     "useful_flops": flops_dense},
+                     "sparse_layer": {"ms": round(sparse_ms, 3), "TFLOP/s": round(flops_sparse / sparse_ms / 1e9, 2),
+                                      "frac": round(flops_sparse / sparse_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                      "useful_flops": flops_sparse, "nnz_blocks": int(len(ci))}},
     }
-    del q, k, v, o
+    if dense_cmp:
+        result["vs_all_dense"] = dense_cmp
+    # the oracle baseline samples one dense and one sparse layer of this stack: keep their bits on the host
+    ld, ls_ = int(np.argmax(plan == 0)), int(np.argmax(plan == 1))
+    result["_oracle_inputs"] = {"plan": plan, "flops_dense": flops_dense, "flops_sparse": flops_sparse,
+                                "useful": useful,
+                                "dense": tuple(host_bits(x[ld]) for x in (qs, ks, vs)),
+                                "sparse": tuple(host_bits(x[ls_]) for x in (qs, ks, vs))}
+    del qs, ks, vs, o
     torch.cuda.empty_cache()
     return result
 
 
-def run_legs(fa, synth, torch, dev, sel, reps):
+def run_layer8k(fa, synth, torch, dev, reps, warmup):
+    """The routed Llama-3.1-8B layer at seq 8192 (batch 1, 32/8 heads, head_dim 128, bf16): router on the layer's
+    queries -> device mode (the head bias selects dense causal, the workload's mode) -> routed prefill kernel."""
+    B, S, Hq, Hkv, d = 1, 8192, 32, 8, 128
+    log("leg: routed layer S=8192")
+    q = synth.torch_normal((B, S, Hq, d), 1002, torch.bfloat16)
+    k = synth.torch_normal((B, S, Hkv, d), 1003, torch.bfloat16)
+    v = synth.torch_normal((B, S, Hkv, d), 1004, torch.bfloat16)
+    o = torch.empty((B, S, Hq, d), dtype=torch.bfloat16, device=dev)
+    w = synth.router_weights(1, Hq * d, 256, seed=1005)
+    w_enc, b_enc, w_head, b_head = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in w)
+    b_head[0, 0] += 8.0
+    modes_dev = torch.empty(1, dtype=torch.int32, device=dev)
+    route_ws = torch.empty(fa.flux_route_workspace_size(1, Hq, d, 256), dtype=torch.uint8, device=dev)
+    timer = KernelTimer()
+    useful = 4.0 * B * Hq * d * causal_pairs(S)
+    rp, ci = fa.flux_build_block_mask(S, S, 64, 128, 2048, 1, fa.FLUX_MODE_SPARSE)
+    rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+
+    def step(record=False):
+        fa.flux_route_layers([q[0]], w_enc, b_enc, w_head, b_head, modes_dev, None, workspace=route_ws,
+                             pool_tokens=100)
+        call = lambda: fa.flux_attn_prefill_layers_routed(modes_dev, [q], [k], [v], [o], None, block=64,
+                                                          sink_tokens=128, window_tokens=2048, blk_row_ptr=rpd,
+                                                          blk_col_idx=cid)
+        if record:
+            timer.record(call)
+        else:
+            call()
+
+    for _ in range(max(warmup, 5)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = max(reps, 20)
+    for _ in range(n):
+        step(record=True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    assert int(modes_dev.cpu()[0]) == fa.FLUX_MODE_DENSE
+    kern_ms = timer.mean_ms()
+    res = {"ms_per_step": round(ms, 4), "step_TFLOP/s": round(useful / ms / 1e9, 2),
+           "kernel_ms": round(kern_ms, 4), "kernel_ms_p10_p50_p90": timer.pct_ms(),
+           "TFLOP/s": round(useful / kern_ms / 1e9, 2), "frac": round(useful / kern_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+           "useful_flops": useful, "traffic": measured_traffic(TRAFFIC_FILE),
+           "algorithmic_bytes": 2 * B * S * (2 * Hq + 2 * Hkv) * d}
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_legs(fa, synth, torch, dev, sel, reps, warmup):
     legs = {}
+    if "layer8k" in sel:
+        legs["routed_layer_s8192"] = run_layer8k(fa, synth, torch, dev, reps, warmup)
     if {"sparse", "dense64k"} & sel:
         # ---- block-sparse prefill, seq 65536 (and optionally dense at the same length)
         B, S, Hq, Hkv, d = 1, 65536, 32, 8, 128
@@ -365,8 +487,6 @@ def run_legs(fa, synth, torch, dev, sel, reps):
         del qd, kc, vc, od
         torch.cuda.empty_cache()
 
-    if "stack" in sel:
-        legs["stack_s131072"] = run_stack(fa, synth, torch, dev)
     if "soft" in sel:
         legs["soft_routed_prefill_s8192"] = run_soft(fa, synth, torch, dev, reps)
     if "backward" in sel:
@@ -596,67 +716,96 @@ def run_microbench(torch, dev):
     return out
 
 
-def run_stack(fa, synth, torch, dev):
-    """36 layers, seq 131072, 12 dense + 24 sparse by a seeded draw encoded in the router's head bias."""
-    L, S, Hq, Hkv, d = 36, 131072, 32, 8, 128
-    log("leg: 36-layer stack, generating inputs")
-    plan = synth.layer_mode_draw(L, 12, seed=1004)
-    qs = [synth.torch_normal((1, S, Hq, d), 2000 + 3 * l, torch.bfloat16) for l in range(L)]
-    ks = [synth.torch_normal((1, S, Hkv, d), 2001 + 3 * l, torch.bfloat16) for l in range(L)]
-    vs = [synth.torch_normal((1, S, Hkv, d), 2002 + 3 * l, torch.bfloat16) for l in range(L)]
-    o = torch.empty((1, S, Hq, d), dtype=torch.bfloat16, device=dev)
-    w = synth.router_weights(L, Hq * d, 256, seed=1006)
-    w_enc, b_enc, w_head, b_head = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in w)
-    for l in range(L):
-        b_head[l, int(plan[l])] += 8.0
-    rp, ci = fa.flux_build_block_mask(S, S, 64, 128, 2048, 1, fa.FLUX_MODE_SPARSE)
-    rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
-    modes_dev = torch.empty(L, dtype=torch.int32, device=dev)
-    route_ws = torch.empty(fa.flux_route_workspace_size(L, Hq, d, 256), dtype=torch.uint8, device=dev)
-    useful = 4.0 * Hq * d * (12 * causal_pairs(S) + 24 * csr_pairs(rp, ci, S))
+def cpu_baseline(synth, stack):
+    """The fp64 CPU oracle (plain two-pass softmax, OpenMP over rows) on bounded samples, timed on the host's
+    cores (the CPU share of this process: OMP_NUM_THREADS, else its affinity set).
 
-    def step():
-        fa.flux_route_layers([x[0] for x in qs], w_enc, b_enc, w_head, b_head, modes_dev, None, workspace=route_ws,
-                             pool_tokens=100)
-        fa.flux_attn_prefill_layers_routed(modes_dev, qs, ks, vs, [o] * L, None, block=64, sink_tokens=128,
-                                           window_tokens=2048, blk_row_ptr=rpd, blk_col_idx=cid)
+    Headline (value): the 36-layer stack at seq 131072, sampled as 64 query positions x 32 heads of one dense
+    and one sparse layer of the benchmarked stack (first/last rows, both sides of the sink and window edges,
+    seeded random rows), each layer's time extrapolated by allowed query-key pairs to the whole layer, then to
+    12 dense + 24 sparse layers (labelled extrapolated).  Beside it: the seq-8192 dense layer (every 4th row of
+    all heads), the seq-65536 block-sparse layer (one row per 256 of all heads) and the batch-8, 262144-token
+    decode (sequence 0, all heads, dense and sparse), each as a rate on the sample."""
+    import torch
 
-    step()
-    torch.cuda.synchronize()
-    m = modes_dev.cpu().numpy()
-    assert np.array_equal(m, plan), (m, plan)
-    ms = time_steps(step, 2, 0)
-    res = {"ms": round(ms, 2), "useful_flops": useful, "TFLOP/s": round(useful / ms / 1e9, 2),
-           "frac": round(useful / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "dense_layers": int((plan == 0).sum())}
-    del qs, ks, vs, o
-    torch.cuda.empty_cache()
-    return res
-
-
-def cpu_baseline(synth, target_s: float = 15.0):
-    """fp64 CPU oracle on a bounded sample of the headline layer: every stride-th query row of
-    all 32 heads, the stride chosen from a short calibration run so the sample takes about
-    target_s seconds on the machine's CPU share (at most 16 threads)."""
     import oracle
-    B, S, Hq, Hkv, d = 1, 8192, 32, 8, 128
-    log("cpu baseline: generating inputs")
-    q, k, v = synth.qkv_bf16(B, S, Hq, Hkv, d, seed=1002)
-    cores = min(16, len(os.sched_getaffinity(0)))
+    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    visible = len(os.sched_getaffinity(0))
+    Hq, d = 32, 128
+    scale = 1.0 / math.sqrt(d)
+    rng = np.random.default_rng(1007)
 
-    def sample(stride, offset):
-        rows = np.array([(0, h, i) for i in range(offset, S, stride) for h in range(Hq)], np.int64)
-        pairs = int(sum(i + 1 for _, _, i in rows))
+    def timed(fn):
         t0 = time.perf_counter()
-        oracle.attention(q, k, v, 1.0 / math.sqrt(d), causal=True, rows=rows, n_threads=cores)
-        return len(rows), 4.0 * d * pairs, time.perf_counter() - t0
+        fn()
+        return time.perf_counter() - t0
 
-    _, f_cal, t_cal = sample(256, 255)
-    stride = int(max(1, min(256, round(256 * t_cal / target_s))))
-    log(f"cpu baseline: calibration {t_cal:.2f} s -> stride {stride} on {cores} threads")
-    n_rows, flops, sec = sample(stride, stride - 1)
-    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"dense causal S=8192 layer, every {stride}th query row x 32 heads ({n_rows} rows, "
-                      f"{flops:.3e} useful flops) in {sec:.2f} s"}
+    # ---- headline stack: one dense and one sparse layer, sampled rows
+    S = 131072
+    pos = sorted({0, 1, 127, 128, 129, 2047, 2048, 2049, S // 2, S - 2049, S - 2048, S - 65, S - 64, S - 2, S - 1}
+                 | set(rng.integers(0, S, 64).tolist()))[:64]
+    rows = np.array([(0, h, i) for i in pos for h in range(Hq)], np.int64)
+    log(f"cpu baseline: stack sample, {len(rows)} rows per layer on {cores} threads")
+    sec, pairs_s = {}, {}
+    for name, sparse in (("dense", False), ("sparse", True)):
+        q, k, v = stack[name]
+        sec[name] = timed(lambda: oracle.attention(q, k, v, scale, causal=True, sparse=sparse, block=64,
+                                                   sink_tokens=128, window_tokens=2048, rows=rows, n_threads=cores))
+        pairs_s[name] = Hq * sum((sparse_row_pairs(i) if sparse else i + 1) for i in pos)
+    layer_pairs = {"dense": stack["flops_dense"] / (4.0 * d), "sparse": stack["flops_sparse"] / (4.0 * d)}
+    layer_sec = {m: sec[m] * layer_pairs[m] / pairs_s[m] for m in sec}
+    n_dense = int((stack["plan"] == 0).sum())
+    stack_sec = n_dense * layer_sec["dense"] + (len(stack["plan"]) - n_dense) * layer_sec["sparse"]
+    out = {"value": round(stack["useful"] / stack_sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+           "host_cpus_visible": visible, "kind": "oracle",
+           "sample": f"36-layer seq-131072 stack, extrapolated: {len(pos)} query positions x {Hq} heads of one dense "
+                     f"layer ({sec['dense']:.2f} s) and one block-sparse layer ({sec['sparse']:.2f} s) of the "
+                     f"benchmarked stack, scaled by allowed query-key pairs to 12 dense + 24 sparse layers = "
+                     f"{stack_sec:.0f} s per step on the CPU"}
+    sub = {}
+
+    # ---- seq-8192 dense layer
+    q, k, v = synth.qkv_bf16(1, 8192, Hq, 8, d, seed=1002)
+    rows = np.array([(0, h, i) for i in range(3, 8192, 4) for h in range(Hq)], np.int64)
+    t = timed(lambda: oracle.attention(q, k, v, scale, causal=True, rows=rows, n_threads=cores))
+    fl = 4.0 * d * Hq * sum(i + 1 for i in range(3, 8192, 4))
+    sub["layer_s8192_dense"] = {"TFLOP/s": round(fl / t / 1e12, 6), "seconds": round(t, 2),
+                                "sample": f"every 4th query row x {Hq} heads ({len(rows)} rows, {fl:.3e} useful flop)"}
+
+    # ---- seq-65536 block-sparse layer
+    S = 65536
+    qd = synth.torch_normal((1, S, Hq, d), 1102, torch.bfloat16)
+    kd = synth.torch_normal((1, S, 8, d), 1103, torch.bfloat16)
+    vd = synth.torch_normal((1, S, 8, d), 1104, torch.bfloat16)
+    q, k, v = (host_bits(x) for x in (qd, kd, vd))
+    del qd, kd, vd
+    prow = list(range(255, S, 256))
+    rows = np.array([(0, h, i) for i in prow for h in range(Hq)], np.int64)
+    t = timed(lambda: oracle.attention(q, k, v, scale, causal=True, sparse=True, block=64, sink_tokens=128,
+                                       window_tokens=2048, rows=rows, n_threads=cores))
+    fl = 4.0 * d * Hq * sum(sparse_row_pairs(i) for i in prow)
+    sub["layer_s65536_sparse"] = {"TFLOP/s": round(fl / t / 1e12, 6), "seconds": round(t, 2),
+                                  "sample": f"every 256th query row x {Hq} heads ({len(rows)} rows, {fl:.3e} useful "
+                                            f"flop)"}
+    del q, k, v
+
+    # ---- decode, batch 8 x 262144-token cache: sequence 0, all 32 heads
+    L = 262144
+    qd = synth.torch_normal((8, Hq, d), 1202, torch.bfloat16)
+    kd = synth.torch_normal((8, L, 8, d), 1203, torch.bfloat16)
+    vd = synth.torch_normal((8, L, 8, d), 1204, torch.bfloat16)
+    q0, k0, v0 = host_bits(qd[:1]), host_bits(kd[:1]), host_bits(vd[:1])
+    del qd, kd, vd
+    torch.cuda.empty_cache()
+    for mode, keys in (("dense", L), ("sparse", 128 + 2048)):
+        t = timed(lambda: oracle.decode(q0, k0, v0, scale, sparse=mode == "sparse", block=64, sink_tokens=128,
+                                        window_tokens=2048, n_threads=cores))
+        nbytes = 8 * keys * d * 2 * 2 + 2 * Hq * d * 2     # K+V of the allowed keys of one sequence, q and o
+        sub[f"decode_L262144_{mode}"] = {"GB/s": round(nbytes / t / 1e9, 4), "tok/s": round(1.0 / t, 3),
+                                         "seconds": round(t, 3),
+                                         "sample": f"sequence 0 of 8, all {Hq} heads ({nbytes} algorithmic bytes)"}
+    out["other_configs"] = sub
+    return out
 
 
 if __name__ == "__main__":
