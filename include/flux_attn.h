@@ -292,6 +292,30 @@ int flux_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
                      int32_t mode, int32_t block, int32_t sink_tokens, int32_t window_tokens,
                      int32_t num_splits, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Bytes of the fixed device scratch flux_attn_decode_noalloc keeps its split partials in. */
+#define FLUX_DECODE_SCRATCH_BYTES (16u << 20)
+
+/*
+ * flux_attn_decode_noalloc -- flux_attn_decode without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).
+ *
+ * Same arguments, meaning and results as flux_attn_decode (same kernels), minus the workspace:
+ * the split partials go to a fixed scratch array of FLUX_DECODE_SCRATCH_BYTES in device memory
+ * that the library holds on each GPU it runs on until the process ends.  Nothing is allocated
+ * and nothing is cleared per call (the partials are written before they are read).  A call whose
+ * partials, flux_decode_workspace_size(...) bytes for the same arguments, exceed the scratch is
+ * rejected with FLUX_ERR_CAPACITY before any launch (batch 8 x 32 query heads at head_dim 128 with
+ * the automatic split count needs 4.03 MiB).  Every call on one GPU shares that GPU's scratch:
+ * calls that may overlap on one GPU (several streams, several threads) race and must be
+ * serialised by the caller; calls in order on one stream are safe.
+ */
+int flux_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                             int32_t in_dtype, int32_t out_dtype, int64_t batch, int64_t kv_len,
+                             int64_t kv_capacity, int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                             int32_t mode, int32_t block, int32_t sink_tokens, int32_t window_tokens,
+                             int32_t num_splits, void* hip_stream);
+
 /*
  * flux_window_cache_rows -- rows of a FLUX_KV_WINDOW cache: sink_tokens + window_tokens.
  * Returns 0 if block != 64 or sink/window are not valid multiples of block (window >= block).

@@ -18,10 +18,10 @@ import numpy as np
 __all__ = [
     "FluxError", "lib", "status_string", "last_error_detail", "flux_version",
     "flux_build_block_mask", "flux_attn_prefill", "flux_attn_prefill_layers", "flux_attn_prefill_layers_routed",
-    "flux_decode_workspace_size", "flux_attn_decode", "flux_window_cache_rows", "flux_decode_step",
-    "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers", "flux_route_soft_weights",
-    "flux_prefill_soft_workspace_size", "flux_attn_prefill_soft", "flux_attn_backward_workspace_size",
-    "flux_attn_backward",
+    "flux_decode_workspace_size", "flux_attn_decode", "flux_attn_decode_noalloc", "flux_window_cache_rows",
+    "flux_decode_step", "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers",
+    "flux_route_soft_weights", "flux_prefill_soft_workspace_size", "flux_attn_prefill_soft",
+    "flux_attn_backward_workspace_size", "flux_attn_backward", "FLUX_DECODE_SCRATCH_BYTES",
     "FLUX_OK", "FLUX_ERR_INVALID_ARG", "FLUX_ERR_UNSUPPORTED", "FLUX_ERR_CAPACITY", "FLUX_ERR_WORKSPACE",
     "FLUX_ERR_HIP", "FLUX_DTYPE_BF16", "FLUX_DTYPE_F32", "FLUX_MODE_DENSE", "FLUX_MODE_SPARSE", "FLUX_KV_FULL",
     "FLUX_KV_WINDOW",
@@ -32,12 +32,13 @@ FLUX_OK, FLUX_ERR_INVALID_ARG, FLUX_ERR_UNSUPPORTED, FLUX_ERR_CAPACITY, FLUX_ERR
 FLUX_DTYPE_BF16, FLUX_DTYPE_F32 = 0, 1
 FLUX_MODE_DENSE, FLUX_MODE_SPARSE = 0, 1
 FLUX_KV_FULL, FLUX_KV_WINDOW = 0, 1
+FLUX_DECODE_SCRATCH_BYTES = 16 << 20
 
 EXPORTED_SYMBOLS = (
     "flux_status_string", "flux_last_error_detail", "flux_version", "flux_build_block_mask",
     "flux_attn_prefill", "flux_attn_prefill_layers", "flux_attn_prefill_layers_routed",
-    "flux_decode_workspace_size", "flux_attn_decode", "flux_window_cache_rows", "flux_decode_step",
-    "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers", "flux_route_soft_weights",
+    "flux_decode_workspace_size", "flux_attn_decode", "flux_attn_decode_noalloc", "flux_window_cache_rows",
+    "flux_decode_step", "flux_decode_step_layers", "flux_route_workspace_size", "flux_route_layers", "flux_route_soft_weights",
     "flux_prefill_soft_workspace_size", "flux_attn_prefill_soft", "flux_attn_backward_workspace_size",
     "flux_attn_backward",
 )
@@ -81,6 +82,9 @@ _lib.flux_decode_workspace_size.restype = _sz
 _lib.flux_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _f32,
                                   _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
 _lib.flux_attn_decode.restype = ctypes.c_int
+_lib.flux_attn_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32,
+                                          _f32, _i32, _i32, _i32, _i32, _i32, _vp]
+_lib.flux_attn_decode_noalloc.restype = ctypes.c_int
 _lib.flux_window_cache_rows.argtypes = [_i32, _i32, _i32]
 _lib.flux_window_cache_rows.restype = _i64
 _lib.flux_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
@@ -360,6 +364,32 @@ def flux_attn_decode(q, k_cache, v_cache, o, lse=None, *, kv_len: int | None = N
                                  _dtype_code(o), B, kv_len, cap, Hq, Hkv, d, scale, mode, block, sink_tokens,
                                  window_tokens, num_splits, _ptr(workspace), ws_bytes, _stream(stream)),
            "flux_attn_decode")
+
+
+def flux_attn_decode_noalloc(q, k_cache, v_cache, o, lse=None, *, kv_len: int | None = None,
+                             mode: int = FLUX_MODE_DENSE, block: int = 64, sink_tokens: int = 128,
+                             window_tokens: int = 2048, num_splits: int = 0, scale: float | None = None, stream=None):
+    """flux_attn_decode without a workspace: the partials go to the library's fixed per-device scratch of
+    FLUX_DECODE_SCRATCH_BYTES (calls that may overlap on one GPU race; calls in order on one stream do not)."""
+    import torch
+    _dev(q, "q", None, (torch.bfloat16,))
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [batch, q_heads, head_dim] and the caches [batch, rows, kv_heads, head_dim]")
+    B, Hq, d = q.shape
+    cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _dev(k_cache, "k_cache", (B, cap, Hkv, d), (torch.bfloat16,), q)
+    _dev(v_cache, "v_cache", (B, cap, Hkv, d), (torch.bfloat16,), q)
+    _dev(o, "o", (B, Hq, d), _float_types(), q)
+    if lse is not None:
+        _dev(lse, "lse", (B, Hq), (torch.float32,), q)
+    if kv_len is None:
+        kv_len = cap
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(_lib.flux_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _dtype_code(q),
+                                         _dtype_code(o), B, kv_len, cap, Hq, Hkv, d, scale, mode, block, sink_tokens,
+                                         window_tokens, num_splits, _stream(stream)),
+           "flux_attn_decode_noalloc")
 
 
 def flux_window_cache_rows(block: int = 64, sink_tokens: int = 128, window_tokens: int = 2048) -> int:

@@ -20,8 +20,18 @@
 // Combine kernel: LSE = M + ln sum_s exp(lse_s - M), O = sum_s exp(lse_s - LSE) O_s.
 #include "flux_internal.h"
 
+#include <mutex>
+
 namespace flux {
 namespace {
+
+// Scratch of the no-allocation decode entry point (flux_attn_decode_noalloc): the split partials
+// live here instead of in a caller workspace.  One copy per device, held until the process ends.
+// Host code never passes this name to a kernel (on the host it is only a stand-in for the symbol);
+// it passes the device address decode_scratch() looks up.
+static __device__ __align__(256) __attribute__((used)) char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16;
@@ -318,6 +328,26 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+    // looked up once per device, with that device current (each device holds its own copy)
+    static std::mutex mu;
+    static void* dev_ptr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!dev_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        dev_ptr[dev] = p;
+    }
+    *ptr = dev_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     if (a.head_dim == 128) return launch_d<128>(a, s);

@@ -640,6 +640,36 @@ int flux_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
                       workspace, workspace_bytes, hip_stream);
 }
 
+int flux_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                             int32_t in_dtype, int32_t out_dtype, int64_t batch, int64_t kv_len, int64_t kv_capacity,
+                             int32_t hq, int32_t hkv, int32_t head_dim, float scale, int32_t mode, int32_t block,
+                             int32_t sink_tokens, int32_t window_tokens, int32_t num_splits, void* hip_stream) {
+    static_assert(flux::kDecodeScratchBytes == (size_t)FLUX_DECODE_SCRATCH_BYTES, "scratch size");
+    if (kv_capacity == 0) kv_capacity = kv_len;
+    if (kv_capacity < kv_len) return fail(FLUX_ERR_INVALID_ARG, "kv_capacity must be 0 or >= kv_len");
+    DecodePlan p;
+    int st = plan_decode(batch, hq, hkv, kv_len, head_dim, mode, block, sink_tokens, window_tokens, num_splits, &p);
+    if (st != FLUX_OK) return st;
+    if (p.ws_bytes > flux::kDecodeScratchBytes)
+        return fail(FLUX_ERR_CAPACITY,
+                    "the split partials need %zu bytes, more than the %zu-byte scratch of the no-allocation "
+                    "decode (fewer sequences, query heads or splits per call, or flux_attn_decode with a workspace)",
+                    p.ws_bytes, flux::kDecodeScratchBytes);
+    // every other argument is validated before the scratch lookup (the first HIP call); the placeholder
+    // stands for the scratch in that check only and is never dereferenced
+    void* const validate_only_ws = reinterpret_cast<void*>(uintptr_t(256));
+    st = run_decode(q, k_cache, v_cache, nullptr, nullptr, o, lse, in_dtype, out_dtype, batch, kv_len, kv_capacity,
+                    FLUX_KV_FULL, hq, hkv, head_dim, scale, mode, block, sink_tokens, window_tokens, num_splits,
+                    validate_only_ws, flux::kDecodeScratchBytes, hip_stream, false);
+    if (st != FLUX_OK) return st;
+    void* scratch = nullptr;
+    hipError_t e = flux::decode_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e, "decode scratch lookup");
+    return run_decode(q, k_cache, v_cache, nullptr, nullptr, o, lse, in_dtype, out_dtype, batch, kv_len, kv_capacity,
+                      FLUX_KV_FULL, hq, hkv, head_dim, scale, mode, block, sink_tokens, window_tokens, num_splits,
+                      scratch, flux::kDecodeScratchBytes, hip_stream);
+}
+
 int64_t flux_window_cache_rows(int32_t block, int32_t sink_tokens, int32_t window_tokens) {
     if (block != flux::kBlock || sink_tokens < 0 || window_tokens < block || sink_tokens % block ||
         window_tokens % block)

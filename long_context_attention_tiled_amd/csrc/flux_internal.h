@@ -127,6 +127,11 @@ struct BackwardArgs {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Bytes of the decode's fixed device scratch (the no-allocation decode entry point); the same value as
+// FLUX_DECODE_SCRATCH_BYTES in flux_attn.h.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+// Device address of that scratch on the current device (looked up on the first call per device).
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_route_soft(const float* logits, const float* uniforms, float tau, int n_layers, float* weights,
                              hipStream_t s);

@@ -365,6 +365,46 @@ def test_decode_validation(fa):
     assert _decode(fa, ws=FAKE + 64) == E                   # workspace alignment
 
 
+def _decode_noalloc(fa, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, in_dtype=0, out_dtype=1, batch=2, kv_len=4096, cap=0,
+                hq=8, hkv=2, d=128, scale=0.088, mode=0, block=64, sink=128, window=2048, ns=0)
+    args.update(kw)
+    return fa.lib().flux_attn_decode_noalloc(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                                             args["in_dtype"], args["out_dtype"], args["batch"], args["kv_len"],
+                                             args["cap"], args["hq"], args["hkv"], args["d"], args["scale"],
+                                             args["mode"], args["block"], args["sink"], args["window"], args["ns"],
+                                             None)
+
+
+def test_decode_noalloc_validation(fa):
+    """The no-allocation decode validates like flux_attn_decode, and rejects split partials larger than its
+    fixed scratch (FLUX_DECODE_SCRATCH_BYTES) with FLUX_ERR_CAPACITY, all before its first HIP call."""
+    E, U, C = fa.FLUX_ERR_INVALID_ARG, fa.FLUX_ERR_UNSUPPORTED, fa.FLUX_ERR_CAPACITY
+    assert _decode_noalloc(fa, q=None) == E
+    assert _decode_noalloc(fa, o=FAKE + 4) == E
+    assert _decode_noalloc(fa, hq=8, hkv=3) == E
+    assert _decode_noalloc(fa, hq=32, hkv=2) == U
+    assert _decode_noalloc(fa, cap=100) == E
+    assert _decode_noalloc(fa, scale=float("nan")) == E
+    assert _decode_noalloc(fa, mode=1, window=0) == E
+    assert _decode_noalloc(fa, d=80) == U
+    assert _decode_noalloc(fa, in_dtype=1) == U
+    # partials over the scratch: batch 64 x 32 heads x 64 splits x 129 floats
+    big = dict(batch=64, hq=32, hkv=8, ns=64)
+    need = fa.flux_decode_workspace_size(64, 32, 8, 4096, 128, 0, 64, 128, 2048, 64)
+    assert need > fa.FLUX_DECODE_SCRATCH_BYTES
+    assert _decode_noalloc(fa, **big) == C
+    assert "scratch" in fa.last_error_detail()
+    # the decode workload's shape (batch 8, 32/8 heads, 262144-token cache, automatic splits) fits
+    assert fa.flux_decode_workspace_size(8, 32, 8, 262144, 128, 0, 64, 128, 2048, 0) <= fa.FLUX_DECODE_SCRATCH_BYTES
+
+
+def test_decode_scratch_constant_matches_header(fa):
+    with open(os.path.join(ROOT, "include", "flux_attn.h")) as f:
+        m = re.search(r"#define FLUX_DECODE_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FLUX_DECODE_SCRATCH_BYTES
+
+
 def test_route_workspace_size(fa):
     align = lambda x: (x + 255) // 256 * 256
     assert fa.flux_route_workspace_size(36, 32, 128, 256) == align(36 * 4096 * 4) + align(36 * 256 * 4) + align(36 * 4)
