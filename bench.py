@@ -278,8 +278,9 @@ def headline(args, fa, synth, torch, dev):
     timers = [KernelTimer() for _ in range(L)]
 
     def layer_call(l):
+        # no CSR: a sparse layer's kernel derives its key blocks from (sink, window)
         fa.flux_attn_prefill_layers_routed(modes_dev[l:l + 1], [qs[l]], [ks[l]], [vs[l]], [o], None, block=64,
-                                           sink_tokens=sink, window_tokens=window, blk_row_ptr=rpd, blk_col_idx=cid)
+                                           sink_tokens=sink, window_tokens=window)
 
     def step(record=False):
         # router -> 36 device modes -> each layer's prefill kernel reads its own mode: no host round trip
@@ -391,15 +392,12 @@ def run_layer8k(fa, synth, torch, dev, reps, warmup):
     route_ws = torch.empty(fa.flux_route_workspace_size(1, Hq, d, 256), dtype=torch.uint8, device=dev)
     timer = KernelTimer()
     useful = 4.0 * B * Hq * d * causal_pairs(S)
-    rp, ci = fa.flux_build_block_mask(S, S, 64, 128, 2048, 1, fa.FLUX_MODE_SPARSE)
-    rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
 
     def step(record=False):
         fa.flux_route_layers([q[0]], w_enc, b_enc, w_head, b_head, modes_dev, None, workspace=route_ws,
                              pool_tokens=100)
         call = lambda: fa.flux_attn_prefill_layers_routed(modes_dev, [q], [k], [v], [o], None, block=64,
-                                                          sink_tokens=128, window_tokens=2048, blk_row_ptr=rpd,
-                                                          blk_col_idx=cid)
+                                                          sink_tokens=128, window_tokens=2048)
         if record:
             timer.record(call)
         else:
@@ -442,13 +440,20 @@ def run_legs(fa, synth, torch, dev, sel, reps, warmup):
         rpd, cid = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
         if "sparse" in sel:
             useful = 4.0 * B * Hq * d * csr_pairs(rp, ci, S)
+            # key blocks derived from (sink, window) in the kernel; the CSR walk timed beside it
             call = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_SPARSE,
-                                                sink_tokens=128, window_tokens=2048, blk_row_ptr=rpd, blk_col_idx=cid)
+                                                sink_tokens=128, window_tokens=2048)
+            call_csr = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_SPARSE,
+                                                    sink_tokens=128, window_tokens=2048, blk_row_ptr=rpd,
+                                                    blk_col_idx=cid)
             ms = time_steps(call, reps, 3)
+            ms_csr = time_steps(call_csr, reps, 3)
             legs["sparse_prefill_s65536"] = {"ms": round(ms, 4), "ms_p10_p50_p90": call_percentiles(call, reps),
                                              "useful_flops": useful, "nnz_blocks": int(len(ci)),
                                              "TFLOP/s": round(useful / ms / 1e9, 2),
-                                             "frac": round(useful / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+                                             "frac": round(useful / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                             "csr_walk_ms": round(ms_csr, 4),
+                                             "csr_walk_TFLOP/s": round(useful / ms_csr / 1e9, 2)}
         if "dense64k" in sel:
             calld = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=fa.FLUX_MODE_DENSE)
             msd = time_steps(calld, 3, 1)

@@ -118,10 +118,13 @@ int flux_build_block_mask(int64_t seq_q, int64_t seq_k, int32_t block, int32_t s
  *   lse [batch, hq, seq] float32 natural-log sum-exp of the scaled scores, or NULL
  * Query head h reads KV head h / (hq / hkv) (grouped-query attention).
  * mode == FLUX_MODE_DENSE: causal (key <= query) if causal != 0, else all keys.
- * mode == FLUX_MODE_SPARSE: requires causal == 1 and the device CSR that
- *   flux_build_block_mask(seq, seq, block, sink_tokens, window_tokens, 1,
- *   FLUX_MODE_SPARSE, ...) produced (blk_row_ptr [nbq+1], blk_col_idx
- *   [blk_nnz], both device int32); blk_nnz is checked against the pattern.
+ * mode == FLUX_MODE_SPARSE: requires causal == 1.  The active key blocks are
+ *   those flux_build_block_mask(seq, seq, block, sink_tokens, window_tokens,
+ *   1, FLUX_MODE_SPARSE, ...) lists.  Either pass that device CSR
+ *   (blk_row_ptr [nbq+1], blk_col_idx [blk_nnz], int32; blk_nnz is checked
+ *   against the pattern) and the kernels walk it, or pass both NULL and the
+ *   kernels derive the same blocks from (sink_tokens, window_tokens) with
+ *   integer arithmetic (no per-tile index loads; bit-identical results).
  *   Inside an active block every key is visible except keys after the query
  *   in the diagonal block.  Dense mode ignores the CSR arguments.
  * Supported: (in, out) = (BF16, BF16), (BF16, F32), (F32, F32);
@@ -142,7 +145,8 @@ int flux_attn_prefill(const void* q, const void* k, const void* v, void* o, floa
  * lse ? lse[l] : NULL, ..., causal = 1, mode = modes_host[l], ...) on
  * `hip_stream`.  modes_host is a HOST array of n_layers entries (the router
  * output copied to the host).  All layers share shape, dtypes, block, sink,
- * window and the sparse CSR.  Layers are validated before the first launch.
+ * window and the optional sparse CSR (as for flux_attn_prefill: the CSR, or
+ * both pointers NULL).  Layers are validated before the first launch.
  */
 int flux_attn_prefill_layers(int32_t n_layers, const int32_t* modes_host, const void* const* q,
                              const void* const* k, const void* const* v, void* const* o,
@@ -162,9 +166,10 @@ int flux_attn_prefill_layers(int32_t n_layers, const int32_t* modes_host, const 
  * block-sparse) when they start.  The router ([FA] router paragraphs: argmax of
  * the router head at inference) and the attention of the layer therefore run
  * back to back on `hip_stream`; the host never waits for the mode.  Because
- * any layer may turn out sparse, the CSR arguments are required and checked as
- * for FLUX_MODE_SPARSE.  modes_device must stay valid until the launches have
- * run.
+ * any layer may turn out sparse, every layer is validated as for
+ * FLUX_MODE_SPARSE (the CSR arguments: that CSR, or both NULL to derive the
+ * blocks from sink and window).  modes_device must stay valid until the
+ * launches have run.
  */
 int flux_attn_prefill_layers_routed(int32_t n_layers, const int32_t* modes_device,
                                     const void* const* q, const void* const* k,

@@ -132,8 +132,8 @@ int check_prefill(const void* q, const void* k, const void* v, void* o, float* l
         return fail(FLUX_ERR_UNSUPPORTED, "batch * hq * ceil(seq/64) exceeds the launch grid");
     if (seq * (int64_t)std::max(hq, hkv) * head_dim > INT32_MAX)
         return fail(FLUX_ERR_UNSUPPORTED, "seq * max(hq, hkv) * head_dim must stay below 2^31 elements");
-    if (ms.sparse) {
-        if (!rp || !ci) return fail(FLUX_ERR_INVALID_ARG, "sparse mode needs blk_row_ptr and blk_col_idx");
+    if (ms.sparse && (rp || ci)) {   // the CSR walk; without a CSR the kernels derive the same blocks
+        if (!rp || !ci) return fail(FLUX_ERR_INVALID_ARG, "blk_row_ptr and blk_col_idx must both be given or both NULL");
         int64_t want = mask_nnz(ms);
         if (nnz != want)
             return fail(FLUX_ERR_INVALID_ARG, "blk_nnz %lld does not match the sparse pattern (%lld)",

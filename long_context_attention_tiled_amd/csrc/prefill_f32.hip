@@ -47,15 +47,22 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
     const float c2 = a.scale_log2;
 
     const bool sparse = a.mode_dev ? a.mode_dev[0] != 0 : a.sparse != 0;
-    int p = 0, e = 0;
-    if (sparse) {
+    // key blocks of query block qb: the CSR row when one is given; else (and in dense mode) position p
+    // of the walk is block p, except that a sparse walk jumps from the end of the sink blocks to the
+    // first block of the window (the same blocks the CSR lists)
+    const bool csr = sparse && a.row_ptr;
+    int p = 0, e = 0, sink_end = 0, win_lo = 0;
+    if (csr) {
         p = a.row_ptr[qb];
         e = a.row_ptr[qb + 1];
     } else {
-        e = a.causal ? qb + 1 : a.n_qblk;
+        e = (a.causal || sparse) ? qb + 1 : a.n_qblk;
+        sink_end = sparse ? min(a.sink_blocks, qb + 1) : e;
+        win_lo = sparse ? max(sink_end, qb - a.window_blocks + 1) : e;
     }
     for (; p < e; ++p) {
-        const int kb = sparse ? a.col_idx[p] : p;
+        if (!csr && p == sink_end && win_lo > p) p = win_lo;
+        const int kb = csr ? a.col_idx[p] : p;
         __syncthreads();
         for (int idx = tid; idx < kTile * D / 4; idx += kThreads) {
             const int row = idx / (D / 4), c4 = idx % (D / 4);

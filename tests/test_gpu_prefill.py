@@ -109,6 +109,43 @@ def test_sparse_full_window_equals_dense(fa):
     assert torch.equal(o_d, o_s) and torch.equal(l_d, l_s)
 
 
+@pytest.mark.parametrize("B,S,Hq,Hkv,d,sink,window", [
+    (1, 1000, 4, 1, 128, 128, 128),     # ragged tail, window 2 blocks
+    (2, 517, 8, 2, 64, 64, 192),
+    (1, 640, 2, 1, 128, 0, 64),          # no sink, one-block window
+    (1, 100, 2, 1, 128, 128, 128),       # shorter than the sink
+    (1, 450, 3, 1, 64, 192, 128),        # odd group (four query blocks per workgroup), 3-block sink
+    (1, 700, 8, 1, 128, 128, 320),       # 8 query heads per KV head
+])
+def test_sparse_without_csr_equals_csr(fa, B, S, Hq, Hkv, d, sink, window):
+    """Block-sparse prefill with no CSR derives the key blocks from (sink, window) arithmetically: the
+    outputs equal the CSR walk's bit for bit, and the oracle's."""
+    say("sparse without CSR", B, S, Hq, Hkv, d, sink, window)
+    (q, k, v), (qd, kd, vd) = bf16_tensors(B, S, Hq, Hkv, d, seed=2400 + S)
+    o_c, l_c = _run_prefill(fa, qd, kd, vd, torch.float32, 1, sink=sink, window=window)
+    o_a = torch.full_like(o_c, float("nan"))
+    l_a = torch.full_like(l_c, float("nan"))
+    fa.flux_attn_prefill(qd, kd, vd, o_a, l_a, causal=1, mode=fa.FLUX_MODE_SPARSE, block=64, sink_tokens=sink,
+                         window_tokens=window)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_c) and torch.equal(l_a, l_c)
+    ref, _ = oracle.attention(q, k, v, default_scale(d), causal=True, sparse=True, block=64, sink_tokens=sink,
+                              window_tokens=window)
+    check_close(o_a.cpu().numpy(), ref, "sparse without CSR")
+
+
+def test_sparse_without_csr_fp32_inputs(fa):
+    """The float32-input kernel's arithmetic walk (tiny layer: 2 heads, head_dim 64, sink 2 blocks, window 2)."""
+    B, S, H, d = 1, 512, 2, 64
+    q, k, v = synth.qkv_f32(B, S, H, H, d, seed=1001)
+    qd, kd, vd = (torch.from_numpy(x).to(DEV) for x in (q, k, v))
+    o_c, _ = _run_prefill(fa, qd, kd, vd, torch.float32, 1, sink=128, window=128)
+    o_a = torch.full_like(o_c, float("nan"))
+    fa.flux_attn_prefill(qd, kd, vd, o_a, None, causal=1, mode=fa.FLUX_MODE_SPARSE, sink_tokens=128, window_tokens=128)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_c)
+
+
 def test_prefill_deterministic(fa):
     B, S, Hq, Hkv, d = 1, 1500, 8, 2, 128
     say("determinism")
@@ -260,6 +297,12 @@ def test_layer_sparse_s65536(fa):
     vd = synth.torch_normal((B, S, Hkv, d), 1005, torch.bfloat16)
     o, lse = _run_prefill(fa, qd, kd, vd, torch.float32, 1)
     _assert_all_written(o, lse)
+    o_a = torch.full_like(o, float("nan"))
+    fa.flux_attn_prefill(qd, kd, vd, o_a, None, causal=1, mode=fa.FLUX_MODE_SPARSE, sink_tokens=128,
+                         window_tokens=2048)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o), "arithmetic walk differs from the CSR walk"
+    del o_a
     rows = _wave_rows(B, Hq, S, 32, 1003)
     ref, ref_lse = oracle.attention(dev_bits_to_host(qd), dev_bits_to_host(kd), dev_bits_to_host(vd),
                                     default_scale(d), causal=True, sparse=True, block=64, sink_tokens=128,
@@ -271,8 +314,9 @@ def test_layer_sparse_s65536(fa):
 
 def test_routed_stack_layers_s131072(fa):
     """Qwen3-8B-shaped stack at seq 131072: one dense and one sparse layer whose modes come from the router
-    (head bias) and stay on the device, run by flux_attn_prefill_layers_routed with bf16 outputs as in the
-    36-layer benchmark, and again by host-mode dispatch: bit-equal, every element written (NaN fill), and
+    (head bias) and stay on the device, run by flux_attn_prefill_layers_routed with bf16 outputs and no CSR
+    as in the 36-layer benchmark, and again by host-mode dispatch with the CSR: bit-equal, every element
+    written (NaN fill), and
     rows against the oracle -- one row of every 32-row wave segment of every head for the sparse layer, of
     every 1024 rows for the dense one."""
     S, Hq, Hkv, d = 131072, 32, 8, 128
@@ -294,9 +338,9 @@ def test_routed_stack_layers_s131072(fa):
     for routed in (True, False):
         os_ = [torch.full((1, S, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
         ls = [torch.full((1, Hq, S), float("nan"), dtype=torch.float32, device=DEV) for _ in range(2)]
-        if routed:
+        if routed:   # as benchmarked: no CSR, the sparse layer derives its blocks from (sink, window)
             fa.flux_attn_prefill_layers_routed(modes, qs, ks, vs, os_, ls, block=64, sink_tokens=128,
-                                               window_tokens=2048, blk_row_ptr=rp, blk_col_idx=ci)
+                                               window_tokens=2048)
         else:
             fa.flux_attn_prefill_layers(plan, qs, ks, vs, os_, ls, block=64, sink_tokens=128, window_tokens=2048,
                                         blk_row_ptr=rp, blk_col_idx=ci)
