@@ -102,8 +102,10 @@ static void validation_checks() {
                             0, nullptr) == U);
     CHECK(flux_attn_prefill(q, k, v, o, nullptr, 0, 1, 1, 512, 8, 2, 128, -1.0f, 1, 0, 64, 128, 2048, nullptr,
                             nullptr, 0, nullptr) == E);
-    CHECK(flux_attn_prefill(q, k, v, o, nullptr, 0, 1, 1, 512, 8, 2, 128, 0.08f, 1, 1, 64, 128, 2048, nullptr,
-                            nullptr, 0, nullptr) == E);   // sparse without a CSR
+    CHECK(flux_attn_prefill(q, k, v, o, nullptr, 0, 1, 1, 512, 8, 2, 128, 0.08f, 1, 1, 64, 128, 2048,
+                            (const int32_t*)ws, nullptr, 0, nullptr) == E);   // half a CSR
+    CHECK(flux_attn_prefill(q, k, v, o, nullptr, 0, 1, 1, 512, 8, 2, 128, 0.08f, 1, 1, 64, 128, 2048,
+                            (const int32_t*)ws, (const int32_t*)ws, 7, nullptr) == E);   // nnz not the pattern's
     // per-layer dispatch: a NULL pointer in layer 1 is found before anything launches
     const void* qs[2] = {q, nullptr};
     const void* ks[2] = {k, k};
