@@ -85,34 +85,6 @@ struct Lay {
     static_assert(INSTS_PER_WAVE * kWaves * 1024 == TILE_B, "tile split over the waves");
 };
 
-// Chunk swizzles of the 16x16x32 layout.  K is read 16 rows at one logical chunk (ds_read_b128);
-// V^T with transposing reads of 8 rows x 32 bytes per 32 lanes, so rows r and r + 4 must land in
-// different 32-byte bank groups as well (physical chunk = logical chunk ^ swizzle(row)).
-template <int D>
-__device__ __forceinline__ int swz16_k(int row) {
-    if constexpr (D == 128) return row & 15;
-    else return (row >> 1) & 7;
-}
-template <int D>
-__device__ __forceinline__ int swz16_v(int row) {
-    if constexpr (D == 128) return 2 * (row & 7);
-    else return 2 * ((row >> 1) & 3);
-}
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// max / sum over the four lanes l, l^16, l^32, l^48 (v_permlane16_swap, v_permlane32_swap)
-__device__ __forceinline__ float max_quarters(float x) {
-    x = max_halves(x);
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_quarters(float x) {
-    x = sum_halves(x);
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // kRouted: causal, dense or sparse as the layer's device-resident mode says (read at start).
 // kSoft: dense causal with the key tiles ordered sink, window (descending), then the rest, so that every
 // row's block-sparse set is a prefix of its walk: the row's sparse output is taken where its window
@@ -224,7 +196,7 @@ struct TileWalk {
 // l%CH, i.e. logical chunk (l%CH) ^ swizzle(row) of that key.  Keys past the end of
 // the sequence are clamped to the last one (masked to -inf in the scores,
 // probability 0 in P.V).
-template <int D, bool IS_V, bool L16 = false>
+template <int D, bool IS_V>
 __device__ __forceinline__ void issue_tile(const u16* __restrict__ gbase, uint32_t row_stride, int kb, int last_key,
                                            uint32_t slot, int wave, int lane, const uint32_t* off) {
     using L = Lay<D>;
@@ -241,7 +213,7 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ gbase, uint32
             const int row = inst * L::ROWS_PER_INST + lane / L::CH;
             const uint32_t key = (uint32_t)min(key0 + row, last_key);
             const int pch = lane % L::CH;
-            const int sw = L16 ? (IS_V ? swz16_v<D>(row) : swz16_k<D>(row)) : (IS_V ? swz_v<D>(row) : swz_k<D>(row));
+            const int sw = IS_V ? swz_v<D>(row) : swz_k<D>(row);
             load_lds_16(uniform_ptr(gbase), 2 * (key * row_stride + 8 * (pch ^ sw)), slot + inst * 1024);
         }
     }
@@ -640,413 +612,21 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
         run(BoolTag<true>{});
 }
 
-// The same tile pipeline with the two contractions on v_mfma_f32_16x16x32_bf16.  A wave's 32
-// query rows are two 16-query sub-tiles qs; a lane holds query q0 + 16qs + (lane & 15) and, in
-// every 16x16 accumulator, the rows 4(lane >> 4) .. +3 (keys of S^T, d of O^T).  Each K or V^T
-// operand read from LDS (1 KB per wave) feeds two MFMAs, one per query sub-tile.  P^T enters
-// P.V straight from the score registers: a lane's keys 32kc + 4g + 0..3 and 32kc + 16 + 4g + 0..3
-// (g = lane >> 4) form its k-slots 8g .. 8g+7 of key chunk kc, and the V^T operand is read with
-// the same key order (two transposing reads).  Row statistics need the four lane groups: one
-// v_permlane16_swap and one v_permlane32_swap per reduction.
-template <int D, int MODE, bool OUT_F32>
-__device__ __forceinline__ void prefill_body16(const PrefillArgs& a, char* smem) {
-    using L = Lay<D>;
-    constexpr int NK = D / 32;   // 32-wide d chunks of the S^T contraction
-    constexpr int ND = D / 16;   // 16-row d tiles of O^T
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2;   // wave group
-    const int wq = wave & 3;     // wave inside its group
-    const int l16 = lane & 15;   // query column inside a 16-query sub-tile
-    const int g4 = lane >> 4;    // lane group: operand k-slots 8g4.., accumulator rows 4g4..
-
-    const int seq = (int)a.seq;          // the host guarantees seq * max(hq, hkv) * d < 2^31
-    const int nqt = (seq + kBR - 1) / kBR;
-    const int G = a.hq / a.hkv;
-    const bool pair_heads = (G & 1) == 0;
-    const int per_g = pair_heads ? (G / 2) * nqt : G * ((nqt + 1) / 2);
-    const int total = (int)a.batch * a.hkv * per_g;
-    const bool persistent = (int)gridDim.x < total;
-    const int xcd = (int)blockIdx.x & 7, wi = (int)blockIdx.x >> 3, nper = (int)gridDim.x >> 3;
-    auto vb_at = [&](int k) -> int {
-        if (!persistent) return k == 0 ? (int)blockIdx.x : total;
-        const int t = k * nper + ((k & 1) ? nper - 1 - wi : wi);
-        return t * 8 + xcd;
-    };
-
-    const uint32_t q_row_stride = (uint32_t)(a.hq * D);
-    const uint32_t kv_row_stride = (uint32_t)(a.hkv * D);
-    const int last_key = seq - 1;
-
-    uint32_t koff[L::INSTS_PER_WAVE], voff[L::INSTS_PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < L::INSTS_PER_WAVE; ++i) {
-        const int row = (wave * L::INSTS_PER_WAVE + i) * L::ROWS_PER_INST + lane / L::CH;
-        const int pch = lane % L::CH;
-        koff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz16_k<D>(row)));   // bytes
-        voff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz16_v<D>(row)));
-    }
-    const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-
-    int b = 0, h = 0, qb_base = 0, my_r = 0, my_qb = 0;
-    int qpos[2] = {0, 0};
-    bool wave_live = false;
-    const u16* kg = nullptr;
-    const u16* vg = nullptr;
-    bf16x8 qreg[2][NK];   // B operand of S^T: lane holds Q[qpos[qs]][32c + 8g4 .. +7]
-    TileWalk<MODE> walk;
-    uint32_t in;
-    int kb_p = 0, kb_c = 0, kb_n = 0;
-    bool mine_p = false, mine_c = false, mine_n = false, have_any = false, have_n = false;
-
-    auto begin_unit = [&](int vb) {
-        int lid = xcd_remap(vb, total);
-        const int unit = lid % per_g;
-        lid /= per_g;
-        const int g = lid % a.hkv;
-        b = lid / a.hkv;
-        int qt, nrows;
-        if (pair_heads) {
-            const int jp = unit % (G / 2);
-            const int rank = unit / (G / 2);
-            qt = (MODE != kDenseFull) ? nqt - 1 - rank : rank;
-            h = g * G + 2 * jp + grp;
-            qb_base = 2 * qt;
-            my_r = wq >> 1;
-            nrows = 2;
-        } else {
-            const int npq = (nqt + 1) / 2;
-            const int j = unit % G;
-            const int rank = unit / G;
-            const int qp = (MODE != kDenseFull) ? npq - 1 - rank : rank;
-            h = g * G + j;
-            qt = 2 * qp + grp;
-            qb_base = 4 * qp;
-            my_r = 2 * grp + (wq >> 1);
-            nrows = 4;
-        }
-        kg = reinterpret_cast<const u16*>(a.k) + ((int64_t)b * a.seq * a.hkv + g) * D;
-        vg = reinterpret_cast<const u16*>(a.v) + ((int64_t)b * a.seq * a.hkv + g) * D;
-        const int q0 = qt * kBR + wq * 32;
-        qpos[0] = q0 + l16;
-        qpos[1] = q0 + 16 + l16;
-        wave_live = q0 < seq;
-        my_qb = qb_base + my_r;
-        walk.init(qb_base, nrows, a.n_qblk, a.row_ptr, a.col_idx, a.sink_blocks, a.window_blocks);
-        have_any = walk.next(kb_c, in);
-        mine_c = have_any && wave_live && ((in >> my_r) & 1);
-        have_n = have_any && walk.next(kb_n, in);
-        mine_n = have_n && wave_live && ((in >> my_r) & 1);
-        mine_p = false;
-        if (have_any)
-            issue_tile<D, false, true>(kg, kv_row_stride, kb_c, last_key, smem_lds + L::K_BASE, wave, lane, koff);
-        const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * D;
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-            const uint32_t qrow = (uint32_t)min(qpos[qs], last_key);
-#pragma unroll
-            for (int c = 0; c < NK; ++c)
-                qreg[qs][c] = *reinterpret_cast<const bf16x8*>(qg + qrow * q_row_stride + 32 * c + 8 * g4);
-        }
-    };
-
-    // LDS byte offsets of this lane's operand reads (slot-relative)
-    // K (ks, c): row 16ks + l16, logical chunk 4c + g4
-    uint32_t kaddr[4][NK];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int c = 0; c < NK; ++c)
-            kaddr[ks][c] = (16 * ks + l16) * L::ROW_B + 16 * ((4 * c + g4) ^ swz16_k<D>(16 * ks + l16));
-    // V^T (transposing reads): lane group g4 -> keys 4g4 .. +3 (+32kc, +16 for the second read), lane
-    // l16 points at key 4g4 + (l16 >> 2), d = 16dt + 4(l16 & 3) .. +3, and receives column 16dt + l16
-    const int vrow = 4 * g4 + (l16 >> 2);
-    uint32_t vaddr[ND];
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-        const int lch = 2 * dt + ((l16 & 3) >> 1);
-        vaddr[dt] = vrow * L::ROW_B + 16 * (lch ^ swz16_v<D>(vrow)) + 8 * (l16 & 1);
-    }
-
-    f32x4 oacc[ND][2];
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) oacc[dt][0] = oacc[dt][1] = f32x4{};
-    f32x4 sacc[4][2];
-    bf16x8 pb[2][2];   // P^T operand [qs][key chunk kc]
-    float m_run[2] = {kNegBig, kNegBig}, l_run[2] = {0.0f, 0.0f};
-    const float c2 = a.scale_log2;
-    bool snapped = false;
-
-    auto out_rows = [&](auto&& write) {   // write(qs, dt, float4 of O^T / l)
-        float inv[2];
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-            const float l_tot = sum_quarters(l_run[qs]);
-            inv[qs] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-            l_run[qs] = l_tot;   // the caller's LSE uses the full sum
-        }
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-            for (int dt = 0; dt < ND; ++dt)
-                write(qs, dt, make_float4(oacc[dt][qs][0] * inv[qs], oacc[dt][qs][1] * inv[qs],
-                                          oacc[dt][qs][2] * inv[qs], oacc[dt][qs][3] * inv[qs]));
-    };
-
-    // kSoft: the rows' block-sparse output over the tiles accumulated so far, to soft_ws in fp32.
-    auto snapshot = [&]() {
-        const float keep[2] = {l_run[0], l_run[1]};
-        out_rows([&](int qs, int dt, float4 v) {
-            if (!wave_live || qpos[qs] >= seq) return;
-            float* dst = a.soft_ws + (((int64_t)b * seq + qpos[qs]) * a.hq + h) * D + 16 * dt + 4 * g4;
-            *reinterpret_cast<float4*>(dst) = v;
-        });
-        l_run[0] = keep[0];
-        l_run[1] = keep[1];
-    };
-
-    constexpr int kPrefetch = 6;
-    auto mseq = [&](auto pv_tag, auto s_tag, int vs, int ks_slot) {
-        constexpr bool PV = decltype(pv_tag)::value;
-        constexpr bool S = decltype(s_tag)::value;
-        constexpr int NPV = PV ? 2 * ND : 0;    // P.V operands: key chunk kc major, d tile dt minor
-        constexpr int NT = NPV + (S ? 4 * NK : 0);
-        const char* vt = smem + L::V_BASE + vs * L::TILE_B;
-        const char* kt = smem + L::K_BASE + ks_slot * L::TILE_B;
-        auto operand = [&](int i) -> bf16x8 {
-            if (i < NPV) {
-                const int kc = i / ND, dt = i % ND;
-                const char* vp = vt + vaddr[dt] + 32 * kc * L::ROW_B;
-                const i16x4 lo = read_tr16(vp);
-                const i16x4 hi = read_tr16(vp + 16 * L::ROW_B);
-                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-            const int j = i - NPV;   // S operand (c, ks): c = j / 4, ks = j % 4
-            return *reinterpret_cast<const bf16x8*>(kt + kaddr[j & 3][j >> 2]);
-        };
-        bf16x8 ring[kPrefetch];
-#pragma unroll
-        for (int i = 0; i < kPrefetch; ++i)
-            if (i < NT) ring[i] = operand(i);
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            const bf16x8 op = ring[i % kPrefetch];
-            if (i + kPrefetch < NT) ring[i % kPrefetch] = operand(i + kPrefetch);
-            if (i < NPV) {
-                const int kc = i / ND, dt = i % ND;
-#pragma unroll
-                for (int qs = 0; qs < 2; ++qs)
-                    oacc[dt][qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, pb[qs][kc], oacc[dt][qs], 0, 0, 0);
-            } else {
-                const int j = i - NPV;
-                const int c = j >> 2, ks = j & 3;
-#pragma unroll
-                for (int qs = 0; qs < 2; ++qs) {
-                    const f32x4 acc = c == 0 ? f32x4{} : sacc[ks][qs];
-                    sacc[ks][qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, qreg[qs][c], acc, 0, 0, 0);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    auto mwork = [&](auto pv_tag, auto s_tag, int vs, int ks_slot) {
-        __builtin_amdgcn_s_setprio(2);
-        mseq(pv_tag, s_tag, vs, ks_slot);
-        __builtin_amdgcn_s_setprio(0);
-    };
-
-    // ---- vector work: online softmax of key tile kb.  Lane holds S[qpos[qs]][key] for
-    // key = kb*64 + 16ks + 4g4 + i.
-    auto vwork = [&](bool mine, int kb) {
-        if constexpr (MODE == kSoft) {
-            if (mine && !snapped && kb >= a.sink_blocks && my_qb - kb >= a.window_blocks) {
-                snapshot();
-                snapped = true;
-            }
-        }
-        if (!mine) {
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs) pb[qs][0] = pb[qs][1] = bf16x8{};
-            return;
-        }
-        const bool need_mask = (MODE != kDenseFull && kb >= my_qb) || (kb + 1) * kBC > seq;
-        if (need_mask) {
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-                const int lim = (MODE != kDenseFull ? min(qpos[qs], last_key) : last_key) - (kb * kBC + 4 * g4);
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (16 * ks + r > lim) sacc[ks][qs][r] = -INFINITY;
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-            }
-        }
-        float mx[2];
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-            float x = sacc[0][qs][0];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) x = fmaxf(x, sacc[ks][qs][r]);
-            mx[qs] = max_quarters(x);
-        }
-        if (__ballot((mx[0] - m_run[0]) * c2 > kRescaleSlack || (mx[1] - m_run[1]) * c2 > kRescaleSlack)) {
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-                const float m_new = fmaxf(m_run[qs], mx[qs]);
-                const float alpha = __builtin_amdgcn_exp2f((m_run[qs] - m_new) * c2);
-                l_run[qs] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) oacc[dt][qs][r] *= alpha;
-                m_run[qs] = m_new;
-            }
-        }
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-            const float mc = m_run[qs] * c2;
-            float lsum[2];
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                float p[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * kc + (e >> 2)][qs][e & 3], c2, -mc));
-                pb[qs][kc] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
-                                    (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
-                lsum[kc] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-            }
-            l_run[qs] += lsum[0] + lsum[1];
-        }
-    };
-
-    // ---- epilogue: O = O^T / l; lane holds O[qpos[qs]][16dt + 4g4 .. +3]
-    auto finish_unit = [&]() {
-        out_rows([&](int qs, int dt, float4 v) {
-            if (!wave_live || qpos[qs] >= seq) return;
-            const int64_t orow = ((int64_t)b * seq + qpos[qs]) * a.hq + h;
-            const int d = 16 * dt + 4 * g4;
-            if constexpr (MODE == kSoft) {
-                const float w0 = a.mix_w[0], w1 = a.mix_w[1];
-                if (snapped) {
-                    const float4 f = *reinterpret_cast<const float4*>(a.soft_ws + orow * D + d);
-                    v = make_float4(fmaf(w1, f.x, w0 * v.x), fmaf(w1, f.y, w0 * v.y), fmaf(w1, f.z, w0 * v.z),
-                                    fmaf(w1, f.w, w0 * v.w));
-                } else {
-                    const float w = w0 + w1;
-                    v = make_float4(v.x * w, v.y * w, v.z * w, v.w * w);
-                }
-            }
-            if constexpr (OUT_F32) {
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + orow * D + d) = v;
-            } else {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                *reinterpret_cast<bf16x4*>(reinterpret_cast<u16*>(a.o) + orow * D + d) =
-                    bf16x4{(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
-            }
-        });
-        if (a.lse && g4 == 0) {
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-                if (!wave_live || qpos[qs] >= seq) continue;
-                const float lse = l_run[qs] > 0.0f ? (m_run[qs] * c2 + __log2f(l_run[qs])) * kLn2 : -INFINITY;
-                a.lse[((int64_t)b * a.hq + h) * a.seq + qpos[qs]] = lse;
-            }
-        }
-    };
-
-    constexpr BoolTag<true> kOn{};
-    constexpr BoolTag<false> kOff{};
-    begin_unit(vb_at(0));
-    auto run = [&](auto group_tag) {
-        constexpr bool kG1 = decltype(group_tag)::value;
-        for (int k = 1;; ++k) {
-            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): Q and K of the unit's first tile in place
-            __syncthreads();
-            if (have_any) {
-                if (have_n)
-                    issue_tile<D, false, true>(kg, kv_row_stride, kb_n, last_key, smem_lds + L::K_BASE + L::TILE_B,
-                                               wave, lane, koff);
-                issue_tile<D, true, true>(vg, kv_row_stride, kb_c, last_key, smem_lds + L::V_BASE, wave, lane, voff);
-                if constexpr (!kG1) mwork(kOff, kOn, 0, 0);
-                __syncthreads();
-                if constexpr (!kG1) vwork(mine_c, kb_c);
-                else mwork(kOff, kOn, 0, 0);
-                __builtin_amdgcn_s_waitcnt(0x0f70);
-                __syncthreads();
-                int sl = 1;
-                while (have_n) {
-                    kb_p = kb_c;
-                    mine_p = mine_c;
-                    kb_c = kb_n;
-                    mine_c = mine_n;
-                    have_n = walk.next(kb_n, in);
-                    mine_n = have_n && wave_live && ((in >> my_r) & 1);
-                    if (have_n)
-                        issue_tile<D, false, true>(kg, kv_row_stride, kb_n, last_key,
-                                                   smem_lds + L::K_BASE + (sl ^ 1) * L::TILE_B, wave, lane, koff);
-                    issue_tile<D, true, true>(vg, kv_row_stride, kb_c, last_key,
-                                              smem_lds + L::V_BASE + sl * L::TILE_B, wave, lane, voff);
-                    if constexpr (!kG1) mwork(kOn, kOn, sl ^ 1, sl);
-                    else vwork(mine_p, kb_p);
-                    __syncthreads();
-                    if constexpr (!kG1) vwork(mine_c, kb_c);
-                    else mwork(kOn, kOn, sl ^ 1, sl);
-                    __builtin_amdgcn_s_waitcnt(0x0f70);
-                    __syncthreads();
-                    sl ^= 1;
-                }
-                if constexpr (!kG1) mwork(kOn, kOff, sl ^ 1, 0);
-                else vwork(mine_c, kb_c);
-                __syncthreads();
-                if constexpr (kG1) mwork(kOn, kOff, sl ^ 1, 0);
-            }
-            finish_unit();
-            const int vb = vb_at(k);
-            if (vb >= total) break;
-#pragma unroll
-            for (int dt = 0; dt < ND; ++dt) oacc[dt][0] = oacc[dt][1] = f32x4{};
-            m_run[0] = m_run[1] = kNegBig;
-            l_run[0] = l_run[1] = 0.0f;
-            snapped = false;
-            begin_unit(vb);
-        }
-    };
-    if (grp == 0)
-        run(BoolTag<false>{});
-    else
-        run(BoolTag<true>{});
-}
-
 // kRouted: one launch whose workgroups read the layer's mode and run the dense-causal or the
 // block-sparse body (two complete code paths, so neither carries the other's state).
-constexpr bool kMfma16 = false;   // MFMA shape of the prefill: 16x16x32 (true) or 32x32x16 (false)
-
-template <int D, int MODE, bool OUT_F32>
-__device__ __forceinline__ void prefill_any(const PrefillArgs& a, char* smem) {
-    if constexpr (kMfma16) prefill_body16<D, MODE, OUT_F32>(a, smem);
-    else prefill_body<D, MODE, OUT_F32>(a, smem);
-}
-
 template <int D, int MODE, bool OUT_F32>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2))) void
 prefill_bf16_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[Lay<D>::SMEM_B];
     if constexpr (MODE == kRouted) {
         if (a.mode_dev[0] == 0)
-            prefill_any<D, kDenseCausal, OUT_F32>(a, smem);
+            prefill_body<D, kDenseCausal, OUT_F32>(a, smem);
         else if (a.row_ptr)
-            prefill_any<D, kSparse, OUT_F32>(a, smem);
+            prefill_body<D, kSparse, OUT_F32>(a, smem);
         else
-            prefill_any<D, kSparseArith, OUT_F32>(a, smem);
+            prefill_body<D, kSparseArith, OUT_F32>(a, smem);
     } else {
-        prefill_any<D, MODE, OUT_F32>(a, smem);
+        prefill_body<D, MODE, OUT_F32>(a, smem);
     }
 }
 
