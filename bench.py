@@ -718,6 +718,22 @@ def run_microbench(torch, dev):
     out["read_decode_pattern_32_splits_GB/s"] = round(nbytes / median_ms(call) / 1e6, 1)
     del buf, kc, vc
     torch.cuda.empty_cache()
+
+    # issue cost of the prefill's direct HBM -> LDS loads: cycles (s_memtime) a wave spends issuing them
+    wgs = cu.value
+    src = torch.zeros(wgs * 65536, dtype=torch.uint8, device=dev)
+    cyc = torch.zeros(wgs * 16, dtype=torch.int64, device=dev)
+
+    def issue_cycles(n_inst, active):
+        for _ in range(3):
+            ceilings.check(lib.ceil_lds_dma_issue(src.data_ptr(), src.numel(), cyc.data_ptr(), cyc.numel(), wgs,
+                                                  n_inst, active, stream), "ceil_lds_dma_issue")
+        torch.cuda.synchronize()
+        return float(np.median(cyc.view(wgs, 8, 2)[:, :active, 0].cpu().numpy()))
+    one, eight = issue_cycles(1, 1), issue_cycles(8, 1)
+    out["lds_dma_issue_cycles_per_load_1_wave"] = round((eight - one) / 7, 1)
+    out["lds_dma_issue_cycles_4_loads_x_8_waves"] = issue_cycles(4, 8)
+    del src, cyc
     return out
 
 

@@ -1,5 +1,5 @@
 """ctypes binding of libceilings.so: device micro-benchmarks (pure MFMA loop, streaming read, the decode's
-read pattern, CU count and clock) that bench.py reports beside the attention kernels' roofline fractions.
+read pattern, the issue cost of direct HBM -> LDS loads, CU count and clock) that bench.py reports beside the attention kernels' roofline fractions.
 Measurement context only; the attention path never calls it."""
 from __future__ import annotations
 
@@ -17,6 +17,7 @@ SIGNATURES = {
     "ceil_mfma_loop": (ctypes.c_int, [_p, _i64, _p, _i64, _i32, _i32, _i32, _p]),
     "ceil_read_stream": (ctypes.c_int, [_p, _i64, _p, _i64, _i32, _p]),
     "ceil_read_decode": (ctypes.c_int, [_p, _p, _i64, _i64, _i32, _i32, _p, _i64, _p]),
+    "ceil_lds_dma_issue": (ctypes.c_int, [_p, _i64, _p, _i64, _i32, _i32, _i32, _p]),
 }
 
 

@@ -7,7 +7,10 @@
 //     the data);
 //   * a streaming read: every byte of a buffer read once with 16-byte loads, four in flight per lane;
 //   * the split-KV decode's read pattern: caches [B, L, H, 128] bf16, workgroup = (split, KV head, batch),
-//     64 rows of 256 B per step for K and for V.
+//     64 rows of 256 B per step for K and for V;
+//   * the issue cost of direct HBM -> LDS loads (global_load_lds_dwordx4, written as the prefill writes it):
+//     cycles a wave spends issuing n such loads back to back (no wait), with 1 or 8 waves of a workgroup
+//     issuing at once -- the prefill issues 32 of them per key tile, 4 per wave.
 // Plus the CU count and peak engine clock the runtime reports.
 //
 // C ABI: every function returns a hipError_t value as int (0 = success, hipErrorInvalidValue for
@@ -117,6 +120,47 @@ __global__ __launch_bounds__(kReadThreads) void read_decode_kernel(const uint4* 
     if (acc == 0x9e3779b9u) sink[threadIdx.x] = 1.0f;
 }
 
+constexpr int kDmaThreads = 512;   // 8 waves, as the prefill workgroup
+constexpr int kDmaMaxInst = 8;
+constexpr int64_t kDmaBytesPerWg = 65536;   // each workgroup reads its own 64 KB; wave w from byte 8192*w
+
+__device__ __forceinline__ void dma_load_16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(voff), "s"(sbase), "s"(lds_base)
+        : "memory");
+}
+
+// Waves < active issue n_inst direct loads of 1 KB each (lane l: 16 bytes at 1024*i + 16*l) into LDS slots
+// ((8*wave + i) mod 64) KB, timed with s_memtime around the issue; then every wave waits for its loads.
+// out[(wg*8 + wave)*2] = issue cycles, [+1] = issue + wait cycles (waves >= active: both about 0).
+__global__ __launch_bounds__(kDmaThreads) void lds_dma_issue_kernel(const char* __restrict__ src, uint64_t* out,
+                                                                    int n_inst, int active) {
+    __shared__ __attribute__((aligned(1024))) char smem[65536];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)smem;
+    const char* base = src + (int64_t)blockIdx.x * kDmaBytesPerWg + wave * 8192;
+    __syncthreads();
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    if (wave < active)
+        for (int i = 0; i < n_inst; ++i)
+            dma_load_16(base, (uint32_t)(i * 1024 + lane * 16), lds + ((wave * 8 + i) & 63) * 1024);
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    const uint64_t t2 = __builtin_amdgcn_s_memtime();
+    __syncthreads();
+    if (lane == 0) {
+        out[((int64_t)blockIdx.x * 8 + wave) * 2] = t1 - t0;
+        out[((int64_t)blockIdx.x * 8 + wave) * 2 + 1] = t2 - t0;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -178,6 +222,20 @@ int ceil_read_decode(const void* k, const void* v, int64_t batch, int64_t L, int
     hipLaunchKernelGGL(read_decode_kernel, dim3(splits, hkv, batch), dim3(kReadThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const uint4*>(k),
                        reinterpret_cast<const uint4*>(v), L, hkv, L / splits, sink);
+    return (int)hipGetLastError();
+}
+
+// src: >= workgroups * 65536 bytes (device, 16-byte aligned); out: >= workgroups * 16 uint64 (device);
+// 1 <= n_inst <= 8, 1 <= active_waves <= 8.
+int ceil_lds_dma_issue(const void* src, int64_t src_bytes, uint64_t* out, int64_t out_elems, int32_t workgroups,
+                       int32_t n_inst, int32_t active_waves, void* stream) {
+    if (!src || !out || workgroups < 1 || n_inst < 1 || n_inst > kDmaMaxInst || active_waves < 1 ||
+        active_waves > 8 || src_bytes < (int64_t)workgroups * kDmaBytesPerWg || out_elems < (int64_t)workgroups * 16 ||
+        (reinterpret_cast<uintptr_t>(src) & 15u))
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(lds_dma_issue_kernel, dim3(workgroups), dim3(kDmaThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const char*>(src), out, n_inst,
+                       active_waves);
     return (int)hipGetLastError();
 }
 

@@ -1,0 +1,171 @@
+"""Phase timeline of the prefill's steady tile loop (measurement tool; the attention path never uses it).
+
+    python ceilings/phase_trace.py build     # on the CPU: instrumented copy of the library, compiled for gfx950
+    python ceilings/phase_trace.py run       # on an MI355X: per-wave phase durations, one JSON line
+
+`build` copies long_context_attention_tiled_amd/ into ceilings/phase_trace_pkg/ and adds, in the copy only,
+s_memtime stamps to every steady step of prefill_bf16.hip's tile loop (step start; end of the first-phase
+work; after the mid-step barrier; end of the second-phase work; after the wait for this step's loads) for
+three workgroups (blockIdx 0, 97, 203) over the first 64 steps of their first work unit, plus an entry point
+flux_probe_set_trace() that hands the kernel a device buffer for them.  The arithmetic, the loads and the
+schedule are those of the library; results stay exact (the parity of the copy is checked by `run`).
+
+`run` times the copy with and without the stamps and reports, per wave (waves 0-3 form the group that runs
+matrix work in the first phase, waves 4-7 the other), the median cycles of each segment over steps 2..63,
+for the seq-8192 dense layer and the seq-131072 dense and block-sparse layers (32/8 heads, head_dim 128, bf16).
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+PKG_PARENT = os.path.join(HERE, "phase_trace_pkg")
+PKG = os.path.join(PKG_PARENT, "long_context_attention_tiled_amd")
+N_SLOTS, N_WAVES, N_STEPS, N_STAMPS = 3, 8, 64, 5
+
+
+def _edit(path, old, new):
+    s = open(path).read()
+    if old not in s:
+        raise RuntimeError(f"{os.path.basename(path)}: pattern not found: {old[:60]!r}")
+    open(path, "w").write(s.replace(old, new, 1))
+
+
+def build() -> str:
+    if os.path.exists(PKG_PARENT):
+        shutil.rmtree(PKG_PARENT)
+    shutil.copytree(os.path.join(ROOT, "long_context_attention_tiled_amd"), PKG,
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__", "_build"))
+    c = os.path.join(PKG, "csrc")
+    inc = os.path.join(ROOT, "include", "flux_attn.h")
+    _edit(os.path.join(c, "flux_api.cpp"), '#include "../../include/flux_attn.h"', f'#include "{inc}"')
+    _edit(os.path.join(c, "flux_internal.h"), "    int window_blocks;\n};",
+          "    int window_blocks;\n    unsigned long long* trace;\n};")
+    _edit(os.path.join(c, "flux_internal.h"), "hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);",
+          "hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);\nextern unsigned long long* g_trace;")
+    _edit(os.path.join(c, "flux_api.cpp"), "    a.num_cu = device_cu_count();\n    hipError_t e = in_dtype",
+          "    a.num_cu = device_cu_count();\n    a.trace = flux::g_trace;\n    hipError_t e = in_dtype")
+    _edit(os.path.join(c, "flux_api.cpp"), 'extern "C" {\n',
+          'namespace flux { unsigned long long* g_trace = nullptr; }\nextern "C" {\n'
+          'void flux_probe_set_trace(void* p) { flux::g_trace = (unsigned long long*)p; }\n')
+    p = os.path.join(c, "prefill_bf16.hip")
+    s = open(p).read()
+    stamp = lambda n: f"                    const unsigned long long {n} = probe ? __builtin_amdgcn_s_memtime() : 0ull;\n"
+    w0 = s.index("                while (have_n) {\n")
+    w1 = s.index("                    sl ^= 1;\n", w0)
+    body = s[w0:w1]
+    sync = "                    __syncthreads();\n"
+    i1 = body.index(sync)
+    body = body[:i1] + stamp("t1") + sync + stamp("t2") + body[i1 + len(sync):]
+    i3 = body.index("                    __builtin_amdgcn_s_waitcnt(0x0f70);")
+    i3e = body.index("\n", i3) + 1
+    body = body[:i3] + stamp("t3") + body[i3:i3e] + stamp("t4") + body[i3e:]
+    i5 = body.index(sync, body.index("t4 ="))
+    body = (body[:i5 + len(sync)] +
+            "                    if (probe && pstep < 64 && lane == 0) {\n"
+            "                        unsigned long long* dst = a.trace + ((size_t)(pslot * 8 + wave) * 64 + pstep) * 5;\n"
+            "                        dst[0] = t0; dst[1] = t1; dst[2] = t2; dst[3] = t3; dst[4] = t4;\n"
+            "                    }\n                    ++pstep;\n" + body[i5 + len(sync):])
+    body = body.replace("                while (have_n) {\n",
+                        "                while (have_n) {\n" + stamp("t0"), 1)
+    pre = ("                int pstep = 0;\n"
+           "                const int pslot = (blockIdx.x == 0) ? 0 : (blockIdx.x == 97) ? 1 : (blockIdx.x == 203) ? 2 : -1;\n"
+           "                const bool probe = a.trace && pslot >= 0 && k == 1;\n")
+    open(p, "w").write(s[:w0] + pre + body + s[w1:])
+    bp = os.path.join(PKG, "build.py")
+    _edit(bp, 'OBJDIR = os.path.join(ROOT, "_build")', 'OBJDIR = os.path.join(HERE, "_build")')
+    r = subprocess.run([sys.executable, bp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(r.stdout[-4000:] + r.stderr[-4000:])
+    shutil.rmtree(os.path.join(PKG, "_build"), ignore_errors=True)
+    return os.path.join(PKG, "libflux_attn.so")
+
+
+def _medians(tr):
+    """tr [slots, waves, steps, 5] -> per-wave medians of the segments over the recorded steady steps (the first
+    two of each traced unit left out; a unit with fewer than 64 steps leaves the rest of its rows at zero)."""
+    import numpy as np
+    seg = {"first_phase_work": (0, 1), "mid_barrier_wait": (1, 2), "second_phase_work": (2, 3),
+           "load_wait": (3, 4)}
+    parts, steps = [], []
+    for sl in range(tr.shape[0]):
+        n = int((tr[sl, :, :, 0] > 0).all(axis=0).sum())
+        if n >= 4:
+            parts.append(tr[sl, :, 2:n])
+            steps.append((tr[sl, :, 3:n, 0] - tr[sl, :, 2:n - 1, 0]).ravel())
+    t = np.concatenate(parts, axis=1)
+    out = {"steps_recorded": int(t.shape[1])}
+    for name, (a, b) in seg.items():
+        out[name] = [int(np.median(t[w, :, b] - t[w, :, a])) for w in range(N_WAVES)]
+    out["step"] = int(np.median(np.concatenate(steps)))
+    busiest = max(out["first_phase_work"][w] + out["mid_barrier_wait"][w] + out["second_phase_work"][w] +
+                  out["load_wait"][w] for w in range(N_WAVES))
+    out["end_of_step_barrier_and_loop"] = out["step"] - busiest
+    return out
+
+
+def run() -> dict:
+    sys.path.insert(0, ROOT)
+    sys.path.insert(0, PKG_PARENT)
+    import numpy as np
+    import torch
+    import long_context_attention_tiled_amd as fa
+    assert os.path.dirname(fa.LIB_PATH) == PKG, fa.LIB_PATH
+    import oracle
+    res = {}
+    for name, S, mode in (("dense_s8192", 8192, 0), ("dense_s131072", 131072, 0), ("sparse_s131072", 131072, 1)):
+        print(f"[phase_trace] {name}", file=sys.stderr, flush=True)
+        B, Hq, Hkv, d = 1, 32, 8, 128
+        g = torch.Generator(device="cuda").manual_seed(11)
+        q = torch.randn((B, S, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+        k = torch.randn((B, S, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+        v = torch.randn((B, S, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+        o = torch.empty((B, S, Hq, d), dtype=torch.bfloat16, device="cuda")
+        trace = torch.zeros(N_SLOTS * N_WAVES * N_STEPS * N_STAMPS, dtype=torch.int64, device="cuda")
+        call = lambda: fa.flux_attn_prefill(q, k, v, o, None, causal=1, mode=mode)
+        reps = 20 if S <= 8192 else 2
+
+        def timed():
+            call()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                call()
+            e.record()
+            torch.cuda.synchronize()
+            return s.elapsed_time(e) / reps
+        ms_plain = timed()
+        fa.lib().flux_probe_set_trace(ctypes.c_void_p(trace.data_ptr()))
+        ms_traced = timed()
+        fa.lib().flux_probe_set_trace(None)
+        tr = trace.view(N_SLOTS, N_WAVES, N_STEPS, N_STAMPS).cpu().numpy().astype(np.int64)
+        r = {"ms_untraced": round(ms_plain, 4), "ms_traced": round(ms_traced, 4), **_medians(tr)}
+        if S == 8192:   # the traced copy computes the same attention: a few rows against the oracle
+            rows = np.array([(0, h, i) for h in (0, 31) for i in (0, 4095, 8191)], np.int64)
+            qh, kh, vh = (x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16) for x in (q, k, v))
+            ref, _ = oracle.attention(qh, kh, vh, 1.0 / np.sqrt(d), causal=True, rows=rows)
+            got = o.float().cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]]
+            r["max_abs_err_vs_oracle"] = float(np.abs(got - ref).max())
+            assert r["max_abs_err_vs_oracle"] < 2e-2
+        res[name] = r
+        del q, k, v, o
+        torch.cuda.empty_cache()
+    return res
+
+
+if __name__ == "__main__":
+    if len(sys.argv) > 1 and sys.argv[1] == "build":
+        print(build())
+    elif len(sys.argv) > 1 and sys.argv[1] == "run":
+        print(json.dumps(run()), flush=True)
+    else:
+        print(__doc__)
+        sys.exit(2)

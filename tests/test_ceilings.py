@@ -35,6 +35,10 @@ def test_validation_before_launch(lib):
     assert lib.ceil_mfma_loop(16, 1, 16, 255, 1, 1, 0, None) == HIP_INVALID_VALUE     # sink too small
     assert lib.ceil_read_stream(16, 24, 16, 256, 1, None) == HIP_INVALID_VALUE        # not a multiple of 16
     assert lib.ceil_read_decode(16, 16, 1, 192, 1, 2, 16, 256, None) == HIP_INVALID_VALUE   # L % (64 splits)
+    assert lib.ceil_lds_dma_issue(16, 65536, 16, 16, 1, 9, 1, None) == HIP_INVALID_VALUE      # more than 8 loads
+    assert lib.ceil_lds_dma_issue(16, 65536, 16, 16, 1, 4, 0, None) == HIP_INVALID_VALUE      # no active wave
+    assert lib.ceil_lds_dma_issue(16, 65535, 16, 16, 1, 4, 8, None) == HIP_INVALID_VALUE      # source too small
+    assert lib.ceil_lds_dma_issue(16, 65536, 16, 15, 1, 4, 8, None) == HIP_INVALID_VALUE      # out too small
 
 
 @pytest.mark.gpu
@@ -69,3 +73,11 @@ def test_kernels_run(lib):
     cu, clk = ctypes.c_int(0), ctypes.c_int(0)
     assert lib.ceil_device_info(ctypes.byref(cu), ctypes.byref(clk)) == 0
     assert cu.value > 0 and clk.value > 0
+
+    # direct-load issue timing: the active waves report positive cycle counts, issue <= issue + wait
+    src = torch.zeros(4 * 65536, dtype=torch.uint8, device=dev)
+    out = torch.zeros(4 * 16, dtype=torch.int64, device=dev)
+    assert lib.ceil_lds_dma_issue(src.data_ptr(), src.numel(), out.data_ptr(), out.numel(), 4, 4, 3, stream) == 0
+    torch.cuda.synchronize()
+    t = out.view(4, 8, 2).cpu()
+    assert bool((t[:, :3, 0] > 0).all()) and bool((t[:, :, 0] <= t[:, :, 1]).all())
