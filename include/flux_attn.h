@@ -216,11 +216,13 @@ int flux_attn_prefill_soft(const void* q, const void* k, const void* v, void* o,
                            void* hip_stream);
 
 /* flux_attn_backward_workspace_size -- bytes flux_attn_backward needs for these sizes and this mask
- * (0 if invalid): per-row statistics (fp32 [batch, hq, ceil(seq/64)*64, 2]), two counters and, with
- * grouped-query attention in block-sparse mode, two fp32 [batch, K, hq, head_dim] per-query-head dK/dV
+ * (0 if invalid): per-row statistics (fp32 [batch, hq, ceil(seq/64)*64, 2]), two counters, with
+ * grouped-query attention in block-sparse mode two fp32 [batch, K, hq, head_dim] per-query-head dK/dV
  * buffers for the K = min(seq, 128 * ceil(sink_blocks / 2)) keys of the key pairs holding sink blocks
- * (every query sees them, so they are not grouped by KV head).  mode, block and sink_tokens as passed
- * to flux_attn_backward. */
+ * (every query sees them, so they are not grouped by KV head), and for bf16 inputs fp16 copies of
+ * q, k, v and d_o (2 * batch * seq * (hq + hkv) * head_dim * 2 bytes) with their per-KV-head scales
+ * (the size covers them for either input type).  mode, block and sink_tokens as passed to
+ * flux_attn_backward. */
 size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq, int32_t hkv,
                                          int32_t head_dim, int32_t mode, int32_t block, int32_t sink_tokens);
 
@@ -247,10 +249,14 @@ size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq,
  * is derived from (block, sink_tokens, window_tokens), the pattern flux_build_block_mask builds.
  * workspace: device, >= flux_attn_backward_workspace_size(...) bytes, 16-byte aligned; its
  * contents on entry do not matter.  Deterministic: no atomics on gradients, fixed summation order.
- * in_dtype BF16: q, k, v, d_o bf16, matrix-core kernels; P and dS enter the matrix products as a
- * bf16 hi + lo pair (fp32 accumulation).  in_dtype F32: q, k, v, d_o float32, vector-ALU kernels
- * for small layers (as the float32 forward).
- * Supported: head_dim 64 or 128, block 64.
+ * in_dtype BF16: q, k, v, d_o bf16, matrix-core kernels on fp16 operands with fp32 accumulation:
+ * the inputs are copied to fp16 scaled by a power of two per (batch, KV head) and tensor (exact for
+ * every value above 2^-29 of its group's largest), S and dP are the products of those copies, and P
+ * and dS enter the gradient products rounded once to fp16.  The scales stay in fp32's range as long
+ * as max|Q| * max|K| and max|dO| * max|V| over each KV head's group lie in [2^-90, 2^150] (inputs
+ * must be finite).  in_dtype F32: q, k, v, d_o float32, vector-ALU kernels for small layers (as the
+ * float32 forward).
+ * Supported: head_dim 64 or 128, block 64; bf16 inputs: batch * hkv < 65536.
  */
 int flux_attn_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
                        const float* lse, float* dq, float* dk, float* dv, int32_t in_dtype,

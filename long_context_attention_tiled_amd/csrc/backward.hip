@@ -11,6 +11,10 @@
 // all keys, or the sink + local window of 64-token blocks, whose other blocks are never read).
 //
 // Kernels, in stream order:
+//   bwd_absmax_kernel     partial maxima of |x| of Q, K, V, dO per (batch, KV head) over token chunks
+//                         (one launch per tensor).
+//   bwd_convert_kernel    fp16 copies of Q, K, V, dO scaled by 2^-e per (batch, KV head) and tensor, e
+//                         chosen from those maxima so the largest magnitude lands in [2^14, 2^15).
 //   bwd_rowstat_kernel    D and -LSE*log2(e) per query row, in 64-row tiles (rows past the end get
 //                         (-inf, 0), so they weigh nothing); clears the two work-queue heads.  It also
 //                         serves the float32 kernels of backward_f32.hip.
@@ -29,10 +33,20 @@
 // Computing dQ apart from dK/dV rebuilds S and dP once more (7 matrix products instead of 5) but
 // needs no atomics: every gradient element is written once, summed in a fixed order.
 //
-// P and dS enter the gradient products as a bf16 pair hi + lo (hi = x truncated to bf16, lo =
-// bf16(x - hi)): the sums over up to seq rows of bf16-rounded P or dS alone would carry a relative error of
-// 2^-9 per term, about 1e-2 absolute on gradients of size 5; the pair brings it near 2^-16 at the
-// cost of a second MFMA on the same A operand.
+// Precision.  Every product runs on v_mfma_f32_32x32x16_f16 with fp32 accumulation.  The bf16 inputs
+// convert to fp16 exactly once scaled into fp16's range (a bf16 value has 8 significant bits, fp16
+// 11), so S and dP are the bf16 products.  P and dS, which the kernels form in fp32, enter the
+// gradient products rounded once to fp16 (relative 2^-12): rounded to bf16 (2^-9) they would put
+// errors of ~1e-2 on the dV of sink keys that 2^16 query rows sum into.  Scales, all powers of two:
+//   Q16 = Q 2^-eQ, K16 = K 2^-eK, V16 = V 2^-eV, dO16 = dO 2^-eDO   (per batch and KV head)
+//   S   = 2^(eQ + eK) (Q16 K16^T),  dP = 2^(eDO + eV) (dO16 V16^T)
+//   P16 = P 2^14 (P <= 1, so small probabilities stay normal fp16 numbers)
+//   dS16 = dS 2^-eS with eS = 23 + eDO + eV: |dP| <= d * 2^30 * 2^(eDO + eV) <= 2^(37 + eDO + eV) and
+//        |dS| <= 2 max|dP|, so |dS16| < 2^15 always; formed as P16 (dP16 2^-37 - D 2^-(37 + eDO + eV))
+//   dV = 2^(eDO - 14) sum P16 dO16,  dK = scale 2^(eS + eQ) sum dS16 Q16,  dQ = scale 2^(eS + eK) sum dS16 K16
+// Values below 2^-29 of their group's maximum lose fp16 bits (absolute error <= 2^-40 of that
+// maximum).  The scale factors stay within fp32's range as long as the largest |Q| times the largest
+// |K| of a KV head, and the largest |dO| times the largest |V|, lie between 2^-90 and 2^150.
 //
 // Both main kernels are persistent, run two waves per SIMD, and take units from a device counter,
 // longest first.  Two LDS slots: the tile in use and the next one in flight.
@@ -109,7 +123,11 @@ __device__ __forceinline__ void load_tile(const u16* base, uint32_t row_stride, 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Lane geometry of the MFMA operands (v_mfma_f32_32x32x16_bf16: lane l feeds row/column l % 32 with
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Lane geometry of the MFMA operands (v_mfma_f32_32x32x16_f16: lane l feeds row/column l % 32 with
 // k-slots 8(l/32) .. +7; the accumulator's register r of lane l is row 8(r/4) + 4(l/32) + r%4).
 template <int D>
 struct Lanes {
@@ -135,14 +153,14 @@ struct Lanes {
     }
     // A operand X^T[32mt + l%32][16kk + k-slots] of a 64-row tile X (k-slot e of lane half hh is
     // row 16kk + 8(e/4) + 4hh + e%4, matching the accumulator layout of the B operand).
-    __device__ __forceinline__ bf16x8 tr(const char* tile, int kk, int mt) const {
+    __device__ __forceinline__ f16x8 tr(const char* tile, int kk, int mt) const {
         const i16x4 lo = read_tr16(tile + kk * 16 * Gm::ROW_B + trl[mt]);
         const i16x4 hi = read_tr16(tile + kk * 16 * Gm::ROW_B + trh[mt]);
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
     // A operand X[32half + l%32][16c + 8(l/32) .. +7] of a 64-row tile X
-    __device__ __forceinline__ bf16x8 row(const char* tile, int half, int c) const {
-        return *reinterpret_cast<const bf16x8*>(tile + half * 32 * Gm::ROW_B + rd[c]);
+    __device__ __forceinline__ f16x8 row(const char* tile, int half, int c) const {
+        return *reinterpret_cast<const f16x8*>(tile + half * 32 * Gm::ROW_B + rd[c]);
     }
 };
 
@@ -169,7 +187,123 @@ struct Queue {
     }
 };
 
+// ------------------------------------------------------------------ fp16 copies of the inputs
+//
+// Tensor t of (Q, K, V, dO) = (0, 1, 2, 3) restricted to one (batch b, KV head g): tokens s in [0, seq),
+// heads [h0, h0 + nh) contiguous per token (Q, dO: the G query heads of g; K, V: head g).
+struct Slice {
+    const u16* src;
+    u16* dst;
+    int64_t heads;   // heads per token of the tensor
+    int64_t off;     // element offset of (b, token 0, h0)
+    int run;         // 16-byte vectors per token of the slice
+};
+
+// The tensor is a template parameter: each is its own launch, and no pointer is picked at run time.
+template <int D, int T>
+__device__ __forceinline__ Slice slice_of(const BackwardArgs& a, int bg) {
+    const int G = a.hq / a.hkv, b = bg / a.hkv, g = bg % a.hkv;
+    constexpr bool qside = T == 0 || T == 3;
+    Slice sl;
+    if constexpr (T == 0) { sl.src = reinterpret_cast<const u16*>(a.q);   sl.dst = reinterpret_cast<u16*>(a.q16); }
+    if constexpr (T == 1) { sl.src = reinterpret_cast<const u16*>(a.k);   sl.dst = reinterpret_cast<u16*>(a.k16); }
+    if constexpr (T == 2) { sl.src = reinterpret_cast<const u16*>(a.v);   sl.dst = reinterpret_cast<u16*>(a.v16); }
+    if constexpr (T == 3) { sl.src = reinterpret_cast<const u16*>(a.d_o); sl.dst = reinterpret_cast<u16*>(a.do16); }
+    sl.heads = qside ? a.hq : a.hkv;
+    sl.off = ((int64_t)b * a.seq * sl.heads + (qside ? (int64_t)g * G : g)) * D;
+    sl.run = (qside ? G : 1) * (D / 8);
+    return sl;
+}
+
+__device__ __forceinline__ uint32_t absmax_bits(uint4 x) {   // largest |x| of 8 bf16 as its bit pattern
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+    return m;
+}
+
+// e with max * 2^-e in [2^14, 2^15) for the bf16 bit pattern of the maximum (0 for an all-zero slice)
+__device__ __forceinline__ int scale_exp(uint32_t m) {
+    if (m == 0) return 0;
+    const int E = (int)((m >> 7) & 0xffu);
+    return (E > 1 ? E : 1) - 141;
+}
+
+// Vector i of a slice (16 bytes, 8 elements): token i / run, vector i % run of that token.  A slice holds
+// at most seq * hq * d / 8 < 2^28 vectors, so 32-bit indices suffice.
+__device__ __forceinline__ int64_t vec_off(const Slice& sl, uint32_t i, int d) {
+    const uint32_t s = i / (uint32_t)sl.run, r = i - s * (uint32_t)sl.run;
+    return sl.off + (int64_t)s * sl.heads * d + 8 * r;
+}
+
+// Maximum over the 256 threads of a block (4 waves).
+__device__ __forceinline__ uint32_t block_max(uint32_t m) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+    __shared__ uint32_t wm[4];
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+    __syncthreads();
+    return max(max(wm[0], wm[1]), max(wm[2], wm[3]));
+}
+
+// grid (kAbsmaxChunks, B * Hkv) per tensor T: block (c, bg) reduces the vectors of tokens
+// [c seq / chunks, (c + 1) seq / chunks), four independent 16-byte loads in flight per thread.
+template <int D, int T>
+__global__ void __launch_bounds__(256) bwd_absmax_kernel(BackwardArgs a) {
+    const int c = blockIdx.x, bg = blockIdx.y;
+    const Slice sl = slice_of<D, T>(a, bg);
+    const uint32_t n0 = (uint32_t)(a.seq * c / kAbsmaxChunks) * sl.run;
+    const uint32_t n1 = (uint32_t)(a.seq * (c + 1) / kAbsmaxChunks) * sl.run;
+    uint32_t m = 0;
+    for (uint32_t i = n0 + threadIdx.x; i < n1; i += 4 * 256) {
+        uint4 x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            x[j] = i + 256 * j < n1 ? *reinterpret_cast<const uint4*>(sl.src + vec_off(sl, i + 256 * j, D))
+                                    : uint4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = max(m, absmax_bits(x[j]));
+    }
+    m = block_max(m);
+    if (threadIdx.x == 0) a.amax[((int64_t)T * gridDim.y + bg) * kAbsmaxChunks + c] = m;
+}
+
+// Same grid: each block takes its slice's scale from the chunk maxima and converts its tokens.
+template <int D, int T>
+__global__ void __launch_bounds__(256) bwd_convert_kernel(BackwardArgs a) {
+    static_assert(kAbsmaxChunks <= 256, "one chunk maximum per thread");
+    const int c = blockIdx.x, bg = blockIdx.y;
+    const Slice sl = slice_of<D, T>(a, bg);
+    const int e = scale_exp(block_max(threadIdx.x < kAbsmaxChunks
+                                          ? a.amax[((int64_t)T * gridDim.y + bg) * kAbsmaxChunks + threadIdx.x]
+                                          : 0u));
+    if (c == 0 && threadIdx.x == 0) a.exps[T * gridDim.y + bg] = e;
+    const uint32_t n0 = (uint32_t)(a.seq * c / kAbsmaxChunks) * sl.run;
+    const uint32_t n1 = (uint32_t)(a.seq * (c + 1) / kAbsmaxChunks) * sl.run;
+    for (uint32_t i = n0 + threadIdx.x; i < n1; i += 4 * 256) {
+        uint4 x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (i + 256 * j < n1) x[j] = *reinterpret_cast<const uint4*>(sl.src + vec_off(sl, i + 256 * j, D));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (i + 256 * j >= n1) break;
+            const uint32_t w[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+            uint32_t y[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                y[q] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)ldexpf(bf16_lo(w[q]), -e),
+                                                          (_Float16)ldexpf(bf16_hi(w[q]), -e)});
+            *reinterpret_cast<uint4*>(sl.dst + vec_off(sl, i + 256 * j, D)) = uint4{y[0], y[1], y[2], y[3]};
+        }
+    }
+}
+
 // ------------------------------------------------------------------ row statistics
+//
+// bf16 inputs (the fp16 matrix-core kernels): the row statistics are stored pre-scaled for them,
+// -LSE*log2(e) + 14 (P16 = P 2^14) and D 2^-(37 + eDO + eV) (so dS16 = P16 (dP16 2^-37 - D')).
 template <int D>
 __global__ void __launch_bounds__(256) bwd_rowstat_kernel(BackwardArgs a) {
     constexpr int LPR = D / 8;            // lanes per row, 8 elements (16 bytes) each
@@ -216,37 +350,27 @@ __global__ void __launch_bounds__(256) bwd_rowstat_kernel(BackwardArgs a) {
     if (c == 0) {
         float* st = a.stat + ((b * a.hq + h) * a.n_qblk + i / 64) * 128 + i % 64;
         const bool live = i < a.seq;
-        st[0] = live ? -a.lse[(b * a.hq + h) * a.seq + i] * kLog2e : -INFINITY;
+        float nl = live ? -a.lse[(b * a.hq + h) * a.seq + i] * kLog2e : -INFINITY;
+        if (!a.in_f32) {
+            const int bg = (int)b * a.hkv + h / (a.hq / a.hkv), nbg = (int)a.batch * a.hkv;
+            nl += 14.0f;
+            acc = ldexpf(acc, -(37 + a.exps[3 * nbg + bg] + a.exps[2 * nbg + bg]));
+        }
+        st[0] = nl;
         st[64] = live ? acc : 0.0f;
     }
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
-}
-
-// (x0, x1) = hi + lo per element, hi = x with its low 16 bits cleared (exact in bf16), lo = bf16(x - hi):
-// two bf16 MFMA operands whose products sum to x * y with a relative error near 2^-16 instead of
-// bf16's 2^-9.  Packed as bf16 pairs (element 2i in the low half of word i).
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-    const float h0 = __uint_as_float(__float_as_uint(x0) & 0xffff0000u);
-    const float h1 = __uint_as_float(__float_as_uint(x1) & 0xffff0000u);
-    hi = pack2(h0, h1);
-    lo = pack2(x0 - h0, x1 - h1);
-}
-
-// 16 accumulator values of one 32x32 block -> hi and lo operands of its two 16-wide k-steps
-__device__ __forceinline__ void split16(const float* x, bf16x8* hi, bf16x8* lo) {
+// 16 accumulator values of one 32x32 block -> fp16 operands (round to nearest even) of its two 16-wide
+// k-steps (element 2i in the low half of word i)
+__device__ __forceinline__ void to_f16(const float* x, f16x8* y) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        uint32_t h[4], l[4];
+        uint32_t h[4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) split2(x[8 * q + 2 * w], x[8 * q + 2 * w + 1], h[w], l[w]);
-        hi[q] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
-        lo[q] = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+        for (int w = 0; w < 4; ++w)
+            h[w] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)x[8 * q + 2 * w], (_Float16)x[8 * q + 2 * w + 1]});
+        y[q] = __builtin_bit_cast(f16x8, u32x4{h[0], h[1], h[2], h[3]});
     }
 }
 
@@ -254,7 +378,7 @@ __device__ __forceinline__ float comp(const float4& v, int e) {
     return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 
-#define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
+#define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_f16((a), (b), (c), 0, 0, 0)
 
 // NS MFMA steps whose A operands come from LDS: operand(i) is read kAhead steps before step(i, op)
 // uses it, and sched_barrier keeps that order (left alone, the scheduler reuses one register and
@@ -263,13 +387,13 @@ constexpr int kAhead = 3;
 template <int NS, typename Operand, typename Step>
 __device__ __forceinline__ void mfma_seq(Operand operand, Step step) {
     __builtin_amdgcn_s_setprio(1);   // the other wave of the SIMD fills the MFMA shadow with its vector work
-    bf16x8 ring[kAhead];
+    f16x8 ring[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i)
         if (i < NS) ring[i] = operand(i);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-        const bf16x8 op = ring[i % kAhead];
+        const f16x8 op = ring[i % kAhead];
         if (i + kAhead < NS) ring[i % kAhead] = operand(i + kAhead);
         step(i, op);
         __builtin_amdgcn_sched_barrier(0);
@@ -277,27 +401,21 @@ __device__ __forceinline__ void mfma_seq(Operand operand, Step step) {
     __builtin_amdgcn_s_setprio(0);
 }
 
-// acc[mt] += X^T[mt, k-steps kk0, kk0 + 1] * (hi + lo): the transposed operand of (kk, mt) is read
-// once and used by its hi and lo MFMAs; the next k-step's operand is read into the register its
-// last use frees.
+// acc[mt] += X^T[mt, k-steps kk0, kk0 + 1] * x16: the transposed operand of (kk0 + 1, mt) is read into
+// the register the MFMA of (kk0, mt) frees.
 template <int D>
-__device__ __forceinline__ void grad_product(const Lanes<D>& L, const char* xt, int kk0, const bf16x8* xh,
-                                             const bf16x8* xl, f32x16* acc) {
+__device__ __forceinline__ void grad_product(const Lanes<D>& L, const char* xt, int kk0, const f16x8* x16,
+                                             f32x16* acc) {
     constexpr int kNM = Geo<D>::NM;
     __builtin_amdgcn_s_setprio(1);
-    bf16x8 ax[kNM];
+    f16x8 ax[kNM];
 #pragma unroll
     for (int mt = 0; mt < kNM; ++mt) ax[mt] = L.tr(xt, kk0, mt);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
 #pragma unroll
         for (int mt = 0; mt < kNM; ++mt) {
-            acc[mt] = MFMA(ax[mt], xh[q], acc[mt]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int mt = 0; mt < kNM; ++mt) {
-            acc[mt] = MFMA(ax[mt], xl[q], acc[mt]);
+            acc[mt] = MFMA(ax[mt], x16[q], acc[mt]);
             if (q == 0) ax[mt] = L.tr(xt, kk0 + 1, mt);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -321,7 +439,7 @@ __host__ __device__ __forceinline__ int dkdv_sink_pairs(const BackwardArgs& a) {
 // 8 waves, two per SIMD, on 128 keys: waves w and w + 4 own the same 32 keys; wave w accumulates
 // dV^T, wave w + 4 dK^T.  Each takes a 64-query tile in two 32-query halves: wave w computes S (D/16
 // MFMAs) and P and hands P to wave w + 4 through LDS, which meanwhile computes dP (as many MFMAs) and
-// then dS; each then runs the 4 * D/32 MFMAs of its gradient product.  At D = 128 that is 48 + 48
+// then dS; each then runs the 2 * D/32 MFMAs of its gradient product.  At D = 128 that is 32 + 32
 // MFMAs per SIMD and tile, S is computed once per key group, and each wave stays within 256
 // registers, so the two waves of a SIMD hide each other's vector work and LDS latency.
 constexpr int kKvWaves = 8;
@@ -348,7 +466,6 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
     const int ph_units = n_sp * bh_total;
     const int total = ph_units + ((nqb + 1) / 2 - n_sp) * bg_total;
     const uint32_t q_stride = (uint32_t)a.hq * D;
-    const float c2 = a.scale_log2;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
     Queue queue{a.counters + 0, qcell, 0};
@@ -374,6 +491,10 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
         }
         const bool partial = nh < G;
         const int g = h0 / G;
+        const int bg = b * a.hkv + g;
+        const int eQ = a.exps[bg], eK = a.exps[bg_total + bg], eV = a.exps[2 * bg_total + bg];
+        const int eDO = a.exps[3 * bg_total + bg];
+        const float c2 = ldexpf(a.scale_log2, eQ + eK);   // exp2 argument per unit of Q16 K16^T
         const int kb = 2 * m + (ks >> 1);                 // this wave's key block
         const int key = 128 * m + 32 * ks + n;            // this lane's key
         int lo = 0, hi = nqb - 1;
@@ -386,8 +507,8 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
 
         // a tile is 32 loads of 1 KB (Q by waves 0-3, dO by waves 4-7) plus 2 of row statistics
         auto issue = [&](int h, int t, int slot) {
-            const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * D;
-            const u16* dog = reinterpret_cast<const u16*>(a.d_o) + ((int64_t)b * a.seq * a.hq + h) * D;
+            const u16* qg = reinterpret_cast<const u16*>(a.q16) + ((int64_t)b * a.seq * a.hq + h) * D;
+            const u16* dog = reinterpret_cast<const u16*>(a.do16) + ((int64_t)b * a.seq * a.hq + h) * D;
             const float* stg = a.stat + ((int64_t)b * a.hq + h) * nqb * 128;
             const uint32_t base = lds0 + slot * kSlotB;
             if (wave < 4) load_tile<D>(qg, q_stride, 64 * t, seq - 1, base, wave, lane);
@@ -402,25 +523,26 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
 
         // this lane's key row as the B operand (k-slots = d): K for the dV wave (S = Q K^T), V for the
         // dK wave (dP = dO V^T)
-        bf16x8 breg[kNC];
+        f16x8 breg[kNC];
         {
             const int kc = min(key, seq - 1);
             const int64_t off = (((int64_t)b * a.seq + kc) * a.hkv + g) * D + 8 * hh;
-            const u16* bp = reinterpret_cast<const u16*>(is_dk ? a.v : a.k) + off;
+            const u16* bp = reinterpret_cast<const u16*>(is_dk ? a.v16 : a.k16) + off;
 #pragma unroll
-            for (int c = 0; c < kNC; ++c) breg[c] = *reinterpret_cast<const bf16x8*>(bp + 16 * c);
+            for (int c = 0; c < kNC; ++c) breg[c] = *reinterpret_cast<const f16x8*>(bp + 16 * c);
         }
 
         f32x16 acc[kNM];   // dV^T or dK^T: lane = key, rows d = 32mt + 8(r/4) + 4hh + r%4
 #pragma unroll
         for (int mt = 0; mt < kNM; ++mt) acc[mt] = f32x16{};
 
-        // One tile, in two 32-query halves.  The dV wave computes S, P (exp2 of the scaled score minus
-        // the row's LSE, zero where masked) and publishes P in LDS; the dK wave computes dP meanwhile,
-        // and after the barrier forms dS = P (dP - D) from the published P.  Then each runs its gradient
-        // product.  Elements with C < lim are masked (C = query - 64t - 4hh).  S is computed once per
-        // key group (48 + 48 MFMAs per SIMD and tile at D = 128), and the barrier staggers the two waves
-        // of a SIMD: one runs its gradient product's MFMAs while the other does its vector work.
+        // One tile, in two 32-query halves.  The dV wave computes S, P16 = P 2^14 (exp2 of the scaled
+        // score minus the row's LSE, plus 14; zero where masked) and publishes it in LDS; the dK wave
+        // computes dP meanwhile, and after the barrier forms dS16 = P16 (dP16 2^-37 - D') from the
+        // published P16.  Then each runs its gradient product.  Elements with C < lim are masked
+        // (C = query - 64t - 4hh).  S is computed once per key group (32 + 32 MFMAs per SIMD and tile
+        // at D = 128), and the barrier staggers the two waves of a SIMD: one runs its gradient product's
+        // MFMAs while the other does its vector work.
         auto tile = [&](const char* qt, int lim, bool need_mask) {
             const char* dot = qt + kTileB;
             const char* st = qt + 2 * kTileB;
@@ -429,8 +551,8 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
             for (int hf = 0; hf < 2; ++hf) {
                 f32x16 sd = f32x16{};   // S (dV wave) or dP (dK wave)
                 mfma_seq<kNC>([&](int i) { return L.row(is_dk ? dot : qt, hf, i); },
-                              [&](int i, bf16x8 op) { sd = MFMA(op, breg[i], sd); });
-                float x[16];   // P, then dS = P (dP - D) for the dK wave
+                              [&](int i, f16x8 op) { sd = MFMA(op, breg[i], sd); });
+                float x[16];   // P16, then dS16 for the dK wave
                 if (!is_dk) {
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
@@ -454,13 +576,14 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
                         const float4 p = pbuf[par][ks][g4][lane];
                         const float4 dd = *reinterpret_cast<const float4*>(st + 256 + 4 * (32 * hf + 8 * g4 + 4 * hh));
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) x[4 * g4 + e] = comp(p, e) * (sd[4 * g4 + e] - comp(dd, e));
+                        for (int e = 0; e < 4; ++e)
+                            x[4 * g4 + e] = comp(p, e) * fmaf(sd[4 * g4 + e], 0x1p-37f, -comp(dd, e));
                     }
                 }
                 par ^= 1;
-                bf16x8 xh[2], xl[2];
-                split16(x, xh, xl);
-                grad_product(L, xt, 2 * hf, xh, xl, acc);
+                f16x8 x16[2];
+                to_f16(x, x16);
+                grad_product(L, xt, 2 * hf, x16, acc);
             }
         };
 
@@ -490,14 +613,16 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
             float* dst;
             if (!partial) dst = (is_dk ? a.dk : a.dv) + (((int64_t)b * a.seq + key) * a.hkv + g) * D;
             else dst = (is_dk ? a.dk_part : a.dv_part) + (((int64_t)b * a.part_keys + key) * a.hq + h0) * D;
+            // dK = scale 2^(eS + eQ) acc with eS = 23 + eDO + eV; dV = 2^(eDO - 14) acc
             const float f = is_dk ? a.scale : 1.0f;
+            const int ex = is_dk ? 23 + eDO + eV + eQ : eDO - 14;
 #pragma unroll
             for (int mt = 0; mt < kNM; ++mt)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4)
                     *reinterpret_cast<float4*>(dst + 32 * mt + 8 * g4 + 4 * hh) =
-                        float4{f * acc[mt][4 * g4], f * acc[mt][4 * g4 + 1], f * acc[mt][4 * g4 + 2],
-                               f * acc[mt][4 * g4 + 3]};
+                        float4{ldexpf(f * acc[mt][4 * g4], ex), ldexpf(f * acc[mt][4 * g4 + 1], ex),
+                               ldexpf(f * acc[mt][4 * g4 + 2], ex), ldexpf(f * acc[mt][4 * g4 + 3], ex)};
         }
         __syncthreads();   // every wave is done with the slots before the next unit loads into them
         u = queue.next();
@@ -508,7 +633,7 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
 //
 // 4 waves of 32 queries, two workgroups per CU (two waves per SIMD).  A 64-key tile is taken in two
 // 32-key halves: S^T and dP^T (D/8 MFMAs, K and V rows from LDS, Q and dO rows in registers), the
-// vector work, then 4 * D/32 MFMAs of dQ^T += K^T dS^T.
+// vector work, then 2 * D/32 MFMAs of dQ^T += K^T dS^T.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
     using Gm = Geo<D>;
@@ -525,7 +650,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
     const int bh_total = (int)a.batch * a.hq;
     const int total = npair * bh_total;
     const uint32_t kv_stride = (uint32_t)a.hkv * D;
-    const float c2 = a.scale_log2;
+    const int bg_total = (int)a.batch * a.hkv;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
     Queue queue{a.counters + 1, qcell, 0};
@@ -534,6 +659,10 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
         const int rank = u / bh_total, bh = u % bh_total;
         const int tp = a.causal ? npair - 1 - rank : rank;   // query-tile pair: causal longest first
         const int b = bh / a.hq, h = bh % a.hq, g = h / G;
+        const int bg = b * a.hkv + g;
+        const int eQ = a.exps[bg], eK = a.exps[bg_total + bg], eV = a.exps[2 * bg_total + bg];
+        const int eDO = a.exps[3 * bg_total + bg];
+        const float c2 = ldexpf(a.scale_log2, eQ + eK);   // exp2 argument per unit of K16 Q16^T
         const int qb = 2 * tp + (wave >> 1);                  // this wave's query block
         const int qpos = 128 * tp + 32 * wave + n;            // this lane's query
 
@@ -548,8 +677,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
         }
         const int nt = e0 + (hi - w0 + 1);
 
-        const u16* kg = reinterpret_cast<const u16*>(a.k) + ((int64_t)b * a.seq * a.hkv + g) * D;
-        const u16* vg = reinterpret_cast<const u16*>(a.v) + ((int64_t)b * a.seq * a.hkv + g) * D;
+        const u16* kg = reinterpret_cast<const u16*>(a.k16) + ((int64_t)b * a.seq * a.hkv + g) * D;
+        const u16* vg = reinterpret_cast<const u16*>(a.v16) + ((int64_t)b * a.seq * a.hkv + g) * D;
         auto kb_of = [&](int i) { return i < e0 ? i : w0 + (i - e0); };
         auto issue = [&](int kb, int slot) {
             const uint32_t base = lds0 + slot * 2 * kTileB;
@@ -559,17 +688,17 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
         issue(kb_of(0), 0);
 
         // Q and dO rows of this lane's query as B operands; the row statistics as scalars
-        bf16x8 qreg[kNC], doreg[kNC];
+        f16x8 qreg[kNC], doreg[kNC];
         float nl = -INFINITY, dd = 0.0f;
         {
             const int qc = min(qpos, seq - 1);
             const int64_t off = (((int64_t)b * a.seq + qc) * a.hq + h) * D + 8 * hh;
-            const u16* qp = reinterpret_cast<const u16*>(a.q) + off;
-            const u16* dop = reinterpret_cast<const u16*>(a.d_o) + off;
+            const u16* qp = reinterpret_cast<const u16*>(a.q16) + off;
+            const u16* dop = reinterpret_cast<const u16*>(a.do16) + off;
 #pragma unroll
             for (int c = 0; c < kNC; ++c) {
-                qreg[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
-                doreg[c] = *reinterpret_cast<const bf16x8*>(dop + 16 * c);
+                qreg[c] = *reinterpret_cast<const f16x8*>(qp + 16 * c);
+                doreg[c] = *reinterpret_cast<const f16x8*>(dop + 16 * c);
             }
             if (qpos < seq) {
                 const float* sp = a.stat + (((int64_t)b * a.hq + h) * nqb + qpos / 64) * 128 + qpos % 64;
@@ -590,11 +719,11 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
             for (int kh = 0; kh < 2; ++kh) {
                 // S^T = K Q^T, dP^T = V dO^T: lane = query n, registers = keys 32kh + 8(r/4) + 4hh + r%4
                 f32x16 s = f32x16{}, dp = f32x16{};
-                mfma_seq<2 * kNC>([&](int i) { return L.row(i < kNC ? kt : vt, kh, i % kNC); }, [&](int i, bf16x8 op) {
+                mfma_seq<2 * kNC>([&](int i) { return L.row(i < kNC ? kt : vt, kh, i % kNC); }, [&](int i, f16x8 op) {
                     if (i < kNC) s = MFMA(op, qreg[i], s);
                     else dp = MFMA(op, doreg[i - kNC], dp);
                 });
-                float x[16];   // P, then dS = P (dP - D)
+                float x[16];   // P16 = P 2^14, then dS16 = P16 (dP16 2^-37 - D')
 #pragma unroll
                 for (int r = 0; r < 16; ++r) x[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, nl));
                 if (need_mask) {
@@ -602,10 +731,10 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
                     for (int r = 0; r < 16; ++r) x[r] = (32 * kh + 8 * (r >> 2) + (r & 3) > lim) ? 0.0f : x[r];
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] *= dp[r] - dd;
-                bf16x8 xh[2], xl[2];
-                split16(x, xh, xl);
-                grad_product(L, kt, 2 * kh, xh, xl, dq);   // dQ^T += K^T dS^T
+                for (int r = 0; r < 16; ++r) x[r] *= fmaf(dp[r], 0x1p-37f, -dd);
+                f16x8 x16[2];
+                to_f16(x, x16);
+                grad_product(L, kt, 2 * kh, x16, dq);   // dQ^T += K^T dS16^T
             }
         };
 
@@ -631,13 +760,14 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
         // lane holds column query, rows d = 32mt + 8(r/4) + 4hh + r%4
         if (qpos < seq) {
             float* dqp = a.dq + (((int64_t)b * a.seq + qpos) * a.hq + h) * D;
+            const int ex = 23 + eDO + eV + eK;   // dQ = scale 2^(eS + eK) acc
 #pragma unroll
             for (int mt = 0; mt < kNM; ++mt)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4)
                     *reinterpret_cast<float4*>(dqp + 32 * mt + 8 * g4 + 4 * hh) =
-                        float4{a.scale * dq[mt][4 * g4], a.scale * dq[mt][4 * g4 + 1], a.scale * dq[mt][4 * g4 + 2],
-                               a.scale * dq[mt][4 * g4 + 3]};
+                        float4{ldexpf(a.scale * dq[mt][4 * g4], ex), ldexpf(a.scale * dq[mt][4 * g4 + 1], ex),
+                               ldexpf(a.scale * dq[mt][4 * g4 + 2], ex), ldexpf(a.scale * dq[mt][4 * g4 + 3], ex)};
         }
         __syncthreads();
         u = queue.next();
@@ -690,6 +820,17 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
         return hipErrorInvalidValue;
     const int64_t rows = a.batch * (int64_t)a.n_qblk * 64 * a.hq;
     constexpr int rpb = 256 / (D / 8);
+    if (!a.in_f32) {   // fp16 copies for the matrix-core kernels; the row statistics read their scales
+        const dim3 grid(kAbsmaxChunks, (unsigned)(a.batch * a.hkv));
+        hipLaunchKernelGGL((bwd_absmax_kernel<D, 0>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_absmax_kernel<D, 1>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_absmax_kernel<D, 2>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_absmax_kernel<D, 3>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_convert_kernel<D, 0>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_convert_kernel<D, 1>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_convert_kernel<D, 2>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_convert_kernel<D, 3>), grid, dim3(256), 0, s, a);
+    }
     hipLaunchKernelGGL(bwd_rowstat_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, a);
     if (a.in_f32) return launch_backward_f32(a, s);   // float32 inputs: vector-ALU kernels
     const int64_t units_kv = n_sp * a.batch * a.hq + (npk - n_sp) * a.batch * a.hkv;

@@ -497,7 +497,7 @@ int flux_attn_prefill_soft(const void* q, const void* k, const void* v, void* o,
 namespace {
 
 struct BackwardLayout {
-    size_t stat, counters, part, total;   // byte offsets inside the workspace, and its size
+    size_t stat, counters, part, amax, exps, q16, k16, v16, do16, total;   // byte offsets, and the size
 };
 
 // Keys whose dK/dV the dK/dV kernel writes per query head (summed over the group afterwards): with
@@ -508,14 +508,22 @@ int64_t backward_part_keys(int64_t seq, int32_t hq, int32_t hkv, bool sparse, in
     return std::min(128 * pairs, seq);
 }
 
-BackwardLayout backward_layout(int64_t batch, int64_t seq, int32_t hq, int32_t head_dim, int64_t part_keys) {
+BackwardLayout backward_layout(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                               int64_t part_keys) {
     BackwardLayout w;
     const int64_t nqb = ceil_div(seq, 64);
     w.stat = 0;
     w.counters = align256((size_t)batch * hq * nqb * 128 * sizeof(float));
     w.part = w.counters + 256;
     const size_t part_bytes = (size_t)batch * part_keys * hq * head_dim * sizeof(float);
-    w.total = w.part + 2 * align256(part_bytes);
+    w.amax = w.part + 2 * align256(part_bytes);
+    w.exps = w.amax + align256((size_t)4 * batch * hkv * flux::kAbsmaxChunks * sizeof(uint32_t));
+    w.q16 = w.exps + align256((size_t)4 * batch * hkv * sizeof(int));
+    const size_t qb = align256((size_t)batch * seq * hq * head_dim * 2), kb = align256((size_t)batch * seq * hkv * head_dim * 2);
+    w.k16 = w.q16 + qb;
+    w.v16 = w.k16 + kb;
+    w.do16 = w.v16 + kb;
+    w.total = w.do16 + qb;
     return w;
 }
 
@@ -527,7 +535,7 @@ size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq,
     if (mode != FLUX_MODE_DENSE && mode != FLUX_MODE_SPARSE) return 0;
     if (block < 1 || sink_tokens < 0 || sink_tokens % block != 0) return 0;
     const int64_t pk = backward_part_keys(seq, hq, hkv, mode == FLUX_MODE_SPARSE, sink_tokens / block);
-    return backward_layout(batch, seq, hq, head_dim, pk).total;
+    return backward_layout(batch, seq, hq, hkv, head_dim, pk).total;
 }
 
 int flux_attn_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
@@ -559,8 +567,10 @@ int flux_attn_backward(const void* q, const void* k, const void* v, const void* 
         return fail(FLUX_ERR_UNSUPPORTED, "batch * hq * seq exceeds the work-unit range");
     if (seq * (int64_t)std::max(hq, hkv) * head_dim > INT32_MAX)
         return fail(FLUX_ERR_UNSUPPORTED, "seq * max(hq, hkv) * head_dim must stay below 2^31 elements");
+    if (in_dtype == FLUX_DTYPE_BF16 && batch * hkv > 65535)
+        return fail(FLUX_ERR_UNSUPPORTED, "batch * hkv must stay below 65536 (one scale group per KV head)");
     const int64_t part_keys = backward_part_keys(seq, hq, hkv, ms.sparse && causal, ms.sink_blocks);
-    const BackwardLayout w = backward_layout(batch, seq, hq, head_dim, part_keys);
+    const BackwardLayout w = backward_layout(batch, seq, hq, hkv, head_dim, part_keys);
     if (!workspace || workspace_bytes < w.total)
         return fail(FLUX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
                     workspace ? workspace_bytes : (size_t)0);
@@ -588,6 +598,12 @@ int flux_attn_backward(const void* q, const void* k, const void* v, const void* 
         a.dv_part = nullptr;
     }
     a.part_keys = part_keys;
+    a.amax = reinterpret_cast<uint32_t*>(ws + w.amax);
+    a.exps = reinterpret_cast<int*>(ws + w.exps);
+    a.q16 = ws + w.q16;
+    a.k16 = ws + w.k16;
+    a.v16 = ws + w.v16;
+    a.do16 = ws + w.do16;
     a.batch = batch;
     a.seq = seq;
     a.hq = hq;

@@ -8,6 +8,7 @@
 namespace flux {
 
 constexpr int kBlock = 64;  // block-sparse granularity and key-tile width
+constexpr int kAbsmaxChunks = 128;  // backward: token chunks of the |x| maximum per (batch, KV head, tensor)
 
 struct PrefillArgs {
     const void* q;
@@ -107,6 +108,14 @@ struct BackwardArgs {
     int64_t part_keys;     // keys held by dk_part / dv_part (the sink key pairs' keys), 0 if none
     float* stat;           // workspace [B, Hq, n_qblk, 2, 64]: -lse*log2(e), then rowsum(dO * O)
     int* counters;         // workspace [2]: work-queue heads of the dK/dV and dQ kernels
+    // bf16 inputs: fp16 copies of Q, K, V, dO (same layouts) scaled by 2^-e per (batch, KV head) and
+    // tensor, the largest magnitude of each group landing in [2^14, 2^15)
+    void* q16;
+    void* k16;
+    void* v16;
+    void* do16;
+    uint32_t* amax;        // workspace [4][B * Hkv][kAbsmaxChunks]: partial maxima of |x| (bf16 bits)
+    int* exps;             // workspace [4][B * Hkv]: e of Q, K, V, dO
     int64_t batch;
     int64_t seq;
     int hq;

@@ -268,16 +268,24 @@ def test_backward_workspace_size(fa):
     B, S, Hq, Hkv, d = 2, 1000, 8, 2, 128
     nqb = (S + 63) // 64
     stat = align(B * Hq * nqb * 128 * 4)
+
+    def fp16_part(B, S):   # chunk maxima, exponents, fp16 copies of Q, K, V, dO
+        q16, k16 = align(B * S * Hq * d * 2), align(B * S * Hkv * d * 2)
+        return align(4 * B * Hkv * 128 * 4) + align(4 * B * Hkv * 4) + 2 * q16 + 2 * k16
+
     SP = fa.FLUX_MODE_SPARSE
     # dense: dK/dV units take a KV head's query heads in turn, no per-head buffers
-    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d) == stat + 256
+    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d) == stat + 256 + fp16_part(B, S)
     # block-sparse GQA: per-head buffers for the key pairs holding sink blocks (128 keys per pair)
-    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d, SP, 64, 128) == stat + 256 + 2 * align(B * 128 * Hq * d * 4)
-    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d, SP, 64, 192) == stat + 256 + 2 * align(B * 256 * Hq * d * 4)
+    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d, SP, 64, 128) == \
+        stat + 256 + 2 * align(B * 128 * Hq * d * 4) + fp16_part(B, S)
+    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d, SP, 64, 192) == \
+        stat + 256 + 2 * align(B * 256 * Hq * d * 4) + fp16_part(B, S)
     assert fa.flux_attn_backward_workspace_size(B, 100, Hq, Hkv, d, SP, 64, 192) == \
-        align(B * Hq * 2 * 128 * 4) + 256 + 2 * align(B * 100 * Hq * d * 4)                # pairs clipped at seq
-    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d, SP, 64, 0) == stat + 256      # no sink
-    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hq, d, SP, 64, 128) == stat + 256     # no grouping
+        align(B * Hq * 2 * 128 * 4) + 256 + 2 * align(B * 100 * Hq * d * 4) + fp16_part(B, 100)   # pairs clipped at seq
+    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d, SP, 64, 0) == stat + 256 + fp16_part(B, S)   # no sink
+    dense_mha = fa.flux_attn_backward_workspace_size(B, S, Hq, Hq, d)
+    assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hq, d, SP, 64, 128) == dense_mha   # no grouping
     assert fa.flux_attn_backward_workspace_size(B, S, Hq, 3, d) == 0                    # hq % hkv
     assert fa.flux_attn_backward_workspace_size(0, S, Hq, Hkv, d) == 0
     assert fa.flux_attn_backward_workspace_size(B, S, Hq, Hkv, d, SP, 64, 100) == 0     # sink not a block multiple

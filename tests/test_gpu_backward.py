@@ -308,6 +308,67 @@ def test_sharp_scores(fa, mode):
         _close(t.cpu().numpy(), r, f"sharp {name} mode {mode}", None)
 
 
+# ------------------------------------------------------------- input magnitudes
+@pytest.mark.parametrize("mode", [0, 1])
+def test_group_magnitudes(fa, mode):
+    """Each KV group's Q, K, V and dO scaled by its own powers of two, 2^-40 .. 2^20 (exact in bf16), with the
+    softmax scale divided by the common Q K factor so the probabilities stay those of the unscaled layer.
+    The gradients scale exactly: dV by e, dK by c e / b, dQ by c e / a (a, b, c, e the group's Q, K, V, dO
+    factors); divided by them they must meet the bar against the oracle's unscaled gradients, which only
+    holds if the kernels' per-group fp16 scaling follows each group's range."""
+    B, S, Hq, Hkv, d = 1, 328, 4, 2, 128
+    G = Hq // Hkv
+    say("backward group magnitudes", mode)
+    scale = default_scale(d)
+    q, k, v, g = _inputs(B, S, Hq, Hkv, seed=5011)
+    sink, window = (64, 128) if mode else (0, 0)
+    o32, lse = _oracle_forward(q, k, v, scale, True, bool(mode), sink, window)
+    rq, rk, rv = oracle.attention_backward(q, k, v, g, scale, causal=True, sparse=bool(mode), block=64,
+                                           sink_tokens=sink, window_tokens=window)
+    fa_, fb, fc, fe = [2.0 ** 20, 2.0 ** -4], [2.0 ** -12, 2.0 ** 12], [2.0 ** -30, 2.0 ** 6], [2.0 ** -40, 2.0 ** 12]
+    qs, ks, vs, gs = (synth.bf16_bits_to_f32(x).copy() for x in (q, k, v, g))
+    os_ = o32.copy()
+    for grp in range(Hkv):
+        hs = slice(grp * G, (grp + 1) * G)
+        qs[:, :, hs] *= fa_[grp]
+        gs[:, :, hs] *= fe[grp]
+        os_[:, :, hs] *= fc[grp]
+        ks[:, :, grp] *= fb[grp]
+        vs[:, :, grp] *= fc[grp]
+    # the Q K factor is 2^8 for both groups: scale / 2^8 keeps every score
+    qd, kd, vd, gd = (synth.torch_bf16_from_bits(synth.f32_to_bf16_bits(x)) for x in (qs, ks, vs, gs))
+    dq = torch.full((B, S, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    dk = torch.full((B, S, Hkv, d), float("nan"), dtype=torch.float32, device=DEV)
+    dv = torch.full((B, S, Hkv, d), float("nan"), dtype=torch.float32, device=DEV)
+    fa.flux_attn_backward(qd, kd, vd, torch.from_numpy(os_).to(DEV), gd, torch.from_numpy(lse).to(DEV), dq, dk, dv,
+                          causal=True, mode=mode, block=64, sink_tokens=sink, window_tokens=window,
+                          scale=scale / 2.0 ** 8)
+    torch.cuda.synchronize()
+    dq, dk, dv = (t.cpu().numpy().astype(np.float64) for t in (dq, dk, dv))
+    for grp in range(Hkv):
+        hs = slice(grp * G, (grp + 1) * G)
+        dq[:, :, hs] /= fc[grp] * fe[grp] / fa_[grp]
+        dk[:, :, grp] /= fc[grp] * fe[grp] / fb[grp]
+        dv[:, :, grp] /= fe[grp]
+    for name, t, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _close(t, r, f"magnitudes {name} mode {mode}", None)
+
+
+def test_zero_output_gradient(fa):
+    """dO = 0 (its scale exponent falls back to 0): every gradient is exactly zero."""
+    B, S, Hq, Hkv, d = 1, 200, 4, 2, 128
+    say("backward zero dO")
+    scale = default_scale(d)
+    q, k, v, _ = _inputs(B, S, Hq, Hkv, seed=5021)
+    o32, lse = _oracle_forward(q, k, v, scale, True, False, 0, 0)
+    qd, kd, vd = (synth.torch_bf16_from_bits(x) for x in (q, k, v))
+    gd = torch.zeros((B, S, Hq, d), dtype=torch.bfloat16, device=DEV)
+    dq, dk, dv = _backward(fa, qd, kd, vd, torch.from_numpy(o32).to(DEV), gd, torch.from_numpy(lse).to(DEV), True, 0,
+                           0, 0)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool((t == 0).all()), name
+
+
 # ------------------------------------------------------------- graph capture
 def test_backward_graph_replay(fa):
     """The backward (row statistics, dK/dV, dQ, sink-key GQA sum) captured in a HIP graph: its work queues
