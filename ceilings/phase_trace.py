@@ -13,6 +13,8 @@ schedule are those of the library; results stay exact (the parity of the copy is
 `run` times the copy with and without the stamps and reports, per wave (waves 0-3 form the group that runs
 matrix work in the first phase, waves 4-7 the other), the median cycles of each segment over steps 2..63,
 for the seq-8192 dense layer and the seq-131072 dense and block-sparse layers (32/8 heads, head_dim 128, bf16).
+At seq 8192 the traced copy's output is compared with the library's own (loaded beside it): the stamps
+change no arithmetic, so the two agree to within the rounding of the bf16 output.
 """
 from __future__ import annotations
 
@@ -118,7 +120,10 @@ def run() -> dict:
     import torch
     import long_context_attention_tiled_amd as fa
     assert os.path.dirname(fa.LIB_PATH) == PKG, fa.LIB_PATH
-    import oracle
+    traced = fa._lib
+    plain = ctypes.CDLL(os.path.join(ROOT, "long_context_attention_tiled_amd", "libflux_attn.so"))
+    plain.flux_attn_prefill.argtypes = traced.flux_attn_prefill.argtypes
+    plain.flux_attn_prefill.restype = traced.flux_attn_prefill.restype
     res = {}
     for name, S, mode in (("dense_s8192", 8192, 0), ("dense_s131072", 131072, 0), ("sparse_s131072", 131072, 1)):
         print(f"[phase_trace] {name}", file=sys.stderr, flush=True)
@@ -148,13 +153,16 @@ def run() -> dict:
         fa.lib().flux_probe_set_trace(None)
         tr = trace.view(N_SLOTS, N_WAVES, N_STEPS, N_STAMPS).cpu().numpy().astype(np.int64)
         r = {"ms_untraced": round(ms_plain, 4), "ms_traced": round(ms_traced, 4), **_medians(tr)}
-        if S == 8192:   # the traced copy computes the same attention: a few rows against the oracle
-            rows = np.array([(0, h, i) for h in (0, 31) for i in (0, 4095, 8191)], np.int64)
-            qh, kh, vh = (x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16) for x in (q, k, v))
-            ref, _ = oracle.attention(qh, kh, vh, 1.0 / np.sqrt(d), causal=True, rows=rows)
-            got = o.float().cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]]
-            r["max_abs_err_vs_oracle"] = float(np.abs(got - ref).max())
-            assert r["max_abs_err_vs_oracle"] < 2e-2
+        if S == 8192:   # the traced copy computes the same attention as the library itself
+            traced_out = o.clone()
+            fa._lib = plain
+            try:
+                call()
+            finally:
+                fa._lib = traced
+            torch.cuda.synchronize()
+            r["max_abs_diff_vs_library"] = float((traced_out.float() - o.float()).abs().max())
+            assert r["max_abs_diff_vs_library"] <= 1e-2
         res[name] = r
         del q, k, v, o
         torch.cuda.empty_cache()
