@@ -309,33 +309,38 @@ def test_sharp_scores(fa, mode):
 
 
 # ------------------------------------------------------------- input magnitudes
-@pytest.mark.parametrize("mode", [0, 1])
-def test_group_magnitudes(fa, mode):
-    """Each KV group's Q, K, V and dO scaled by its own powers of two, 2^-40 .. 2^20 (exact in bf16), with the
-    softmax scale divided by the common Q K factor so the probabilities stay those of the unscaled layer.
-    The gradients scale exactly: dV by e, dK by c e / b, dQ by c e / a (a, b, c, e the group's Q, K, V, dO
-    factors); divided by them they must meet the bar against the oracle's unscaled gradients, which only
-    holds if the kernels' per-group fp16 scaling follows each group's range."""
-    B, S, Hq, Hkv, d = 1, 328, 4, 2, 128
+@pytest.mark.parametrize("mode,d", [(0, 128), (1, 128), (1, 64)])
+def test_group_magnitudes(fa, mode, d):
+    """Each (batch, KV group)'s Q, K, V and dO scaled by its own powers of two, 2^-40 .. 2^20 (exact in bf16),
+    with the softmax scale divided by the common Q K factor so the probabilities stay those of the unscaled
+    layer.  The gradients scale exactly: dV by e, dK by c e / b, dQ by c e / a (a, b, c, e the group's Q, K,
+    V, dO factors); divided by them they must meet the bar against the oracle's unscaled gradients, which
+    only holds if the kernels' fp16 scaling follows each (batch, KV group)'s own range."""
+    B, S, Hq, Hkv = 2, 328, 4, 2
     G = Hq // Hkv
-    say("backward group magnitudes", mode)
+    say("backward group magnitudes", mode, d)
     scale = default_scale(d)
-    q, k, v, g = _inputs(B, S, Hq, Hkv, seed=5011)
+    q, k, v, g = _inputs(B, S, Hq, Hkv, seed=5011, d=d)
     sink, window = (64, 128) if mode else (0, 0)
     o32, lse = _oracle_forward(q, k, v, scale, True, bool(mode), sink, window)
     rq, rk, rv = oracle.attention_backward(q, k, v, g, scale, causal=True, sparse=bool(mode), block=64,
                                            sink_tokens=sink, window_tokens=window)
-    fa_, fb, fc, fe = [2.0 ** 20, 2.0 ** -4], [2.0 ** -12, 2.0 ** 12], [2.0 ** -30, 2.0 ** 6], [2.0 ** -40, 2.0 ** 12]
+    # per (batch, group): Q factor a, K factor b (a * b = 2^8 everywhere), V factor c, dO factor e
+    fq = [[2.0 ** 20, 2.0 ** -4], [2.0 ** 3, 2.0 ** 9]]
+    fk = [[2.0 ** -12, 2.0 ** 12], [2.0 ** 5, 2.0 ** -1]]
+    fv = [[2.0 ** -30, 2.0 ** 6], [2.0 ** 11, 2.0 ** -17]]
+    fo = [[2.0 ** -40, 2.0 ** 12], [2.0 ** -3, 2.0 ** -25]]
     qs, ks, vs, gs = (synth.bf16_bits_to_f32(x).copy() for x in (q, k, v, g))
     os_ = o32.copy()
-    for grp in range(Hkv):
-        hs = slice(grp * G, (grp + 1) * G)
-        qs[:, :, hs] *= fa_[grp]
-        gs[:, :, hs] *= fe[grp]
-        os_[:, :, hs] *= fc[grp]
-        ks[:, :, grp] *= fb[grp]
-        vs[:, :, grp] *= fc[grp]
-    # the Q K factor is 2^8 for both groups: scale / 2^8 keeps every score
+    for bb in range(B):
+        for grp in range(Hkv):
+            assert fq[bb][grp] * fk[bb][grp] == 2.0 ** 8
+            hs = slice(grp * G, (grp + 1) * G)
+            qs[bb, :, hs] *= fq[bb][grp]
+            gs[bb, :, hs] *= fo[bb][grp]
+            os_[bb, :, hs] *= fv[bb][grp]
+            ks[bb, :, grp] *= fk[bb][grp]
+            vs[bb, :, grp] *= fv[bb][grp]
     qd, kd, vd, gd = (synth.torch_bf16_from_bits(synth.f32_to_bf16_bits(x)) for x in (qs, ks, vs, gs))
     dq = torch.full((B, S, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
     dk = torch.full((B, S, Hkv, d), float("nan"), dtype=torch.float32, device=DEV)
@@ -345,13 +350,14 @@ def test_group_magnitudes(fa, mode):
                           scale=scale / 2.0 ** 8)
     torch.cuda.synchronize()
     dq, dk, dv = (t.cpu().numpy().astype(np.float64) for t in (dq, dk, dv))
-    for grp in range(Hkv):
-        hs = slice(grp * G, (grp + 1) * G)
-        dq[:, :, hs] /= fc[grp] * fe[grp] / fa_[grp]
-        dk[:, :, grp] /= fc[grp] * fe[grp] / fb[grp]
-        dv[:, :, grp] /= fe[grp]
+    for bb in range(B):
+        for grp in range(Hkv):
+            hs = slice(grp * G, (grp + 1) * G)
+            dq[bb, :, hs] /= fv[bb][grp] * fo[bb][grp] / fq[bb][grp]
+            dk[bb, :, grp] /= fv[bb][grp] * fo[bb][grp] / fk[bb][grp]
+            dv[bb, :, grp] /= fo[bb][grp]
     for name, t, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        _close(t, r, f"magnitudes {name} mode {mode}", None)
+        _close(t, r, f"magnitudes {name} mode {mode} d {d}", None)
 
 
 def test_zero_output_gradient(fa):
