@@ -44,8 +44,9 @@
 //   dS16 = dS 2^-eS with eS = 23 + eDO + eV: |dP| <= d * 2^30 * 2^(eDO + eV) <= 2^(37 + eDO + eV) and
 //        |dS| <= 2 max|dP|, so |dS16| < 2^15 always; formed as P16 (dP16 2^-37 - D 2^-(37 + eDO + eV))
 //   dV = 2^(eDO - 14) sum P16 dO16,  dK = scale 2^(eS + eQ) sum dS16 Q16,  dQ = scale 2^(eS + eK) sum dS16 K16
-// Values below 2^-29 of their group's maximum lose fp16 bits (absolute error <= 2^-40 of that
-// maximum).  The scale factors stay within fp32's range as long as the largest |Q| times the largest
+// Values below 2^-29 of their group's maximum are subnormal in fp16 and may lose bits or be flushed
+// (absolute error below 2^-29 of that maximum); likewise probabilities below 2^-28 and dS below 2^-29 of
+// its bound.  The scale factors stay within fp32's range as long as the largest |Q| times the largest
 // |K| of a KV head, and the largest |dO| times the largest |V|, lie between 2^-90 and 2^150.
 //
 // Both main kernels are persistent, run two waves per SIMD, and take units from a device counter,
