@@ -251,10 +251,10 @@ size_t flux_attn_backward_workspace_size(int64_t batch, int64_t seq, int32_t hq,
  * contents on entry do not matter.  Deterministic: no atomics on gradients, fixed summation order.
  * in_dtype BF16: q, k, v, d_o bf16, matrix-core kernels on fp16 operands with fp32 accumulation:
  * the inputs are copied to fp16 scaled by a power of two per (batch, KV head) and tensor (exact for
- * every value above 2^-29 of its group's largest; smaller ones may be flushed), S and dP are the products of those copies, and P
- * and dS enter the gradient products rounded once to fp16.  The scales stay in fp32's range as long
- * as max|Q| * max|K| and max|dO| * max|V| over each KV head's group lie in [2^-90, 2^150] (inputs
- * must be finite).  in_dtype F32: q, k, v, d_o float32, vector-ALU kernels for small layers (as the
+ * every value above 2^-29 of its group's largest; smaller ones may be flushed), S and dP are the
+ * products of those copies, and P and dS enter the gradient products rounded once to fp16.  The
+ * scales stay in fp32's range as long as max|Q| * max|K| and max|dO| * max|V| over each KV head's
+ * group lie in [2^-90, 2^150] (inputs must be finite).  in_dtype F32: q, k, v, d_o float32, vector-ALU kernels for small layers (as the
  * float32 forward).
  * Supported: head_dim 64 or 128, block 64; bf16 inputs: batch * hkv < 65536.
  */
