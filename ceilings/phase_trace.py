@@ -6,7 +6,9 @@
 `build` copies long_context_attention_tiled_amd/ into ceilings/phase_trace_pkg/ and adds, in the copy only,
 s_memtime stamps to every steady step of prefill_bf16.hip's tile loop (step start; end of the first-phase
 work; after the mid-step barrier; end of the second-phase work; after the wait for this step's loads) for
-three workgroups (blockIdx 0, 97, 203) over the first 64 steps of their first work unit, plus an entry point
+three workgroups (blockIdx 0, 97, 203) over the first 64 steps of their first work unit, with an
+s_memrealtime stamp (a constant 100 MHz count) at each step start to give the rate s_memtime counts at
+during the kernel, plus an entry point
 flux_probe_set_trace() that hands the kernel a device buffer for them.  The arithmetic, the loads and the
 schedule are those of the library; results stay exact (the parity of the copy is checked by `run`).
 
@@ -30,7 +32,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PKG_PARENT = os.path.join(HERE, "phase_trace_pkg")
 PKG = os.path.join(PKG_PARENT, "long_context_attention_tiled_amd")
-N_SLOTS, N_WAVES, N_STEPS, N_STAMPS = 3, 8, 64, 5
+N_SLOTS, N_WAVES, N_STEPS, N_STAMPS = 3, 8, 64, 6
 
 
 def _edit(path, old, new):
@@ -72,11 +74,12 @@ def build() -> str:
     i5 = body.index(sync, body.index("t4 ="))
     body = (body[:i5 + len(sync)] +
             "                    if (probe && pstep < 64 && lane == 0) {\n"
-            "                        unsigned long long* dst = a.trace + ((size_t)(pslot * 8 + wave) * 64 + pstep) * 5;\n"
-            "                        dst[0] = t0; dst[1] = t1; dst[2] = t2; dst[3] = t3; dst[4] = t4;\n"
+            "                        unsigned long long* dst = a.trace + ((size_t)(pslot * 8 + wave) * 64 + pstep) * 6;\n"
+            "                        dst[0] = t0; dst[1] = t1; dst[2] = t2; dst[3] = t3; dst[4] = t4; dst[5] = r0;\n"
             "                    }\n                    ++pstep;\n" + body[i5 + len(sync):])
     body = body.replace("                while (have_n) {\n",
-                        "                while (have_n) {\n" + stamp("t0"), 1)
+                        "                while (have_n) {\n" + stamp("t0") +
+                        "                    const unsigned long long r0 = probe ? __builtin_amdgcn_s_memrealtime() : 0ull;\n", 1)
     pre = ("                int pstep = 0;\n"
            "                const int pslot = (blockIdx.x == 0) ? 0 : (blockIdx.x == 97) ? 1 : (blockIdx.x == 203) ? 2 : -1;\n"
            "                const bool probe = a.trace && pslot >= 0 && k == 1;\n")
@@ -110,6 +113,15 @@ def _medians(tr):
     busiest = max(out["first_phase_work"][w] + out["mid_barrier_wait"][w] + out["second_phase_work"][w] +
                   out["load_wait"][w] for w in range(N_WAVES))
     out["end_of_step_barrier_and_loop"] = out["step"] - busiest
+    # s_memtime ticks per s_memrealtime tick (the latter counts a constant 100 MHz) over each traced unit
+    ratios = []
+    for sl in range(tr.shape[0]):
+        n = int((tr[sl, :, :, 0] > 0).all(axis=0).sum())
+        if n >= 4:
+            dm = tr[sl, :, n - 1, 0] - tr[sl, :, 1, 0]
+            dr = tr[sl, :, n - 1, 5] - tr[sl, :, 1, 5]
+            ratios += list(dm[dr > 0] / dr[dr > 0])
+    out["memtime_MHz"] = round(100.0 * float(np.median(ratios)), 1) if ratios else None
     return out
 
 
