@@ -219,6 +219,29 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ gbase, uint32
     }
 }
 
+// The K-tile loads of one wave: NI direct-load instructions of the tile, starting at instruction `first`
+// (the K tile's instructions are not split evenly over the waves; see prefill_body).
+template <int D, int NI>
+__device__ __forceinline__ void issue_k(const u16* __restrict__ gbase, uint32_t row_stride, int kb, int last_key,
+                                        uint32_t slot, int first, int lane, const uint32_t* off) {
+    using L = Lay<D>;
+    const int key0 = kb * kBC;
+    if (key0 + kBC - 1 <= last_key) {
+        const u16* t = uniform_ptr(gbase + (uint32_t)key0 * row_stride);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) load_lds_16(t, off[i], slot + (first + i) * 1024);
+    } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int inst = first + i;
+            const int row = inst * L::ROWS_PER_INST + lane / L::CH;
+            const uint32_t key = (uint32_t)min(key0 + row, last_key);
+            const int pch = lane % L::CH;
+            load_lds_16(uniform_ptr(gbase), 2 * (key * row_stride + 8 * (pch ^ swz_k<D>(row))), slot + inst * 1024);
+        }
+    }
+}
+
 template <int D, int MODE, bool OUT_F32>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     using L = Lay<D>;
@@ -258,13 +281,27 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     const int last_key = seq - 1;
 
     // per-lane byte offsets of the direct loads inside a tile (tile-invariant)
-    uint32_t koff[L::INSTS_PER_WAVE], voff[L::INSTS_PER_WAVE];
+    uint32_t koff[4], voff[L::INSTS_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < L::INSTS_PER_WAVE; ++i) {
         const int row = (wave * L::INSTS_PER_WAVE + i) * L::ROWS_PER_INST + lane / L::CH;
         const int pch = lane % L::CH;
-        koff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz_k<D>(row)));   // bytes
         voff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz_v<D>(row)));
+    }
+    // Each step opens with every wave issuing its share of the next tiles' direct loads (~100 cycles per
+    // instruction when all eight waves issue together), and group 1 then runs the softmax phase, the
+    // longer of the two first phases: at head_dim 128 the waves of group 0 take 3 of the K tile's 16
+    // instructions each and those of group 1 take 1 (0.6-0.7% faster at seq 131072 dense than 2 and 2).
+    constexpr int KI = L::TILE_B / 1024;          // K-tile instructions per workgroup
+    constexpr int KA = D == 128 ? 3 : KI / 8;     // per wave of group 0 (matrix work first)
+    constexpr int KB = (KI - 4 * KA) / 4;         // per wave of group 1
+    static_assert(4 * KA + 4 * KB == KI && KA <= 4, "K tile split over the waves");
+    const int kfirst = grp == 0 ? KA * wq : 4 * KA + KB * wq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = (kfirst + i) * L::ROWS_PER_INST + lane / L::CH;
+        const int pch = lane % L::CH;
+        koff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz_k<D>(row)));
     }
     const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
@@ -273,6 +310,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     bool wave_live = false;
     const u16* kg = nullptr;
     const u16* vg = nullptr;
+    auto issue_ktile = [&](int kb, uint32_t slot) {
+        if (grp == 0) issue_k<D, KA>(kg, kv_row_stride, kb, last_key, slot, kfirst, lane, koff);
+        else issue_k<D, KB>(kg, kv_row_stride, kb, last_key, slot, kfirst, lane, koff);
+    };
     bf16x8 qreg[NC];   // Q rows as the B operand of S^T = K Q^T: lane holds Q[qpos][16c + 8hh .. +7]
     TileWalk<MODE> walk;
     uint32_t in;
@@ -320,7 +361,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
         have_n = have_any && walk.next(kb_n, in);
         mine_n = have_n && wave_live && ((in >> my_r) & 1);
         mine_p = false;
-        if (have_any) issue_tile<D, false>(kg, kv_row_stride, kb_c, last_key, smem_lds + L::K_BASE, wave, lane, koff);
+        if (have_any) issue_ktile(kb_c, smem_lds + L::K_BASE);
         const u16* qg = reinterpret_cast<const u16*>(a.q) + ((int64_t)b * a.seq * a.hq + h) * D;
         const uint32_t qrow = (uint32_t)min(qpos, last_key);
 #pragma unroll
@@ -557,8 +598,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
             if (have_any) {
                 // step 0
                 if (have_n)
-                    issue_tile<D, false>(kg, kv_row_stride, kb_n, last_key, smem_lds + L::K_BASE + L::TILE_B, wave,
-                                         lane, koff);
+                    issue_ktile(kb_n, smem_lds + L::K_BASE + L::TILE_B);
                 issue_tile<D, true>(vg, kv_row_stride, kb_c, last_key, smem_lds + L::V_BASE, wave, lane, voff);
                 if constexpr (!kG1) mwork(kOff, kOn, 0, 0);
                 __syncthreads();
@@ -576,8 +616,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
                     have_n = walk.next(kb_n, in);
                     mine_n = have_n && wave_live && ((in >> my_r) & 1);
                     if (have_n)
-                        issue_tile<D, false>(kg, kv_row_stride, kb_n, last_key,
-                                             smem_lds + L::K_BASE + (sl ^ 1) * L::TILE_B, wave, lane, koff);
+                        issue_ktile(kb_n, smem_lds + L::K_BASE + (sl ^ 1) * L::TILE_B);
                     issue_tile<D, true>(vg, kv_row_stride, kb_c, last_key, smem_lds + L::V_BASE + sl * L::TILE_B,
                                         wave, lane, voff);
                     if constexpr (!kG1) mwork(kOn, kOn, sl ^ 1, sl);
