@@ -733,6 +733,11 @@ def run_microbench(torch, dev):
     one, eight = issue_cycles(1, 1), issue_cycles(8, 1)
     out["lds_dma_issue_cycles_per_load_1_wave"] = round((eight - one) / 7, 1)
     out["lds_dma_issue_cycles_4_loads_x_8_waves"] = issue_cycles(4, 8)
+    for _ in range(3):   # the same four loads per wave as one run with M0 set once (the prefill's form)
+        ceilings.check(lib.ceil_lds_dma_issue4(src.data_ptr(), src.numel(), cyc.data_ptr(), cyc.numel(), wgs, 1, 8,
+                                               None, 0, stream), "ceil_lds_dma_issue4")
+    torch.cuda.synchronize()
+    out["lds_dma_issue_cycles_4_loads_x_8_waves_one_m0_write"] = float(np.median(cyc.view(wgs, 8, 2)[:, :, 0].cpu().numpy()))
     del src, cyc
     return out
 

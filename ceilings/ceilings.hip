@@ -161,6 +161,73 @@ __global__ __launch_bounds__(kDmaThreads) void lds_dma_issue_kernel(const char* 
     }
 }
 
+// Four 1 KB direct loads per active wave issued as one block, timed as above.  FORM 1: M0 is set once and
+// the loads step through LDS by their immediate offsets (0, 1024, 2048, 3072; the offset is added to the
+// global address too, so every lane's per-load offset is the same 16*l).  FORM 2: M0 is set before every
+// load, as with a separate base per load, and restored once after the four.  With check, each active wave
+// then copies its 4 KB of LDS there (check[(wg*8 + wave)*4096 ..]), which shows where the loads landed.
+template <int FORM>
+__global__ __launch_bounds__(kDmaThreads) void lds_dma_issue4_kernel(const char* __restrict__ src, uint64_t* out,
+                                                                     int active, uint4* check) {
+    __shared__ __attribute__((aligned(1024))) char smem[65536];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)smem + wave * 4096;
+    const char* base = src + (int64_t)blockIdx.x * kDmaBytesPerWg + wave * 8192;
+    const uint32_t o = (uint32_t)lane * 16;
+    __syncthreads();
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    if (wave < active) {
+        uint32_t saved_m0;
+        if constexpr (FORM == 1) {
+            asm volatile(
+                "s_mov_b32 %0, m0\n\t"
+                "s_mov_b32 m0, %3\n\t"
+                "s_nop 0\n\t"
+                "global_load_lds_dwordx4 %1, %2\n\t"
+                "global_load_lds_dwordx4 %1, %2 offset:1024\n\t"
+                "global_load_lds_dwordx4 %1, %2 offset:2048\n\t"
+                "global_load_lds_dwordx4 %1, %2 offset:3072\n\t"
+                "s_mov_b32 m0, %0"
+                : "=&s"(saved_m0)
+                : "v"(o), "s"(base), "s"(lds)
+                : "memory");
+        } else {
+            asm volatile(
+                "s_mov_b32 %0, m0\n\t"
+                "s_mov_b32 m0, %3\n\t"
+                "s_nop 0\n\t"
+                "global_load_lds_dwordx4 %1, %2\n\t"
+                "s_mov_b32 m0, %4\n\t"
+                "s_nop 0\n\t"
+                "global_load_lds_dwordx4 %1, %2 offset:1024\n\t"
+                "s_mov_b32 m0, %5\n\t"
+                "s_nop 0\n\t"
+                "global_load_lds_dwordx4 %1, %2 offset:2048\n\t"
+                "s_mov_b32 m0, %6\n\t"
+                "s_nop 0\n\t"
+                "global_load_lds_dwordx4 %1, %2 offset:3072\n\t"
+                "s_mov_b32 m0, %0"
+                : "=&s"(saved_m0)
+                : "v"(o), "s"(base), "s"(lds), "s"(lds), "s"(lds), "s"(lds)
+                : "memory");
+        }
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    const uint64_t t2 = __builtin_amdgcn_s_memtime();
+    __syncthreads();
+    if (lane == 0) {
+        out[((int64_t)blockIdx.x * 8 + wave) * 2] = t1 - t0;
+        out[((int64_t)blockIdx.x * 8 + wave) * 2 + 1] = t2 - t0;
+    }
+    if (check && wave < active) {
+        const uint4* l = reinterpret_cast<const uint4*>(smem + wave * 4096);
+        uint4* c = check + ((int64_t)blockIdx.x * 8 + wave) * 256;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i * 64 + lane] = l[i * 64 + lane];
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -236,6 +303,25 @@ int ceil_lds_dma_issue(const void* src, int64_t src_bytes, uint64_t* out, int64_
     hipLaunchKernelGGL(lds_dma_issue_kernel, dim3(workgroups), dim3(kDmaThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const char*>(src), out, n_inst,
                        active_waves);
+    return (int)hipGetLastError();
+}
+
+// The four-load forms above (form 1 or 2); arguments as ceil_lds_dma_issue with n_inst = 4, plus check:
+// null, or >= workgroups * 8 * 4096 bytes of device memory (16-byte aligned) for the LDS contents.
+int ceil_lds_dma_issue4(const void* src, int64_t src_bytes, uint64_t* out, int64_t out_elems, int32_t workgroups,
+                        int32_t form, int32_t active_waves, void* check, int64_t check_bytes, void* stream) {
+    if (!src || !out || workgroups < 1 || (form != 1 && form != 2) || active_waves < 1 || active_waves > 8 ||
+        src_bytes < (int64_t)workgroups * kDmaBytesPerWg || out_elems < (int64_t)workgroups * 16 ||
+        (reinterpret_cast<uintptr_t>(src) & 15u) ||
+        (check && (check_bytes < (int64_t)workgroups * 8 * 4096 || (reinterpret_cast<uintptr_t>(check) & 15u))))
+        return (int)hipErrorInvalidValue;
+    uint4* c = reinterpret_cast<uint4*>(check);
+    if (form == 1)
+        hipLaunchKernelGGL(lds_dma_issue4_kernel<1>, dim3(workgroups), dim3(kDmaThreads), 0,
+                           reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const char*>(src), out, active_waves, c);
+    else
+        hipLaunchKernelGGL(lds_dma_issue4_kernel<2>, dim3(workgroups), dim3(kDmaThreads), 0,
+                           reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const char*>(src), out, active_waves, c);
     return (int)hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
 """Phase timeline of the prefill's steady tile loop (measurement tool; the attention path never uses it).
 
     python ceilings/phase_trace.py build     # on the CPU: instrumented copy of the library, compiled for gfx950
-    python ceilings/phase_trace.py run       # on an MI355X: per-wave phase durations, one JSON line
+    python ceilings/phase_trace.py run [DIR] # on an MI355X: per-wave phase durations, one JSON line
+                                             # (with DIR, also the raw stamps as .npy files there)
 
 `build` copies long_context_attention_tiled_amd/ into ceilings/phase_trace_pkg/ and adds, in the copy only,
 s_memtime stamps to every steady step of prefill_bf16.hip's tile loop (step start; end of the first-phase
@@ -32,7 +33,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PKG_PARENT = os.path.join(HERE, "phase_trace_pkg")
 PKG = os.path.join(PKG_PARENT, "long_context_attention_tiled_amd")
-N_SLOTS, N_WAVES, N_STEPS, N_STAMPS = 3, 8, 64, 6
+N_SLOTS, N_WAVES, N_STEPS, N_STAMPS = 3, 8, 64, 7
 
 
 def _edit(path, old, new):
@@ -62,23 +63,24 @@ def build() -> str:
     p = os.path.join(c, "prefill_bf16.hip")
     s = open(p).read()
     stamp = lambda n: f"                    const unsigned long long {n} = probe ? __builtin_amdgcn_s_memtime() : 0ull;\n"
-    w0 = s.index("                while (have_n) {\n")
-    w1 = s.index("                    sl ^= 1;\n", w0)
+    w0 = s.index("                auto step = [&](auto slot_tag) {\n")
+    w1 = s.index("\n                };\n", w0) + 1
     body = s[w0:w1]
     sync = "                    __syncthreads();\n"
-    i1 = body.index(sync)
+    i1 = body.index("\n" + sync) + 1
     body = body[:i1] + stamp("t1") + sync + stamp("t2") + body[i1 + len(sync):]
     i3 = body.index("                    __builtin_amdgcn_s_waitcnt(0x0f70);")
     i3e = body.index("\n", i3) + 1
     body = body[:i3] + stamp("t3") + body[i3:i3e] + stamp("t4") + body[i3e:]
-    i5 = body.index(sync, body.index("t4 ="))
-    body = (body[:i5 + len(sync)] +
+    i5 = body.index("\n" + sync, body.index("t4 =")) + 1
+    body = (body[:i5 + len(sync)] + stamp("t5") +
             "                    if (probe && pstep < 64 && lane == 0) {\n"
-            "                        unsigned long long* dst = a.trace + ((size_t)(pslot * 8 + wave) * 64 + pstep) * 6;\n"
+            "                        unsigned long long* dst = a.trace + ((size_t)(pslot * 8 + wave) * 64 + pstep) * 7;\n"
             "                        dst[0] = t0; dst[1] = t1; dst[2] = t2; dst[3] = t3; dst[4] = t4; dst[5] = r0;\n"
+            "                        dst[6] = t5;\n"
             "                    }\n                    ++pstep;\n" + body[i5 + len(sync):])
-    body = body.replace("                while (have_n) {\n",
-                        "                while (have_n) {\n" + stamp("t0") +
+    head = "                    constexpr int sl = decltype(slot_tag)::value;\n"
+    body = body.replace(head, head + stamp("t0") +
                         "                    const unsigned long long r0 = probe ? __builtin_amdgcn_s_memrealtime() : 0ull;\n", 1)
     pre = ("                int pstep = 0;\n"
            "                const int pslot = (blockIdx.x == 0) ? 0 : (blockIdx.x == 97) ? 1 : (blockIdx.x == 203) ? 2 : -1;\n"
@@ -94,7 +96,7 @@ def build() -> str:
 
 
 def _medians(tr):
-    """tr [slots, waves, steps, 5] -> per-wave medians of the segments over the recorded steady steps (the first
+    """tr [slots, waves, steps, 7] -> per-wave medians of the segments over the recorded steady steps (the first
     two of each traced unit left out; a unit with fewer than 64 steps leaves the rest of its rows at zero)."""
     import numpy as np
     seg = {"first_phase_work": (0, 1), "mid_barrier_wait": (1, 2), "second_phase_work": (2, 3),
@@ -113,6 +115,29 @@ def _medians(tr):
     busiest = max(out["first_phase_work"][w] + out["mid_barrier_wait"][w] + out["second_phase_work"][w] +
                   out["load_wait"][w] for w in range(N_WAVES))
     out["end_of_step_barrier_and_loop"] = out["step"] - busiest
+    # per step, across the 8 waves: from the last wave's arrival at a barrier to the first wave's stamp right
+    # after it (the barrier's release), how far apart the waves arrive at the end-of-step one, and per wave
+    # from that barrier's release to the next step's first stamp (the loop's branch back to its head)
+    mid_rel, end_rel, end_spread, top, top_on, top_back = [], [], [], [], [], []
+    for sl in range(tr.shape[0]):
+        n = int((tr[sl, :, :, 0] > 0).all(axis=0).sum())
+        if n >= 4:
+            x = tr[sl, :, 2:n]
+            mid_rel.append(x[:, :, 2].min(axis=0) - x[:, :, 1].max(axis=0))
+            end_rel.append(x[:, :, 6].min(axis=0) - x[:, :, 4].max(axis=0))
+            gap = x[:, 1:, 0] - x[:, :-1, 6]
+            top.append(gap.ravel())
+            # the loop runs two steps per pass: an even step is followed by the second copy (straight on),
+            # an odd one by the branch back to the loop head
+            top_on.append(gap[:, 0::2].ravel())
+            top_back.append(gap[:, 1::2].ravel())
+            end_spread.append(x[:, :, 4].max(axis=0) - x[:, :, 4].min(axis=0))
+    out["mid_barrier_release"] = int(np.median(np.concatenate(mid_rel)))
+    out["end_barrier_release"] = int(np.median(np.concatenate(end_rel)))
+    out["end_barrier_to_next_step"] = int(np.median(np.concatenate(top)))
+    out["end_barrier_to_next_step_straight_on"] = int(np.median(np.concatenate(top_on)))
+    out["end_barrier_to_next_step_via_loop_branch"] = int(np.median(np.concatenate(top_back)))
+    out["end_barrier_arrival_spread"] = int(np.median(np.concatenate(end_spread)))
     # s_memtime ticks per s_memrealtime tick (the latter counts a constant 100 MHz) over each traced unit
     ratios = []
     for sl in range(tr.shape[0]):
@@ -125,7 +150,8 @@ def _medians(tr):
     return out
 
 
-def run() -> dict:
+def run(dump_dir: str = "") -> dict:
+    """Time and trace the three workloads; with dump_dir, also save each raw stamp array there (.npy)."""
     sys.path.insert(0, ROOT)
     sys.path.insert(0, PKG_PARENT)
     import numpy as np
@@ -165,6 +191,8 @@ def run() -> dict:
         fa.lib().flux_probe_set_trace(None)
         tr = trace.view(N_SLOTS, N_WAVES, N_STEPS, N_STAMPS).cpu().numpy().astype(np.int64)
         r = {"ms_untraced": round(ms_plain, 4), "ms_traced": round(ms_traced, 4), **_medians(tr)}
+        if dump_dir:
+            np.save(os.path.join(dump_dir, f"phase_trace_{name}.npy"), tr)
         if S == 8192:   # the traced copy computes the same attention as the library itself
             traced_out = o.clone()
             fa._lib = plain
@@ -185,7 +213,7 @@ if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "build":
         print(build())
     elif len(sys.argv) > 1 and sys.argv[1] == "run":
-        print(json.dumps(run()), flush=True)
+        print(json.dumps(run(sys.argv[2] if len(sys.argv) > 2 else "")), flush=True)
     else:
         print(__doc__)
         sys.exit(2)

@@ -202,10 +202,8 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ gbase, uint32
     using L = Lay<D>;
     const int key0 = kb * kBC;
     if (key0 + kBC - 1 <= last_key) {
-        const u16* t = uniform_ptr(gbase + (uint32_t)key0 * row_stride);
-#pragma unroll
-        for (int i = 0; i < L::INSTS_PER_WAVE; ++i)
-            load_lds_16(t, off[i], slot + (wave * L::INSTS_PER_WAVE + i) * 1024);
+        load_lds_run<L::INSTS_PER_WAVE>(uniform_ptr(gbase + (uint32_t)key0 * row_stride), off,
+                                        slot + wave * L::INSTS_PER_WAVE * 1024);
     } else {
 #pragma unroll
         for (int i = 0; i < L::INSTS_PER_WAVE; ++i) {
@@ -227,9 +225,7 @@ __device__ __forceinline__ void issue_k(const u16* __restrict__ gbase, uint32_t 
     using L = Lay<D>;
     const int key0 = kb * kBC;
     if (key0 + kBC - 1 <= last_key) {
-        const u16* t = uniform_ptr(gbase + (uint32_t)key0 * row_stride);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) load_lds_16(t, off[i], slot + (first + i) * 1024);
+        if constexpr (NI > 0) load_lds_run<NI>(uniform_ptr(gbase + (uint32_t)key0 * row_stride), off, slot + first * 1024);
     } else {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -286,12 +282,13 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     for (int i = 0; i < L::INSTS_PER_WAVE; ++i) {
         const int row = (wave * L::INSTS_PER_WAVE + i) * L::ROWS_PER_INST + lane / L::CH;
         const int pch = lane % L::CH;
-        voff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz_v<D>(row)));
+        voff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz_v<D>(row))) - 1024 * i;   // see load_lds_run
     }
-    // Each step opens with every wave issuing its share of the next tiles' direct loads (~100 cycles per
-    // instruction when all eight waves issue together), and group 1 then runs the softmax phase, the
-    // longer of the two first phases: at head_dim 128 the waves of group 0 take 3 of the K tile's 16
-    // instructions each and those of group 1 take 1 (0.6-0.7% faster at seq 131072 dense than 2 and 2).
+    // Each step opens with every wave issuing its share of the next tiles' direct loads (one run per tile,
+    // ~60 cycles per instruction and wave when all eight waves issue together), and group 1 then runs the
+    // softmax phase, the longer of the two first phases: at head_dim 128 the waves of group 0 take 3 of
+    // the K tile's 16 instructions each and those of group 1 take 1 (0.6-0.7% faster at seq 131072 dense
+    // than 2 and 2 when each load set and restored M0 itself; within noise with the runs).
     constexpr int KI = L::TILE_B / 1024;          // K-tile instructions per workgroup
     constexpr int KA = D == 128 ? 3 : KI / 8;     // per wave of group 0 (matrix work first)
     constexpr int KB = (KI - 4 * KA) / 4;         // per wave of group 1
@@ -301,7 +298,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     for (int i = 0; i < 4; ++i) {
         const int row = (kfirst + i) * L::ROWS_PER_INST + lane / L::CH;
         const int pch = lane % L::CH;
-        koff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz_k<D>(row)));
+        koff[i] = 2 * (row * kv_row_stride + 8 * (pch ^ swz_k<D>(row))) - 1024 * i;   // see load_lds_run
     }
     const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
@@ -606,9 +603,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
                 else mwork(kOff, kOn, 0, 0);
                 __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of K(1), V(0) landed
                 __syncthreads();
-                // steps 1 .. T-1
-                int sl = 1;
-                while (have_n) {
+                // steps 1 .. T-1: step u reads K slot u&1 and V slot (u-1)&1 and loads into the others.
+                // Two steps per pass of the loop, so that each copy has its slots as constants and the
+                // branch back to the loop head comes once per two steps.
+                auto step = [&](auto slot_tag) {
+                    constexpr int sl = decltype(slot_tag)::value;
                     kb_p = kb_c;
                     mine_p = mine_c;
                     kb_c = kb_n;
@@ -626,7 +625,15 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
                     else mwork(kOn, kOn, sl ^ 1, sl);
                     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of K(u+1), V(u) landed
                     __syncthreads();
-                    sl ^= 1;
+                };
+                int sl = 1;   // the slot the next step's V goes to
+                while (have_n) {
+                    step(IntTag<1>{});
+                    if (!have_n) {
+                        sl = 0;
+                        break;
+                    }
+                    step(IntTag<0>{});
                 }
                 // final step: P.V of the last tile (its V is in slot sl ^ 1)
                 if constexpr (!kG1) mwork(kOn, kOff, sl ^ 1, 0);

@@ -39,6 +39,9 @@ def test_validation_before_launch(lib):
     assert lib.ceil_lds_dma_issue(16, 65536, 16, 16, 1, 4, 0, None) == HIP_INVALID_VALUE      # no active wave
     assert lib.ceil_lds_dma_issue(16, 65535, 16, 16, 1, 4, 8, None) == HIP_INVALID_VALUE      # source too small
     assert lib.ceil_lds_dma_issue(16, 65536, 16, 15, 1, 4, 8, None) == HIP_INVALID_VALUE      # out too small
+    assert lib.ceil_lds_dma_issue4(16, 65536, 16, 16, 1, 3, 8, None, 0, None) == HIP_INVALID_VALUE   # unknown form
+    assert lib.ceil_lds_dma_issue4(16, 65536, 16, 16, 1, 1, 9, None, 0, None) == HIP_INVALID_VALUE   # 9 waves
+    assert lib.ceil_lds_dma_issue4(16, 65536, 16, 16, 1, 1, 8, 16, 32767, None) == HIP_INVALID_VALUE  # check short
 
 
 @pytest.mark.gpu
@@ -81,3 +84,18 @@ def test_kernels_run(lib):
     torch.cuda.synchronize()
     t = out.view(4, 8, 2).cpu()
     assert bool((t[:, :3, 0] > 0).all()) and bool((t[:, :, 0] <= t[:, :, 1]).all())
+
+    # the four-load runs (M0 set once, immediate offsets 0..3072; or M0 set per load): every active wave's
+    # 4 KB of LDS holds bytes [8192*wave, +4096) of its workgroup's 64 KB, i.e. the immediate offset moved
+    # the LDS destination and the global source alike
+    src.copy_(torch.arange(src.numel(), device=dev, dtype=torch.int64).remainder(251).to(torch.uint8))
+    chk = torch.zeros(4 * 8 * 4096, dtype=torch.uint8, device=dev)
+    want = src.view(4, 8, 8192)[:, :, :4096].cpu()
+    for form in (1, 2):
+        chk.zero_()
+        assert lib.ceil_lds_dma_issue4(src.data_ptr(), src.numel(), out.data_ptr(), out.numel(), 4, form, 5,
+                                       chk.data_ptr(), chk.numel(), stream) == 0
+        torch.cuda.synchronize()
+        got = chk.view(4, 8, 4096).cpu()
+        assert torch.equal(got[:, :5], want[:, :5]), form
+        assert bool((got[:, 5:] == 0).all()) and bool((out.view(4, 8, 2)[:, :5, 0] > 0).all().cpu())
