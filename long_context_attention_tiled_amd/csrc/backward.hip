@@ -440,15 +440,19 @@ __host__ __device__ __forceinline__ int dkdv_sink_pairs(const BackwardArgs& a) {
 // 8 waves, two per SIMD, on 128 keys: waves w and w + 4 own the same 32 keys; wave w accumulates
 // dV^T, wave w + 4 dK^T.  Each takes a 64-query tile in two 32-query halves: wave w computes S (D/16
 // MFMAs) and P and hands P to wave w + 4 through LDS, which meanwhile computes dP (as many MFMAs) and
-// then dS; each then runs the 2 * D/32 MFMAs of its gradient product.  At D = 128 that is 32 + 32
-// MFMAs per SIMD and tile, S is computed once per key group, and each wave stays within 256
-// registers, so the two waves of a SIMD hide each other's vector work and LDS latency.
+// then dS; each runs the 2 * D/32 MFMAs of its gradient product, the dK wave one half late (at the start
+// of the next half, before its dP), so that the matrix core has the dK wave's product to run while the
+// dV wave computes exp2.  At D = 128 that is 32 + 32 MFMAs per SIMD and tile, S is computed once per
+// key group, and the two roles are compiled as separate code paths (191 registers at D = 128).
 constexpr int kKvWaves = 8;
+// Q/dO tile slots of the dK/dV pass: the tile in use, the next one in flight, and the previous one, whose
+// Q the dK waves still read during the current tile's first half (their gradient product runs one half late).
+constexpr int kKvSlots = 3;
 template <int D>
 __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs a) {
     using Gm = Geo<D>;
     constexpr int kNC = Gm::NC, kNM = Gm::NM, kTileB = Gm::TILE_B, kSlotB = Gm::SLOT_B;
-    __shared__ __attribute__((aligned(1024))) char smem[kSlots * kSlotB];
+    __shared__ __attribute__((aligned(1024))) char smem[kKvSlots * kSlotB];
     // P of one 32-query half, handed from the dV wave to the dK wave of each key group: two halves in
     // flight, [parity][key group][accumulator quad][lane] (lane-contiguous float4: conflict-free)
     __shared__ float4 pbuf[2][4][4][64];
@@ -522,109 +526,137 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
         };
         issue(h0, lo, 0);
 
-        // this lane's key row as the B operand (k-slots = d): K for the dV wave (S = Q K^T), V for the
-        // dK wave (dP = dO V^T)
-        f16x8 breg[kNC];
-        {
-            const int kc = min(key, seq - 1);
-            const int64_t off = (((int64_t)b * a.seq + kc) * a.hkv + g) * D + 8 * hh;
-            const u16* bp = reinterpret_cast<const u16*>(is_dk ? a.v16 : a.k16) + off;
+        // The rest of the unit, compiled once per role (dV: DK false, dK: DK true), so that each role's
+        // registers are allocated for its own code path.
+        auto role_body = [&](auto dk_tag) {
+            constexpr bool DK = decltype(dk_tag)::value;
+            // this lane's key row as the B operand (k-slots = d): K for the dV wave (S = Q K^T), V for the
+            // dK wave (dP = dO V^T)
+            f16x8 breg[kNC];
+            {
+                const int kc = min(key, seq - 1);
+                const int64_t off = (((int64_t)b * a.seq + kc) * a.hkv + g) * D + 8 * hh;
+                const u16* bp = reinterpret_cast<const u16*>(DK ? a.v16 : a.k16) + off;
 #pragma unroll
-            for (int c = 0; c < kNC; ++c) breg[c] = *reinterpret_cast<const f16x8*>(bp + 16 * c);
-        }
+                for (int c = 0; c < kNC; ++c) breg[c] = *reinterpret_cast<const f16x8*>(bp + 16 * c);
+            }
 
-        f32x16 acc[kNM];   // dV^T or dK^T: lane = key, rows d = 32mt + 8(r/4) + 4hh + r%4
+            f32x16 acc[kNM];   // dV^T or dK^T: lane = key, rows d = 32mt + 8(r/4) + 4hh + r%4
 #pragma unroll
-        for (int mt = 0; mt < kNM; ++mt) acc[mt] = f32x16{};
+            for (int mt = 0; mt < kNM; ++mt) acc[mt] = f32x16{};
+            // dK wave: dS16 of the previous half, whose gradient product runs at the start of the next half
+            // (beside the dV wave's S and exp2 rather than after the dV wave's product), with its Q tile
+            f16x8 dk_pend[2];
+            const char* pend_xt = smem;   // the Q tile of a pending second half
+            bool pend = false;            // a second half is pending (from the previous tile)
 
-        // One tile, in two 32-query halves.  The dV wave computes S, P16 = P 2^14 (exp2 of the scaled
-        // score minus the row's LSE, plus 14; zero where masked) and publishes it in LDS; the dK wave
-        // computes dP meanwhile, and after the barrier forms dS16 = P16 (dP16 2^-37 - D') from the
-        // published P16.  Then each runs its gradient product.  Elements with C < lim are masked
-        // (C = query - 64t - 4hh).  S is computed once per key group (32 + 32 MFMAs per SIMD and tile
-        // at D = 128), and the barrier staggers the two waves of a SIMD: one runs its gradient product's
-        // MFMAs while the other does its vector work.
-        auto tile = [&](const char* qt, int lim, bool need_mask) {
-            const char* dot = qt + kTileB;
-            const char* st = qt + 2 * kTileB;
-            const char* xt = is_dk ? qt : dot;   // tile read transposed for the gradient product
+            // One tile, in two 32-query halves.  The dV wave computes S, P16 = P 2^14 (exp2 of the scaled
+            // score minus the row's LSE, plus 14; zero where masked) and publishes it in LDS; the dK wave
+            // computes dP meanwhile, and after the barrier forms dS16 = P16 (dP16 2^-37 - D') from the
+            // published P16.  Then the dV wave runs its gradient product beside the dK wave's dS; the dK
+            // wave's product of that half runs at the start of the next half, beside the dV wave's S and
+            // exp2 (the unit's last one after its last tile).  Elements with C < lim are masked
+            // (C = query - 64t - 4hh).
+            auto tile = [&](const char* qt, int lim, bool need_mask) {
+                const char* dot = qt + kTileB;
+                const char* st = qt + 2 * kTileB;
+                const char* xt = DK ? qt : dot;   // tile read transposed for the gradient product
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                f32x16 sd = f32x16{};   // S (dV wave) or dP (dK wave)
-                mfma_seq<kNC>([&](int i) { return L.row(is_dk ? dot : qt, hf, i); },
-                              [&](int i, f16x8 op) { sd = MFMA(op, breg[i], sd); });
-                float x[16];   // P16, then dS16 for the dK wave
-                if (!is_dk) {
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const float4 nl = *reinterpret_cast<const float4*>(st + 4 * (32 * hf + 8 * g4 + 4 * hh));
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            x[4 * g4 + e] = __builtin_amdgcn_exp2f(fmaf(sd[4 * g4 + e], c2, comp(nl, e)));
+                for (int hf = 0; hf < 2; ++hf) {
+                    if constexpr (DK) {
+                        if (hf == 1) grad_product(L, xt, 0, dk_pend, acc);   // this tile's first half
+                        else if (pend) grad_product(L, pend_xt, 2, dk_pend, acc);
                     }
-                    if (need_mask) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    f32x16 sd = f32x16{};   // S (dV wave) or dP (dK wave)
+                    mfma_seq<kNC>([&](int i) { return L.row(DK ? dot : qt, hf, i); },
+                                  [&](int i, f16x8 op) { sd = MFMA(op, breg[i], sd); });
+                    float x[16];   // P16, then dS16 for the dK wave
+                    if constexpr (!DK) {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) x[r] = (32 * hf + 8 * (r >> 2) + (r & 3) < lim) ? 0.0f : x[r];
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const float4 nl = *reinterpret_cast<const float4*>(st + 4 * (32 * hf + 8 * g4 + 4 * hh));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                x[4 * g4 + e] = __builtin_amdgcn_exp2f(fmaf(sd[4 * g4 + e], c2, comp(nl, e)));
+                        }
+                        if (need_mask) {
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) x[r] = (32 * hf + 8 * (r >> 2) + (r & 3) < lim) ? 0.0f : x[r];
+                        }
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4)
+                            pbuf[par][ks][g4][lane] = float4{x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]};
                     }
+                    __syncthreads();   // P of this half published
+                    if constexpr (DK) {
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const float4 p = pbuf[par][ks][g4][lane];
+                            const float4 dd = *reinterpret_cast<const float4*>(st + 256 + 4 * (32 * hf + 8 * g4 + 4 * hh));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                x[4 * g4 + e] = comp(p, e) * fmaf(sd[4 * g4 + e], 0x1p-37f, -comp(dd, e));
+                        }
+                    }
+                    par ^= 1;
+                    if constexpr (!DK) {
+                        f16x8 x16[2];
+                        to_f16(x, x16);
+                        grad_product(L, xt, 2 * hf, x16, acc);
+                    } else {
+                        to_f16(x, dk_pend);
+                        if (hf == 1) {
+                            pend_xt = xt;
+                            pend = true;
+                        }
+                    }
+                }
+            };
+
+            int slot = 0, t = lo, h = h0;
+            for (int i = 0; i < nsteps; ++i) {
+                const int t_next = t < hi ? t + 1 : lo, h_next = t < hi ? h : h + 1;
+                const int slot_next = slot == kKvSlots - 1 ? 0 : slot + 1;
+                __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's share of tile t landed
+                __syncthreads();   // tile t complete; every wave is done with tile t-2 (the dK waves with t-1)
+                if (i + 1 < nsteps) issue(h_next, t_next, slot_next);
+                else queue.prefetch();   // the next unit is taken when this one ends (keeps the queue dynamic)
+                const char* qt = smem + slot * kSlotB;
+                // masked iff query < key, i.e. C < lim with C = query - 64t - 4hh
+                int lim = key - 64 * t - 4 * hh;
+                if (!a.causal) lim = -1000;
+                else if (a.sparse && kb >= a.sink_blocks && t - kb >= a.window_blocks) lim = 1000;
+                // this wave masks something only on its diagonal tile, on tiles before it, and on tiles the
+                // sparse pattern hides from its key block
+                const bool need_mask = a.causal && (t <= kb || lim == 1000);
+                tile(qt, lim, need_mask);
+                slot = slot_next;
+                t = t_next;
+                h = h_next;
+            }
+            if constexpr (DK)
+                if (pend) grad_product(L, pend_xt, 2, dk_pend, acc);   // the unit's last half
+
+            // lane holds column key, rows d = 32mt + 8(r/4) + 4hh + r%4
+            if (key < seq) {
+                float* dst;
+                if (!partial) dst = (DK ? a.dk : a.dv) + (((int64_t)b * a.seq + key) * a.hkv + g) * D;
+                else dst = (DK ? a.dk_part : a.dv_part) + (((int64_t)b * a.part_keys + key) * a.hq + h0) * D;
+                // dK = scale 2^(eS + eQ) acc with eS = 23 + eDO + eV; dV = 2^(eDO - 14) acc
+                const float f = DK ? a.scale : 1.0f;
+                const int ex = DK ? 23 + eDO + eV + eQ : eDO - 14;
+#pragma unroll
+                for (int mt = 0; mt < kNM; ++mt)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4)
-                        pbuf[par][ks][g4][lane] = float4{x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]};
-                }
-                __syncthreads();   // P of this half published
-                if (is_dk) {
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const float4 p = pbuf[par][ks][g4][lane];
-                        const float4 dd = *reinterpret_cast<const float4*>(st + 256 + 4 * (32 * hf + 8 * g4 + 4 * hh));
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            x[4 * g4 + e] = comp(p, e) * fmaf(sd[4 * g4 + e], 0x1p-37f, -comp(dd, e));
-                    }
-                }
-                par ^= 1;
-                f16x8 x16[2];
-                to_f16(x, x16);
-                grad_product(L, xt, 2 * hf, x16, acc);
+                        *reinterpret_cast<float4*>(dst + 32 * mt + 8 * g4 + 4 * hh) =
+                            float4{ldexpf(f * acc[mt][4 * g4], ex), ldexpf(f * acc[mt][4 * g4 + 1], ex),
+                                   ldexpf(f * acc[mt][4 * g4 + 2], ex), ldexpf(f * acc[mt][4 * g4 + 3], ex)};
             }
         };
-
-        int slot = 0, t = lo, h = h0;
-        for (int i = 0; i < nsteps; ++i) {
-            const int t_next = t < hi ? t + 1 : lo, h_next = t < hi ? h : h + 1;
-            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's share of tile t landed
-            __syncthreads();                       // tile t complete; every wave is done with tile t-1
-            if (i + 1 < nsteps) issue(h_next, t_next, slot ^ 1);
-            else queue.prefetch();   // the next unit is taken when this one ends (keeps the queue dynamic)
-            const char* qt = smem + slot * kSlotB;
-            // masked iff query < key, i.e. C < lim with C = query - 64t - 4hh
-            int lim = key - 64 * t - 4 * hh;
-            if (!a.causal) lim = -1000;
-            else if (a.sparse && kb >= a.sink_blocks && t - kb >= a.window_blocks) lim = 1000;
-            // this wave masks something only on its diagonal tile, on tiles before it, and on tiles the
-            // sparse pattern hides from its key block
-            const bool need_mask = a.causal && (t <= kb || lim == 1000);
-            tile(qt, lim, need_mask);
-            slot ^= 1;
-            t = t_next;
-            h = h_next;
-        }
-
-        // lane holds column key, rows d = 32mt + 8(r/4) + 4hh + r%4
-        if (key < seq) {
-            float* dst;
-            if (!partial) dst = (is_dk ? a.dk : a.dv) + (((int64_t)b * a.seq + key) * a.hkv + g) * D;
-            else dst = (is_dk ? a.dk_part : a.dv_part) + (((int64_t)b * a.part_keys + key) * a.hq + h0) * D;
-            // dK = scale 2^(eS + eQ) acc with eS = 23 + eDO + eV; dV = 2^(eDO - 14) acc
-            const float f = is_dk ? a.scale : 1.0f;
-            const int ex = is_dk ? 23 + eDO + eV + eQ : eDO - 14;
-#pragma unroll
-            for (int mt = 0; mt < kNM; ++mt)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4)
-                    *reinterpret_cast<float4*>(dst + 32 * mt + 8 * g4 + 4 * hh) =
-                        float4{ldexpf(f * acc[mt][4 * g4], ex), ldexpf(f * acc[mt][4 * g4 + 1], ex),
-                               ldexpf(f * acc[mt][4 * g4 + 2], ex), ldexpf(f * acc[mt][4 * g4 + 3], ex)};
-        }
+        if (is_dk) role_body(BoolTag<true>{});
+        else role_body(BoolTag<false>{});
         __syncthreads();   // every wave is done with the slots before the next unit loads into them
         u = queue.next();
     }
@@ -634,7 +666,8 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
 //
 // 4 waves of 32 queries, two workgroups per CU (two waves per SIMD).  A 64-key tile is taken in two
 // 32-key halves: S^T and dP^T (D/8 MFMAs, K and V rows from LDS, Q and dO rows in registers), the
-// vector work, then 2 * D/32 MFMAs of dQ^T += K^T dS^T.
+// vector work, then 2 * D/32 MFMAs of dQ^T += K^T dS^T; the first half's product runs after the second
+// half's S^T and dP^T, beside its vector work (0.8% faster than in order).
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
     using Gm = Geo<D>;
@@ -716,6 +749,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
         // unmasked tiles (the mask is a short branch): two bodies would cost registers and spill.
         auto tile = [&](const char* kt, int lim, bool need_mask) {
             const char* vt = kt + kTileB;
+            f16x8 pend16[2];   // dS16 of the first half: its product runs beside the second half's vector work
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 // S^T = K Q^T, dP^T = V dO^T: lane = query n, registers = keys 32kh + 8(r/4) + 4hh + r%4
@@ -724,6 +758,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
                     if (i < kNC) s = MFMA(op, qreg[i], s);
                     else dp = MFMA(op, doreg[i - kNC], dp);
                 });
+                if (kh == 1) grad_product(L, kt, 0, pend16, dq);
                 float x[16];   // P16 = P 2^14, then dS16 = P16 (dP16 2^-37 - D')
 #pragma unroll
                 for (int r = 0; r < 16; ++r) x[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, nl));
@@ -733,9 +768,13 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) x[r] *= fmaf(dp[r], 0x1p-37f, -dd);
-                f16x8 x16[2];
-                to_f16(x, x16);
-                grad_product(L, kt, 2 * kh, x16, dq);   // dQ^T += K^T dS16^T
+                if (kh == 0) {
+                    to_f16(x, pend16);
+                } else {
+                    f16x8 x16[2];
+                    to_f16(x, x16);
+                    grad_product(L, kt, 2, x16, dq);   // dQ^T += K^T dS16^T
+                }
             }
         };
 

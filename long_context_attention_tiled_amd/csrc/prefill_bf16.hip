@@ -93,10 +93,6 @@ struct Lay {
 // blocks the CSR of flux_build_block_mask lists (kSparse walks that CSR with scalar loads each step).
 enum Mode { kDenseCausal = 0, kDenseFull = 1, kSparse = 2, kRouted = 3, kSoft = 4, kSparseArith = 5 };
 
-template <bool B>
-struct BoolTag {
-    static constexpr bool value = B;
-};
 
 // Walks the key tiles of a workgroup, whose query rows span the 64-row query blocks
 // qb_base .. qb_base + nrows - 1 (nrows = 2 or 4): dense -- tiles 0..last; sparse -- the

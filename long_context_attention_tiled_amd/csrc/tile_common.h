@@ -109,7 +109,13 @@ __device__ __forceinline__ void load_lds_run(const void* sbase, const uint32_t* 
     }
 }
 
-// An int as a type, for lambdas that take a compile-time constant (a buffer slot) as an argument.
+// A bool and an int as types, for lambdas that take a compile-time constant (a role, a buffer slot) as
+// an argument.
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 template <int N>
 struct IntTag {
     static constexpr int value = N;
