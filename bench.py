@@ -739,6 +739,21 @@ def run_microbench(torch, dev):
     torch.cuda.synchronize()
     out["lds_dma_issue_cycles_4_loads_x_8_waves_one_m0_write"] = float(np.median(cyc.view(wgs, 8, 2)[:, :, 0].cpu().numpy()))
     del src, cyc
+
+    # LDS read rate per CU (bytes per shader clock): one 8-wave workgroup per CU, and two sharing each CU
+    sink = torch.zeros(512, dtype=torch.int32, device=dev)
+    for per_cu in (1, 2):
+        n = cu.value * per_cu
+        o = torch.zeros(n * 16, dtype=torch.int64, device=dev)
+        for form, name in ((0, "b128"), (1, "b64_tr_b16")):
+            for _ in range(2):
+                ceilings.check(lib.ceil_lds_read(o.data_ptr(), o.numel(), sink.data_ptr(), sink.numel(), n, form,
+                                                 2000, stream), "ceil_lds_read")
+            torch.cuda.synchronize()
+            t = o.view(n, 8, 2).cpu().numpy()
+            bw = t[:, :, 1].sum(axis=1) / t[:, :, 0].max(axis=1)
+            out[f"lds_read_{name}_B_per_clk_per_cu_{per_cu}_wg"] = round(float(np.median(bw)) * per_cu, 1)
+        del o
     return out
 
 

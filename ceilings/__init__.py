@@ -19,6 +19,7 @@ SIGNATURES = {
     "ceil_read_decode": (ctypes.c_int, [_p, _p, _i64, _i64, _i32, _i32, _p, _i64, _p]),
     "ceil_lds_dma_issue": (ctypes.c_int, [_p, _i64, _p, _i64, _i32, _i32, _i32, _p]),
     "ceil_lds_dma_issue4": (ctypes.c_int, [_p, _i64, _p, _i64, _i32, _i32, _i32, _p, _i64, _p]),
+    "ceil_lds_read": (ctypes.c_int, [_p, _i64, _p, _i64, _i32, _i32, _i32, _p]),
 }
 
 

@@ -228,6 +228,45 @@ __global__ __launch_bounds__(kDmaThreads) void lds_dma_issue4_kernel(const char*
     }
 }
 
+// LDS read bandwidth: 8 waves (one workgroup per CU) read a 64 KB LDS buffer in a loop, iters x 8 reads
+// per wave, conflict-free (each read instruction covers consecutive 16-byte or 8-byte lane addresses),
+// the values folded into a register so that no read is dropped.  FORM 0: ds_read_b128 (1 KB per
+// instruction); FORM 1: ds_read_b64_tr_b16, the transposing read of the prefill's V operand (512 B).
+// out[(wg*8 + wave)*2] = s_memtime cycles of the loop, [+1] = bytes this wave read.
+typedef short lds_i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) lds_i16x4_t lds_i16x4_p;
+template <int FORM>
+__global__ __launch_bounds__(512) void lds_read_kernel(uint64_t* out, uint32_t* sink, int iters) {
+    __shared__ __attribute__((aligned(1024))) uint4 buf[4096];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < 4096; i += 512) buf[i] = make_uint4(i, 3u * i, 5u * i, 7u * i);
+    __syncthreads();
+    uint32_t acc = 0;
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int blk = (it * 8 + j + wave * 5) & 63;   // a 1 KB block of the buffer
+            if constexpr (FORM == 0) {
+                const uint4 v = buf[blk * 64 + lane];
+                acc ^= v.x ^ v.y ^ v.z ^ v.w;
+            } else {
+                const char* p = reinterpret_cast<const char*>(buf) + blk * 1024 + lane * 8;
+                const lds_i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p*)(p));
+                acc ^= (uint32_t)(uint16_t)v[0] ^ ((uint32_t)(uint16_t)v[1] << 16) ^ (uint32_t)(uint16_t)v[2] ^
+                       ((uint32_t)(uint16_t)v[3] << 16);
+            }
+        }
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    __syncthreads();
+    if (lane == 0) {
+        out[((int64_t)blockIdx.x * 8 + wave) * 2] = t1 - t0;
+        out[((int64_t)blockIdx.x * 8 + wave) * 2 + 1] = (uint64_t)iters * 8 * (FORM == 0 ? 1024 : 512);
+    }
+    if (acc == 0x9e3779b9u) sink[threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -322,6 +361,22 @@ int ceil_lds_dma_issue4(const void* src, int64_t src_bytes, uint64_t* out, int64
     else
         hipLaunchKernelGGL(lds_dma_issue4_kernel<2>, dim3(workgroups), dim3(kDmaThreads), 0,
                            reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const char*>(src), out, active_waves, c);
+    return (int)hipGetLastError();
+}
+
+// LDS read bandwidth (form 0: ds_read_b128, 1: ds_read_b64_tr_b16).  out: >= workgroups * 16 uint64;
+// sink: >= 512 uint32 (device; written only in the impossible case that keeps the reads alive).
+int ceil_lds_read(uint64_t* out, int64_t out_elems, uint32_t* sink, int64_t sink_elems, int32_t workgroups,
+                  int32_t form, int32_t iters, void* stream) {
+    if (!out || !sink || workgroups < 1 || (form != 0 && form != 1) || iters < 1 ||
+        out_elems < (int64_t)workgroups * 16 || sink_elems < 512)
+        return (int)hipErrorInvalidValue;
+    if (form == 0)
+        hipLaunchKernelGGL(lds_read_kernel<0>, dim3(workgroups), dim3(512), 0, reinterpret_cast<hipStream_t>(stream),
+                           out, sink, iters);
+    else
+        hipLaunchKernelGGL(lds_read_kernel<1>, dim3(workgroups), dim3(512), 0, reinterpret_cast<hipStream_t>(stream),
+                           out, sink, iters);
     return (int)hipGetLastError();
 }
 

@@ -42,6 +42,9 @@ def test_validation_before_launch(lib):
     assert lib.ceil_lds_dma_issue4(16, 65536, 16, 16, 1, 3, 8, None, 0, None) == HIP_INVALID_VALUE   # unknown form
     assert lib.ceil_lds_dma_issue4(16, 65536, 16, 16, 1, 1, 9, None, 0, None) == HIP_INVALID_VALUE   # 9 waves
     assert lib.ceil_lds_dma_issue4(16, 65536, 16, 16, 1, 1, 8, 16, 32767, None) == HIP_INVALID_VALUE  # check short
+    assert lib.ceil_lds_read(16, 16, 16, 512, 1, 2, 10, None) == HIP_INVALID_VALUE      # unknown form
+    assert lib.ceil_lds_read(16, 15, 16, 512, 1, 0, 10, None) == HIP_INVALID_VALUE      # out too small
+    assert lib.ceil_lds_read(16, 16, 16, 511, 1, 0, 10, None) == HIP_INVALID_VALUE      # sink too small
 
 
 @pytest.mark.gpu
@@ -99,3 +102,13 @@ def test_kernels_run(lib):
         got = chk.view(4, 8, 4096).cpu()
         assert torch.equal(got[:, :5], want[:, :5]), form
         assert bool((got[:, 5:] == 0).all()) and bool((out.view(4, 8, 2)[:, :5, 0] > 0).all().cpu())
+
+    # LDS read loop: every wave reports a positive cycle count and the bytes its 10 x 8 reads cover
+    sink = torch.zeros(512, dtype=torch.int32, device=dev)
+    for form, per_read in ((0, 1024), (1, 512)):
+        out.zero_()
+        assert lib.ceil_lds_read(out.data_ptr(), out.numel(), sink.data_ptr(), sink.numel(), 4, form, 10,
+                                 stream) == 0
+        torch.cuda.synchronize()
+        t = out.view(4, 8, 2).cpu()
+        assert bool((t[:, :, 0] > 0).all()) and bool((t[:, :, 1] == 10 * 8 * per_read).all()), form
