@@ -38,8 +38,10 @@
 //     4x4 blocks of 16-bit elements across lanes: every lane receives 4 keys of its
 //     own d column per read, so V never needs a transposed copy.
 //   * two LDS slots for K and two for V; K runs one tile ahead of V: at the start of
-//     step u the loads of K(u+1) and V(u) are issued and they only have to land by
-//     the end of step u (two phases later).
+//     step u the loads of K(u+1) and V(u) are issued (each wave's share of a tile as
+//     one run of loads with M0 set once) and they only have to land by the end of
+//     step u (two phases later).  The tile loop runs two steps per pass, so that each
+//     copy of the step has its slots as constants.
 //   * exp2 with scale*log2(e) folded into one FMA.  The running maximum is raised
 //     only when some row's new maximum exceeds it by more than 8 (log2 units):
 //     until then probabilities up to 2^8 are accumulated against the old
