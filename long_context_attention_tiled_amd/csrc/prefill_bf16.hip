@@ -390,6 +390,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     bf16x8 pb[2][2];
     float m_run = kNegBig, l_run = 0.0f;
     const float c2 = a.scale_log2;
+    const float slack_s = kRescaleSlack / c2;   // the slack in score units
+    float m_thr = kNegBig;                       // m_run + slack_s (kNegBig absorbs the slack)
     bool snapped = false;   // kSoft: this wave's block-sparse output has been written to soft_ws
 
     // kSoft: the rows' block-sparse output O / l over the tiles accumulated so far (the row's sink and
@@ -495,14 +497,17 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
         }
+        // row max as a chain of v_maximum3_f32 (the IEEE maximum needs no canonicalising of the MFMA
+        // results, which fmaxf's maxnum does; the scores are finite or -inf, where the two agree)
         float mx = sacc[0][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+        for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sacc[0][r]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+        for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sacc[1][r]);
         mx = max_halves(mx);
-        // raise the reference max only when some row outgrows it by more than the slack
-        if (__ballot((mx - m_run) * c2 > kRescaleSlack)) {
+        // raise the reference max only when some row outgrows it by more than the slack, i.e. exceeds
+        // m_thr = m_run + slack / c2 (c2 > 0)
+        if (__ballot(mx > m_thr)) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
             l_run *= alpha;
@@ -511,6 +516,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[mt][r] *= alpha;
             m_run = m_new;
+            m_thr = m_new + slack_s;
         }
         const float mc = m_run * c2;
         float lsum[2][2];
@@ -645,6 +651,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
 #pragma unroll
             for (int mt = 0; mt < NM; ++mt) oacc[mt] = f32x16{};
             m_run = kNegBig;
+            m_thr = kNegBig;
             l_run = 0.0f;
             snapped = false;
             begin_unit(vb);

@@ -144,7 +144,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 __device__ __forceinline__ float max_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));   // no canonicalising
 }
 
 // Bijection blockIdx -> logical work id that keeps consecutive logical ids on one
