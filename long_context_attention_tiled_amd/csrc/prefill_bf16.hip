@@ -100,9 +100,16 @@ enum Mode { kDenseCausal = 0, kDenseFull = 1, kSparse = 2, kRouted = 3, kSoft = 
 // qb_base .. qb_base + nrows - 1 (nrows = 2 or 4): dense -- tiles 0..last; sparse -- the
 // sorted union of those blocks' CSR rows.  next() also returns which of the query
 // blocks use the tile (bit r: block qb_base + r).
+// Row bits [lo, 4) (lo <= 4) and [0, hi) (hi >= 0) of a 4-row mask: integer arithmetic on workgroup-
+// uniform values, which stays on the scalar unit (a bool turned into a bit costs a vector select per
+// row, and a clamp from both sides is selected as a vector med3).
+__device__ __forceinline__ uint32_t rows_from(int lo) { return (0xFu << max(lo, 0)) & 0xFu; }
+__device__ __forceinline__ uint32_t rows_below(int hi) { return (1u << min(hi, 4)) - 1u; }
+
 template <int MODE>
 struct TileWalk {
     int next_kb, last_kb, qb_base, nvalid;
+    uint32_t valid;   // rows of the workgroup inside the sequence: bits [0, nvalid)
     int p0, p1, p2, p3, e0, e1, e2, e3;   // CSR cursors and ends of the (up to 4) query blocks
     int n_sink, desc_lo, sink_b, win_b;   // kSoft / kSparseArith: sink tiles, lowest window tile, sink and
                                           // window blocks
@@ -113,6 +120,7 @@ struct TileWalk {
                          int wb = 0) {
         qb_base = qb_base_;
         nvalid = max(0, min(nrows, n_qblk - qb_base));
+        valid = rows_below(nvalid);
         ci = ci_;
         next_kb = 0;
         last_kb = MODE == kDenseFull ? n_qblk - 1 : qb_base + nvalid - 1;
@@ -159,12 +167,10 @@ struct TileWalk {
             kb = next_kb < n_sink ? next_kb : max(next_kb, desc_lo);
             if (kb > last_kb) return false;
             next_kb = kb + 1;
-            in = 0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int I = qb_base + r;   // query block r of the workgroup: kb <= I, sink or within the window
-                in |= (uint32_t)(r < nvalid && kb <= I && (kb < sink_b || I - kb < win_b)) << r;
-            }
+            // query block I = qb_base + r of the workgroup uses the tile iff kb <= I and (kb is a sink
+            // block or I - kb < win_b): rows r >= kb - qb_base, and r < kb - qb_base + win_b unless sink
+            const int d = kb - qb_base;
+            in = valid & rows_from(d) & (kb < sink_b ? 0xFu : rows_below(d + win_b));
             return true;
         } else {
             if constexpr (MODE == kSoft) {
@@ -179,10 +185,7 @@ struct TileWalk {
                 if (next_kb > last_kb) return false;
                 kb = next_kb++;
             }
-            in = 0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                in |= (uint32_t)(r < nvalid && (MODE == kDenseFull || kb <= qb_base + r)) << r;
+            in = MODE == kDenseFull ? valid : valid & rows_from(kb - qb_base);   // causal: rows r >= kb - qb_base
             return true;
         }
     }
