@@ -147,7 +147,7 @@ struct TileWalk {
         }
     }
 
-    __device__ bool next(int& kb, uint32_t& in) {
+    __device__ int next(int& kb, uint32_t& in) {   // 1: kb and in hold the next tile; 0: the walk is over
         if constexpr (sparse) {
             const int big = 0x7fffffff;
             const int c0 = p0 < e0 ? ci[p0] : big;
@@ -165,13 +165,14 @@ struct TileWalk {
             return true;
         } else if constexpr (MODE == kSparseArith) {
             kb = next_kb < n_sink ? next_kb : max(next_kb, desc_lo);
-            if (kb > last_kb) return false;
-            next_kb = kb + 1;
+            // branch-free on scalars (an early return would make the result a lane mask): have = kb <= last_kb
+            const int have = (int)(((uint32_t)(last_kb - kb) >> 31) ^ 1u);
+            next_kb = have ? kb + 1 : next_kb;
             // query block I = qb_base + r of the workgroup uses the tile iff kb <= I and (kb is a sink
             // block or I - kb < win_b): rows r >= kb - qb_base, and r < kb - qb_base + win_b unless sink
-            const int d = kb - qb_base;
+            const int d = have ? kb - qb_base : 4;   // kb - qb_base <= 3 when the tile exists
             in = valid & rows_from(d) & (kb < sink_b ? 0xFu : rows_below(d + win_b));
-            return true;
+            return have;
         } else {
             if constexpr (MODE == kSoft) {
                 const int i = next_kb;   // position in the walk
@@ -181,12 +182,17 @@ struct TileWalk {
                 else kb = sink_b + (i - n_sink - n_desc);
                 if (i >= n_sink + n_desc && kb >= min(desc_lo, last_kb + 1)) return false;
                 ++next_kb;
+                in = MODE == kDenseFull ? valid : valid & rows_from(kb - qb_base);
+                return true;
             } else {
-                if (next_kb > last_kb) return false;
-                kb = next_kb++;
+                // branch-free on scalars (an early return would make the result a lane mask)
+                kb = next_kb;
+                const int have = (int)(((uint32_t)(last_kb - kb) >> 31) ^ 1u);   // kb <= last_kb
+                next_kb += have;
+                // causal: rows r >= kb - qb_base (<= nvalid <= 4 even one past the last tile)
+                in = MODE == kDenseFull ? valid : valid & rows_from(kb - qb_base);
+                return have;
             }
-            in = MODE == kDenseFull ? valid : valid & rows_from(kb - qb_base);   // causal: rows r >= kb - qb_base
-            return true;
         }
     }
 };
@@ -316,7 +322,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     TileWalk<MODE> walk;
     uint32_t in;
     int kb_p = 0, kb_c = 0, kb_n = 0;
-    bool mine_p = false, mine_c = false, mine_n = false, have_any = false, have_n = false;
+    bool mine_p = false, mine_c = false, mine_n = false, have_any = false;
+    int have_n = 0;   // an int rather than a bool, kept on the scalar unit across the loop's blocks
 
     // Set up unit vb and issue its first loads (K of its first tile into K slot 0, its Q rows into
     // registers).  Called before the first unit and, for the next unit, after the current unit's
@@ -356,7 +363,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
         walk.init(qb_base, nrows, a.n_qblk, a.row_ptr, a.col_idx, a.sink_blocks, a.window_blocks);
         have_any = walk.next(kb_c, in);      // uniform over the workgroup; true for every valid launch
         mine_c = have_any && wave_live && ((in >> my_r) & 1);
-        have_n = have_any && walk.next(kb_n, in);
+        have_n = have_any ? walk.next(kb_n, in) : 0;
         mine_n = have_n && wave_live && ((in >> my_r) & 1);
         mine_p = false;
         if (have_any) issue_ktile(kb_c, smem_lds + L::K_BASE);
