@@ -12,12 +12,13 @@
 //
 // Kernels, in stream order:
 //   bwd_absmax_kernel     partial maxima of |x| of Q, K, V, dO per (batch, KV head) over token chunks
-//                         (one launch per tensor).
-//   bwd_convert_kernel    fp16 copies of Q, K, V, dO scaled by 2^-e per (batch, KV head) and tensor, e
-//                         chosen from those maxima so the largest magnitude lands in [2^14, 2^15).
+//                         (one launch for the four tensors).
+//   bwd_convert_kernel    fp16 copies of Q, K, V scaled by 2^-e per (batch, KV head) and tensor, e
+//                         chosen from those maxima so the largest magnitude lands in [2^14, 2^15); also
+//                         stores dO's e.
 //   bwd_rowstat_kernel    D and -LSE*log2(e) per query row, in 64-row tiles (rows past the end get
-//                         (-inf, 0), so they weigh nothing); clears the two work-queue heads.  It also
-//                         serves the float32 kernels of backward_f32.hip.
+//                         (-inf, 0), so they weigh nothing), and the fp16 copy of dO; clears the two
+//                         work-queue heads.  It also serves the float32 kernels of backward_f32.hip.
 //   bwd_dkdv_kernel       one work unit = 128 keys (4 groups of 32) of one KV head with its query heads
 //                         taken in turn (a single query head for the sink key pairs of block-sparse
 //                         GQA), 8 waves: per key group one wave accumulates dV, one dK; they walk the
@@ -200,7 +201,7 @@ struct Slice {
     int run;         // 16-byte vectors per token of the slice
 };
 
-// The tensor is a template parameter: each is its own launch, and no pointer is picked at run time.
+// The tensor is a template parameter (each a compile-time instance), so no pointer is picked at run time.
 template <int D, int T>
 __device__ __forceinline__ Slice slice_of(const BackwardArgs& a, int bg) {
     const int G = a.hq / a.hkv, b = bg / a.hkv, g = bg % a.hkv;
@@ -231,6 +232,16 @@ __device__ __forceinline__ int scale_exp(uint32_t m) {
     return (E > 1 ? E : 1) - 141;
 }
 
+// One 16-byte vector of 8 bf16 as 8 fp16 of x 2^-e (round to nearest even), element order kept.
+__device__ __forceinline__ uint4 to_f16_scaled(uint4 x, int e) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t y[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        y[q] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)ldexpf(bf16_lo(w[q]), -e), (_Float16)ldexpf(bf16_hi(w[q]), -e)});
+    return uint4{y[0], y[1], y[2], y[3]};
+}
+
 // Vector i of a slice (16 bytes, 8 elements): token i / run, vector i % run of that token.  A slice holds
 // at most seq * hq * d / 8 < 2^28 vectors, so 32-bit indices suffice.
 __device__ __forceinline__ int64_t vec_off(const Slice& sl, uint32_t i, int d) {
@@ -248,11 +259,10 @@ __device__ __forceinline__ uint32_t block_max(uint32_t m) {
     return max(max(wm[0], wm[1]), max(wm[2], wm[3]));
 }
 
-// grid (kAbsmaxChunks, B * Hkv) per tensor T: block (c, bg) reduces the vectors of tokens
-// [c seq / chunks, (c + 1) seq / chunks), four independent 16-byte loads in flight per thread.
+// Block (c, bg) of tensor T reduces the vectors of tokens [c seq / chunks, (c + 1) seq / chunks) of its
+// slice, four independent 16-byte loads in flight per thread.
 template <int D, int T>
-__global__ void __launch_bounds__(256) bwd_absmax_kernel(BackwardArgs a) {
-    const int c = blockIdx.x, bg = blockIdx.y;
+__device__ __forceinline__ void absmax_slice(const BackwardArgs& a, int c, int bg) {
     const Slice sl = slice_of<D, T>(a, bg);
     const uint32_t n0 = (uint32_t)(a.seq * c / kAbsmaxChunks) * sl.run;
     const uint32_t n1 = (uint32_t)(a.seq * (c + 1) / kAbsmaxChunks) * sl.run;
@@ -270,15 +280,33 @@ __global__ void __launch_bounds__(256) bwd_absmax_kernel(BackwardArgs a) {
     if (threadIdx.x == 0) a.amax[((int64_t)T * gridDim.y + bg) * kAbsmaxChunks + c] = m;
 }
 
-// Same grid: each block takes its slice's scale from the chunk maxima and converts its tokens.
-template <int D, int T>
-__global__ void __launch_bounds__(256) bwd_convert_kernel(BackwardArgs a) {
-    static_assert(kAbsmaxChunks <= 256, "one chunk maximum per thread");
+// grid (kAbsmaxChunks, B * Hkv, 4): blockIdx.z is the tensor (Q, K, V, dO), each case its own
+// compile-time instance, so no tensor pointer is picked by a run-time index.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_absmax_kernel(BackwardArgs a) {
     const int c = blockIdx.x, bg = blockIdx.y;
+    switch (blockIdx.z) {
+        case 0: absmax_slice<D, 0>(a, c, bg); break;
+        case 1: absmax_slice<D, 1>(a, c, bg); break;
+        case 2: absmax_slice<D, 2>(a, c, bg); break;
+        default: absmax_slice<D, 3>(a, c, bg); break;
+    }
+}
+
+// The scale exponent of tensor T for (batch, KV head) bg from its chunk maxima (every thread gets it).
+template <int T>
+__device__ __forceinline__ int slice_exp(const BackwardArgs& a, int bg) {
+    static_assert(kAbsmaxChunks <= 256, "one chunk maximum per thread");
+    return scale_exp(block_max(threadIdx.x < kAbsmaxChunks
+                                   ? a.amax[((int64_t)T * gridDim.y + bg) * kAbsmaxChunks + threadIdx.x]
+                                   : 0u));
+}
+
+// Converts block (c, bg)'s tokens of tensor T (Q, K or V) to fp16 scaled by 2^-e.
+template <int D, int T>
+__device__ __forceinline__ void convert_slice(const BackwardArgs& a, int c, int bg) {
     const Slice sl = slice_of<D, T>(a, bg);
-    const int e = scale_exp(block_max(threadIdx.x < kAbsmaxChunks
-                                          ? a.amax[((int64_t)T * gridDim.y + bg) * kAbsmaxChunks + threadIdx.x]
-                                          : 0u));
+    const int e = slice_exp<T>(a, bg);
     if (c == 0 && threadIdx.x == 0) a.exps[T * gridDim.y + bg] = e;
     const uint32_t n0 = (uint32_t)(a.seq * c / kAbsmaxChunks) * sl.run;
     const uint32_t n1 = (uint32_t)(a.seq * (c + 1) / kAbsmaxChunks) * sl.run;
@@ -290,21 +318,34 @@ __global__ void __launch_bounds__(256) bwd_convert_kernel(BackwardArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (i + 256 * j >= n1) break;
-            const uint32_t w[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
-            uint32_t y[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                y[q] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)ldexpf(bf16_lo(w[q]), -e),
-                                                          (_Float16)ldexpf(bf16_hi(w[q]), -e)});
-            *reinterpret_cast<uint4*>(sl.dst + vec_off(sl, i + 256 * j, D)) = uint4{y[0], y[1], y[2], y[3]};
+            *reinterpret_cast<uint4*>(sl.dst + vec_off(sl, i + 256 * j, D)) = to_f16_scaled(x[j], e);
         }
+    }
+}
+
+// Same grid: Q, K and V are converted here; dO is converted by the row statistics kernel, which reads it
+// anyway, so the blocks of z = 3 only store dO's exponent.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_convert_kernel(BackwardArgs a) {
+    const int c = blockIdx.x, bg = blockIdx.y;
+    switch (blockIdx.z) {
+        case 0: convert_slice<D, 0>(a, c, bg); break;
+        case 1: convert_slice<D, 1>(a, c, bg); break;
+        case 2: convert_slice<D, 2>(a, c, bg); break;
+        default:
+            if (c == 0) {
+                const int e = slice_exp<3>(a, bg);
+                if (threadIdx.x == 0) a.exps[3 * gridDim.y + bg] = e;
+            }
+            break;
     }
 }
 
 // ------------------------------------------------------------------ row statistics
 //
 // bf16 inputs (the fp16 matrix-core kernels): the row statistics are stored pre-scaled for them,
-// -LSE*log2(e) + 14 (P16 = P 2^14) and D 2^-(37 + eDO + eV) (so dS16 = P16 (dP16 2^-37 - D')).
+// -LSE*log2(e) + 14 (P16 = P 2^14) and D 2^-(37 + eDO + eV) (so dS16 = P16 (dP16 2^-37 - D')), and the
+// kernel writes the fp16 copy of dO, which it reads for D anyway.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_rowstat_kernel(BackwardArgs a) {
     constexpr int LPR = D / 8;            // lanes per row, 8 elements (16 bytes) each
@@ -330,6 +371,9 @@ __global__ void __launch_bounds__(256) bwd_rowstat_kernel(BackwardArgs a) {
             const uint4 x = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(a.d_o) + off);
             gv[0] = bf16_lo(x.x); gv[1] = bf16_hi(x.x); gv[2] = bf16_lo(x.y); gv[3] = bf16_hi(x.y);
             gv[4] = bf16_lo(x.z); gv[5] = bf16_hi(x.z); gv[6] = bf16_lo(x.w); gv[7] = bf16_hi(x.w);
+            // the fp16 copy of dO (the matrix-core kernels' operand) from the same load
+            const int bg = (int)b * a.hkv + h / (a.hq / a.hkv), nbg = (int)a.batch * a.hkv;
+            *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(a.do16) + off) = to_f16_scaled(x, a.exps[3 * nbg + bg]);
         }
         float o[8];
         if (a.o_f32) {
@@ -861,15 +905,9 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     const int64_t rows = a.batch * (int64_t)a.n_qblk * 64 * a.hq;
     constexpr int rpb = 256 / (D / 8);
     if (!a.in_f32) {   // fp16 copies for the matrix-core kernels; the row statistics read their scales
-        const dim3 grid(kAbsmaxChunks, (unsigned)(a.batch * a.hkv));
-        hipLaunchKernelGGL((bwd_absmax_kernel<D, 0>), grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_absmax_kernel<D, 1>), grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_absmax_kernel<D, 2>), grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_absmax_kernel<D, 3>), grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_convert_kernel<D, 0>), grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_convert_kernel<D, 1>), grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_convert_kernel<D, 2>), grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL((bwd_convert_kernel<D, 3>), grid, dim3(256), 0, s, a);
+        const dim3 grid(kAbsmaxChunks, (unsigned)(a.batch * a.hkv), 4);   // z: Q, K, V, dO
+        hipLaunchKernelGGL(bwd_absmax_kernel<D>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_convert_kernel<D>, grid, dim3(256), 0, s, a);
     }
     hipLaunchKernelGGL(bwd_rowstat_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, a);
     if (a.in_f32) return launch_backward_f32(a, s);   // float32 inputs: vector-ALU kernels
