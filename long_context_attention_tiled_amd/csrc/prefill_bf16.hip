@@ -81,7 +81,10 @@ struct Lay {
     static constexpr int TILE_B = kBC * ROW_B;             // bytes per K (or V) tile
     static constexpr int K_BASE = 0;                       // two K slots
     static constexpr int V_BASE = 2 * TILE_B;              // two V slots
-    static constexpr int SMEM_B = 4 * TILE_B;
+    static constexpr int STAGE_BASE = 4 * TILE_B;          // bf16 output stage: 32 rows per wave,
+    static constexpr int STAGE_ROW_B = ROW_B + 16;         // each padded by one chunk (bank spread)
+    static constexpr int STAGE_B = kWaves * 32 * STAGE_ROW_B;
+    static constexpr int SMEM_B = 4 * TILE_B + STAGE_B;
     static constexpr int ROWS_PER_INST = 1024 / ROW_B;     // rows one direct-load instruction fills
     static constexpr int INSTS_PER_WAVE = TILE_B / 1024 / kWaves;
     static_assert(INSTS_PER_WAVE * kWaves * 1024 == TILE_B, "tile split over the waves");
@@ -546,12 +549,26 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
         l_run += (lsum[0][0] + lsum[0][1]) + (lsum[1][0] + lsum[1][1]);
     };
 
-    // ---- epilogue of the current unit: O = O^T / l, lane holds O[qpos][32mt + 8(r/4) + 4hh + r%4]
+    // ---- epilogue of the current unit: O = O^T / l, lane holds O[qpos][32mt + 8(r/4) + 4hh + r%4].
+    // bf16 outputs (but the soft form's) pass through the wave's own LDS stage (32 rows, each padded by 16 bytes so that the
+    // row-wise writes and the chunk-wise reads both spread over the banks, with constant offsets) and
+    // leave as 16-byte stores of whole rows, 4 rows (1 KB) per instruction at head_dim 128, where the
+    // lane layout would give 8-byte stores to 32 rows per instruction.
     auto finish_unit = [&]() {
+        // the soft form writes directly: its mixing reads leave no registers for the stage
+        constexpr bool kStaged = !OUT_F32 && MODE != kSoft;
         const float l_tot = sum_halves(l_run);
-        if (!wave_live || qpos >= seq) return;
+        if (!wave_live) return;   // wave-uniform
+        const bool row_ok = qpos < seq;
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         const int64_t orow = ((int64_t)b * seq + qpos) * a.hq + h;
+        const int64_t orow_in = ((int64_t)b * seq + min(qpos, seq - 1)) * a.hq + h;
+        // the stage addresses are formed here from an opaque copy of the lane index: hoisted out of the
+        // unit loop they would hold registers across the whole tile loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int sn = ln & 31, shh = ln >> 5;
+        char* stage = smem + L::STAGE_BASE + wave * 32 * L::STAGE_ROW_B;
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt)
 #pragma unroll
@@ -562,7 +579,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
                 if constexpr (MODE == kSoft) {   // w_FA * dense + w_SA * block-sparse
                     const float w0 = a.mix_w[0], w1 = a.mix_w[1];
                     if (snapped) {
-                        const float4 f = *reinterpret_cast<const float4*>(a.soft_ws + orow * D + d);
+                        // rows past seq (never stored) read the last row instead: in bounds, no select
+                        const float4 f = *reinterpret_cast<const float4*>(a.soft_ws + orow_in * D + d);
                         v0 = fmaf(w1, f.x, w0 * v0);
                         v1 = fmaf(w1, f.y, w0 * v1);
                         v2 = fmaf(w1, f.z, w0 * v2);
@@ -576,15 +594,38 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
                     }
                 }
                 if constexpr (OUT_F32) {
-                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + orow * D + d) =
-                        make_float4(v0, v1, v2, v3);
+                    if (row_ok)
+                        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + orow * D + d) =
+                            make_float4(v0, v1, v2, v3);
+                } else if constexpr (!kStaged) {
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    if (row_ok)
+                        *reinterpret_cast<bf16x4*>(reinterpret_cast<u16*>(a.o) + orow * D + d) =
+                            bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
                 } else {
                     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                    bf16x4 pk = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-                    *reinterpret_cast<bf16x4*>(reinterpret_cast<u16*>(a.o) + orow * D + d) = pk;
+                    *reinterpret_cast<bf16x4*>(stage + sn * L::STAGE_ROW_B + 8 * shh + 2 * (d - 4 * hh)) =
+                        bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
                 }
             }
-        if (a.lse && hh == 0) {
+        if constexpr (kStaged) {
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's stage writes done
+            constexpr int kRowsPerRead = 64 / L::CH;   // rows one 1 KB read covers
+            const int c = ln % L::CH;
+            const int r0 = ln / L::CH;
+            const int rows_left = seq - (qpos - n) - r0;   // rows of this lane's column still inside seq
+            const int64_t step = (int64_t)kRowsPerRead * a.hq * D;
+            u16* op = reinterpret_cast<u16*>(a.o) + (((int64_t)b * seq + qpos - n + r0) * a.hq + h) * D + 8 * c;
+            const char* sp = stage + r0 * L::STAGE_ROW_B + 16 * c;
+#pragma unroll
+            for (int i = 0; i < 32 / kRowsPerRead; ++i) {
+                const uint4 val = *reinterpret_cast<const uint4*>(sp + i * kRowsPerRead * L::STAGE_ROW_B);
+                if (i * kRowsPerRead < rows_left) *reinterpret_cast<uint4*>(op) = val;
+                op += step;
+                __builtin_amdgcn_sched_barrier(0);   // one read, one store: no stage registers held
+            }
+        }
+        if (a.lse && hh == 0 && row_ok) {
             const float lse = l_tot > 0.0f ? (m_run * c2 + __log2f(l_tot)) * kLn2 : -INFINITY;
             a.lse[((int64_t)b * a.hq + h) * a.seq + qpos] = lse;
         }
