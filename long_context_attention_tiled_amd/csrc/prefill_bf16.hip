@@ -550,10 +550,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
     };
 
     // ---- epilogue of the current unit: O = O^T / l, lane holds O[qpos][32mt + 8(r/4) + 4hh + r%4].
-    // bf16 outputs (but the soft form's) pass through the wave's own LDS stage (32 rows, each padded by 16 bytes so that the
-    // row-wise writes and the chunk-wise reads both spread over the banks, with constant offsets) and
-    // leave as 16-byte stores of whole rows, 4 rows (1 KB) per instruction at head_dim 128, where the
-    // lane layout would give 8-byte stores to 32 rows per instruction.
+    // bf16 outputs (but the soft form's) pass through the wave's own LDS stage (32 rows, each padded by 16
+    // bytes so that the 16-byte row-wise writes and the chunk-wise reads both spread over the banks, with
+    // constant offsets) and leave as 16-byte stores of whole rows, 4 rows (1 KB) per instruction at
+    // head_dim 128, where the lane layout would give 8-byte stores to 32 rows per instruction.
     auto finish_unit = [&]() {
         // the soft form writes directly: its mixing reads leave no registers for the stage
         constexpr bool kStaged = !OUT_F32 && MODE != kSoft;
@@ -569,6 +569,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
         asm volatile("" : "+v"(ln));
         const int sn = ln & 31, shh = ln >> 5;
         char* stage = smem + L::STAGE_BASE + wave * 32 * L::STAGE_ROW_B;
+        uint32_t pa0 = 0, pa1 = 0;   // packed bf16 of the even r4 of a pair, until its odd partner
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt)
 #pragma unroll
@@ -603,9 +604,21 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, char* smem) {
                         *reinterpret_cast<bf16x4*>(reinterpret_cast<u16*>(a.o) + orow * D + d) =
                             bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
                 } else {
-                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                    *reinterpret_cast<bf16x4*>(stage + sn * L::STAGE_ROW_B + 8 * shh + 2 * (d - 4 * hh)) =
-                        bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                    // r4 pairs (2j, 2j + 1): one v_permlane32_swap per dword hands each lane 16 contiguous
+                    // bytes of its row (lanes 0-31 the pair's first 8 d values, lanes 32-63 its last 8), so
+                    // that the stage takes 16-byte writes, 16 rows per bank sweep
+                    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                    const uint32_t w0 = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v0, (__bf16)v1});
+                    const uint32_t w1 = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v2, (__bf16)v3});
+                    if ((r4 & 1) == 0) {
+                        pa0 = w0;
+                        pa1 = w1;
+                    } else {
+                        const auto x = __builtin_amdgcn_permlane32_swap(pa0, w0, false, false);
+                        const auto y = __builtin_amdgcn_permlane32_swap(pa1, w1, false, false);
+                        *reinterpret_cast<uint4*>(stage + sn * L::STAGE_ROW_B + 16 * (4 * mt + (r4 & 2) + shh)) =
+                            uint4{x[0], y[0], x[1], y[1]};
+                    }
                 }
             }
         if constexpr (kStaged) {
