@@ -468,6 +468,56 @@ __device__ __forceinline__ void grad_product(const Lanes<D>& L, const char* xt, 
     __builtin_amdgcn_s_setprio(0);
 }
 
+// Epilogue store of the fp32 gradient rows a wave holds in the transposed accumulator layout (lane l: row
+// l % 32 of the wave's 32 rows; acc[mt][4 g4 + e] is d = 32 mt + 8 g4 + 4 (l / 32) + e), each value
+// f * acc * 2^ex, through the wave's own LDS stage: 64 d values (256 bytes) of every row at a time, rows
+// padded to 272 bytes so that the 16-byte writes and reads both spread over the banks.  Each store then
+// writes 256 contiguous bytes of each of 4 rows, where the accumulator layout gives 16 bytes of each of
+// 32 rows.  One v_permlane32_swap per dword gives every lane 32 contiguous bytes of its row for the stage
+// writes.  dst(r) is row r's destination, nullptr for a row not stored.  Every lane of the wave takes
+// part; the caller has made the stage memory free for the whole workgroup.
+constexpr int kStageRowB = 256 + 16;
+template <int D, typename Dst>
+__device__ __forceinline__ void store_rows_staged(const f32x16* acc, float f, int ex, char* stage, int lane,
+                                                  Dst dst) {
+    constexpr int kNM = Geo<D>::NM;
+    const int n = lane & 31, hh = lane >> 5;
+    const int c = lane & 15, r0 = lane >> 4;
+#pragma unroll
+    for (int p = 0; p < kNM / 2; ++p) {   // d values 64p .. 64p + 63
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                // lane half 0 gets its own then its partner's 4 values of g4 = 2j, half 1 its partner's
+                // then its own of g4 = 2j + 1: d = 32 (2p + m) + 16j + 8hh .. + 7 either way
+                const f32x16& x = acc[2 * p + m];
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ldexpf(f * x[8 * j + k], ex)),
+                                                                     __float_as_uint(ldexpf(f * x[8 * j + 4 + k], ex)),
+                                                                     false, false);
+                    lo[k] = sw[0];
+                    hi[k] = sw[1];
+                }
+                char* sp = stage + n * kStageRowB + 128 * m + 64 * j + 32 * hh;
+                *reinterpret_cast<uint4*>(sp) = uint4{lo[0], lo[1], lo[2], lo[3]};
+                *reinterpret_cast<uint4*>(sp + 16) = uint4{hi[0], hi[1], hi[2], hi[3]};
+            }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the stage writes done
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 4 * i + r0;
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + r * kStageRowB + 16 * c);
+            float* d = dst(r);
+            if (d) *reinterpret_cast<uint4*>(d + 64 * p + 4 * c) = v;
+            __builtin_amdgcn_sched_barrier(0);   // one read, one store: no stage registers held
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the stage reads done before it is written again
+    }
+}
+
 // Key pairs (128 keys) that hold sink blocks when the pattern is block-sparse and query heads are grouped:
 // every query sees them, so they are split by query head (one unit per head, partial dK/dV summed by
 // bwd_group_sum_kernel) rather than taking a KV head's G heads in one unit, which would make them the
@@ -496,7 +546,9 @@ template <int D>
 __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs a) {
     using Gm = Geo<D>;
     constexpr int kNC = Gm::NC, kNM = Gm::NM, kTileB = Gm::TILE_B, kSlotB = Gm::SLOT_B;
-    __shared__ __attribute__((aligned(1024))) char smem[kKvSlots * kSlotB];
+    // the Q/dO tile slots, which also hold the epilogue's output stage
+    constexpr int kSmemB = kKvSlots * kSlotB > kKvWaves * 32 * kStageRowB ? kKvSlots * kSlotB : kKvWaves * 32 * kStageRowB;
+    __shared__ __attribute__((aligned(1024))) char smem[kSmemB];
     // P of one 32-query half, handed from the dV wave to the dK wave of each key group: two halves in
     // flight, [parity][key group][accumulator quad][lane] (lane-contiguous float4: conflict-free)
     __shared__ float4 pbuf[2][4][4][64];
@@ -683,20 +735,20 @@ __global__ void __launch_bounds__(64 * kKvWaves, 2) bwd_dkdv_kernel(BackwardArgs
                 if (pend) grad_product(L, pend_xt, 2, dk_pend, acc);   // the unit's last half
 
             // lane holds column key, rows d = 32mt + 8(r/4) + 4hh + r%4
-            if (key < seq) {
-                float* dst;
-                if (!partial) dst = (DK ? a.dk : a.dv) + (((int64_t)b * a.seq + key) * a.hkv + g) * D;
-                else dst = (DK ? a.dk_part : a.dv_part) + (((int64_t)b * a.part_keys + key) * a.hq + h0) * D;
+            __syncthreads();   // every wave is done with the tile slots: they hold the output stage now
+            {
                 // dK = scale 2^(eS + eQ) acc with eS = 23 + eDO + eV; dV = 2^(eDO - 14) acc
                 const float f = DK ? a.scale : 1.0f;
                 const int ex = DK ? 23 + eDO + eV + eQ : eDO - 14;
-#pragma unroll
-                for (int mt = 0; mt < kNM; ++mt)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4)
-                        *reinterpret_cast<float4*>(dst + 32 * mt + 8 * g4 + 4 * hh) =
-                            float4{ldexpf(f * acc[mt][4 * g4], ex), ldexpf(f * acc[mt][4 * g4 + 1], ex),
-                                   ldexpf(f * acc[mt][4 * g4 + 2], ex), ldexpf(f * acc[mt][4 * g4 + 3], ex)};
+                const int key0 = 128 * m + 32 * ks;
+                int ln = lane;
+                asm volatile("" : "+v"(ln));   // stage addresses formed here, not hoisted out of the unit loop
+                store_rows_staged<D>(acc, f, ex, smem + wave * 32 * kStageRowB, ln, [&](int r) -> float* {
+                    const int k = key0 + r;
+                    if (k >= seq) return nullptr;
+                    if (!partial) return (DK ? a.dk : a.dv) + (((int64_t)b * a.seq + k) * a.hkv + g) * D;
+                    return (DK ? a.dk_part : a.dv_part) + (((int64_t)b * a.part_keys + k) * a.hq + h0) * D;
+                });
             }
         };
         if (is_dk) role_body(BoolTag<true>{});
@@ -716,7 +768,9 @@ template <int D>
 __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
     using Gm = Geo<D>;
     constexpr int kNC = Gm::NC, kNM = Gm::NM, kTileB = Gm::TILE_B;
-    __shared__ __attribute__((aligned(1024))) char smem[kSlots * 2 * kTileB];
+    // the K/V tile slots, which also hold the epilogue's output stage
+    constexpr int kSmemB = kSlots * 2 * kTileB > 4 * 32 * kStageRowB ? kSlots * 2 * kTileB : 4 * 32 * kStageRowB;
+    __shared__ __attribute__((aligned(1024))) char smem[kSmemB];
     __shared__ int qcell[2];
     Lanes<D> L;
     L.init(threadIdx.x & 63);
@@ -842,16 +896,16 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BackwardArgs a) {
         }
 
         // lane holds column query, rows d = 32mt + 8(r/4) + 4hh + r%4
-        if (qpos < seq) {
-            float* dqp = a.dq + (((int64_t)b * a.seq + qpos) * a.hq + h) * D;
+        __syncthreads();   // every wave is done with the K/V slots: they hold the output stage now
+        {
             const int ex = 23 + eDO + eV + eK;   // dQ = scale 2^(eS + eK) acc
-#pragma unroll
-            for (int mt = 0; mt < kNM; ++mt)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4)
-                    *reinterpret_cast<float4*>(dqp + 32 * mt + 8 * g4 + 4 * hh) =
-                        float4{ldexpf(a.scale * dq[mt][4 * g4], ex), ldexpf(a.scale * dq[mt][4 * g4 + 1], ex),
-                               ldexpf(a.scale * dq[mt][4 * g4 + 2], ex), ldexpf(a.scale * dq[mt][4 * g4 + 3], ex)};
+            const int q0 = 128 * tp + 32 * wave;
+            int ln = lane;
+            asm volatile("" : "+v"(ln));   // stage addresses formed here, not hoisted out of the unit loop
+            store_rows_staged<D>(dq, a.scale, ex, smem + wave * 32 * kStageRowB, ln, [&](int r) -> float* {
+                const int q = q0 + r;
+                return q < seq ? a.dq + (((int64_t)b * a.seq + q) * a.hq + h) * D : nullptr;
+            });
         }
         __syncthreads();
         u = queue.next();
