@@ -32,7 +32,9 @@
 //   bwd_group_sum_kernel  block-sparse grouped-query attention: adds the per-query-head dK/dV of the
 //                         sink keys, in head order, into dK/dV.
 // Computing dQ apart from dK/dV rebuilds S and dP once more (7 matrix products instead of 5) but
-// needs no atomics: every gradient element is written once, summed in a fixed order.
+// needs no atomics: every gradient element is written once, summed in a fixed order.  Both kernels
+// write their fp32 gradient rows through a per-wave LDS stage (in their tile slots, after a barrier),
+// 256 contiguous bytes of 4 rows per store.
 //
 // Precision.  Every product runs on v_mfma_f32_32x32x16_f16 with fp32 accumulation.  The bf16 inputs
 // convert to fp16 exactly once scaled into fp16's range (a bf16 value has 8 significant bits, fp16

@@ -50,6 +50,9 @@
 //     FlashAttention-4 section describes the m_new <= m_old special case of this.
 //   * P enters P.V rounded to bf16; the row sum is accumulated in fp32 from the
 //     unrounded probabilities.
+//   * epilogue: bf16 outputs pass through a per-wave LDS stage placed after the K/V
+//     slots and leave as 16-byte stores of whole rows, 4 rows per instruction (the
+//     accumulator layout alone would put 8 bytes into each of 32 rows per store).
 //   * workgroup order: kv-head groups are kept on one XCD (blockIdx % 8 picks the
 //     XCD) so the query heads sharing K/V hit the same L2, and query tiles are
 //     issued longest-first for causal masks.
