@@ -168,6 +168,26 @@ def test_gqa_matches_repeated_kv(fa):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("B,S,Hq,Hkv,d,mode", [
+    (1, 4000, 32, 8, 128, 0),   # persistent schedule (512 units), ragged last tile
+    (1, 4000, 32, 8, 128, 1),
+    (2, 1337, 6, 3, 64, 0),     # odd query-head group: two row tiles of one head per workgroup
+    (1, 777, 4, 4, 64, 1),
+])
+def test_bf16_output_is_rounded_f32_output(fa, B, S, Hq, Hkv, d, mode):
+    """bf16 outputs leave through a per-wave LDS stage as whole rows; fp32 outputs are written straight
+    from the accumulator layout.  Both come from the same fp32 values, so the bf16 output must equal the
+    fp32 output rounded to bf16 (round to nearest even) element for element, and the LSE must be equal:
+    an element the stage put in the wrong row or column fails."""
+    say("bf16 out == rounded fp32 out", B, S, Hq, Hkv, d, "mode", mode)
+    _, (qd, kd, vd) = bf16_tensors(B, S, Hq, Hkv, d, seed=34 + S)
+    o32, l32 = _run_prefill(fa, qd, kd, vd, torch.float32, mode, sink=128, window=512)
+    o16, l16 = _run_prefill(fa, qd, kd, vd, torch.bfloat16, mode, sink=128, window=512)
+    assert torch.isfinite(o32).all()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(l16, l32)
+
+
 # ------------------------------------------------------------- full-size layers
 def _wave_rows(B, Hq, S, stride, seed):
     """(b, h, i) rows: for every batch and head, one seeded row in each `stride`-row segment (so every
