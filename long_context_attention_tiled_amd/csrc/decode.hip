@@ -268,21 +268,50 @@ __global__ __launch_bounds__(D / 4) void decode_append_kernel(DecodeArgs a) {
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
 }
 
+// LSE combine of one (batch, query head) row over its splits.  The splits are read in batches of 8
+// independent loads and summed in ascending split order: a loop of single loads would wait one memory
+// round trip per split (32 of them for a full-cache decode).
+constexpr int kCombineBatch = 8;
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     const int64_t row = blockIdx.x;  // b * hq + h
     const float* pl = a.part_lse + row * a.n_split;
+    const int ns = a.n_split;
+    auto weight = [](float l, float mx) { return l == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((l - mx) * kLog2e); };
     float mx = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s) mx = fmaxf(mx, pl[s]);
+    int s = 0;
+    for (; s + kCombineBatch <= ns; s += kCombineBatch) {
+        float x[kCombineBatch];
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) x[i] = pl[s + i];
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) mx = fmaxf(mx, x[i]);
+    }
+    for (; s < ns; ++s) mx = fmaxf(mx, pl[s]);
     float wsum = 0.0f;
-    for (int s = 0; s < a.n_split; ++s) wsum += pl[s] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((pl[s] - mx) * kLog2e);
+    for (s = 0; s + kCombineBatch <= ns; s += kCombineBatch) {
+        float x[kCombineBatch];
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) x[i] = pl[s + i];
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) wsum += weight(x[i], mx);
+    }
+    for (; s < ns; ++s) wsum += weight(pl[s], mx);
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        const float* po = a.part_o + row * a.n_split * D + d;
         float acc = 0.0f;
-        for (int s = 0; s < a.n_split; ++s) {
-            const float w = pl[s] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((pl[s] - mx) * kLog2e);
-            acc = fmaf(w, a.part_o[(row * a.n_split + s) * D + d], acc);
+        for (s = 0; s + kCombineBatch <= ns; s += kCombineBatch) {
+            float x[kCombineBatch], o[kCombineBatch];
+#pragma unroll
+            for (int i = 0; i < kCombineBatch; ++i) {
+                x[i] = pl[s + i];
+                o[i] = po[(int64_t)(s + i) * D];
+            }
+#pragma unroll
+            for (int i = 0; i < kCombineBatch; ++i) acc = fmaf(weight(x[i], mx), o[i], acc);
         }
+        for (; s < ns; ++s) acc = fmaf(weight(pl[s], mx), po[(int64_t)s * D], acc);
         acc *= inv;
         if constexpr (OUT_F32)
             reinterpret_cast<float*>(a.o)[row * D + d] = acc;
