@@ -197,7 +197,7 @@ struct DecodePlan {
 };
 
 constexpr int kDecodeTargetGroups = 2048;  // workgroups the automatic split count aims for
-constexpr int64_t kDecodeMinSplit = 256;   // keys per split at least
+constexpr int64_t kDecodeMinSplit = 192;   // keys per split at least (12 splits for a sink + window row)
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
